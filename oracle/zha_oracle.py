@@ -1,0 +1,347 @@
+"""CPU oracle for the Zyphra Hierarchical Attention (ZHA) decode path.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything in ``oracle/``.
+The product path (the HIP library and its Python binding) never touches it and
+shares no code with it.
+
+Plain, slow, obviously correct NumPy. Arithmetic is fp64 unless stated. Inputs
+are fp32 arrays (bf16 caches are widened exactly before they get here).
+
+Sources (cited by title and section; formulas are restated, not quoted):
+
+* [SAHTI] "Subquadratic Attention with a Hierarchical Tree-Structured Indexer"
+  (summary page of the technical report):
+    - §Key Insight, eq. (1): top-p decomposition of attention.
+    - §Tree Construction: chunk log-mass F_C, the reference-query summary
+      k_hat_r = Attn(q_hat_r, K_C, K_C), recursion over children.
+    - §Routing: the per-level cut m_l(q), the index set I(q), o(q).
+* [ZHA-END] "Zyphra Hierarchical Attention: The End of Quadratic Attention?":
+    - §How the tree is built and searched: contiguous chunks, recursive
+      grouping, full KV kept at the leaves, top-p per level, token 0 kept as a
+      sink.
+    - §A query's path through the tree: level spans (4096/1024/.../4 for C4-L6).
+
+Readings where the pages leave a step open (each restated where used):
+
+* R-1 summary: a node's summary is the softmax(r_l . c / sqrt(d))-weighted mean
+  of its children c (raw keys at level 1, child summaries above), one reference
+  query r_l per (level, kv head); no tangent offset enters the score.
+* R-2 score: s_i = q . x_i / sqrt(d); the cut runs on scores rounded to fp32
+  (the precision fixed for scoring), masses exp(s - max) are fp64.
+* R-3 cut: order by (score desc, node index asc); keep the smallest prefix whose
+  cumulative mass is >= p times the candidates' total; p >= 1 keeps all.
+* R-4 geometry: only complete nodes exist (node i of level l covers tokens
+  [i b^l, (i+1) b^l) and exists once all of them are present). Complete nodes
+  whose parent is not complete ("orphans") enter as candidates at their own
+  level; at the top level every complete node is a candidate.
+* R-5 current chunk: C_cur = [b floor((N-1)/b), N) for a query that sees N
+  tokens (its own token included); token 0 is always attended; I(q) is a set.
+* R-6 causal rows: a query at position t sees N = t + 1 tokens and only nodes
+  complete within them.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+F64 = np.float64
+F32 = np.float32
+
+
+# ----------------------------------------------------------------------------
+# Geometry [ZHA-END §How the tree is built and searched; SAHTI §Tree Construction]
+# ----------------------------------------------------------------------------
+def node_span(b: int, level: int) -> int:
+    """Tokens covered by one node of ``level`` (level 1 = leaf chunk of b keys)."""
+    return b ** level
+
+
+def complete_nodes(n_tokens: int, b: int, n_levels: int) -> List[int]:
+    """[n_1, ..., n_L]: complete nodes per level among the first ``n_tokens`` tokens (R-4)."""
+    return [n_tokens // (b ** l) for l in range(1, n_levels + 1)]
+
+
+# ----------------------------------------------------------------------------
+# Tree build [SAHTI §Tree Construction: k_hat_r; recursion over children]
+# ----------------------------------------------------------------------------
+def pool_children(children: np.ndarray, r: np.ndarray, b: int, scale: float) -> np.ndarray:
+    """Summaries of consecutive groups of ``b`` rows of ``children`` (R-1).
+
+    For each group C: weights w = softmax(scale * C r) and summary sum_j w_j C_j,
+    i.e. single-query attention of r over C with C as both keys and values.
+    Returned in fp32, the storage precision of summaries.
+    """
+    X = np.asarray(children, dtype=F64)
+    m = X.shape[0] // b
+    X = X[: m * b].reshape(m, b, X.shape[-1])
+    z = scale * (X @ np.asarray(r, dtype=F64))           # (m, b)
+    z = z - z.max(axis=1, keepdims=True)
+    w = np.exp(z)
+    w = w / w.sum(axis=1, keepdims=True)
+    s = np.einsum("mj,mjd->md", w, X)
+    return s.astype(F32)
+
+
+def build_tree(K: np.ndarray, R: np.ndarray, b: int, scale: Optional[float] = None) -> List[np.ndarray]:
+    """All levels for one (sequence, kv head).
+
+    K: (N, d) keys of the visible tokens. R: (L, d) reference queries of this kv
+    head. Returns [X_1, ..., X_L] with X_l of shape (floor(N / b^l), d), fp32.
+    """
+    d = K.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    levels = []
+    X = np.asarray(K, dtype=F64)
+    for l in range(R.shape[0]):
+        X = pool_children(X, R[l], b, scale)
+        levels.append(X)
+    return levels
+
+
+def build_tree_incremental(K: np.ndarray, R: np.ndarray, b: int, scale: Optional[float] = None) -> List[np.ndarray]:
+    """Same tree, grown one appended token at a time [ZHA-END §A query's path: built on the fly].
+
+    After token t arrives (N = t + 1 tokens), every node that N completes is
+    summarised once from its children, lowest level first; nothing is ever
+    rewritten.
+    """
+    d = K.shape[-1]
+    L = R.shape[0]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    levels: List[List[np.ndarray]] = [[] for _ in range(L)]
+    for t in range(K.shape[0]):
+        n = t + 1
+        for l in range(1, L + 1):
+            span = b ** l
+            if n % span:
+                break
+            i = n // span - 1
+            if l == 1:
+                ch = np.asarray(K[i * b:(i + 1) * b], dtype=F64)
+            else:
+                ch = np.stack(levels[l - 2][i * b:(i + 1) * b]).astype(F64)
+            levels[l - 1].append(pool_children(ch, R[l - 1], b, scale)[0])
+    return [np.stack(v) if v else np.zeros((0, d), F32) for v in levels]
+
+
+# ----------------------------------------------------------------------------
+# Top-p cut [SAHTI §Routing, m_l(q); R-3]
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class CutResult:
+    ids: np.ndarray          # candidate node ids, as enumerated
+    scores: np.ndarray       # decision scores (fp32 values held in fp64)
+    scores64: np.ndarray     # exact fp64 scores (ties are judged on these)
+    masses: np.ndarray       # normalised masses, fp64, aligned with ids
+    order: np.ndarray        # positions into ids in (score desc, id asc) order
+    prefix: np.ndarray       # prefix[k] = mass of the first k in order (prefix[0] = 0)
+    m: int                   # number kept
+    selected: np.ndarray     # kept ids, ascending
+
+
+def topp_cut(ids: np.ndarray, scores: np.ndarray, p: float, scores64: Optional[np.ndarray] = None) -> CutResult:
+    """Smallest (score desc, id asc)-prefix holding at least fraction p of the mass."""
+    ids = np.asarray(ids, dtype=np.int64)
+    s = np.asarray(scores, dtype=F64)
+    s64 = s if scores64 is None else np.asarray(scores64, dtype=F64)
+    n = len(ids)
+    if n == 0:
+        z = np.zeros(0)
+        return CutResult(ids, s, s64, z, np.zeros(0, np.int64), np.zeros(1), 0, ids.copy())
+    order = np.lexsort((ids, -s))
+    e = np.exp(s - s.max())
+    E = e.sum()
+    masses = e / E
+    c = np.cumsum(e[order])
+    prefix = np.concatenate([[0.0], np.cumsum(masses[order])])
+    if p >= 1.0:
+        m = n
+    else:
+        hit = np.nonzero(c >= p * E)[0]
+        m = int(hit[0]) + 1 if len(hit) else n
+    sel = np.sort(ids[order[:m]])
+    return CutResult(ids, s, s64, masses, order, prefix, m, sel)
+
+
+def cut_exemptions(cut: CutResult, p: float, margin: float = 1e-5) -> np.ndarray:
+    """Ids whose membership may legitimately differ from this cut at precision ``margin``.
+
+    A candidate at sorted rank k is exempt when (i) the mass before it is within
+    ``margin`` of p (its inclusion hinges on less than ``margin`` of mass), or
+    (ii) a candidate on the other side of the cut has a different exact score and
+    a mass within ``margin`` of its own (the two could swap places). Exact ties
+    are never exempt: the index rule decides them.
+    """
+    n = len(cut.ids)
+    if n == 0 or p >= 1.0:
+        return np.zeros(0, np.int64)
+    ex = set()
+    for k in range(n):
+        if abs(cut.prefix[k] - p) < margin:
+            ex.add(int(cut.ids[cut.order[k]]))
+    inside = cut.order[: cut.m]
+    outside = cut.order[cut.m:]
+    if len(inside) and len(outside):
+        wi, wo = cut.masses[inside], cut.masses[outside]
+        si, so = cut.scores64[inside], cut.scores64[outside]
+        # only the candidates nearest the boundary can be within margin of the other side
+        lo_in = wi.min()
+        hi_out = wo.max()
+        cand_in = inside[wi < hi_out + margin]
+        cand_out = outside[wo > lo_in - margin]
+        for x in cand_in:
+            close = np.abs(cut.masses[cand_out] - cut.masses[x]) < margin
+            diff = cut.scores64[cand_out] != cut.scores64[x]
+            if np.any(close & diff):
+                ex.add(int(cut.ids[x]))
+                for y in cand_out[close & diff]:
+                    ex.add(int(cut.ids[y]))
+    return np.array(sorted(ex), dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------
+# Routing [SAHTI §Routing; ZHA-END §How the tree is built and searched; R-4]
+# ----------------------------------------------------------------------------
+def level_candidates(level: int, parents: Optional[np.ndarray], n_visible: int, b: int, n_levels: int) -> np.ndarray:
+    """Candidates at ``level``: children of the kept parents, then the level's orphans.
+
+    ``parents`` are kept ids at level + 1 (ignored at the top level). Orphans are
+    the complete nodes [b * nc_{l+1}, nc_l) whose parent is not complete; at the
+    top level nc_{L+1} = 0 so every complete node is a candidate.
+    """
+    nc = complete_nodes(n_visible, b, n_levels) + [0]
+    out = []
+    if level < n_levels and parents is not None:
+        for pnode in np.sort(np.asarray(parents, dtype=np.int64)):
+            out.append(np.arange(pnode * b, pnode * b + b, dtype=np.int64))
+    lo = b * nc[level] if level < n_levels else 0
+    out.append(np.arange(lo, nc[level - 1], dtype=np.int64))
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+def score_nodes(q: np.ndarray, X: np.ndarray, ids: np.ndarray, scale: float):
+    """(fp32-rounded scores, exact fp64 scores) of nodes ``ids`` of one level (R-2)."""
+    s64 = scale * (np.asarray(X, dtype=F64)[ids] @ np.asarray(q, dtype=F64))
+    return s64.astype(F32).astype(F64), s64
+
+
+@dataclasses.dataclass
+class RouteResult:
+    levels: List[CutResult]          # levels[l - 1] is level l
+    selected: List[np.ndarray]       # selected[l - 1]: kept ids at level l (ascending)
+
+
+def route_level(q, X_level, level, parents, n_visible, b, n_levels, p, scale, score_dtype=F32) -> CutResult:
+    ids = level_candidates(level, parents, n_visible, b, n_levels)
+    if len(ids) == 0:
+        return topp_cut(ids, np.zeros(0), p)
+    s, s64 = score_nodes(q, X_level, ids, scale)
+    if score_dtype == F64:
+        s = s64
+    return topp_cut(ids, s, p, s64)
+
+
+def route(q: np.ndarray, tree: Sequence[np.ndarray], n_visible: int, b: int, p: float,
+          scale: Optional[float] = None, score_dtype=F32) -> RouteResult:
+    """Top-down routing of one query through one (sequence, kv head) tree."""
+    L = len(tree)
+    scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+    cuts: List[Optional[CutResult]] = [None] * L
+    parents = None
+    for level in range(L, 0, -1):
+        c = route_level(q, tree[level - 1], level, parents, n_visible, b, L, p, scale, score_dtype)
+        cuts[level - 1] = c
+        parents = c.selected
+    return RouteResult(cuts, [c.selected for c in cuts])
+
+
+def index_set(leaf_ids: np.ndarray, n_visible: int, b: int) -> np.ndarray:
+    """I(q) = {0} U (union of kept leaf chunks) U C_cur, ascending token ids (R-5)."""
+    if n_visible <= 0:
+        return np.zeros(0, np.int64)
+    toks = np.zeros(n_visible, dtype=bool)
+    toks[0] = True
+    for i in np.asarray(leaf_ids, dtype=np.int64):
+        toks[i * b:(i + 1) * b] = True
+    toks[b * ((n_visible - 1) // b):n_visible] = True
+    return np.nonzero(toks)[0]
+
+
+# ----------------------------------------------------------------------------
+# Attention [SAHTI §Routing, o(q); §The Quadratic Bottleneck (dense decode)]
+# ----------------------------------------------------------------------------
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray, scale: Optional[float] = None):
+    """Exact softmax attention of q over tokens ``idx``: returns (o (d,), lse)."""
+    scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+    idx = np.asarray(idx, dtype=np.int64)
+    k = np.asarray(K, dtype=F64)[idx]
+    v = np.asarray(V, dtype=F64)[idx]
+    z = scale * (k @ np.asarray(q, dtype=F64))
+    mx = z.max()
+    e = np.exp(z - mx)
+    l = e.sum()
+    return (e @ v) / l, mx + math.log(l)
+
+
+def dense_attend(q, K, V, n_visible, scale=None):
+    return attend(q, K, V, np.arange(n_visible), scale)
+
+
+# ----------------------------------------------------------------------------
+# Diagnostics (not parity) [SAHTI §Key Insight, eq. (1)]
+# ----------------------------------------------------------------------------
+def key_probs(q, K, n_visible, scale=None) -> np.ndarray:
+    scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+    z = scale * (np.asarray(K[:n_visible], dtype=F64) @ np.asarray(q, dtype=F64))
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+def topp_key_set(q, K, n_visible, p, scale=None) -> np.ndarray:
+    """Exact key-level top-p set K_p: smallest set of keys with probability >= p."""
+    pr = key_probs(q, K, n_visible, scale)
+    order = np.lexsort((np.arange(n_visible), -pr))
+    c = np.cumsum(pr[order])
+    m = int(np.nonzero(c >= p)[0][0]) + 1 if p < 1 else n_visible
+    return np.sort(order[:m])
+
+
+def realised_mass(q, K, n_visible, idx, scale=None) -> float:
+    return float(key_probs(q, K, n_visible, scale)[np.asarray(idx, dtype=np.int64)].sum())
+
+
+# ----------------------------------------------------------------------------
+# Whole-batch helpers (GQA: query head h uses kv head h // (H_q / H_kv))
+# ----------------------------------------------------------------------------
+def build_all(K: np.ndarray, R: np.ndarray, seq_lens: Sequence[int], b: int, scale=None):
+    """trees[s][h] for K [B, H_kv, N_cap, d] (fp32 values) and R [L, H_kv, d]."""
+    B, H = K.shape[:2]
+    return [[build_tree(K[s, h, :int(seq_lens[s])], R[:, h], b, scale) for h in range(H)] for s in range(B)]
+
+
+def decode_all(q: np.ndarray, q_pos: np.ndarray, K: np.ndarray, V: np.ndarray, trees, b: int, p: float,
+               scale=None, dense: bool = False):
+    """Route and attend every (sequence, row, query head): returns dict of arrays/lists."""
+    B, T, Hq, d = q.shape
+    Hkv = K.shape[1]
+    g = Hq // Hkv
+    out = np.zeros((B, T, Hq, d))
+    lse = np.zeros((B, T, Hq))
+    routes = [[[None] * Hq for _ in range(T)] for _ in range(B)]
+    for s in range(B):
+        for t in range(T):
+            n = int(q_pos[s, t]) + 1
+            for h in range(Hq):
+                kv = h // g
+                if dense:
+                    idx = np.arange(n)
+                else:
+                    r = route(q[s, t, h], trees[s][kv], n, b, p, scale)
+                    routes[s][t][h] = r
+                    idx = index_set(r.selected[0], n, b)
+                out[s, t, h], lse[s, t, h] = attend(q[s, t, h], K[s, kv], V[s, kv], idx, scale)
+    return {"out": out, "lse": lse, "routes": routes}

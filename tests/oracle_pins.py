@@ -1,0 +1,407 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+Every pin is a plain function of the oracle module so that the same checks can
+be run against deliberately broken copies of the oracle (see
+``test_oracle_mutants.py``): each plausible mistake must trip at least one pin.
+
+What pins what:
+* geometry       - spans and node counts printed on the pages (golden file).
+* summaries      - torch's scaled_dot_product_attention in fp64 with the chunk as
+                   keys and values (the pages define the summary as exactly that
+                   attention); closed forms (zero reference query -> mean,
+                   identical children -> the child, huge reference query -> the
+                   arg-max child); permutation invariance; append order.
+* cut            - hand-worked cases (golden file), brute force over all subsets
+                   for small candidate sets, the uniform-mass closed form ceil(p n).
+* routing        - hand-worked trees (golden file); an independent mask-based
+                   formulation; causal prefixes.
+* attention      - torch SDPA with a boolean mask; p = 1 equals dense; the
+                   top-p decomposition identity; split-and-merge by LSE.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+from scipy.special import logsumexp
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _sdpa64(q, k, v):
+    """torch SDPA in fp64, single query: q (d,), k/v (n, d) -> (d,)."""
+    qt = torch.from_numpy(np.asarray(q, np.float64))[None, None, None, :]
+    kt = torch.from_numpy(np.asarray(k, np.float64))[None, None]
+    vt = torch.from_numpy(np.asarray(v, np.float64))[None, None]
+    return F.scaled_dot_product_attention(qt, kt, vt)[0, 0, 0].numpy()
+
+
+def _sdpa64_masked(q, k, v, mask):
+    qt = torch.from_numpy(np.asarray(q, np.float64))[None, None, None, :]
+    kt = torch.from_numpy(np.asarray(k, np.float64))[None, None]
+    vt = torch.from_numpy(np.asarray(v, np.float64))[None, None]
+    mt = torch.from_numpy(np.asarray(mask, bool))[None, None, None, :]
+    return F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mt)[0, 0, 0].numpy()
+
+
+def _ranges(rs):
+    out = []
+    for a, b in rs:
+        out.extend(range(a, b))
+    return np.array(out, dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------
+# geometry
+# ----------------------------------------------------------------------------
+def pin_geometry(orc):
+    g = _load("geometry_pages.json")
+    for c in g["cases"]:
+        if "spans_top_down" in c:
+            spans = [orc.node_span(c["b"], l) for l in range(c["levels"], 0, -1)]
+            assert spans == c["spans_top_down"], (spans, c)
+        elif "pairs" in c:
+            for b, L in c["pairs"]:
+                assert orc.node_span(b, L) == c["span"]
+        elif "n_top" in c:
+            assert orc.complete_nodes(c["n_tokens"], c["b"], c["levels"])[-1] == c["n_top"]
+        else:
+            assert orc.node_span(c["b"], c["levels"]) == c["span"]
+    # complete nodes only: 4095 tokens leave the last leaf of b=16 and the top node incomplete
+    assert orc.complete_nodes(4095, 16, 3) == [255, 15, 0]
+    assert orc.complete_nodes(4096, 16, 3) == [256, 16, 1]
+
+
+# ----------------------------------------------------------------------------
+# summaries
+# ----------------------------------------------------------------------------
+def pin_summary_sdpa(orc):
+    rng = np.random.default_rng(11)
+    for b, d, L, n in [(4, 8, 3, 200), (16, 64, 2, 600), (3, 5, 2, 40)]:
+        K = rng.standard_normal((n, d)).astype(np.float32)
+        R = rng.standard_normal((L, d)).astype(np.float32)
+        tree = orc.build_tree(K, R, b)
+        X = K.astype(np.float64)
+        for l in range(L):
+            m = X.shape[0] // b
+            assert tree[l].shape == (m, d), (tree[l].shape, m, d)
+            assert tree[l].dtype == np.float32
+            ref = np.stack([_sdpa64(R[l], X[i * b:(i + 1) * b], X[i * b:(i + 1) * b]) for i in range(m)]) \
+                if m else np.zeros((0, d))
+            err = np.abs(tree[l].astype(np.float64) - ref).max() if m else 0.0
+            tol = 4 * np.finfo(np.float32).eps * max(1.0, np.abs(ref).max() if m else 1.0)
+            assert err <= tol, (b, d, l, err, tol)
+            X = tree[l].astype(np.float64)      # the next level is built from stored (fp32) summaries
+
+
+def pin_summary_closed_forms(orc):
+    rng = np.random.default_rng(12)
+    b, d = 8, 16
+    C = rng.standard_normal((b, d)).astype(np.float32)
+    # zero reference query: plain mean
+    s0 = orc.pool_children(C, np.zeros(d, np.float32), b, 1 / math.sqrt(d))[0]
+    assert np.abs(s0 - C.astype(np.float64).mean(0)).max() < 1e-6
+    # identical children: the child itself
+    same = np.repeat(C[:1], b, axis=0)
+    s1 = orc.pool_children(same, rng.standard_normal(d).astype(np.float32), b, 1 / math.sqrt(d))[0]
+    assert np.array_equal(s1, C[0])
+    # a huge reference query along e_0 picks the child with the largest e_0 component
+    r = np.zeros(d, np.float32)
+    r[0] = 1e5
+    s2 = orc.pool_children(C, r, b, 1 / math.sqrt(d))[0]
+    assert np.abs(s2 - C[np.argmax(C[:, 0])]).max() < 1e-6
+    # and the smallest one for the opposite direction (sign of the pooling logits)
+    s3 = orc.pool_children(C, -r, b, 1 / math.sqrt(d))[0]
+    assert np.abs(s3 - C[np.argmin(C[:, 0])]).max() < 1e-6
+    # permutation of the children does not change the summary
+    rr = rng.standard_normal(d).astype(np.float32)
+    perm = rng.permutation(b)
+    a1 = orc.pool_children(C, rr, b, 1 / math.sqrt(d))[0]
+    a2 = orc.pool_children(C[perm], rr, b, 1 / math.sqrt(d))[0]
+    assert np.abs(a1.astype(np.float64) - a2).max() < 1e-6
+    # one summary per group of b consecutive rows; a partial group makes no summary
+    K = rng.standard_normal((3 * b + 5, d)).astype(np.float32)
+    out = orc.pool_children(K, rr, b, 1 / math.sqrt(d))
+    assert out.shape == (3, d)
+    assert np.abs(out[1] - orc.pool_children(K[b:2 * b], rr, b, 1 / math.sqrt(d))[0]).max() == 0
+
+
+def pin_incremental_equals_batch(orc):
+    rng = np.random.default_rng(13)
+    for b, L, n in [(4, 3, 150), (2, 5, 77), (8, 2, 130)]:
+        K = rng.standard_normal((n, 8)).astype(np.float32)
+        R = rng.standard_normal((L, 8)).astype(np.float32)
+        t1 = orc.build_tree(K, R, b)
+        t2 = orc.build_tree_incremental(K, R, b)
+        for a, c in zip(t1, t2):
+            assert a.shape == c.shape and np.array_equal(a, c), (b, L, n)
+
+
+# ----------------------------------------------------------------------------
+# cut
+# ----------------------------------------------------------------------------
+def _parse_score(s):
+    return math.log(float(s[2:])) if s.startswith("ln") else float(s)
+
+
+def pin_cut_golden(orc):
+    for c in _load("cut_cases.json")["cases"]:
+        s = np.array([_parse_score(x) for x in c["scores"]])
+        r = orc.topp_cut(np.array(c["ids"]), s, c["p"])
+        assert list(r.selected) == c["kept"], (c, list(r.selected))
+
+
+def pin_cut_bruteforce(orc):
+    rng = np.random.default_rng(14)
+    checked = 0
+    for trial in range(400):
+        n = int(rng.integers(1, 10))
+        if trial % 3 == 0:
+            s = rng.integers(-2, 3, size=n).astype(np.float64) * 0.7     # many exact ties
+        else:
+            s = rng.standard_normal(n) * rng.choice([0.3, 1.0, 4.0])
+        ids = rng.permutation(50)[:n]
+        p = float(rng.choice([0.05, 0.3, 0.5, 0.77, 0.9, 0.95, 0.999]))
+        w = np.exp(s - s.max())
+        w = w / w.sum()
+        masses = {}
+        best = None
+        near = False
+        for k in range(1, n + 1):
+            for sub in itertools.combinations(range(n), k):
+                m = w[list(sub)].sum()
+                if abs(m - p) < 1e-9:
+                    near = True
+                if m >= p and best is None:
+                    best = k
+            if best is not None:
+                break
+        if near:
+            continue
+        r = orc.topp_cut(ids, s, p)
+        kept = set(int(i) for i in r.selected)
+        pos = {int(i): j for j, i in enumerate(ids)}
+        assert len(kept) == best, (s, p, kept, best)
+        assert w[[pos[i] for i in kept]].sum() >= p
+        out = [j for j in range(n) if int(ids[j]) not in kept]
+        inn = [pos[i] for i in kept]
+        if out:
+            lo_in = min(s[j] for j in inn)
+            hi_out = max(s[j] for j in out)
+            assert lo_in >= hi_out, (s, kept)
+            if lo_in == hi_out:       # a tie straddles the cut: lower ids must be inside
+                tie_in = max(int(ids[j]) for j in inn if s[j] == lo_in)
+                tie_out = min(int(ids[j]) for j in out if s[j] == hi_out)
+                assert tie_in < tie_out, (s, ids, kept)
+        checked += 1
+    assert checked > 300
+
+
+def pin_cut_uniform(orc):
+    for n in [1, 2, 3, 7, 16, 100, 240, 257]:
+        for p in [0.1, 0.33, 0.5, 0.91, 0.95, 0.999]:
+            if abs(p * n - round(p * n)) < 1e-6:
+                continue
+            r = orc.topp_cut(np.arange(n)[::-1].copy(), np.full(n, 0.25), p)
+            assert list(r.selected) == list(range(math.ceil(p * n))), (n, p, r.m)
+
+
+# ----------------------------------------------------------------------------
+# routing
+# ----------------------------------------------------------------------------
+def _golden_inputs(c):
+    b, L, N, d = c["b"], c["L"], c["N"], c["d"]
+    u = np.zeros(d, np.float32)
+    u[0] = 1.0
+    if c["keys"] == "identical":
+        rng = np.random.default_rng(15)
+        k0 = rng.standard_normal(d).astype(np.float32)
+        K = np.repeat(k0[None], N, axis=0)
+        R = rng.standard_normal((L, d)).astype(np.float32)
+        q = rng.standard_normal(d).astype(np.float32)
+    else:
+        K = np.zeros((N, d), np.float32)
+        for leaf, val in c["values"].items():
+            i = int(leaf)
+            K[i * b:(i + 1) * b] = np.float32(val) * u
+        R = np.zeros((L, d), np.float32)
+        q = (np.float32(c["qscale"] * math.sqrt(d)) * u).astype(np.float32)
+    return K, R, q
+
+
+def pin_route_golden(orc):
+    for c in _load("route_closed_forms.json")["cases"]:
+        K, R, q = _golden_inputs(c)
+        tree = orc.build_tree(K, R, c["b"])
+        r = orc.route(q, tree, c["N"], c["b"], c["p"])
+        for lvl, rs in c["kept"].items():
+            got = list(r.selected[int(lvl) - 1])
+            assert got == list(_ranges(rs)), (c["name"], lvl, got)
+        I = orc.index_set(r.selected[0], c["N"], c["b"])
+        assert list(I) == list(_ranges(c["I"])), (c["name"], list(I))
+
+
+def route_by_masks(q, tree, N, b, p, scale):
+    """Independent formulation: score every complete node, restrict by masks.
+
+    A node is allowed at level l if it is complete and either l is the top level,
+    or its parent is kept, or its parent is not complete.
+    """
+    L = len(tree)
+    nc = [N // b ** l for l in range(1, L + 1)]
+    kept = [None] * L
+    parent_kept = None
+    for level in range(L, 0, -1):
+        n = nc[level - 1]
+        allowed = []
+        for i in range(n):
+            par = i // b
+            if level == L or par >= nc[level] or par in parent_kept:
+                allowed.append(i)
+        s64 = scale * (tree[level - 1][:n].astype(np.float64) @ q.astype(np.float64)) if n else np.zeros(0)
+        s = s64.astype(np.float32).astype(np.float64)
+        if not allowed:
+            kept[level - 1] = []
+            parent_kept = set()
+            continue
+        pairs = sorted(allowed, key=lambda i: (-s[i], i))
+        mx = max(s[i] for i in allowed)
+        tot = sum(math.exp(s[i] - mx) for i in allowed)
+        acc, take = 0.0, []
+        for i in pairs:
+            if p < 1.0 and acc >= p * tot:
+                break
+            take.append(i)
+            acc += math.exp(s[i] - mx)
+        kept[level - 1] = sorted(take)
+        parent_kept = set(take)
+    return kept
+
+
+def pin_route_dense_mask(orc):
+    rng = np.random.default_rng(16)
+    for b, L, N, d, p in [(4, 3, 203, 8, 0.8), (3, 4, 250, 6, 0.9), (8, 2, 500, 16, 0.95), (2, 5, 61, 4, 0.7)]:
+        K = rng.standard_normal((N, d)).astype(np.float32)
+        R = rng.standard_normal((L, d)).astype(np.float32)
+        tree = orc.build_tree(K, R, b)
+        for _ in range(6):
+            q = (rng.standard_normal(d) * 2).astype(np.float32)
+            r = orc.route(q, tree, N, b, p)
+            want = route_by_masks(q, tree, N, b, p, 1 / math.sqrt(d))
+            for l in range(L):
+                assert list(r.selected[l]) == want[l], (b, L, N, l, list(r.selected[l]), want[l])
+
+
+def pin_causal_prefix(orc):
+    rng = np.random.default_rng(17)
+    b, L, N, d = 4, 3, 180, 8
+    K = rng.standard_normal((N, d)).astype(np.float32)
+    R = rng.standard_normal((L, d)).astype(np.float32)
+    full = orc.build_tree(K, R, b)
+    for t in [0, 3, 4, 15, 16, 63, 64, 65, 130, 179]:
+        q = rng.standard_normal(d).astype(np.float32) * 3
+        part = orc.build_tree(K[:t + 1], R, b)
+        a = orc.route(q, full, t + 1, b, 0.85)
+        c = orc.route(q, part, t + 1, b, 0.85)
+        for l in range(L):
+            assert list(a.selected[l]) == list(c.selected[l]), (t, l)
+
+
+# ----------------------------------------------------------------------------
+# attention
+# ----------------------------------------------------------------------------
+def pin_attend_sdpa(orc):
+    rng = np.random.default_rng(18)
+    for N, d in [(50, 8), (300, 64), (1, 16)]:
+        K = rng.standard_normal((N, d)).astype(np.float32)
+        V = rng.standard_normal((N, d)).astype(np.float32)
+        q = (rng.standard_normal(d) * 2).astype(np.float32)
+        idx = np.sort(rng.choice(N, size=max(1, N // 3), replace=False))
+        o, lse = orc.attend(q, K, V, idx)
+        mask = np.zeros(N, bool)
+        mask[idx] = True
+        ref = _sdpa64_masked(q, K, V, mask)
+        assert np.abs(o - ref).max() < 1e-12
+        z = (K[idx].astype(np.float64) @ q.astype(np.float64)) / math.sqrt(d)
+        assert abs(lse - logsumexp(z)) < 1e-12
+        od, _ = orc.dense_attend(q, K, V, N)
+        assert np.abs(od - _sdpa64(q, K, V)).max() < 1e-12
+
+
+def pin_p1_dense(orc):
+    rng = np.random.default_rng(19)
+    for b, L, N, d in [(16, 3, 4096, 16), (4, 3, 203, 8), (32, 2, 2000, 8)]:
+        K = (rng.standard_normal((N, d)) / math.sqrt(d)).astype(np.float32)
+        V = rng.standard_normal((N, d)).astype(np.float32)
+        R = rng.standard_normal((L, d)).astype(np.float32)
+        tree = orc.build_tree(K, R, b)
+        q = (rng.standard_normal(d) * 3).astype(np.float32)
+        r = orc.route(q, tree, N, b, 1.0)
+        I = orc.index_set(r.selected[0], N, b)
+        assert list(I) == list(range(N))
+        o, lse = orc.attend(q, K, V, I)
+        od, lsed = orc.dense_attend(q, K, V, N)
+        assert np.abs(o - od).max() / np.abs(od).max() <= 1e-6
+        assert abs(lse - lsed) <= 1e-6 * max(1.0, abs(lsed))
+
+
+def pin_eq1_identity(orc):
+    """Top-p decomposition: o_dense = P_S o_S + (1 - P_S) o_rest with P_S the mass of S."""
+    rng = np.random.default_rng(20)
+    b, L, N, d, p = 8, 2, 700, 16, 0.9
+    K = rng.standard_normal((N, d)).astype(np.float32)
+    V = rng.standard_normal((N, d)).astype(np.float32)
+    R = rng.standard_normal((L, d)).astype(np.float32)
+    tree = orc.build_tree(K, R, b)
+    for _ in range(4):
+        q = (rng.standard_normal(d) * 3).astype(np.float32)
+        od, _ = orc.dense_attend(q, K, V, N)
+        r = orc.route(q, tree, N, b, p)
+        for S in (orc.index_set(r.selected[0], N, b), orc.topp_key_set(q, K, N, p)):
+            rest = np.setdiff1d(np.arange(N), S)
+            P = orc.realised_mass(q, K, N, S)
+            oS, _ = orc.attend(q, K, V, S)
+            mix = P * oS
+            if len(rest):
+                oR, _ = orc.attend(q, K, V, rest)
+                mix = mix + (1 - P) * oR
+            assert np.abs(mix - od).max() <= 1e-6 * max(1.0, np.abs(od).max())
+        Kp = orc.topp_key_set(q, K, N, p)
+        assert orc.realised_mass(q, K, N, Kp) >= p
+        if len(Kp) > 1:   # minimal: dropping its smallest member falls below p
+            pr = orc.key_probs(q, K, N)
+            assert pr[Kp].sum() - pr[Kp].min() < p
+
+
+def pin_split_merge(orc):
+    rng = np.random.default_rng(21)
+    N, d = 400, 32
+    K = rng.standard_normal((N, d)).astype(np.float32)
+    V = rng.standard_normal((N, d)).astype(np.float32)
+    q = (rng.standard_normal(d) * 2).astype(np.float32)
+    I = np.sort(rng.choice(N, size=150, replace=False))
+    o, lse = orc.attend(q, K, V, I)
+    parts = np.array_split(I[rng.permutation(len(I))], 4)
+    os_, ls = zip(*[orc.attend(q, K, V, np.sort(pp)) for pp in parts])
+    M = logsumexp(ls)
+    merged = sum(math.exp(l - M) * x for l, x in zip(ls, os_))
+    assert np.abs(merged - o).max() < 1e-12
+    assert abs(M - lse) < 1e-12
+
+
+ALL_PINS = [
+    pin_geometry, pin_summary_sdpa, pin_summary_closed_forms, pin_incremental_equals_batch,
+    pin_cut_golden, pin_cut_bruteforce, pin_cut_uniform,
+    pin_route_golden, pin_route_dense_mask, pin_causal_prefix,
+    pin_attend_sdpa, pin_p1_dense, pin_eq1_identity, pin_split_merge,
+]
