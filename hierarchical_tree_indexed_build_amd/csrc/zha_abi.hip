@@ -1,0 +1,362 @@
+// zha_abi.hip - the extern "C" entry points of libzha: argument validation,
+// size and offset arithmetic, workspace layout, and kernel sequencing on the
+// caller's stream. Every host-detectable error is returned before any launch.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "zha_internal.h"
+
+namespace zha {
+namespace {
+
+thread_local std::string g_last_error;
+
+zha_status fail(zha_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+zha_status fail(zha_status code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+zha_status hip_fail(hipError_t e, const char* what) {
+    return fail(ZHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+zha_status make_geo(const zha_geom* in, Geo* g) {
+    if (!in) return fail(ZHA_ERR_NULL, "geom is NULL");
+    if (in->batch < 1 || in->n_kv_heads < 1 || in->n_q_heads < 1)
+        return fail(ZHA_ERR_SHAPE, "batch, n_q_heads and n_kv_heads must be >= 1");
+    if (in->n_q_heads % in->n_kv_heads)
+        return fail(ZHA_ERR_SHAPE, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", in->n_q_heads,
+                    in->n_kv_heads);
+    const int G = in->n_q_heads / in->n_kv_heads;
+    if (!is_pow2_in(G, 1, kMaxGroup))
+        return fail(ZHA_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4, 8 or 16 (got %d)", G);
+    if (in->head_dim != 64 && in->head_dim != 128)
+        return fail(ZHA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", in->head_dim);
+    if (!is_pow2_in(in->branching, 2, 64))
+        return fail(ZHA_ERR_UNSUPPORTED, "branching must be 2, 4, 8, 16, 32 or 64 (got %d)", in->branching);
+    if (in->n_levels < 1 || in->n_levels > ZHA_MAX_LEVELS)
+        return fail(ZHA_ERR_SHAPE, "n_levels must be in [1, %d] (got %d)", ZHA_MAX_LEVELS, in->n_levels);
+    if (in->capacity < 1 || in->capacity >= (int64_t(1) << 31))
+        return fail(ZHA_ERR_SHAPE, "capacity must be in [1, 2^31) (got %lld)", static_cast<long long>(in->capacity));
+    if (in->kv_dtype != ZHA_KV_BF16 && in->kv_dtype != ZHA_KV_F32)
+        return fail(ZHA_ERR_UNSUPPORTED, "kv_dtype must be ZHA_KV_BF16 or ZHA_KV_F32");
+    if (!(in->scale >= 0.f) || std::isinf(in->scale)) return fail(ZHA_ERR_SHAPE, "scale must be finite and >= 0");
+    g->B = in->batch;
+    g->Hq = in->n_q_heads;
+    g->Hkv = in->n_kv_heads;
+    g->G = G;
+    g->D = in->head_dim;
+    g->b = in->branching;
+    g->L = in->n_levels;
+    g->kv_dtype = in->kv_dtype;
+    g->cap = in->capacity;
+    g->scale = in->scale > 0.f ? in->scale : 1.0f / std::sqrt(static_cast<float>(in->head_dim));
+    int64_t span = 1;
+    int64_t soff = 0, loff = 0;
+    for (int l = 0; l < ZHA_MAX_LEVELS + 1; ++l) {
+        // spans beyond 2^62 are clamped: no node of such a level can be complete
+        span = (span > (int64_t(1) << 56)) ? span : span * g->b;
+        g->span[l] = span;
+        if (l < ZHA_MAX_LEVELS) {
+            g->nodes[l] = (l < g->L) ? g->cap / span : 0;
+            g->sum_off[l] = soff;
+            g->sel_off[l] = loff;
+            soff += static_cast<int64_t>(g->B) * g->Hkv * g->nodes[l] * g->D;
+            loff += g->nodes[l];
+        }
+    }
+    g->nodes_total = loff;
+    return ZHA_OK;
+}
+
+int splits_for(const Geo& g, int rows) {
+    const int pairs = rows * g.Hkv;
+    const int s = (2048 + pairs - 1) / pairs;
+    return s < 1 ? 1 : (s > kAttnSplitsMax ? kAttnSplitsMax : s);
+}
+
+WsLayout layout(const Geo& g, int rows) {
+    WsLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    const size_t R = static_cast<size_t>(rows);
+    L.status = take(256);
+    L.grp_ctr = take(R * g.Hkv * g.L * 4);
+    L.scores = take(R * g.Hq * g.nodes_total * 4);
+    L.kept = take(R * g.Hq * g.nodes_total * 4);
+    L.kept_cnt = take(R * g.Hq * g.L * 4);
+    int64_t bw = 0;
+    for (int l = 0; l < ZHA_MAX_LEVELS; ++l) {
+        L.bm_off[l] = static_cast<size_t>(bw);
+        bw += (g.nodes[l] + 31) / 32;
+    }
+    L.bm_words_total = bw;
+    L.bitmap = take(R * g.Hq * static_cast<size_t>(bw) * 4);
+    L.ulist = take(R * g.Hkv * g.nodes_total * 4);
+    L.ucnt = take(R * g.Hkv * g.L * 4);
+    L.abm_words = g.nodes[0] / 32 + 1;
+    L.abm = take(R * g.Hq * static_cast<size_t>(L.abm_words) * 4);
+    L.aitems = take(R * g.Hkv * static_cast<size_t>(g.nodes[0] + 2) * 8);
+    L.acnt = take(R * g.Hkv * 4);
+    L.splits = splits_for(g, rows);
+    L.partial = take(R * g.Hq * static_cast<size_t>(L.splits) * (g.D + 2) * 4);
+    L.total = off;
+    return L;
+}
+
+zha_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+    if (!ws) return fail(ZHA_ERR_NULL, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(ZHA_ERR_SHAPE, "workspace must be 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(ZHA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+    return ZHA_OK;
+}
+
+zha_status check_rows(const Geo& g, int32_t t, int* rows) {
+    if (t < 1) return fail(ZHA_ERR_SHAPE, "t (query rows per sequence) must be >= 1 (got %d)", t);
+    const int64_t r = static_cast<int64_t>(g.B) * t;
+    if (r > (int64_t(1) << 24)) return fail(ZHA_ERR_SHAPE, "too many query rows (%lld)", static_cast<long long>(r));
+    *rows = static_cast<int>(r);
+    return ZHA_OK;
+}
+
+}  // namespace
+}  // namespace zha
+
+using namespace zha;
+
+extern "C" {
+
+zha_status zha_query_sizes(const zha_geom* geom, int32_t max_t, zha_sizes* out) {
+    Geo g;
+    zha_status st = make_geo(geom, &g);
+    if (st) return st;
+    if (!out) return fail(ZHA_ERR_NULL, "out is NULL");
+    int rows;
+    if ((st = check_rows(g, max_t, &rows))) return st;
+    const WsLayout L = layout(g, rows);
+    *out = zha_sizes{};
+    out->summaries_bytes = static_cast<size_t>(g.sum_off[ZHA_MAX_LEVELS - 1] +
+                                               int64_t(g.B) * g.Hkv * g.nodes[ZHA_MAX_LEVELS - 1] * g.D) * 4;
+    out->workspace_bytes = L.total;
+    for (int l = 0; l < ZHA_MAX_LEVELS; ++l) {
+        out->level_nodes[l] = g.nodes[l];
+        out->level_offset[l] = g.sum_off[l];
+        out->level_sel_offset[l] = g.sel_off[l];
+    }
+    out->level_sel_bytes = static_cast<size_t>(rows) * g.Hq * g.nodes_total * 4;
+    out->max_rows = rows;
+    return ZHA_OK;
+}
+
+zha_status zha_build_tree(const zha_geom* geom, const void* K, const float* ref_q, const int32_t* seq_lens,
+                          float* summaries, void* ws, size_t ws_bytes, void* stream) {
+    Geo g;
+    zha_status st = make_geo(geom, &g);
+    if (st) return st;
+    if (!K || !ref_q || !seq_lens || !summaries) return fail(ZHA_ERR_NULL, "K, ref_q, seq_lens and summaries are required");
+    if ((st = check_ws(ws, ws_bytes, 256))) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int level = 1; level <= g.L; ++level) {
+        const hipError_t e = launch_build_level(g, level, K, ref_q, summaries, seq_lens, 0, 0, s);
+        if (e != hipSuccess) return hip_fail(e, "build level launch");
+    }
+    return ZHA_OK;
+}
+
+zha_status zha_append(const zha_geom* geom, void* K, void* V, const void* k_new, const void* v_new, int32_t t_new,
+                      int32_t* seq_lens, const float* ref_q, float* summaries, void* ws, size_t ws_bytes,
+                      void* stream) {
+    Geo g;
+    zha_status st = make_geo(geom, &g);
+    if (st) return st;
+    if (!K || !V || !k_new || !v_new || !seq_lens || !ref_q || !summaries)
+        return fail(ZHA_ERR_NULL, "K, V, k_new, v_new, seq_lens, ref_q and summaries are required");
+    if (t_new < 1 || t_new > g.cap) return fail(ZHA_ERR_SHAPE, "t_new must be in [1, capacity] (got %d)", t_new);
+    if ((st = check_ws(ws, ws_bytes, 256))) return st;
+    uint32_t* status = static_cast<uint32_t*>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (t_new <= 64) {
+        e = launch_append_fused(g, K, V, k_new, v_new, t_new, seq_lens, ref_q, summaries, status, s);
+        if (e != hipSuccess) return hip_fail(e, "append launch");
+        return ZHA_OK;
+    }
+    e = launch_append_rows(g, K, V, k_new, v_new, t_new, seq_lens, status, s);
+    if (e != hipSuccess) return hip_fail(e, "append rows launch");
+    for (int level = 1; level <= g.L; ++level) {
+        e = launch_build_level(g, level, K, ref_q, summaries, seq_lens, 1, t_new, s);
+        if (e != hipSuccess) return hip_fail(e, "append level launch");
+    }
+    e = launch_advance_seq(g, seq_lens, t_new, s);
+    if (e != hipSuccess) return hip_fail(e, "append advance launch");
+    return ZHA_OK;
+}
+
+static zha_status route_impl(const Geo& g, const float* q, int32_t t, const int32_t* q_pos, const float* summaries,
+                             const int32_t* seq_lens, float top_p, int32_t sel_capacity, int32_t* sel_blocks,
+                             int32_t* n_sel, int32_t* level_stats, int32_t* level_sel, void* ws, const WsLayout& L,
+                             int rows, hipStream_t s) {
+    RouteArgs a{};
+    a.q = q;
+    a.ri = RowInfo{seq_lens, q_pos, t};
+    a.rows = rows;
+    a.summaries = summaries;
+    a.top_p = top_p;
+    a.sel_cap = sel_capacity;
+    a.sel_blocks = sel_blocks;
+    a.n_sel = n_sel;
+    a.level_stats = level_stats;
+    a.level_sel = level_sel;
+    a.ws = static_cast<char*>(ws);
+    a.lay = &L;
+    const hipError_t e = launch_route(g, a, s);
+    if (e != hipSuccess) return hip_fail(e, "route launch");
+    return ZHA_OK;
+}
+
+static zha_status check_route_args(const float* q, const float* summaries, const int32_t* seq_lens, float top_p,
+                                   int32_t sel_capacity, int32_t* sel_blocks, int32_t* n_sel) {
+    if (!q || !summaries || !seq_lens || !sel_blocks || !n_sel)
+        return fail(ZHA_ERR_NULL, "q, summaries, seq_lens, sel_blocks and n_sel are required");
+    if (!(top_p > 0.f && top_p <= 1.f)) return fail(ZHA_ERR_SHAPE, "top_p must be in (0, 1]");
+    if (sel_capacity < 1) return fail(ZHA_ERR_SHAPE, "sel_capacity must be >= 1");
+    return ZHA_OK;
+}
+
+zha_status zha_route(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos, const float* summaries,
+                     const int32_t* seq_lens, float top_p, int32_t sel_capacity, int32_t* sel_blocks, int32_t* n_sel,
+                     int32_t* level_stats, int32_t* level_sel, void* ws, size_t ws_bytes, void* stream) {
+    Geo g;
+    zha_status st = make_geo(geom, &g);
+    if (st) return st;
+    if ((st = check_route_args(q, summaries, seq_lens, top_p, sel_capacity, sel_blocks, n_sel))) return st;
+    int rows;
+    if ((st = check_rows(g, t, &rows))) return st;
+    const WsLayout L = layout(g, rows);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+    return route_impl(g, q, t, q_pos, summaries, seq_lens, top_p, sel_capacity, sel_blocks, n_sel, level_stats,
+                      level_sel, ws, L, rows, static_cast<hipStream_t>(stream));
+}
+
+static zha_status attend_impl(const Geo& g, const float* q, int32_t t, const int32_t* q_pos, const void* K,
+                              const void* V, const int32_t* seq_lens, const int32_t* sel_blocks, const int32_t* n_sel,
+                              int32_t sel_capacity, float* out, float* lse, void* ws, const WsLayout& L, int rows,
+                              bool dense, hipStream_t s) {
+    AttendArgs a{};
+    a.q = q;
+    a.ri = RowInfo{seq_lens, q_pos, t};
+    a.rows = rows;
+    a.K = K;
+    a.V = V;
+    a.sel_blocks = sel_blocks;
+    a.n_sel = n_sel;
+    a.sel_cap = sel_capacity;
+    a.out = out;
+    a.lse = lse;
+    a.ws = static_cast<char*>(ws);
+    a.lay = &L;
+    a.dense = dense;
+    const hipError_t e = launch_attend(g, a, s);
+    if (e != hipSuccess) return hip_fail(e, "attend launch");
+    return ZHA_OK;
+}
+
+zha_status zha_sparse_attend(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos, const void* K,
+                             const void* V, const int32_t* seq_lens, const int32_t* sel_blocks, const int32_t* n_sel,
+                             int32_t sel_capacity, float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    Geo g;
+    zha_status st = make_geo(geom, &g);
+    if (st) return st;
+    if (!q || !K || !V || !seq_lens || !sel_blocks || !n_sel || !out || !lse)
+        return fail(ZHA_ERR_NULL, "q, K, V, seq_lens, sel_blocks, n_sel, out and lse are required");
+    if (sel_capacity < 1) return fail(ZHA_ERR_SHAPE, "sel_capacity must be >= 1");
+    int rows;
+    if ((st = check_rows(g, t, &rows))) return st;
+    const WsLayout L = layout(g, rows);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+    return attend_impl(g, q, t, q_pos, K, V, seq_lens, sel_blocks, n_sel, sel_capacity, out, lse, ws, L, rows, false,
+                       static_cast<hipStream_t>(stream));
+}
+
+zha_status zha_attend(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos, const void* K,
+                      const void* V, const float* summaries, const int32_t* seq_lens, float top_p,
+                      int32_t sel_capacity, int32_t* sel_blocks, int32_t* n_sel, int32_t* level_stats,
+                      int32_t* level_sel, float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    Geo g;
+    zha_status st = make_geo(geom, &g);
+    if (st) return st;
+    if ((st = check_route_args(q, summaries, seq_lens, top_p, sel_capacity, sel_blocks, n_sel))) return st;
+    if (!K || !V || !out || !lse) return fail(ZHA_ERR_NULL, "K, V, out and lse are required");
+    int rows;
+    if ((st = check_rows(g, t, &rows))) return st;
+    const WsLayout L = layout(g, rows);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = route_impl(g, q, t, q_pos, summaries, seq_lens, top_p, sel_capacity, sel_blocks, n_sel, level_stats,
+                         level_sel, ws, L, rows, s)))
+        return st;
+    return attend_impl(g, q, t, q_pos, K, V, seq_lens, sel_blocks, n_sel, sel_capacity, out, lse, ws, L, rows, false,
+                       s);
+}
+
+zha_status zha_dense_attend(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos, const void* K,
+                            const void* V, const int32_t* seq_lens, float* out, float* lse, void* ws, size_t ws_bytes,
+                            void* stream) {
+    Geo g;
+    zha_status st = make_geo(geom, &g);
+    if (st) return st;
+    if (!q || !K || !V || !seq_lens || !out || !lse)
+        return fail(ZHA_ERR_NULL, "q, K, V, seq_lens, out and lse are required");
+    int rows;
+    if ((st = check_rows(g, t, &rows))) return st;
+    const WsLayout L = layout(g, rows);
+    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
+    return attend_impl(g, q, t, q_pos, K, V, seq_lens, nullptr, nullptr, 1, out, lse, ws, L, rows, true,
+                       static_cast<hipStream_t>(stream));
+}
+
+zha_status zha_read_device_status(void* ws, void* stream, uint32_t* out, int32_t clear) {
+    if (!ws || !out) return fail(ZHA_ERR_NULL, "ws and out are required");
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    e = hipMemcpy(out, ws, sizeof(uint32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "status read");
+    if (clear) {
+        const uint32_t zero = 0;
+        e = hipMemcpy(ws, &zero, sizeof(uint32_t), hipMemcpyHostToDevice);
+        if (e != hipSuccess) return hip_fail(e, "status clear");
+    }
+    return ZHA_OK;
+}
+
+const char* zha_status_string(zha_status s) {
+    switch (s) {
+        case ZHA_OK: return "ok";
+        case ZHA_ERR_NULL: return "null pointer";
+        case ZHA_ERR_SHAPE: return "inconsistent shape";
+        case ZHA_ERR_UNSUPPORTED: return "unsupported size";
+        case ZHA_ERR_WORKSPACE: return "workspace too small";
+        case ZHA_ERR_CAPACITY: return "capacity exceeded";
+        case ZHA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* zha_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// zha_internal.h - layout arithmetic and kernel parameter blocks shared by the
+// host entry points and the kernel launchers of libzha. Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/zha.h"
+
+namespace zha {
+
+constexpr int kWave = 64;
+constexpr int kMaxGroup = 16;          // H_q / H_kv handled by one kernel group
+constexpr int kAttnSplitsMax = 256;    // split-K partitions per (row, kv head)
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// Geometry after validation, with everything the kernels need precomputed.
+struct Geo {
+    int B, Hq, Hkv, G, D, b, L, kv_dtype;
+    int64_t cap;                       // tokens per sequence
+    float scale;
+    int64_t nodes[ZHA_MAX_LEVELS];     // node slots per (batch, kv) per level
+    int64_t span[ZHA_MAX_LEVELS + 1];  // tokens per node of level l (index l-1); span[L] = b^(L+1)
+    int64_t sum_off[ZHA_MAX_LEVELS];   // element offset of each level in the summary buffer
+    int64_t sel_off[ZHA_MAX_LEVELS];   // element offset of each level in a level_sel buffer (per row count)
+    int64_t nodes_total;               // sum of nodes[l]
+};
+
+// Byte layout of the workspace for `rows` query rows.
+struct WsLayout {
+    size_t status;        // uint32 status word + group counters header
+    size_t grp_ctr;       // uint32 [rows, Hkv, L]   last-of-group counters (cut kernels)
+    size_t scores;        // float  [rows, Hq, nodes_total] dense-by-node scores, level offsets = sel_off
+    size_t kept;          // int32  [rows, Hq, nodes_total] kept lists per level (level 1 unused)
+    size_t kept_cnt;      // int32  [rows, Hq, L]
+    size_t bitmap;        // uint32 [rows, Hq, bm_words_total] kept bitmaps per level
+    size_t bm_off[ZHA_MAX_LEVELS];    // word offset of each level inside a row-head bitmap
+    int64_t bm_words_total;
+    size_t ulist;         // int32  [rows, Hkv, nodes_total] union of kept nodes per level (parents for the level below)
+    size_t ucnt;          // int32  [rows, Hkv, L]
+    size_t abm;           // uint32 [rows, Hq, abm_words] attention head bitmaps (leaf chunks + current chunk)
+    int64_t abm_words;
+    size_t aitems;        // int2   [rows, Hkv, nodes[0] + 2] attention items (block, head mask)
+    size_t acnt;          // int32  [rows, Hkv]
+    size_t partial;       // float  [rows, Hq, splits, D + 2] split-K partial states
+    int splits;
+    size_t total;
+};
+
+// Parameters shared by every kernel that reads queries.
+struct RowInfo {
+    const int32_t* seq_lens;  // [B]
+    const int32_t* q_pos;     // [B, T] or null
+    int T;                    // rows per sequence
+};
+
+__host__ __device__ inline int row_visible(const RowInfo& ri, int row) {
+    const int s = row / ri.T, t = row % ri.T;
+    const int pos = ri.q_pos ? ri.q_pos[row] : (ri.seq_lens[s] - ri.T + t);
+    return pos + 1;
+}
+
+// Launchers (defined in the kernel translation units). All return hipError_t.
+hipError_t launch_build_level(const Geo& g, int level, const void* K, const float* ref_q, float* summaries,
+                              const int32_t* seq_lens, int mode, int t_new, hipStream_t st);
+hipError_t launch_append_rows(const Geo& g, void* K, void* V, const void* k_new, const void* v_new, int t_new,
+                              const int32_t* seq_lens, uint32_t* status, hipStream_t st);
+hipError_t launch_append_fused(const Geo& g, void* K, void* V, const void* k_new, const void* v_new, int t_new,
+                               int32_t* seq_lens, const float* ref_q, float* summaries, uint32_t* status,
+                               hipStream_t st);
+hipError_t launch_advance_seq(const Geo& g, int32_t* seq_lens, int t_new, hipStream_t st);
+
+struct RouteArgs {
+    const float* q;
+    RowInfo ri;
+    int rows;
+    const float* summaries;
+    float top_p;
+    int sel_cap;
+    int32_t* sel_blocks;
+    int32_t* n_sel;
+    int32_t* level_stats;
+    int32_t* level_sel;
+    char* ws;
+    const WsLayout* lay;
+};
+hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st);
+
+struct AttendArgs {
+    const float* q;
+    RowInfo ri;
+    int rows;
+    const void* K;
+    const void* V;
+    const int32_t* sel_blocks;
+    const int32_t* n_sel;
+    int sel_cap;
+    float* out;
+    float* lse;
+    char* ws;
+    const WsLayout* lay;
+    bool dense;
+};
+hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st);
+
+}  // namespace zha

@@ -1,0 +1,189 @@
+/*
+ * zha.h - C ABI of libzha: the decode hot path of Zyphra Hierarchical
+ * Attention (ZHA) on MI355X (gfx950).
+ *
+ * The method (sources cited by page title and section):
+ *  - "Subquadratic Attention with a Hierarchical Tree-Structured Indexer"
+ *    (summary page of the technical report), §Tree Construction: every chunk
+ *    of b contiguous keys is compressed to a summary key, the attention of a
+ *    reference query over the chunk with the chunk as keys and values; higher
+ *    levels are built the same way from their children's summaries.
+ *  - same page, §Routing: at each level keep the smallest score-ordered prefix
+ *    of candidate nodes holding a fraction p of the softmax mass, expand the
+ *    kept nodes' children, down to leaf chunks; attend exactly over
+ *    {token 0} U kept leaf chunks U the query's current chunk.
+ *  - "Zyphra Hierarchical Attention: The End of Quadratic Attention?",
+ *    §How the tree is built and searched: contiguous chunks, the full KV
+ *    cache stays at the leaves, token 0 is always kept as a sink.
+ *
+ * Fixed readings (the pages leave these open):
+ *  - one reference query per (level, kv head); a summary is the
+ *    softmax(r . c * scale)-weighted mean of its children c;
+ *  - a node's score is q . summary * scale, computed in fp32; the cut orders
+ *    candidates by (score desc, node id asc) and keeps the smallest prefix
+ *    with cumulative mass >= p of the candidates' total; p >= 1 keeps all;
+ *  - only complete nodes exist (node i of level l covers tokens
+ *    [i*b^l, (i+1)*b^l)); complete nodes whose parent is incomplete enter as
+ *    candidates at their own level; at the top level every complete node is a
+ *    candidate;
+ *  - a query that sees N tokens attends {0} U kept leaf chunks U
+ *    [b*floor((N-1)/b), N), each token once.
+ *
+ * Conventions for every function:
+ *  - All tensor pointers are DEVICE pointers, owned by the caller, and must
+ *    stay valid until the work enqueued on `stream` has finished. The library
+ *    never allocates or frees memory and keeps no pointer after returning.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *    work is enqueued asynchronously on it; no call synchronises except
+ *    zha_read_device_status.
+ *  - Host-detectable errors (null pointers, unsupported shapes, a workspace
+ *    that is too small) are returned before anything is enqueued. Conditions
+ *    only the device can see (a selection larger than sel_capacity, an append
+ *    past capacity) set bits in a status word inside the workspace, read with
+ *    zha_read_device_status.
+ *  - Layouts (row-major, innermost last):
+ *      K, V           [B, H_kv, capacity, d]   bf16 or fp32 (geom.kv_dtype)
+ *      ref_q          [L, H_kv, d]             fp32
+ *      summaries      fp32; level l (1-based) starts at element
+ *                     sizes.level_offset[l-1]; node i of (batch s, kv head h)
+ *                     is row (s*H_kv + h)*sizes.level_nodes[l-1] + i
+ *      q, out         [B, T, H_q, d]           fp32
+ *      lse            [B, T, H_q]              fp32 (natural log, scale included)
+ *      seq_lens       [B]                      int32, tokens present per sequence
+ *      q_pos          [B, T]                   int32 position of each query row,
+ *                     or NULL for the last T positions (seq_lens[s]-T+t); a
+ *                     row at position t sees tokens [0, t] and only the tree
+ *                     nodes complete within them
+ *      sel_blocks     [B, T, H_q, sel_capacity] int32 kept leaf-chunk ids, ascending
+ *      n_sel          [B, T, H_q]              int32 true number kept
+ *    Query head h reads kv head h / (H_q / H_kv).
+ */
+#ifndef ZHA_H
+#define ZHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define ZHA_API __attribute__((visibility("default")))
+#else
+#define ZHA_API
+#endif
+
+typedef int32_t zha_status;
+
+#define ZHA_OK               0
+#define ZHA_ERR_NULL         1  /* a required pointer is NULL */
+#define ZHA_ERR_SHAPE        2  /* inconsistent sizes (H_q % H_kv, T, capacity, ...) */
+#define ZHA_ERR_UNSUPPORTED  3  /* a size this build has no kernel for */
+#define ZHA_ERR_WORKSPACE    4  /* workspace smaller than zha_query_sizes asks for */
+#define ZHA_ERR_CAPACITY     5  /* device: selection or append exceeded a capacity */
+#define ZHA_ERR_HIP          6  /* the HIP runtime reported an error */
+
+/* Device status bits (zha_read_device_status). */
+#define ZHA_DEV_SEL_OVERFLOW     1u  /* some n_sel exceeded sel_capacity: list truncated */
+#define ZHA_DEV_APPEND_OVERFLOW  2u  /* an append would pass capacity: nothing written */
+
+#define ZHA_KV_BF16 0
+#define ZHA_KV_F32  1
+
+#define ZHA_MAX_LEVELS 8
+
+typedef struct zha_geom {
+    int32_t batch;       /* B >= 1 */
+    int32_t n_q_heads;   /* H_q, a multiple of H_kv, H_q / H_kv <= 16 */
+    int32_t n_kv_heads;  /* H_kv >= 1 */
+    int32_t head_dim;    /* d: 64 or 128 */
+    int32_t branching;   /* b: 2, 4, 8, 16, 32 or 64 */
+    int32_t n_levels;    /* L: 1..ZHA_MAX_LEVELS */
+    int64_t capacity;    /* tokens allocated per sequence, < 2^31 */
+    int32_t kv_dtype;    /* ZHA_KV_BF16 or ZHA_KV_F32 */
+    float   scale;       /* score scale; 0 selects 1/sqrt(d) */
+} zha_geom;
+
+typedef struct zha_sizes {
+    size_t  summaries_bytes;                 /* fp32 summary buffer for all levels */
+    size_t  workspace_bytes;                 /* scratch for every call with up to max_rows query rows */
+    int64_t level_nodes[ZHA_MAX_LEVELS];     /* node slots per (batch, kv head) and level: capacity / b^l */
+    int64_t level_offset[ZHA_MAX_LEVELS];    /* element offset of each level inside summaries */
+    int64_t level_sel_offset[ZHA_MAX_LEVELS];/* element offset of each level inside a level_sel buffer */
+    size_t  level_sel_bytes;                 /* bytes of a level_sel buffer for max_rows rows */
+    int32_t max_rows;                        /* B*T rows the workspace was sized for */
+} zha_sizes;
+
+/* Sizes of the summary buffer and workspace for `geom` and calls with at most
+ * `max_t` query rows per sequence (max_t >= 1). Host only, enqueues nothing. */
+ZHA_API zha_status zha_query_sizes(const zha_geom* geom, int32_t max_t, zha_sizes* out);
+
+/* Build every complete node of every level for the first seq_lens[s] tokens of
+ * each sequence [Tree Construction]. K is read, summaries are written. ws must
+ * hold zha_query_sizes(...).workspace_bytes (any max_t). */
+ZHA_API zha_status zha_build_tree(const zha_geom* geom, const void* K, const float* ref_q,
+                          const int32_t* seq_lens, float* summaries,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Append t_new tokens to every sequence: k_new, v_new are [B, H_kv, t_new, d]
+ * in the cache dtype. Rows are written at seq_lens[s] .. seq_lens[s]+t_new-1,
+ * every node they complete is summarised (bit-identical to zha_build_tree),
+ * then seq_lens[s] += t_new. A sequence that would pass capacity is left
+ * untouched and ZHA_DEV_APPEND_OVERFLOW is raised. [the tree is built on the
+ * fly as the context grows: A query's path through the tree, step by step] */
+ZHA_API zha_status zha_append(const zha_geom* geom, void* K, void* V, const void* k_new, const void* v_new,
+                      int32_t t_new, int32_t* seq_lens, const float* ref_q, float* summaries,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Route T query rows per sequence top-down through the tree [Routing].
+ * Writes sel_blocks / n_sel. level_stats (nullable) receives
+ * [B, T, H_q, L, 2] int32 (candidates, kept) per level (index l-1).
+ * level_sel (nullable) receives every level's kept ids, ascending: with
+ * R = B*T rows, level l of row r = s*T + t, head h starts at element
+ * R*H_q*sizes.level_sel_offset[l-1] + (r*H_q + h) * sizes.level_nodes[l-1]
+ * (sizes from zha_query_sizes for the same geom; R*H_q*sum(level_nodes)
+ * elements in all).
+ * top_p in (0, 1]. sel_capacity >= 1. */
+ZHA_API zha_status zha_route(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos,
+                     const float* summaries, const int32_t* seq_lens, float top_p,
+                     int32_t sel_capacity, int32_t* sel_blocks, int32_t* n_sel,
+                     int32_t* level_stats, int32_t* level_sel,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Exact attention of each query row over {0} U its kept leaf chunks U its
+ * current chunk [Routing, o(q)]. Uses the first min(n_sel, sel_capacity)
+ * entries of each list. out and lse as in the layouts above. */
+ZHA_API zha_status zha_sparse_attend(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos,
+                             const void* K, const void* V, const int32_t* seq_lens,
+                             const int32_t* sel_blocks, const int32_t* n_sel, int32_t sel_capacity,
+                             float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* zha_route followed by zha_sparse_attend on one stream. */
+ZHA_API zha_status zha_attend(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos,
+                      const void* K, const void* V, const float* summaries, const int32_t* seq_lens,
+                      float top_p, int32_t sel_capacity, int32_t* sel_blocks, int32_t* n_sel,
+                      int32_t* level_stats, int32_t* level_sel, float* out, float* lse,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Dense baseline: exact attention of each row over all tokens it sees
+ * [The Quadratic Bottleneck: decode re-reads the whole cache per token]. */
+ZHA_API zha_status zha_dense_attend(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos,
+                            const void* K, const void* V, const int32_t* seq_lens,
+                            float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Wait for `stream`, then read (and, if clear != 0, reset) the device status
+ * word of workspace `ws` into *out (ZHA_DEV_* bits). The only synchronising call. */
+ZHA_API zha_status zha_read_device_status(void* ws, void* stream, uint32_t* out, int32_t clear);
+
+/* Static text for a status code. */
+ZHA_API const char* zha_status_string(zha_status s);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+ZHA_API const char* zha_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZHA_H */

@@ -1,0 +1,311 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on seeded inputs.
+
+Sizes are chosen so the oracle finishes in seconds while the kernels still see
+several tiles, ragged tails and every kernel specialisation the workloads use
+(d = 64 / 128, b = 16 / 32, GQA groups of 1 / 4 / 8, fp32 and bf16 caches).
+
+Bars (fixed by the method's precision statement):
+* summaries: within an fp32 accumulation bound derived in gpu_helpers.summary_tol;
+* kept sets per level, teacher-forced on the GPU's own kept parents: equal up to
+  candidates whose cumulative-mass margin at the cut is below 1e-5;
+* candidate counts per level: exact;
+* attention on the GPU's own index set: 1e-5 max-abs for fp32 caches, 2e-3 for bf16;
+* append-built and build-built summaries: bit-identical.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import hierarchical_tree_indexed_build_amd as Z
+import workloads as W
+from oracle import zha_oracle as O
+from tests.gpu_helpers import (Staged, attn_tol, check_sets, level_kept, say, summary_tol, torch)
+
+pytestmark = pytest.mark.gpu
+
+# (workload, shrink, batch)
+CASES = [("tiny", 0, None), ("gqa128k", 2, 2), ("decode1m", 2, 1), ("decode16m", 2, 1), ("gqa128k", 1, 1)]
+IDS = [f"{n}-s{s}" for n, s, _ in CASES]
+
+
+def _w(name, shrink, batch):
+    return W.get_workload(name, shrink=shrink, batch=batch)
+
+
+def _qpos(st, rows_per_seq, pos=None):
+    t = torch()
+    w = st.w
+    if pos is None:
+        pos = w.n_tokens - 1
+    return t.full((w.batch, rows_per_seq), pos, dtype=t.int32, device="cuda")
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_build_parity(case):
+    w = _w(*case)
+    say(f"[build] {w.name} B={w.batch} N={w.n_tokens} b={w.branching} L={w.n_levels} {w.kv_dtype}")
+    st = Staged(w)
+    trees = st.oracle_trees()
+    for level in range(1, w.n_levels + 1):
+        gpu = st.gpu_level(level)
+        for s in range(w.batch):
+            for h in range(w.n_kv_heads):
+                ref = trees[s][h][level - 1]
+                n = ref.shape[0]
+                children = st.Kf[s, h, :w.n_tokens] if level == 1 else trees[s][h][level - 2]
+                tol = summary_tol(children.astype(np.float64), st.R[level - 1, h].astype(np.float64), w.scale)
+                err = np.abs(gpu[s, h, :n].astype(np.float64) - ref).max() if n else 0.0
+                assert err <= tol, (level, s, h, err, tol)
+
+
+def _route(st, rows_per_seq, q_pos, top_p=None, sel_cap=None, step=0):
+    t = torch()
+    w = st.w
+    p = w.top_p if top_p is None else top_p
+    qn, q = st.queries(step, rows=rows_per_seq)
+    rows = w.batch * rows_per_seq
+    sel, nsel, stats, lsel = st.route_buffers(rows, sel_cap)
+    Z.route(st.geom, q, q_pos, st.cache.summaries, st.cache.seq_lens, p, sel, nsel, st.cache.ws,
+            level_stats=stats, level_sel=lsel)
+    t.cuda.synchronize()
+    return qn, q, sel, nsel, stats, lsel, p
+
+
+def _teacher_forced(st, qn, qpos_np, stats, lsel, p, trees):
+    w = st.w
+    rows = qn.shape[0] * qn.shape[1]
+    kept = {l: level_kept(st, lsel, stats, rows, l) for l in range(1, w.n_levels + 1)}
+    flips = 0
+    for s in range(w.batch):
+        for t_ in range(qn.shape[1]):
+            r = s * qn.shape[1] + t_
+            N = int(qpos_np[s, t_]) + 1
+            for hq in range(w.n_q_heads):
+                kv = hq // w.group
+                tree = trees[s][kv]
+                parents = None
+                for level in range(w.n_levels, 0, -1):
+                    v, cnt, cand = kept[level]
+                    gpu_ids = v[r, hq, :cnt[r, hq]]
+                    cut = O.route_level(qn[s, t_, hq], tree[level - 1], level, parents, N, w.branching,
+                                        w.n_levels, p, w.scale)
+                    assert cand[r, hq] == len(cut.ids), (s, t_, hq, level, cand[r, hq], len(cut.ids))
+                    assert np.all(np.diff(gpu_ids) > 0), "kept ids must be ascending"
+                    flips += check_sets(gpu_ids, cut, p, f"row {r} head {hq} level {level}")
+                    parents = gpu_ids
+    return flips
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_route_parity(case):
+    w = _w(*case)
+    say(f"[route] {w.name}")
+    st = Staged(w)
+    T = w.queries_per_step
+    q_pos = _qpos(st, T)
+    qn, q, sel, nsel, stats, lsel, p = _route(st, T, q_pos)
+    flips = _teacher_forced(st, qn, q_pos.cpu().numpy(), stats, lsel, p, st.oracle_trees())
+    say(f"  margin-exempt differences: {flips}")
+    # level-1 outputs agree with the level_sel copy
+    v1, c1, _ = level_kept(st, lsel, stats, w.batch * T, 1)
+    assert np.array_equal(nsel.cpu().numpy().reshape(-1), c1.reshape(-1))
+    s_np = sel.cpu().numpy().reshape(w.batch * T, w.n_q_heads, -1)
+    for r in range(w.batch * T):
+        for h in range(w.n_q_heads):
+            n = c1[r, h]
+            assert np.array_equal(s_np[r, h, :n], v1[r, h, :n])
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_sparse_attend_parity(case):
+    t = torch()
+    w = _w(*case)
+    say(f"[sparse] {w.name}")
+    st = Staged(w)
+    T = w.queries_per_step
+    q_pos = _qpos(st, T)
+    qn, q, sel, nsel, stats, lsel, p = _route(st, T, q_pos)
+    out = t.zeros_like(q)
+    lse = t.zeros(q.shape[:3], dtype=t.float32, device="cuda")
+    Z.sparse_attend(st.geom, q, q_pos, st.cache.K, st.cache.V, st.cache.seq_lens, sel, nsel, out, lse, st.cache.ws)
+    t.cuda.synchronize()
+    o_np, l_np = out.cpu().numpy(), lse.cpu().numpy()
+    s_np, n_np = sel.cpu().numpy(), nsel.cpu().numpy()
+    tol = attn_tol(w)
+    N = w.n_tokens
+    worst = 0.0
+    for s in range(w.batch):
+        for t_ in range(T):
+            for hq in range(w.n_q_heads):
+                kv = hq // w.group
+                I = O.index_set(s_np[s, t_, hq, :n_np[s, t_, hq]], N, w.branching)
+                o, l = O.attend(qn[s, t_, hq], st.Kf[s, kv], st.Vf[s, kv], I, w.scale)
+                e = max(np.abs(o_np[s, t_, hq] - o).max(), abs(l_np[s, t_, hq] - l))
+                worst = max(worst, e)
+                assert e <= tol, (s, t_, hq, e)
+    say(f"  worst |gpu - oracle| = {worst:.3g} (tol {tol})")
+    # zha_attend is route + sparse attend on one stream: identical bits
+    out2 = t.zeros_like(q)
+    lse2 = t.zeros_like(lse)
+    sel2, nsel2 = t.zeros_like(sel), t.zeros_like(nsel)
+    Z.attend(st.geom, q, q_pos, st.cache.K, st.cache.V, st.cache.summaries, st.cache.seq_lens, p, sel2, nsel2,
+             out2, lse2, st.cache.ws)
+    t.cuda.synchronize()
+    assert t.equal(out, out2) and t.equal(lse, lse2) and t.equal(nsel, nsel2)
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_dense_parity(case):
+    t = torch()
+    w = _w(*case)
+    say(f"[dense] {w.name}")
+    st = Staged(w, build=False)
+    T = w.queries_per_step
+    q_pos = _qpos(st, T)
+    qn, q = st.queries(0)
+    out = t.zeros_like(q)
+    lse = t.zeros(q.shape[:3], dtype=t.float32, device="cuda")
+    Z.dense_attend(st.geom, q, q_pos, st.cache.K, st.cache.V, st.cache.seq_lens, out, lse, st.cache.ws)
+    t.cuda.synchronize()
+    o_np, l_np = out.cpu().numpy(), lse.cpu().numpy()
+    tol = attn_tol(w)
+    for s in range(w.batch):
+        for t_ in range(T):
+            for hq in range(w.n_q_heads):
+                kv = hq // w.group
+                o, l = O.dense_attend(qn[s, t_, hq], st.Kf[s, kv], st.Vf[s, kv], w.n_tokens, w.scale)
+                e = max(np.abs(o_np[s, t_, hq] - o).max(), abs(l_np[s, t_, hq] - l))
+                assert e <= tol, (s, t_, hq, e)
+
+
+def test_p1_selects_everything_and_matches_dense():
+    t = torch()
+    w = _w("gqa128k", 2, 1)
+    say("[p=1] gqa128k shrink 2")
+    st = Staged(w)
+    q_pos = _qpos(st, 1)
+    qn, q, sel, nsel, stats, lsel, p = _route(st, 1, q_pos, top_p=1.0)
+    n1 = w.n_tokens // w.branching
+    assert np.all(nsel.cpu().numpy() == n1)
+    out = t.zeros_like(q)
+    lse = t.zeros(q.shape[:3], dtype=t.float32, device="cuda")
+    Z.sparse_attend(st.geom, q, q_pos, st.cache.K, st.cache.V, st.cache.seq_lens, sel, nsel, out, lse, st.cache.ws)
+    od = t.zeros_like(q)
+    ld = t.zeros_like(lse)
+    Z.dense_attend(st.geom, q, q_pos, st.cache.K, st.cache.V, st.cache.seq_lens, od, ld, st.cache.ws)
+    t.cuda.synchronize()
+    assert (out - od).abs().max().item() <= 1e-5
+    assert (lse - ld).abs().max().item() <= 1e-5
+
+
+def test_causal_rows_and_short_prefixes():
+    """Rows at every position 0..N-1 (prefill-style q_pos), including rows that see fewer than b tokens."""
+    t = torch()
+    w = W.get_workload("tiny")
+    w.n_tokens = 300
+    w.capacity = 320
+    w.branching = 4
+    w.n_levels = 3
+    w.queries_per_step = 300
+    w.top_p = 0.8
+    say("[causal] tiny-like b=4 L=3 N=300, 300 causal rows")
+    st = Staged(w, max_t=300)
+    q_pos = t.arange(300, dtype=t.int32, device="cuda").view(1, 300)
+    qn, q, sel, nsel, stats, lsel, p = _route(st, 300, q_pos)
+    trees = st.oracle_trees()
+    _teacher_forced(st, qn, q_pos.cpu().numpy(), stats, lsel, p, trees)
+    out = t.zeros_like(q)
+    lse = t.zeros(q.shape[:3], dtype=t.float32, device="cuda")
+    Z.sparse_attend(st.geom, q, q_pos, st.cache.K, st.cache.V, st.cache.seq_lens, sel, nsel, out, lse, st.cache.ws)
+    t.cuda.synchronize()
+    o_np, s_np, n_np = out.cpu().numpy(), sel.cpu().numpy(), nsel.cpu().numpy()
+    for t_ in range(300):
+        I = O.index_set(s_np[0, t_, 0, :n_np[0, t_, 0]], t_ + 1, w.branching)
+        o, _ = O.attend(qn[0, t_, 0], st.Kf[0, 0], st.Vf[0, 0], I, w.scale)
+        assert np.abs(o_np[0, t_, 0] - o).max() <= 1e-5, t_
+
+
+def test_append_bit_identical_to_build():
+    t = torch()
+    w = W.get_workload("decode1m", shrink=2)     # b = 32, L = 2, bf16, 8 kv heads
+    w.capacity = 1400
+    n0 = 1000
+    say("[append] decode1m shrink 2: 60 single-token appends, then a 200-token chunk")
+    st = Staged(w, n_tokens=n0)
+    for step in range(60):
+        kn, vn = W.appended_tokens(w, step, 1)
+        kt, vt = (t.from_numpy(x).view(t.bfloat16).cuda() for x in (kn, vn))
+        Z.append(st.geom, st.cache.K, st.cache.V, kt, vt, st.cache.seq_lens, st.ref_q, st.cache.summaries,
+                 st.cache.ws)
+    kn, vn = W.appended_tokens(w, 999, 200)
+    kt, vt = (t.from_numpy(x).view(t.bfloat16).cuda() for x in (kn, vn))
+    Z.append(st.geom, st.cache.K, st.cache.V, kt, vt, st.cache.seq_lens, st.ref_q, st.cache.summaries, st.cache.ws)
+    t.cuda.synchronize()
+    assert int(st.cache.seq_lens[0].item()) == n0 + 260
+    assert Z.read_device_status(st.cache.ws) == 0
+    # the appended rows landed where they should
+    assert t.equal(st.cache.K[:, :, n0 + 60:n0 + 260], kt)
+    ref = Z.Cache(st.geom, 1)
+    ref.K.copy_(st.cache.K)
+    ref.seq_lens.copy_(st.cache.seq_lens)
+    Z.build_tree(st.geom, ref.K, st.ref_q, ref.seq_lens, ref.summaries, ref.ws)
+    t.cuda.synchronize()
+    for level in range(1, w.n_levels + 1):
+        a, b = st.cache.level(level), ref.level(level)
+        n = (n0 + 260) // w.branching ** level
+        assert t.equal(a[:, :, :n], b[:, :, :n]), level
+
+
+def test_append_past_capacity_writes_nothing():
+    t = torch()
+    w = W.get_workload("decode1m", shrink=2)
+    w.capacity = 1030
+    say("[append overflow]")
+    st = Staged(w, n_tokens=1024)
+    before = st.cache.K.clone()
+    summ = st.cache.summaries.clone()
+    kn, vn = W.appended_tokens(w, 0, 10)
+    kt, vt = (t.from_numpy(x).view(t.bfloat16).cuda() for x in (kn, vn))
+    Z.append(st.geom, st.cache.K, st.cache.V, kt, vt, st.cache.seq_lens, st.ref_q, st.cache.summaries, st.cache.ws)
+    status = Z.read_device_status(st.cache.ws, clear=True)
+    assert status & Z.ZHA_DEV_APPEND_OVERFLOW
+    assert int(st.cache.seq_lens[0].item()) == 1024
+    assert t.equal(before, st.cache.K) and t.equal(summ, st.cache.summaries)
+    assert Z.read_device_status(st.cache.ws) == 0
+
+
+def test_selection_capacity_overflow_truncates():
+    t = torch()
+    w = _w("tiny", 0, None)
+    say("[sel overflow] tiny, sel_capacity 50")
+    st = Staged(w)
+    q_pos = _qpos(st, 16)
+    _, _, sel_full, nsel_full, _, _, _ = _route(st, 16, q_pos)
+    Z.read_device_status(st.cache.ws, clear=True)
+    _, _, sel, nsel, _, _, _ = _route(st, 16, q_pos, sel_cap=50)
+    status = Z.read_device_status(st.cache.ws, clear=True)
+    assert t.equal(nsel, nsel_full)
+    assert int(nsel.max().item()) > 50
+    assert status & Z.ZHA_DEV_SEL_OVERFLOW
+    assert t.equal(sel[..., :50], sel_full[..., :50])
+
+
+def test_repeatable_bits():
+    t = torch()
+    w = _w("decode1m", 2, 1)
+    say("[determinism]")
+    st = Staged(w)
+    q_pos = _qpos(st, 1)
+    qn, q = st.queries(3)
+    outs = []
+    for _ in range(3):
+        sel, nsel, stats, lsel = st.route_buffers(w.batch)
+        out = t.zeros_like(q)
+        lse = t.zeros(q.shape[:3], dtype=t.float32, device="cuda")
+        Z.attend(st.geom, q, q_pos, st.cache.K, st.cache.V, st.cache.summaries, st.cache.seq_lens, w.top_p, sel,
+                 nsel, out, lse, st.cache.ws, level_stats=stats)
+        t.cuda.synchronize()
+        outs.append((out.clone(), lse.clone(), nsel.clone(), stats.clone()))
+    for o in outs[1:]:
+        assert all(t.equal(a, b) for a, b in zip(outs[0], o))
