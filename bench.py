@@ -1,0 +1,385 @@
+"""Benchmark of the ZHA decode hot path on one MI355X.
+
+One step = one decode token for every sequence: append its K/V row (completing
+any tree nodes it closes), route its query through the tree and attend exactly
+over the selected keys (zha_append + zha_attend). Default workload: 1,048,576
+bf16 tokens, batch 1, 32 query / 8 kv heads, d=128, b=32, 4 levels, p=0.95.
+
+Printed: one JSON line with queries/s, the dominant kernel's roofline, the
+in-run dense kernel on the same cache and queries, and the CPU oracle timed on
+the host on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps 256] [--warmup 8] [--workload decode1m]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import hierarchical_tree_indexed_build_amd as Z  # noqa: E402
+import workloads as W  # noqa: E402
+
+HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+METRIC = "ZHA decode queries/sec at 1M-token KV; % HBM roofline; speedup vs dense"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="decode1m", choices=["decode1m", "gqa128k", "decode16m"])
+    ap.add_argument("--kernel", default="route_score@1", help="kernel label timed live for the roofline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed run")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# staging
+# ----------------------------------------------------------------------------
+class Bench:
+    def __init__(self, w, steps, warmup):
+        import torch
+        self.t = torch
+        self.w = w
+        self.steps, self.warmup = steps, warmup
+        total = steps + warmup
+        if w.append_per_step:
+            w.capacity = w.n_tokens + total * w.append_per_step
+        self.geom = Z.make_geom(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.branching, w.n_levels,
+                                w.capacity, w.kv_dtype)
+        self.c = Z.Cache(self.geom, 1)
+        self.sizes = self.c.sizes
+        t0 = time.time()
+        kdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+        self.K_host = np.zeros((w.batch, w.n_kv_heads, w.capacity, w.head_dim),
+                               np.uint16 if w.kv_dtype == "bf16" else np.float32)
+        self.V_host = np.zeros_like(self.K_host)
+        for s in range(w.batch):
+            lay = W.cluster_layout(w, s)
+            for h in range(w.n_kv_heads):
+                k, v = W.kv_chunk(w, s, h, 0, w.n_tokens, lay)
+                self.K_host[s, h, :w.n_tokens] = k
+                self.V_host[s, h, :w.n_tokens] = v
+                self.c.K[s, h, :w.n_tokens].copy_(torch.from_numpy(k).view(kdt))
+                self.c.V[s, h, :w.n_tokens].copy_(torch.from_numpy(v).view(kdt))
+        log(f"[bench] generated and uploaded the {w.n_tokens}-token cache in {time.time() - t0:.1f}s")
+        self.R = W.ref_queries(w)
+        self.ref_q = torch.from_numpy(self.R).cuda()
+        self.c.seq_lens.fill_(w.n_tokens)
+        # per-step inputs, resident in HBM before any timing
+        qs = np.stack([W.queries(w, i) for i in range(total)])             # [S, B, 1, Hq, d]
+        self.q = torch.from_numpy(qs).cuda()
+        self.q_host = qs
+        if w.append_per_step:
+            kv = [W.appended_tokens(w, i) for i in range(total)]
+            self.k_new = torch.stack([torch.from_numpy(k).view(kdt) for k, _ in kv]).cuda()
+            self.v_new = torch.stack([torch.from_numpy(v).view(kdt) for _, v in kv]).cuda()
+            self.kv_host = kv
+        n1 = self.sizes.level_nodes[0]
+        self.sel = torch.zeros((w.batch, 1, w.n_q_heads, n1), dtype=torch.int32, device="cuda")
+        self.nsel = torch.zeros((w.batch, 1, w.n_q_heads), dtype=torch.int32, device="cuda")
+        self.out = torch.zeros((w.batch, 1, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+        self.lse = torch.zeros((w.batch, 1, w.n_q_heads), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.time()
+        Z.build_tree(self.geom, self.c.K, self.ref_q, self.c.seq_lens, self.c.summaries, self.c.ws)
+        torch.cuda.synchronize()
+        self.build_s = time.time() - t0
+        log(f"[bench] tree built in {self.build_s * 1e3:.1f} ms (first call, includes module load)")
+
+    def step(self, i, level_stats=None, level_sel=None):
+        w, c = self.w, self.c
+        if w.append_per_step:
+            Z.append(self.geom, c.K, c.V, self.k_new[i], self.v_new[i], c.seq_lens, self.ref_q, c.summaries, c.ws)
+        Z.attend(self.geom, self.q[i], None, c.K, c.V, c.summaries, c.seq_lens, w.top_p, self.sel, self.nsel,
+                 self.out, self.lse, c.ws, level_stats=level_stats, level_sel=level_sel)
+
+    def snapshot(self):
+        return self.c.summaries.clone(), self.c.seq_lens.clone()
+
+    def restore(self, snap):
+        self.c.summaries.copy_(snap[0])
+        self.c.seq_lens.copy_(snap[1])
+
+
+# ----------------------------------------------------------------------------
+# algorithmic bytes (each unique byte the method must move, once)
+# ----------------------------------------------------------------------------
+def _lsel_level(b: Bench, lsel: np.ndarray, rows: int, level: int) -> np.ndarray:
+    n = b.sizes.level_nodes[level - 1]
+    off = rows * b.geom.n_q_heads * b.sizes.level_sel_offset[level - 1]
+    return lsel[off:off + rows * b.geom.n_q_heads * n].reshape(rows, b.geom.n_q_heads, n)
+
+
+def step_bytes(b: Bench, stats, lsel, sel, nsel, N):
+    """Algorithmic bytes per kernel family for one decode step.
+
+    route_score@l: every summary row of level l scored for a kv group, read once
+      (4d bytes), plus one fp32 score per (query head, row) written.
+    route_cut@l: every candidate score read once (4 B) plus kept ids written (4 B).
+    attend: K and V rows of the union of the group's index sets, read once
+      (2 d s_kv bytes per token), plus the query (4d) and partial writes.
+    append: one K and one V row per kv head.
+    """
+    w = b.w
+    d, g, bb, L = w.head_dim, w.group, w.branching, w.n_levels
+    skv = 2 if w.kv_dtype == "bf16" else 4
+    rows = w.batch
+    out = {}
+    nc = [N // bb ** l for l in range(1, L + 1)] + [0]
+    stats = stats.reshape(rows, w.n_q_heads, L, 2)
+    for level in range(L, 0, -1):
+        scored = 0
+        for s in range(rows):
+            for kv in range(w.n_kv_heads):
+                if level == L:
+                    scored += nc[L - 1]
+                    continue
+                v = _lsel_level(b, lsel, rows, level + 1)
+                par = set()
+                for h in range(kv * g, kv * g + g):
+                    cnt = int(stats[s, h, level, 1])
+                    par.update(v[s, h, :cnt].tolist())
+                scored += len(par) * bb + (nc[level - 1] - nc[level] * bb)
+        out[f"route_score@{level}"] = scored * (4 * d + 4 * g) + rows * w.n_q_heads * 4 * d
+        cands = int(stats[:, :, level - 1, 0].sum())
+        kept = int(stats[:, :, level - 1, 1].sum())
+        out[f"route_cut@{level}"] = 4 * cands + 4 * kept
+    toks = 0
+    for s in range(rows):
+        for kv in range(w.n_kv_heads):
+            blocks = {0, (N - 1) // bb}
+            for h in range(kv * g, kv * g + g):
+                blocks.update(sel[s, 0, h, :nsel[s, 0, h]].tolist())
+            toks += sum(min(bb, N - x * bb) for x in blocks)
+    out["attend"] = toks * 2 * d * skv + rows * w.n_q_heads * 4 * d
+    out["append"] = rows * w.n_kv_heads * 2 * d * skv if w.append_per_step else 0
+    return out
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle baseline
+# ----------------------------------------------------------------------------
+def cpu_baseline(b: Bench, budget_s: float):
+    """Time the oracle's per-query work (route + attend, every head) on host cores.
+
+    The oracle routes against the tree the GPU built (copied to the host): the
+    tree is built once per cache, the metric counts per-query work. Sampled
+    queries are the timed steps' queries, in order, until the budget is spent.
+    """
+    from threadpoolctl import threadpool_limits
+    from oracle import zha_oracle as O
+    w, t = b.w, b.t
+    N = int(b.c.seq_lens[0].item())
+    summ = b.c.summaries.cpu().numpy()
+    trees = []
+    for s in range(w.batch):
+        per = []
+        for h in range(w.n_kv_heads):
+            lv = []
+            for level in range(1, w.n_levels + 1):
+                n = N // w.branching ** level
+                off = b.sizes.level_offset[level - 1]
+                rows = b.sizes.level_nodes[level - 1]
+                base = off + (s * w.n_kv_heads + h) * rows * w.head_dim
+                lv.append(summ[base:base + n * w.head_dim].reshape(n, w.head_dim))
+            per.append(lv)
+        trees.append(per)
+    Kh, Vh = b.K_host, b.V_host
+    if w.append_per_step:
+        for i, (k, v) in enumerate(b.kv_host):
+            Kh[:, :, w.n_tokens + i] = k[:, :, 0]
+            Vh[:, :, w.n_tokens + i] = v[:, :, 0]
+    Kf = [[W.as_f32(w, Kh[s, h, :N]) for h in range(w.n_kv_heads)] for s in range(w.batch)]
+    Vf = [[W.as_f32(w, Vh[s, h, :N]) for h in range(w.n_kv_heads)] for s in range(w.batch)]
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < budget_s and done < b.q_host.shape[0]:
+            q = b.q_host[done]
+            for s in range(w.batch):
+                for hq in range(w.n_q_heads):
+                    kv = hq // w.group
+                    r = O.route(q[s, 0, hq], trees[s][kv], N, w.branching, w.top_p)
+                    I = O.index_set(r.selected[0], N, w.branching)
+                    O.attend(q[s, 0, hq], Kf[s][kv], Vf[s][kv], I)
+            done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(done * w.batch / el, 3), "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} decode queries x {w.batch} sequence(s) x {w.n_q_heads} heads (route + exact "
+                      f"attention per head, NumPy fp64, one BLAS thread) against the GPU-built tree at "
+                      f"N={N}, {el:.1f}s"}
+
+
+# ----------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
+              f"multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    w = W.get_workload(args.workload)
+    steps = args.steps if args.steps is not None else w.steps
+    warm = args.warmup
+    log(f"[bench] workload {w.name}: {w.description}; steps {steps}, warmup {warm}")
+    b = Bench(w, steps, warm)
+
+    # ---- warmup ----
+    for i in range(warm):
+        b.step(i)
+    torch.cuda.synchronize()
+    if Z.read_device_status(b.c.ws):
+        raise RuntimeError("device status raised during warmup")
+    snap = b.snapshot()
+
+    # ---- timed pass: product calls only, one kernel family timed with events ----
+    Z.profile_start(args.kernel)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warm, warm + steps):
+        b.step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms, k_launch, k_drop = Z.profile_collect()
+    Z.profile_start(None)
+    out_timed = b.out.clone()
+    status = Z.read_device_status(b.c.ws)
+    log(f"[bench] timed {steps} steps in {wall * 1e3:.2f} ms; {args.kernel}: {k_launch} launches, "
+        f"{k_ms / max(1, k_launch) * 1e3:.2f} us avg")
+
+    # ---- replay for byte accounting (deterministic: identical routing) ----
+    b.restore(snap)
+    L = w.n_levels
+    rows = w.batch
+    stats = torch.zeros((w.batch, 1, w.n_q_heads, L, 2), dtype=torch.int32, device="cuda")
+    lsel = torch.zeros(max(1, b.sizes.level_sel_bytes // 4), dtype=torch.int32, device="cuda")
+    totals = {}
+    kept1 = []
+    for i in range(warm, warm + steps):
+        b.step(i, level_stats=stats, level_sel=lsel)
+        N = int(b.c.seq_lens[0].item())
+        by = step_bytes(b, stats.cpu().numpy(), lsel.cpu().numpy(), b.sel.cpu().numpy(), b.nsel.cpu().numpy(), N)
+        for k, v in by.items():
+            totals[k] = totals.get(k, 0) + v
+        kept1.append(b.nsel.cpu().numpy().reshape(-1))
+        if i == warm:
+            st0 = stats.cpu().numpy().reshape(w.n_q_heads, L, 2)
+    torch.cuda.synchronize()
+    replay_same = bool(torch.equal(out_timed, b.out))
+    step_total = sum(totals.values())
+
+    # ---- attend-only and dense on the final cache, same queries ----
+    qs = [b.q[i] for i in range(warm, warm + steps)]
+    c = b.c
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for q in qs:
+        Z.attend(b.geom, q, None, c.K, c.V, c.summaries, c.seq_lens, w.top_p, b.sel, b.nsel, b.out, b.lse, c.ws)
+    torch.cuda.synchronize()
+    zha_ms = (time.perf_counter() - t0) * 1e3 / steps
+    od = torch.zeros_like(b.out)
+    ld = torch.zeros_like(b.lse)
+    ndense = min(steps, 64)
+    for q in qs[:4]:
+        Z.dense_attend(b.geom, q, None, c.K, c.V, c.seq_lens, od, ld, c.ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for q in qs[:ndense]:
+        Z.dense_attend(b.geom, q, None, c.K, c.V, c.seq_lens, od, ld, c.ws)
+    torch.cuda.synchronize()
+    dense_ms = (time.perf_counter() - t0) * 1e3 / ndense
+    Nf = int(c.seq_lens[0].item())
+    skv = 2 if w.kv_dtype == "bf16" else 4
+    dense_bytes = w.batch * w.n_kv_heads * Nf * 2 * w.head_dim * skv
+    # dense vs zha outputs for the last query: sparse attention is an approximation
+    Z.attend(b.geom, qs[-1], None, c.K, c.V, c.summaries, c.seq_lens, w.top_p, b.sel, b.nsel, b.out, b.lse, c.ws)
+    Z.dense_attend(b.geom, qs[-1], None, c.K, c.V, c.seq_lens, od, ld, c.ws)
+    torch.cuda.synchronize()
+    approx_err = float((b.out - od).abs().max().item())
+
+    # ---- cold run: flush MALL / L2 between steps, time each step with events ----
+    cold_qps = None
+    if not args.no_cold:
+        b.restore(snap)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for j, i in enumerate(range(warm, warm + steps)):
+            flush.fill_(j & 0xff)
+            ev[j][0].record()
+            b.step(i)
+            ev[j][1].record()
+        torch.cuda.synchronize()
+        cold_ms = sum(a.elapsed_time(z) for a, z in ev) / steps
+        cold_qps = w.batch / (cold_ms / 1e3)
+        del flush
+
+    cpu = None
+    if not args.no_cpu:
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f}s")
+        cpu = cpu_baseline(b, args.cpu_seconds)
+
+    ms_step = wall * 1e3 / steps
+    kb = sum(v for k, v in totals.items() if k == args.kernel or k.split("@")[0] == args.kernel)
+    k_avg_s = (k_ms / 1e3) / max(1, k_launch)
+    achieved = (kb / steps) / k_avg_s if k_avg_s > 0 else 0.0
+    res = {
+        "metric": METRIC,
+        "value": round(w.batch * steps / wall, 2),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_tokens": w.n_tokens, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "branching": w.branching,
+                   "levels": w.n_levels, "top_p": w.top_p, "kv_cache": w.kv_dtype,
+                   "append_per_step": w.append_per_step},
+        "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 2), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
+                     "kernel": args.kernel, "bytes_per_launch": int(kb / steps),
+                     "avg_launch_us": round(k_avg_s * 1e6, 3), "launches": k_launch},
+        "cpu_baseline": cpu,
+        "step_hbm_frac": round((step_total / steps) / (ms_step / 1e3) / HBM_PEAK, 4),
+        "step_bytes": int(step_total / steps),
+        "bytes_by_kernel": {k: int(v / steps) for k, v in sorted(totals.items())},
+        "zha_attend_ms": round(zha_ms, 5),
+        "dense_ms": round(dense_ms, 5),
+        "dense_hbm_frac": round(dense_bytes / (dense_ms / 1e3) / HBM_PEAK, 4),
+        "speedup_vs_dense": round(dense_ms / zha_ms, 3),
+        "cold_queries_per_s": round(cold_qps, 2) if cold_qps else None,
+        "keys_attended_frac": round(float(totals.get("attend", 0) / steps /
+                                          (w.batch * w.n_kv_heads * Nf * 2 * w.head_dim * skv)), 6),
+        "kept_leaves_mean": round(float(np.mean(np.concatenate(kept1))), 2),
+        "level_counts_first_step": st0.tolist(),
+        "max_abs_sparse_vs_dense": round(approx_err, 5),
+        "replay_identical": replay_same,
+        "device_status": status,
+        "tree_build_ms": round(b.build_s * 1e3, 3),
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,7 +23,8 @@ ZHA_KV_BF16, ZHA_KV_F32 = 0, 1
 ZHA_MAX_LEVELS = 8
 
 EXPORTED = ("zha_query_sizes", "zha_build_tree", "zha_append", "zha_route", "zha_sparse_attend", "zha_attend",
-            "zha_dense_attend", "zha_read_device_status", "zha_status_string", "zha_last_error")
+            "zha_dense_attend", "zha_read_device_status", "zha_profile_start", "zha_profile_collect",
+            "zha_status_string", "zha_last_error")
 
 
 class Geom(ctypes.Structure):
@@ -72,6 +73,11 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = args
             f.restype = ctypes.c_int32
+        L.zha_profile_start.argtypes = [ctypes.c_char_p]
+        L.zha_profile_start.restype = ctypes.c_int32
+        L.zha_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_int64)]
+        L.zha_profile_collect.restype = ctypes.c_int32
         L.zha_status_string.argtypes = [ctypes.c_int32]
         L.zha_status_string.restype = ctypes.c_char_p
         L.zha_last_error.argtypes = []
@@ -165,6 +171,18 @@ def read_device_status(ws, clear: bool = False, stream=None) -> int:
     _check(lib().zha_read_device_status(_ptr(ws), _stream(stream), ctypes.byref(v), 1 if clear else 0),
            "zha_read_device_status")
     return int(v.value)
+
+
+def profile_start(label: Optional[str]):
+    """Time every launch of kernel `label` ("name" or "name@level") with HIP events; None stops."""
+    _check(lib().zha_profile_start(label.encode() if label else None), "zha_profile_start")
+
+
+def profile_collect():
+    """(summed kernel ms, launches timed, launches dropped) since the last collect."""
+    ms, n, d = ctypes.c_double(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib().zha_profile_collect(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(d)), "zha_profile_collect")
+    return ms.value, int(n.value), int(d.value)
 
 
 def level_sel_view(level_sel, sizes: Sizes, geom: Geom, rows: int, level: int):

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void build_level_kernel(BuildParams p) {
         const int bh = static_cast<int>(wv / p.slots);
         const int64_t k = wv % p.slots;
         const int s = bh / p.Hkv, h = bh % p.Hkv;
-        const int64_t len = min<int64_t>(max<int64_t>(p.seq_lens[s], 0), p.cap);
+        const int64_t len = imin(imax(p.seq_lens[s], 0), p.cap);
         int64_t i, hi;
         if (p.mode == kModeBuild) {
             i = k;
@@ -208,22 +208,23 @@ __global__ __launch_bounds__(1024) void append_fused_kernel(FusedParams p) {
 // launchers
 // ----------------------------------------------------------------------------
 template <typename CT, int B, int D>
-static hipError_t launch_level_t(const BuildParams& bp, int64_t total_waves, hipStream_t st) {
+static hipError_t launch_level_t(const BuildParams& bp, int64_t total_waves, int level, hipStream_t st) {
     const int64_t blocks = std::min<int64_t>((total_waves + 3) / 4, 16384);
     if (blocks <= 0) return hipSuccess;
+    ProfScope ps("build_level", level, st);
     hipLaunchKernelGGL((build_level_kernel<CT, B, D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, bp);
     return hipGetLastError();
 }
 
 template <typename CT, int D>
-static hipError_t dispatch_b(int b, const BuildParams& bp, int64_t tw, hipStream_t st) {
+static hipError_t dispatch_b(int b, const BuildParams& bp, int64_t tw, int lv, hipStream_t st) {
     switch (b) {
-        case 2: return launch_level_t<CT, 2, D>(bp, tw, st);
-        case 4: return launch_level_t<CT, 4, D>(bp, tw, st);
-        case 8: return launch_level_t<CT, 8, D>(bp, tw, st);
-        case 16: return launch_level_t<CT, 16, D>(bp, tw, st);
-        case 32: return launch_level_t<CT, 32, D>(bp, tw, st);
-        case 64: return launch_level_t<CT, 64, D>(bp, tw, st);
+        case 2: return launch_level_t<CT, 2, D>(bp, tw, lv, st);
+        case 4: return launch_level_t<CT, 4, D>(bp, tw, lv, st);
+        case 8: return launch_level_t<CT, 8, D>(bp, tw, lv, st);
+        case 16: return launch_level_t<CT, 16, D>(bp, tw, lv, st);
+        case 32: return launch_level_t<CT, 32, D>(bp, tw, lv, st);
+        case 64: return launch_level_t<CT, 64, D>(bp, tw, lv, st);
     }
     return hipErrorInvalidValue;
 }
@@ -254,9 +255,9 @@ hipError_t launch_build_level(const Geo& g, int level, const void* K, const floa
     const int64_t tw = static_cast<int64_t>(bp.BH) * bp.slots;
     const bool f32 = (level > 1) || g.kv_dtype == ZHA_KV_F32;
     if (g.D == 128) {
-        return f32 ? dispatch_b<float, 128>(g.b, bp, tw, st) : dispatch_b<uint16_t, 128>(g.b, bp, tw, st);
+        return f32 ? dispatch_b<float, 128>(g.b, bp, tw, level, st) : dispatch_b<uint16_t, 128>(g.b, bp, tw, level, st);
     }
-    return f32 ? dispatch_b<float, 64>(g.b, bp, tw, st) : dispatch_b<uint16_t, 64>(g.b, bp, tw, st);
+    return f32 ? dispatch_b<float, 64>(g.b, bp, tw, level, st) : dispatch_b<uint16_t, 64>(g.b, bp, tw, level, st);
 }
 
 hipError_t launch_append_rows(const Geo& g, void* K, void* V, const void* k_new, const void* v_new, int t_new,
@@ -274,11 +275,13 @@ hipError_t launch_append_rows(const Geo& g, void* K, void* V, const void* k_new,
     cp.t_new = t_new;
     const int64_t chunks = (cp.row_bytes * t_new / 16 + 255) / 256;
     const unsigned gx = static_cast<unsigned>(std::min<int64_t>(std::max<int64_t>(chunks, 1), 1024));
+    ProfScope ps("append_rows", 0, st);
     hipLaunchKernelGGL(append_rows_kernel, dim3(gx, g.B * g.Hkv), dim3(256), 0, st, cp);
     return hipGetLastError();
 }
 
 hipError_t launch_advance_seq(const Geo& g, int32_t* seq_lens, int t_new, hipStream_t st) {
+    ProfScope ps("advance_seq", 0, st);
     hipLaunchKernelGGL(advance_seq_kernel, dim3((g.B + 255) / 256), dim3(256), 0, st, seq_lens, g.B, t_new, g.cap);
     return hipGetLastError();
 }
@@ -286,6 +289,7 @@ hipError_t launch_advance_seq(const Geo& g, int32_t* seq_lens, int t_new, hipStr
 template <typename KT, int B, int D>
 static hipError_t launch_fused_t(const FusedParams& fp, int B_, int Hkv, hipStream_t st) {
     const int waves = std::min(Hkv, 16);
+    ProfScope ps("append_fused", 0, st);
     hipLaunchKernelGGL((append_fused_kernel<KT, B, D>), dim3(B_), dim3(waves * kWave), 0, st, fp);
     return hipGetLastError();
 }

@@ -449,6 +449,7 @@ __global__ __launch_bounds__(kCutThreads) void route_cut_kernel(CutParams p) {
 // ----------------------------------------------------------------------------
 template <int D, int G>
 static void launch_score_t(dim3 grid, const ScoreParams& sp, hipStream_t st) {
+    ProfScope ps("route_score", sp.li + 1, st);
     hipLaunchKernelGGL((route_score_kernel<D, G>), grid, dim3(256), 0, st, sp);
 }
 
@@ -542,7 +543,10 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
         cp.G = g.G;
         cp.T = a.ri.T;
         cp.top_p = a.top_p;
-        hipLaunchKernelGGL(route_cut_kernel, dim3(g.Hq, a.rows), dim3(kCutThreads), 0, st, cp);
+        {
+            ProfScope ps("route_cut", li + 1, st);
+            hipLaunchKernelGGL(route_cut_kernel, dim3(g.Hq, a.rows), dim3(kCutThreads), 0, st, cp);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -4,7 +4,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
+#include <vector>
 
 #include "zha_internal.h"
 
@@ -134,7 +137,40 @@ zha_status check_rows(const Geo& g, int32_t t, int* rows) {
     return ZHA_OK;
 }
 
+// ---- opt-in kernel timing ----
+struct Profiler {
+    std::string target;          // empty: inactive
+    std::vector<hipEvent_t> ev;  // pairs (start, stop)
+    int used = 0;
+    int64_t dropped = 0;
+};
+Profiler g_prof;
+constexpr int kProfSlots = 8192;
+
+bool prof_matches(const char* label, int level) {
+    if (g_prof.target.empty()) return false;
+    const std::string& t = g_prof.target;
+    const size_t at = t.find('@');
+    if (at == std::string::npos) return t == label;
+    return t.compare(0, at, label) == 0 && std::strlen(label) == at && std::atoi(t.c_str() + at + 1) == level;
+}
+
 }  // namespace
+
+ProfScope::ProfScope(const char* label, int level, hipStream_t st) : st_(st) {
+    if (!prof_matches(label, level)) return;
+    if (g_prof.used >= kProfSlots) {
+        ++g_prof.dropped;
+        return;
+    }
+    slot_ = g_prof.used++;
+    (void)hipEventRecord(g_prof.ev[2 * slot_], st_);
+}
+
+ProfScope::~ProfScope() {
+    if (slot_ >= 0) (void)hipEventRecord(g_prof.ev[2 * slot_ + 1], st_);
+}
+
 }  // namespace zha
 
 using namespace zha;
@@ -358,5 +394,45 @@ const char* zha_status_string(zha_status s) {
 }
 
 const char* zha_last_error(void) { return g_last_error.c_str(); }
+
+zha_status zha_profile_start(const char* label) {
+    if (!label || !*label) {
+        g_prof.target.clear();
+        return ZHA_OK;
+    }
+    if (g_prof.ev.empty()) {
+        g_prof.ev.resize(2 * kProfSlots);
+        for (auto& e : g_prof.ev) {
+            const hipError_t r = hipEventCreate(&e);
+            if (r != hipSuccess) {
+                g_prof.ev.clear();
+                return hip_fail(r, "profile event pool");
+            }
+        }
+    }
+    g_prof.target = label;
+    g_prof.used = 0;
+    g_prof.dropped = 0;
+    return ZHA_OK;
+}
+
+zha_status zha_profile_collect(double* total_ms, int64_t* launches, int64_t* dropped) {
+    if (!total_ms || !launches || !dropped) return fail(ZHA_ERR_NULL, "outputs are required");
+    double tot = 0.0;
+    for (int i = 0; i < g_prof.used; ++i) {
+        hipError_t r = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+        if (r != hipSuccess) return hip_fail(r, "profile event wait");
+        float ms = 0.f;
+        r = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+        if (r != hipSuccess) return hip_fail(r, "profile event time");
+        tot += ms;
+    }
+    *total_ms = tot;
+    *launches = g_prof.used;
+    *dropped = g_prof.dropped;
+    g_prof.used = 0;
+    g_prof.dropped = 0;
+    return ZHA_OK;
+}
 
 }  // extern "C"

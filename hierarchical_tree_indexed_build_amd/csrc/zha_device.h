@@ -8,6 +8,10 @@
 
 namespace zha {
 
+// Integer min / max written out, so 64-bit operands stay in integer registers.
+__device__ __forceinline__ int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -69,6 +73,13 @@ __device__ __forceinline__ void load_few(const float* __restrict__ p, float (&x)
     }
 }
 
+// Load N consecutive elements, N in {1, 2, 4} or a multiple of 8 (bf16) / 4 (fp32).
+template <int N, typename T>
+__device__ __forceinline__ void load_vec(const T* __restrict__ p, float (&x)[N]) {
+    if constexpr (N <= 2 || (N == 4 && sizeof(T) == 2)) load_few<N>(p, x);
+    else load_row<N>(p, x);
+}
+
 // Sum / max over aligned groups of W lanes (W a power of two <= 64). Every lane
 // of a group ends with the group's result; the combination order is fixed.
 template <int W>
@@ -83,6 +94,33 @@ __device__ __forceinline__ float group_max(float v) {
     for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
     return v;
 }
+// Sum over aligned groups of W <= 16 lanes with DPP lane permutes (one VALU op
+// per step: swap within pairs, within quads, mirror within 8, mirror within 16).
+// Every lane of a group ends with the group's sum; the order is fixed.
+template <int W>
+__device__ __forceinline__ float dpp_group_sum(float v) {
+    static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16, "DPP groups of 1..16 lanes");
+    if constexpr (W >= 2) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    if constexpr (W >= 4) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    if constexpr (W >= 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    if constexpr (W >= 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
+// Sum over aligned groups of any W <= 64 lanes: DPP inside rows of 16, then
+// cross-row exchanges.
+template <int W>
+__device__ __forceinline__ float fast_group_sum(float v) {
+    if constexpr (W <= 16) {
+        return dpp_group_sum<W>(v);
+    } else {
+        v = dpp_group_sum<16>(v);
+#pragma unroll
+        for (int o = 16; o < W; o <<= 1) v += __shfl_xor(v, o, 64);
+        return v;
+    }
+}
+
 // Reduce over lanes that differ only in the bits of [LO, 64): sums across the
 // lane index's high part, keeping the low part (lanes with equal lane % LO).
 template <int LO>

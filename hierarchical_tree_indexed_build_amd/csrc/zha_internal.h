@@ -63,6 +63,20 @@ __host__ __device__ inline int row_visible(const RowInfo& ri, int row) {
     return pos + 1;
 }
 
+// Opt-in kernel timing (zha_profile_start): brackets a launch with two events
+// when `label` (optionally "label@level") matches the active target.
+class ProfScope {
+   public:
+    ProfScope(const char* label, int level, hipStream_t st);
+    ~ProfScope();
+    ProfScope(const ProfScope&) = delete;
+    ProfScope& operator=(const ProfScope&) = delete;
+
+   private:
+    int slot_ = -1;
+    hipStream_t st_;
+};
+
 // Launchers (defined in the kernel translation units). All return hipError_t.
 hipError_t launch_build_level(const Geo& g, int level, const void* K, const float* ref_q, float* summaries,
                               const int32_t* seq_lens, int mode, int t_new, hipStream_t st);

@@ -176,6 +176,23 @@ ZHA_API zha_status zha_dense_attend(const zha_geom* geom, const float* q, int32_
  * word of workspace `ws` into *out (ZHA_DEV_* bits). The only synchronising call. */
 ZHA_API zha_status zha_read_device_status(void* ws, void* stream, uint32_t* out, int32_t clear);
 
+/* Kernel timing for benchmarks, the per-kernel terms of the latency model
+ * ("Subquadratic Attention with a Hierarchical Tree-Structured Indexer",
+ * §Latency Scaling, eqs. (3)-(4)). While active, every launch whose label
+ * matches `label` is bracketed by two HIP events on its own stream. Labels:
+ * build_level@l, append_fused, append_rows, advance_seq, route_score@l,
+ * route_cut@l, attn_union, attend, attend_combine; a label without "@l"
+ * matches every level. NULL stops recording. At most 8192 launches are kept
+ * (later ones are counted as dropped). Host-side state shared by all threads:
+ * for single-threaded benchmarks only. Creating the event pool is the only
+ * allocation; it happens here, never in the timed calls. */
+ZHA_API zha_status zha_profile_start(const char* label);
+
+/* Wait for the recorded events, return the summed kernel time in milliseconds,
+ * the number of launches timed and the number dropped, then clear the record
+ * (recording stays active). */
+ZHA_API zha_status zha_profile_collect(double* total_ms, int64_t* launches, int64_t* dropped);
+
 /* Static text for a status code. */
 ZHA_API const char* zha_status_string(zha_status s);
 

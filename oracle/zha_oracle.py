@@ -225,7 +225,7 @@ def level_candidates(level: int, parents: Optional[np.ndarray], n_visible: int, 
 
 def score_nodes(q: np.ndarray, X: np.ndarray, ids: np.ndarray, scale: float):
     """(fp32-rounded scores, exact fp64 scores) of nodes ``ids`` of one level (R-2)."""
-    s64 = scale * (np.asarray(X, dtype=F64)[ids] @ np.asarray(q, dtype=F64))
+    s64 = scale * (np.asarray(X[ids], dtype=F64) @ np.asarray(q, dtype=F64))
     return s64.astype(F32).astype(F64), s64
 
 
@@ -278,8 +278,8 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray, scale: 
     """Exact softmax attention of q over tokens ``idx``: returns (o (d,), lse)."""
     scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
     idx = np.asarray(idx, dtype=np.int64)
-    k = np.asarray(K, dtype=F64)[idx]
-    v = np.asarray(V, dtype=F64)[idx]
+    k = np.asarray(K[idx], dtype=F64)
+    v = np.asarray(V[idx], dtype=F64)
     z = scale * (k @ np.asarray(q, dtype=F64))
     mx = z.max()
     e = np.exp(z - mx)

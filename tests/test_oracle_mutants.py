@@ -32,8 +32,8 @@ MUTANTS = {
                             "return [-(-n_tokens // (b ** l)) for l in range(1, n_levels + 1)]"),
     "no-sink": ("toks[0] = True", "toks[0] = toks[0]"),
     "cur-chunk-off": ("toks[b * ((n_visible - 1) // b):n_visible] = True", "toks[b * (n_visible // b):n_visible] = True"),
-    "score-no-scale": ("s64 = scale * (np.asarray(X, dtype=F64)[ids] @ np.asarray(q, dtype=F64))",
-                       "s64 = (np.asarray(X, dtype=F64)[ids] @ np.asarray(q, dtype=F64))"),
+    "score-no-scale": ("s64 = scale * (np.asarray(X[ids], dtype=F64) @ np.asarray(q, dtype=F64))",
+                       "s64 = (np.asarray(X[ids], dtype=F64) @ np.asarray(q, dtype=F64))"),
     "attend-no-scale": ("z = scale * (k @ np.asarray(q, dtype=F64))", "z = (k @ np.asarray(q, dtype=F64))"),
     "attend-unnormalised": ("return (e @ v) / l, mx + math.log(l)", "return (e @ v) / e.max(), mx + math.log(l)"),
     "lse-no-max": ("return (e @ v) / l, mx + math.log(l)", "return (e @ v) / l, math.log(l)"),
