@@ -42,7 +42,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="decode1m", choices=["decode1m", "gqa128k", "decode16m"])
-    ap.add_argument("--kernel", default="route_score@1", help="kernel label timed live for the roofline")
+    ap.add_argument("--kernel", default="attend", help="kernel label timed live for the roofline")
+    ap.add_argument("--timed-only", action="store_true",
+                    help="run the warmup and timed steps only (for profiler runs), print a short line")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -261,6 +263,11 @@ def main():
     Z.profile_start(None)
     out_timed = b.out.clone()
     status = Z.read_device_status(b.c.ws)
+    if args.timed_only:
+        print(json.dumps({"workload": w.name, "steps": steps, "warmup": warm, "ms_per_step": wall * 1e3 / steps,
+                          "kernel": args.kernel, "kernel_avg_us": k_ms / max(1, k_launch) * 1e3,
+                          "launches": k_launch, "device_status": status}), flush=True)
+        return
     log(f"[bench] timed {steps} steps in {wall * 1e3:.2f} ms; {args.kernel}: {k_launch} launches, "
         f"{k_ms / max(1, k_launch) * 1e3:.2f} us avg")
 

@@ -60,6 +60,8 @@ zha_status make_geo(const zha_geom* in, Geo* g) {
     g->G = G;
     g->D = in->head_dim;
     g->b = in->branching;
+    g->lb = 0;
+    while ((1 << g->lb) < g->b) ++g->lb;
     g->L = in->n_levels;
     g->kv_dtype = in->kv_dtype;
     g->cap = in->capacity;
@@ -98,19 +100,16 @@ WsLayout layout(const Geo& g, int rows) {
     };
     const size_t R = static_cast<size_t>(rows);
     L.status = take(256);
-    L.grp_ctr = take(R * g.Hkv * g.L * 4);
     L.scores = take(R * g.Hq * g.nodes_total * 4);
     L.kept = take(R * g.Hq * g.nodes_total * 4);
     L.kept_cnt = take(R * g.Hq * g.L * 4);
     int64_t bw = 0;
     for (int l = 0; l < ZHA_MAX_LEVELS; ++l) {
         L.bm_off[l] = static_cast<size_t>(bw);
-        bw += (g.nodes[l] + 31) / 32;
+        bw += (l < g.L) ? (g.nodes[l] + 32) / 32 : 0;     // one spare bit for index nodes[l]
     }
     L.bm_words_total = bw;
     L.bitmap = take(R * g.Hq * static_cast<size_t>(bw) * 4);
-    L.ulist = take(R * g.Hkv * g.nodes_total * 4);
-    L.ucnt = take(R * g.Hkv * g.L * 4);
     L.abm_words = g.nodes[0] / 32 + 1;
     L.abm = take(R * g.Hq * static_cast<size_t>(L.abm_words) * 4);
     L.aitems = take(R * g.Hkv * static_cast<size_t>(g.nodes[0] + 2) * 8);

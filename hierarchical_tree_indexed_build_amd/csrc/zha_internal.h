@@ -19,7 +19,7 @@ inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a
 
 // Geometry after validation, with everything the kernels need precomputed.
 struct Geo {
-    int B, Hq, Hkv, G, D, b, L, kv_dtype;
+    int B, Hq, Hkv, G, D, b, lb, L, kv_dtype;   // lb = log2(b)
     int64_t cap;                       // tokens per sequence
     float scale;
     int64_t nodes[ZHA_MAX_LEVELS];     // node slots per (batch, kv) per level
@@ -31,16 +31,13 @@ struct Geo {
 
 // Byte layout of the workspace for `rows` query rows.
 struct WsLayout {
-    size_t status;        // uint32 status word + group counters header
-    size_t grp_ctr;       // uint32 [rows, Hkv, L]   last-of-group counters (cut kernels)
+    size_t status;        // uint32 device status word (256-byte header)
     size_t scores;        // float  [rows, Hq, nodes_total] dense-by-node scores, level offsets = sel_off
     size_t kept;          // int32  [rows, Hq, nodes_total] kept lists per level (level 1 unused)
     size_t kept_cnt;      // int32  [rows, Hq, L]
-    size_t bitmap;        // uint32 [rows, Hq, bm_words_total] kept bitmaps per level
+    size_t bitmap;        // uint32 [rows, Hq, bm_words_total] kept bitmaps per level (a spare bit for index nodes[l])
     size_t bm_off[ZHA_MAX_LEVELS];    // word offset of each level inside a row-head bitmap
     int64_t bm_words_total;
-    size_t ulist;         // int32  [rows, Hkv, nodes_total] union of kept nodes per level (parents for the level below)
-    size_t ucnt;          // int32  [rows, Hkv, L]
     size_t abm;           // uint32 [rows, Hq, abm_words] attention head bitmaps (leaf chunks + current chunk)
     int64_t abm_words;
     size_t aitems;        // int2   [rows, Hkv, nodes[0] + 2] attention items (block, head mask)
