@@ -14,6 +14,7 @@ Usage: python bench.py [--gpus 1] [--steps 256] [--warmup 8] [--workload decode1
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -29,6 +30,8 @@ import hierarchical_tree_indexed_build_amd as Z  # noqa: E402
 import workloads as W  # noqa: E402
 
 HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode1m_attend_traffic.json")
+KERNEL_SOURCES = {"attend": "attend.hip", "route_score": "route.hip", "route_cut": "route.hip"}
 METRIC = "ZHA decode queries/sec at 1M-token KV; % HBM roofline; speedup vs dense"
 
 
@@ -43,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="decode1m", choices=["decode1m", "gqa128k", "decode16m"])
     ap.add_argument("--kernel", default="attend", help="kernel label timed live for the roofline")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="copy a buffer of this many MiB once before the timed steps (calibrates byte counters)")
     ap.add_argument("--timed-only", action="store_true",
                     help="run the warmup and timed steps only (for profiler runs), print a short line")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -229,6 +234,24 @@ def cpu_baseline(b: Bench, budget_s: float):
                       f"N={N}, {el:.1f}s"}
 
 
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter runs (FETCH_SIZE, WRITE_SIZE,
+    each scaled by its reading for a copy of known size), or None when no counters were taken
+    for this workload or the kernel's source changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    name = kernel.split("@")[0]
+    src = os.path.join(ROOT, "hierarchical_tree_indexed_build_amd", "csrc", KERNEL_SOURCES.get(name, ""))
+    if rec.get("kernel") != kernel or rec.get("workload") != workload or not os.path.isfile(src):
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec.get("source_sha256"):
+            return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 # ----------------------------------------------------------------------------
 def main():
     args = parse()
@@ -250,6 +273,14 @@ def main():
     if Z.read_device_status(b.c.ws):
         raise RuntimeError("device status raised during warmup")
     snap = b.snapshot()
+
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- timed pass: product calls only, one kernel family timed with events ----
     Z.profile_start(args.kernel)
@@ -364,7 +395,7 @@ def main():
                    "levels": w.n_levels, "top_p": w.top_p, "kv_cache": w.kv_dtype,
                    "append_per_step": w.append_per_step},
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 2), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK, 4), "traffic": measured_traffic(args.kernel, w.name),
                      "kernel": args.kernel, "bytes_per_launch": int(kb / steps),
                      "avg_launch_us": round(k_avg_s * 1e6, 3), "launches": k_launch},
         "cpu_baseline": cpu,

@@ -6,16 +6,18 @@
 // "Zyphra Hierarchical Attention: The End of Quadratic Attention?", §How the
 // tree is built and searched). The dense baseline attends [0, N).
 //
-// Kernels:
-//  * attn_union_kernel  - per (row, kv head): OR the g query heads' kept leaf
-//    chunks into one ascending list of (chunk, head mask) items, adding chunk
-//    0 (sink) and the current chunk; K/V of a chunk are then read once for the
-//    whole GQA group.
+// The kept leaf chunks arrive as one bitmap per query head: the level-1 cut
+// writes them in zha_attend, attn_bitmap_kernel builds them from id lists for a
+// standalone sparse call. Kernels:
+//  * attn_items_kernel  - per (row, kv head): OR the g query heads' bitmaps,
+//    add chunk 0 (sink) and the current chunk, and compact them into one
+//    ascending list of (chunk, head mask) items; K/V of a chunk are then read
+//    once for the whole GQA group.
 //  * attend_kernel      - split-K flash decoding. Workgroup = (split, row, kv
-//    head); each wave streams 16-token groups of its split with an online
-//    softmax for all g heads (scores: lanes own a slice of d, reduced within
-//    the token's lanes; values: lanes own d/64 dimensions); waves merge in LDS
-//    and write one (max, sum, acc[d]) partial per head and split.
+//    head); each wave streams 16-token groups of its split through a two-stage
+//    register pipeline with an online softmax for all g heads; lanes own a
+//    slice of d; waves merge in LDS and write one (max, sum, acc[d]) partial
+//    per head and split.
 //  * attend_combine_kernel - per (row, head): LSE merge of the splits.
 #include <algorithm>
 
@@ -29,150 +31,203 @@ constexpr uint32_t kAllHeads = 1u << 30;     // item flag: every head attends th
 __device__ __forceinline__ int visible_clamped(const RowInfo& ri, int row, int64_t cap) {
     const int s = row / ri.T;
     int n = row_visible(ri, row);
-    const int lim = static_cast<int>(min<int64_t>(ri.seq_lens[s], cap));
+    const int lim = static_cast<int>(imin(ri.seq_lens[s], cap));
     n = n < 0 ? 0 : n;
     return n > lim ? lim : n;
 }
 
-__device__ __forceinline__ uint32_t ld_relaxed_a(const uint32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ----------------------------------------------------------------------------
-// union of the group's kept leaf chunks
-// One workgroup per (row, kv head). Leaf ids are walked in chunks of
-// kUnionChunk ids: each head's ascending list is cut at the chunk end by a
-// binary search, bits are set in LDS, and the chunk's words are compacted with
-// a block scan. No global atomics, no device-scope fences.
+// kept leaf chunks -> per-head bitmaps (standalone sparse calls only; the cut
+// of zha_attend writes these bitmaps itself)
 // ----------------------------------------------------------------------------
-struct UnionParams {
-    RowInfo ri;
+struct BitmapParams {
     const int32_t* sel_blocks;
     const int32_t* n_sel;
     int sel_cap;
+    uint32_t* bm;              // level-1 bitmaps, (row*Hq + hq)*stride
+    int64_t stride;            // words per row-head
+    int64_t words;             // words of the level-1 bitmap
+};
+
+__global__ __launch_bounds__(256) void attn_bitmap_kernel(BitmapParams p) {
+    const int64_t rh = blockIdx.x;
+    uint32_t* bm = p.bm + rh * p.stride;
+    for (int64_t w = threadIdx.x; w < p.words; w += blockDim.x) bm[w] = 0u;
+    __threadfence_block();
+    __syncthreads();
+    const int n = max(0, min(p.n_sel[rh], p.sel_cap));
+    const int32_t* lst = p.sel_blocks + rh * p.sel_cap;
+    for (int j = threadIdx.x; j < n; j += blockDim.x) {
+        const int64_t node = lst[j];
+        if (node >= 0 && (node >> 5) < p.words)
+            __hip_atomic_fetch_or(bm + (node >> 5), 1u << (node & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// the group's attention items
+// One workgroup per (row, kv head): OR the g heads' level-1 bitmaps, add the
+// sink chunk and the current chunk, and compact the set bits in ascending
+// chunk order into (chunk, head mask) items with a block scan. Each thread
+// owns a contiguous run of bitmap words.
+// ----------------------------------------------------------------------------
+struct ItemsParams {
+    RowInfo ri;
+    const uint32_t* bm;        // level-1 bitmaps, (row*Hq + hq)*stride
+    int64_t stride;
     int2* items;               // [rows, Hkv, item_stride]
     int64_t item_stride;
     int32_t* acnt;             // [rows, Hkv]
     int64_t cap;
-    int b, Hq, Hkv, G;
+    int lb, Hq, Hkv;
 };
 
-constexpr int kUnionThreads = 1024;
-constexpr int kUnionWords = 512;                  // bitmap words per head per chunk
-constexpr int64_t kUnionChunk = kUnionWords * 32; // leaf ids per chunk
+constexpr int kItemsThreads = 1024;
 
-__global__ __launch_bounds__(kUnionThreads) void attn_union_kernel(UnionParams p) {
-    __shared__ uint32_t bm[kMaxGroup][kUnionWords];
-    __shared__ int cur_pos[kMaxGroup], end_pos[kMaxGroup];
-    __shared__ uint32_t wsum[kUnionThreads / kWave];
+template <int G>
+__global__ __launch_bounds__(kItemsThreads) void attn_items_kernel(ItemsParams p) {
+    __shared__ uint64_t red[kItemsThreads / kWave];
     const int y = blockIdx.x;
     const int row = y / p.Hkv, kv = y % p.Hkv;
-    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, w = tid >> 6;
     const int N = visible_clamped(p.ri, row, p.cap);
-    if (N <= 0) {
-        if (tid == 0) p.acnt[y] = 0;
-        return;
-    }
-    const int64_t cur = (N - 1) / p.b;
-    const int64_t nblk = cur + 1;
-    const int64_t nc1 = N / p.b;
-    const int64_t rh0 = static_cast<int64_t>(row) * p.Hq + kv * p.G;
-    if (tid < p.G) cur_pos[tid] = 0;
-    int2* items = p.items + static_cast<int64_t>(y) * p.item_stride;
-    uint32_t total = 0;
-    for (int64_t cb = 0; cb < nblk; cb += kUnionChunk) {
-        const int64_t ce = cb + kUnionChunk;
-        for (int i = tid; i < p.G * kUnionWords; i += nt) (&bm[0][0])[i] = 0u;
-        if (tid < p.G) {
-            const int32_t* lst = p.sel_blocks + (rh0 + tid) * p.sel_cap;
-            int lo = cur_pos[tid], hi = max(0, min(p.n_sel[rh0 + tid], p.sel_cap));
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (lst[mid] < ce) lo = mid + 1;
-                else hi = mid;
-            }
-            end_pos[tid] = lo;
-        }
-        __syncthreads();
-        for (int h = 0; h < p.G; ++h) {
-            const int32_t* lst = p.sel_blocks + (rh0 + h) * p.sel_cap;
-            for (int j = cur_pos[h] + tid; j < end_pos[h]; j += nt) {
-                const int64_t node = lst[j];
-                if (node >= cb && node < ce && node < nc1)
-                    atomicOr(&bm[h][(node - cb) >> 5], 1u << (node & 31));
-            }
-        }
-        __syncthreads();
+    const int64_t nc1 = static_cast<int64_t>(N) >> p.lb;                        // complete leaf chunks
+    const int64_t nblk = N > 0 ? ((static_cast<int64_t>(N) - 1) >> p.lb) + 1 : 0;  // chunks incl. the current one
+    const int64_t cur = nblk - 1;
+    const int64_t words = (nblk + 31) >> 5;
+    const uint32_t* bm0 = p.bm + (static_cast<int64_t>(row) * p.Hq + static_cast<int64_t>(kv) * G) * p.stride;
+    // word wd of the union: kept complete chunks of any head, the sink, the current chunk
+    auto word = [&](int64_t wd, uint32_t (&heads)[G]) -> uint32_t {
+        const int64_t base = wd << 5;
+        const uint32_t valid = base >= nc1 ? 0u : (nc1 - base >= 32 ? 0xffffffffu : ((1u << (nc1 - base)) - 1u));
         uint32_t u = 0;
-        const int w = tid;
-        const int64_t wbase = cb + static_cast<int64_t>(w) * 32;
-        if (w < kUnionWords && wbase < nblk) {
-            for (int h = 0; h < p.G; ++h) u |= bm[h][w];
-            if (wbase == 0) u |= 1u;                                         // sink chunk
-            if (cur >= wbase && cur < wbase + 32) u |= 1u << (cur - wbase);  // current chunk
-        }
-        const uint32_t cnt = __popc(u);
-        // block exclusive scan of cnt
-        uint32_t inc = cnt;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t v = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += v;
+        for (int h = 0; h < G; ++h) {
+            heads[h] = bm0[static_cast<int64_t>(h) * p.stride + wd] & valid;
+            u |= heads[h];
         }
-        if (lane == 63) wsum[wave] = inc;
-        __syncthreads();
-        uint32_t before = 0, ctot = 0;
-        for (int i = 0; i < nt / kWave; ++i) {
-            if (i < wave) before += wsum[i];
-            ctot += wsum[i];
-        }
-        uint32_t pos = total + before + inc - cnt;
+        if (wd == 0 && nblk > 0) u |= 1u;
+        if ((cur >> 5) == wd) u |= 1u << (cur & 31);
+        return u;
+    };
+    const int64_t per = (words + nt - 1) / nt;
+    const int64_t w0 = imin(static_cast<int64_t>(tid) * per, words);
+    const int64_t w1 = imin(w0 + per, words);
+    uint32_t heads[G];
+    uint64_t cnt = 0;
+    for (int64_t wd = w0; wd < w1; ++wd) cnt += __popc(word(wd, heads));
+    // block exclusive scan of the counts, in thread order
+    uint64_t inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t lo = __shfl_up(static_cast<uint32_t>(inc), o, 64);
+        const uint32_t hi = __shfl_up(static_cast<uint32_t>(inc >> 32), o, 64);
+        if (lane >= o) inc += (static_cast<uint64_t>(hi) << 32) | lo;
+    }
+    if (lane == 63) red[w] = inc;
+    __syncthreads();
+    uint64_t before = 0, total = 0;
+    for (int i = 0; i < nt / kWave; ++i) {
+        if (i < w) before += red[i];
+        total += red[i];
+    }
+    int2* items = p.items + static_cast<int64_t>(y) * p.item_stride;
+    int64_t pos = static_cast<int64_t>(before + inc - cnt);
+    for (int64_t wd = w0; wd < w1; ++wd) {
+        uint32_t u = word(wd, heads);
         while (u) {
             const int bit = __ffs(static_cast<int>(u)) - 1;
             u &= u - 1;
-            const int64_t node = wbase + bit;
+            const int64_t chunk = (wd << 5) + bit;
             uint32_t mask = 0;
-            for (int h = 0; h < p.G; ++h) mask |= ((bm[h][w] >> bit) & 1u) << h;
-            if (node == cur) mask |= kAllHeads;
-            items[pos++] = make_int2(static_cast<int>(node), static_cast<int>(mask));
+#pragma unroll
+            for (int h = 0; h < G; ++h) mask |= ((heads[h] >> bit) & 1u) << h;
+            if (chunk == cur) mask |= kAllHeads;
+            items[pos++] = make_int2(static_cast<int>(chunk), static_cast<int>(mask));
         }
-        total += ctot;
-        __syncthreads();
-        if (tid < p.G) cur_pos[tid] = end_pos[tid];
-        __syncthreads();
     }
     if (tid == 0) p.acnt[y] = static_cast<int32_t>(total);
 }
 
 // ----------------------------------------------------------------------------
-// split-K attention
+// split-K attention, balanced over the whole chip
+// Work unit: a group of kGroupTokens tokens of one item (chunk) of one (row,
+// kv head) pair. attn_plan_kernel takes the exclusive prefix of the groups
+// over the pairs; attend_kernel then gives each of its nwg workgroups an equal
+// slice of that global range, whatever pairs it spans: a heavy pair is spread
+// over many workgroups and light pairs share one. A workgroup writes one
+// partial state per pair segment of its slice, at slot (workgroup + pair),
+// which is unique because consecutive segments belong to consecutive pairs.
+// Scores are kept in log2 units (q is pre-scaled by scale * log2(e)), so
+// every exponential is one native exp2.
 // ----------------------------------------------------------------------------
+constexpr int kGroupTokens = 16;          // tokens a wave handles per pipeline stage
+
+constexpr int kMinChunk = 8;              // a workgroup gets at least 8 groups (128 tokens) of work
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
 struct AttnParams {
     const float* q;
     RowInfo ri;
     const void* K;
     const void* V;
-    const int2* items;
-    const int32_t* acnt;
+    const int2* items;         // [pairs, item_stride] (sparse)
+    const int32_t* acnt;       // [pairs] items per pair (sparse)
     int64_t item_stride;
-    float* partial;            // [rows, Hq, S, D + 2]
+    int64_t* plan;             // [pairs + 1] exclusive prefix of groups per pair
+    float* partial;            // [nwg + pairs, G, D + 2]
     int64_t cap;
-    int b, Hq, Hkv, S, dense;
-    float scale;
+    int b, lb, lgpi, Hq, Hkv, pairs, nwg, dense;
+    float qscale;              // scale * log2(e)
 };
 
-constexpr int kGroupTokens = 16;          // tokens a wave handles per pipeline stage
-constexpr int kMinGroupsPerSplit = 8;     // a split gets at least 8 groups (128 tokens) of work
+__device__ __forceinline__ int64_t attn_chunk(int64_t total, int nwg) {
+    const int64_t c = (total + nwg - 1) / nwg;
+    return c < kMinChunk ? kMinChunk : c;
+}
 
-// Items (chunks) of one (row, kv head) and the number of splits that share them;
-// the attention and the combine must agree on both.
-__device__ __forceinline__ void attn_work(const AttnParams& p, int row, int kv, int N, int64_t* groups, int* seff) {
-    const int64_t U = p.dense ? (N + p.b - 1) / p.b : p.acnt[static_cast<int64_t>(row) * p.Hkv + kv];
-    const int gpi = p.b >= kGroupTokens ? p.b / kGroupTokens : 1;
-    const int64_t ng = U * gpi;
-    const int64_t s = (ng + kMinGroupsPerSplit - 1) / kMinGroupsPerSplit;
-    *groups = ng;
-    *seff = static_cast<int>(s < 1 ? 1 : (s > p.S ? p.S : s));
+// groups of one pair: its items (sparse) or all its chunks (dense), times groups per chunk
+__device__ __forceinline__ int64_t pair_groups(const AttnParams& p, int pr) {
+    const int row = pr / p.Hkv;
+    int64_t nitems;
+    if (p.dense) {
+        const int N = visible_clamped(p.ri, row, p.cap);
+        nitems = N > 0 ? ((static_cast<int64_t>(N) - 1) >> p.lb) + 1 : 0;
+    } else {
+        nitems = p.acnt[pr];
+    }
+    return nitems << p.lgpi;
+}
+
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnParams p) {
+    __shared__ int64_t red[kPlanThreads / kWave];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nt = blockDim.x;
+    int64_t carry = 0;
+    for (int base = 0; base < p.pairs; base += nt) {
+        const int pr = base + tid;
+        const int64_t v = pr < p.pairs ? pair_groups(p, pr) : 0;
+        uint64_t inc = static_cast<uint64_t>(v);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t lo = __shfl_up(static_cast<uint32_t>(inc), o, 64);
+            const uint32_t hi = __shfl_up(static_cast<uint32_t>(inc >> 32), o, 64);
+            if (lane >= o) inc += (static_cast<uint64_t>(hi) << 32) | lo;
+        }
+        if (lane == 63) red[w] = static_cast<int64_t>(inc);
+        __syncthreads();
+        int64_t before = 0, total = 0;
+        for (int i = 0; i < nt / kWave; ++i) {
+            if (i < w) before += red[i];
+            total += red[i];
+        }
+        if (pr < p.pairs) p.plan[pr] = carry + before + static_cast<int64_t>(inc) - v;
+        carry += total;
+        __syncthreads();
+    }
+    if (tid == 0) p.plan[p.pairs] = carry;
 }
 
 template <typename KT, int D, int G>
@@ -217,6 +272,8 @@ __device__ __forceinline__ void widen(const uint32_t (&w)[W], float (&x)[N]) {
     }
 }
 
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <typename KT, int D, int G>
 __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
     using C = AttnCfg<KT, D, G>;
@@ -225,257 +282,301 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
     __shared__ float sm_m[NW][G], sm_l[NW][G];
     __shared__ float sm_acc[NW][G][D];
 
-    const int split = blockIdx.x;
-    const int y = blockIdx.y;
-    const int row = y / p.Hkv, kv = y % p.Hkv;
-    const int s = row / p.ri.T;
+    const int wg = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int N = visible_clamped(p.ri, row, p.cap);
-    int64_t ng;
-    int seff;
-    attn_work(p, row, kv, N, &ng, &seff);
-    if (split >= seff) return;                       // the combine reads only seff partials
-    const int64_t g0 = ng * split / seff, g1 = ng * (split + 1) / seff;
-    const int gpi = p.b >= kGroupTokens ? p.b / kGroupTokens : 1;
+    const int part = lane % LPT, tsub = lane / LPT;
+    const int64_t total = p.plan[p.pairs];
+    const int64_t chunk = attn_chunk(total, p.nwg);
+    const int64_t r0 = static_cast<int64_t>(wg) * chunk;
+    if (r0 >= total) return;
+    const int64_t r1 = imin(r0 + chunk, total);
+    // first pair of the slice: the last pr with plan[pr] <= r0
+    int lo = 0, hi = p.pairs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.plan[mid] <= r0) lo = mid;
+        else hi = mid - 1;
+    }
+    const int gpi = 1 << p.lgpi;
     const int tg = p.b >= kGroupTokens ? kGroupTokens : p.b;
 
-    const int part = lane % LPT, tsub = lane / LPT;
-    float qv[G][DPL];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-        load_vec<DPL>(p.q + (static_cast<int64_t>(row) * p.Hq + kv * G + h) * D + part * DPL, qv[h]);
+    for (int pr = lo; pr < p.pairs; ++pr) {
+        const int64_t pg0 = p.plan[pr];
+        if (pg0 >= r1) break;
+        const int64_t ga = imax(r0, pg0) - pg0, gb = imin(r1, p.plan[pr + 1]) - pg0;   // this pair's groups here
+        if (ga >= gb) continue;                                  // a pair with no groups
+        const int row = pr / p.Hkv, kv = pr % p.Hkv;
+        const int s = row / p.ri.T;
+        const int N = visible_clamped(p.ri, row, p.cap);
 
-    const KT* Kb = static_cast<const KT*>(p.K) + (static_cast<int64_t>(s) * p.Hkv + kv) * p.cap * D + part * DPL;
-    const KT* Vb = static_cast<const KT*>(p.V) + (static_cast<int64_t>(s) * p.Hkv + kv) * p.cap * D + part * DPL;
-    const int2* items = p.items + static_cast<int64_t>(y) * p.item_stride;
-
-    float m[G], l[G], acc[G][DPL];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
-    }
-
-    // group g -> (chunk id, head mask). For the sparse path the chunk ids of 64
-    // of this wave's upcoming groups are loaded at once, one per lane, and read
-    // back with readlane, so no dependent load sits in the pipeline.
-    int64_t batch_k0 = -1;
-    int2 batch = make_int2(0, 0);
-    auto item_of = [&](int64_t g) -> int2 {
-        const int64_t it = g / gpi;
-        if (p.dense) return make_int2(static_cast<int>(it), static_cast<int>(kAllHeads));
-        const int64_t k = (g - g0 - wave) / NW;                 // this wave's k-th group
-        if (batch_k0 < 0 || k >= batch_k0 + kWave) {
-            batch_k0 = k;
-            const int64_t gl = g + static_cast<int64_t>(lane) * NW;
-            batch = gl < g1 ? items[gl / gpi] : make_int2(0, 0);
-        }
-        const int src = static_cast<int>(k - batch_k0);
-        return make_int2(__builtin_amdgcn_readlane(batch.x, src), __builtin_amdgcn_readlane(batch.y, src));
-    };
-    auto first_token = [&](int64_t g, int2 e) -> int64_t {
-        return static_cast<int64_t>(e.x) * p.b + (g % gpi) * kGroupTokens;
-    };
-    auto issue = [&](int64_t t0, uint32_t (&kb)[NP][WPP], uint32_t (&vb)[NP][WPP]) {
-#pragma unroll
-        for (int ps = 0; ps < NP; ++ps) {
-            const int j = min(ps * TPP + tsub, tg - 1);
-            const int64_t t = min<int64_t>(t0 + j, N - 1);     // always a present row
-            load_words<WPP>(Kb + t * D, kb[ps]);
-            load_words<WPP>(Vb + t * D, vb[ps]);
-        }
-    };
-    auto consume = [&](int64_t t0, uint32_t mask, const uint32_t (&kb)[NP][WPP], const uint32_t (&vb)[NP][WPP]) {
-        float sc[NP][G];
-#pragma unroll
-        for (int ps = 0; ps < NP; ++ps) {
-            const int j = ps * TPP + tsub;
-            const int64_t t = t0 + j;
-            const bool inb = (j < tg) && (t < N);
-            float x[DPL];
-            widen<KT, DPL, WPP>(kb[ps], x);
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float a = 0.f;
-#pragma unroll
-                for (int e = 0; e < DPL; ++e) a = fmaf(qv[h][e], x[e], a);
-                a = fast_group_sum<LPT>(a) * p.scale;
-                const bool ok = inb && ((mask & kAllHeads) || ((mask >> h) & 1u) || t == 0);
-                sc[ps][h] = ok ? a : -INFINITY;
-            }
-        }
-        float mn[G];
+        float qv[G][DPL];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float gm = sc[0][h];
+            load_vec<DPL>(p.q + (static_cast<int64_t>(row) * p.Hq + kv * G + h) * D + part * DPL, qv[h]);
 #pragma unroll
-            for (int ps = 1; ps < NP; ++ps) gm = fmaxf(gm, sc[ps][h]);
-            mn[h] = fmaxf(m[h], gm);
-            const float alpha = (mn[h] == -INFINITY) ? 1.f : expf(m[h] - mn[h]);   // 0 while nothing was seen
-            l[h] *= alpha;
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) acc[h][e] *= alpha;
-            m[h] = mn[h];
+            for (int e = 0; e < DPL; ++e) qv[h][e] *= p.qscale;
         }
+        const KT* Kb = static_cast<const KT*>(p.K) + (static_cast<int64_t>(s) * p.Hkv + kv) * p.cap * D + part * DPL;
+        const KT* Vb = static_cast<const KT*>(p.V) + (static_cast<int64_t>(s) * p.Hkv + kv) * p.cap * D + part * DPL;
+        const int2* items = p.items + static_cast<int64_t>(pr) * p.item_stride;
+
+        float m[G], l[G], acc[G][DPL];
 #pragma unroll
-        for (int ps = 0; ps < NP; ++ps) {
-            float v[DPL];
-            widen<KT, DPL, WPP>(vb[ps], v);
+        for (int h = 0; h < G; ++h) {
+            m[h] = -INFINITY;
+            l[h] = 0.f;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+        }
+
+        // group g -> (chunk id, head mask). For the sparse path the chunk ids of
+        // 64 of this wave's upcoming groups are loaded at once, one per lane, and
+        // read back with readlane, so no dependent load sits in the pipeline.
+        int64_t batch_k0 = -1;
+        int2 batch = make_int2(0, 0);
+        auto item_of = [&](int64_t g) -> int2 {
+            const int64_t it = g >> p.lgpi;
+            if (p.dense) return make_int2(static_cast<int>(it), static_cast<int>(kAllHeads));
+            const int64_t k = (g - ga - wave) / NW;                 // this wave's k-th group
+            if (batch_k0 < 0 || k >= batch_k0 + kWave) {
+                batch_k0 = k;
+                const int64_t gl = g + static_cast<int64_t>(lane) * NW;
+                batch = gl < gb ? items[gl >> p.lgpi] : make_int2(0, 0);
+            }
+            const int src = static_cast<int>(k - batch_k0);
+            return make_int2(__builtin_amdgcn_readlane(batch.x, src), __builtin_amdgcn_readlane(batch.y, src));
+        };
+        auto first_token = [&](int64_t g, int2 e) -> int64_t {
+            return (static_cast<int64_t>(e.x) << p.lb) + (g & (gpi - 1)) * kGroupTokens;
+        };
+        auto issue = [&](int64_t t0, uint32_t (&kb)[NP][WPP], uint32_t (&vb)[NP][WPP]) {
+#pragma unroll
+            for (int ps = 0; ps < NP; ++ps) {
+                const int j = min(ps * TPP + tsub, tg - 1);
+                const int64_t t = imin(t0 + j, N - 1);     // always a present row
+                load_words<WPP>(Kb + t * D, kb[ps]);
+                load_words<WPP>(Vb + t * D, vb[ps]);
+            }
+        };
+        auto consume = [&](int64_t t0, uint32_t mask, const uint32_t (&kb)[NP][WPP], const uint32_t (&vb)[NP][WPP]) {
+            float sc[NP][G];
+#pragma unroll
+            for (int ps = 0; ps < NP; ++ps) {
+                const int j = ps * TPP + tsub;
+                const int64_t t = t0 + j;
+                const bool inb = (j < tg) && (t < N);
+                float x[DPL];
+                widen<KT, DPL, WPP>(kb[ps], x);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    float a = 0.f;
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) a = fmaf(qv[h][e], x[e], a);
+                    a = fast_group_sum<LPT>(a);
+                    const bool ok = inb && ((mask & kAllHeads) || ((mask >> h) & 1u) || t == 0);
+                    sc[ps][h] = ok ? a : -INFINITY;
+                }
+            }
+            float mn[G];
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float pr = (mn[h] == -INFINITY) ? 0.f : expf(sc[ps][h] - mn[h]);   // 0 when masked
-                l[h] += pr;
+                float gm = sc[0][h];
 #pragma unroll
-                for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(pr, v[e], acc[h][e]);
+                for (int ps = 1; ps < NP; ++ps) gm = fmaxf(gm, sc[ps][h]);
+                mn[h] = fmaxf(m[h], gm);
+                const float alpha = (mn[h] == -INFINITY) ? 1.f : fast_exp2(m[h] - mn[h]);   // 0 while nothing was seen
+                l[h] *= alpha;
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) acc[h][e] *= alpha;
+                m[h] = mn[h];
             }
-        }
-    };
+#pragma unroll
+            for (int ps = 0; ps < NP; ++ps) {
+                float v[DPL];
+                widen<KT, DPL, WPP>(vb[ps], v);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float pr_ = (mn[h] == -INFINITY) ? 0.f : fast_exp2(sc[ps][h] - mn[h]);   // 0 when masked
+                    l[h] += pr_;
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(pr_, v[e], acc[h][e]);
+                }
+            }
+        };
 
-    // Software pipeline over this wave's groups g0+wave, +NW, +2NW, ...: while a
-    // group is consumed, the K/V rows of the next one and the chunk id of the
-    // one after are already in flight. Buffers A and B alternate.
-    uint32_t kA[NP][WPP], vA[NP][WPP], kB[NP][WPP], vB[NP][WPP];
-    int64_t g = g0 + wave;
-    if (g < g1) {
-        int2 e0 = item_of(g);                                          // chunk of group g
-        int2 e1 = (g + NW < g1) ? item_of(g + NW) : make_int2(0, 0);   // chunk of group g + NW
-        issue(first_token(g, e0), kA, vA);
-        for (;;) {
-            int64_t gn = g + NW;
-            int2 e2 = make_int2(0, 0);
-            if (gn < g1) {
-                issue(first_token(gn, e1), kB, vB);
-                if (gn + NW < g1) e2 = item_of(gn + NW);
+        // Software pipeline over this wave's groups ga+wave, +NW, +2NW, ...: while a
+        // group is consumed, the K/V rows of the next one and the chunk id of the
+        // one after are already in flight. Buffers A and B alternate.
+        uint32_t kA[NP][WPP], vA[NP][WPP], kB[NP][WPP], vB[NP][WPP];
+        int64_t g = ga + wave;
+        if (g < gb) {
+            int2 e0 = item_of(g);                                          // chunk of group g
+            int2 e1 = (g + NW < gb) ? item_of(g + NW) : make_int2(0, 0);   // chunk of group g + NW
+            issue(first_token(g, e0), kA, vA);
+            for (;;) {
+                int64_t gn = g + NW;
+                int2 e2 = make_int2(0, 0);
+                if (gn < gb) {
+                    issue(first_token(gn, e1), kB, vB);
+                    if (gn + NW < gb) e2 = item_of(gn + NW);
+                }
+                consume(first_token(g, e0), static_cast<uint32_t>(e0.y), kA, vA);
+                if (gn >= gb) break;
+                g = gn;
+                e0 = e1;
+                e1 = e2;
+                gn = g + NW;
+                e2 = make_int2(0, 0);
+                if (gn < gb) {
+                    issue(first_token(gn, e1), kA, vA);
+                    if (gn + NW < gb) e2 = item_of(gn + NW);
+                }
+                consume(first_token(g, e0), static_cast<uint32_t>(e0.y), kB, vB);
+                if (gn >= gb) break;
+                g = gn;
+                e0 = e1;
+                e1 = e2;
             }
-            consume(first_token(g, e0), static_cast<uint32_t>(e0.y), kA, vA);
-            if (gn >= g1) break;
-            g = gn;
-            e0 = e1;
-            e1 = e2;
-            gn = g + NW;
-            e2 = make_int2(0, 0);
-            if (gn < g1) {
-                issue(first_token(gn, e1), kA, vA);
-                if (gn + NW < g1) e2 = item_of(gn + NW);
-            }
-            consume(first_token(g, e0), static_cast<uint32_t>(e0.y), kB, vB);
-            if (gn >= g1) break;
-            g = gn;
-            e0 = e1;
-            e1 = e2;
         }
-    }
 
-    // ---- merge the token slots of each wave ----
+        // ---- merge the token slots of each wave, then the waves ----
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float M = strided_max<LPT>(m[h]);
-        const float f = (m[h] == -INFINITY) ? 0.f : expf(m[h] - M);
-        const float lw = strided_sum<LPT>(l[h] * f);
+        for (int h = 0; h < G; ++h) {
+            const float M = strided_max<LPT>(m[h]);
+            const float f = (m[h] == -INFINITY) ? 0.f : fast_exp2(m[h] - M);
+            const float lw = strided_sum<LPT>(l[h] * f);
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[h][e] = strided_sum<LPT>(acc[h][e] * f);
-        if (lane < LPT) {
+            for (int e = 0; e < DPL; ++e) acc[h][e] = strided_sum<LPT>(acc[h][e] * f);
+            if (lane < LPT) {
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) sm_acc[wave][h][part * DPL + e] = acc[h][e];
-        }
-        if (lane == 0) {
-            sm_m[wave][h] = M;
-            sm_l[wave][h] = lw;
-        }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * (D + 2); idx += blockDim.x) {
-        const int h = idx / (D + 2), c = idx % (D + 2);
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
-        float out = 0.f;
-        if (c == 0) {
-            out = M;
-        } else {
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float f = (sm_m[w][h] == -INFINITY) ? 0.f : expf(sm_m[w][h] - M);
-                out += f * (c == 1 ? sm_l[w][h] : sm_acc[w][h][c - 2]);
+                for (int e = 0; e < DPL; ++e) sm_acc[wave][h][part * DPL + e] = acc[h][e];
+            }
+            if (lane == 0) {
+                sm_m[wave][h] = M;
+                sm_l[wave][h] = lw;
             }
         }
-        const int64_t rh = static_cast<int64_t>(row) * p.Hq + kv * G + h;
-        p.partial[(rh * p.S + split) * (D + 2) + c] = out;
+        __syncthreads();
+        float* pout = p.partial + static_cast<int64_t>(wg + pr) * G * (D + 2);
+        for (int idx = threadIdx.x; idx < G * (D + 2); idx += blockDim.x) {
+            const int h = idx / (D + 2), c = idx % (D + 2);
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+            float out = 0.f;
+            if (c == 0) {
+                out = M;
+            } else {
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const float f = (sm_m[w][h] == -INFINITY) ? 0.f : fast_exp2(sm_m[w][h] - M);
+                    out += f * (c == 1 ? sm_l[w][h] : sm_acc[w][h][c - 2]);
+                }
+            }
+            pout[idx] = out;
+        }
+        __syncthreads();                                         // sm_* are reused by the next segment
     }
 }
 
 // ----------------------------------------------------------------------------
-// LSE merge of the splits: one workgroup per (row, query head)
+// LSE merge of a pair's segments: one workgroup per (row, query head)
 // ----------------------------------------------------------------------------
-constexpr int kCombineThreads = 256;
+constexpr int kCombineThreads = 1024;   // 1024/D slot subsets per dimension: many loads in flight
+constexpr int kCombineChunk = 1024;     // slots staged in LDS at a time
 
-template <int D>
-__global__ __launch_bounds__(kCombineThreads) void attend_combine_kernel(AttnParams p, float* out, float* lse, int G) {
-    __shared__ float fs[kAttnSplitsMax];
+template <int D, int G>
+__global__ __launch_bounds__(kCombineThreads) void attend_combine_kernel(AttnParams p, float* out, float* lse) {
+    __shared__ float fs[kCombineChunk];
     __shared__ float red[kCombineThreads / kWave];
     __shared__ float part_acc[kCombineThreads];
     const int64_t rh = blockIdx.x;
-    const int row = static_cast<int>(rh / p.Hq), kv = static_cast<int>((rh % p.Hq) / G);
+    const int row = static_cast<int>(rh / p.Hq), hq = static_cast<int>(rh % p.Hq);
+    const int kv = hq / G, h = hq % G;
+    const int pr = row * p.Hkv + kv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int N = visible_clamped(p.ri, row, p.cap);
-    int64_t ng;
-    int seff;
-    attn_work(p, row, kv, N, &ng, &seff);
-    const float* pp = p.partial + rh * p.S * (D + 2);
-    const float ms = tid < seff ? pp[tid * (D + 2)] : -INFINITY;
-    float M = group_max<kWave>(ms);
+    const int64_t total = p.plan[p.pairs];
+    const int64_t chunk = attn_chunk(total, p.nwg);
+    const int64_t g0 = p.plan[pr], g1 = p.plan[pr + 1];
+    if (g0 >= g1) {                                              // nothing visible
+        if (tid < D) out[rh * D + tid] = 0.f;
+        if (tid == 0 && lse) lse[rh] = -INFINITY;
+        return;
+    }
+    const int64_t w0 = g0 / chunk, w1 = (g1 - 1) / chunk;
+    const int nslot = static_cast<int>(w1 - w0 + 1);
+    const float* pp = p.partial + ((w0 + pr) * G + h) * (D + 2);   // slot i at pp + i * G * (D + 2)
+    constexpr int64_t SS = static_cast<int64_t>(G) * (D + 2);
+    float M = -INFINITY;
+    for (int i = tid; i < nslot; i += kCombineThreads) M = fmaxf(M, pp[i * SS]);
+    M = group_max<kWave>(M);
     if (lane == 0) red[wave] = M;
     __syncthreads();
     M = red[0];
 #pragma unroll
     for (int i = 1; i < kCombineThreads / kWave; ++i) M = fmaxf(M, red[i]);
     __syncthreads();
-    const float f = (ms == -INFINITY) ? 0.f : expf(ms - M);
-    if (tid < kAttnSplitsMax) fs[tid] = f;
-    float Lp = group_sum<kWave>(tid < seff ? f * pp[tid * (D + 2) + 1] : 0.f);
+    constexpr int R = kCombineThreads / D;                      // slot subsets per dimension
+    const int dim = tid % D, sub = tid / D;
+    float a = 0.f, Lp = 0.f;
+    for (int c0 = 0; c0 < nslot; c0 += kCombineChunk) {
+        const int c1 = min(nslot, c0 + kCombineChunk);
+        for (int i = c0 + tid; i < c1; i += kCombineThreads) {
+            const float mi = pp[i * SS];
+            const float f = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M);
+            fs[i - c0] = f;
+            if (f != 0.f) Lp = fmaf(f, pp[i * SS + 1], Lp);
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int i = c0 + sub; i < c1; i += R) {
+            const float f = fs[i - c0];
+            if (f != 0.f) a = fmaf(f, pp[i * SS + 2 + dim], a);
+        }
+        __syncthreads();
+    }
+    Lp = group_sum<kWave>(Lp);
     if (lane == 0) red[wave] = Lp;
+    part_acc[tid] = a;
     __syncthreads();
     float L = 0.f;
 #pragma unroll
     for (int i = 0; i < kCombineThreads / kWave; ++i) L += red[i];
-    constexpr int R = kCombineThreads / D;         // split subsets per dimension
-    const int dim = tid % D, sub = tid / D;
-    float a = 0.f;
-#pragma unroll 4
-    for (int sp = sub; sp < seff; sp += R) a = fmaf(fs[sp], pp[sp * (D + 2) + 2 + dim], a);
-    part_acc[tid] = a;
-    __syncthreads();
     if (tid < D) {
         float t = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) t += part_acc[r * D + tid];
         out[rh * D + tid] = (L > 0.f) ? t / L : 0.f;
     }
-    if (tid == 0 && lse) lse[rh] = (L > 0.f) ? M + logf(L) : -INFINITY;
+    if (tid == 0 && lse) lse[rh] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ----------------------------------------------------------------------------
 // launchers
 // ----------------------------------------------------------------------------
 template <typename KT, int D, int G>
-static void launch_attn_t(dim3 grid, const AttnParams& ap, hipStream_t st) {
-    ProfScope ps("attend", 0, st);
-    hipLaunchKernelGGL((attend_kernel<KT, D, G>), grid, dim3(256), 0, st, ap);
+static hipError_t launch_attn_t(const AttnParams& ap, int rows, int Hq, float* out, float* lse, hipStream_t st) {
+    {
+        ProfScope ps("attend", 0, st);
+        hipLaunchKernelGGL((attend_kernel<KT, D, G>), dim3(ap.nwg), dim3(256), 0, st, ap);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ProfScope ps("attend_combine", 0, st);
+    hipLaunchKernelGGL((attend_combine_kernel<D, G>), dim3(rows * Hq), dim3(kCombineThreads), 0, st, ap, out, lse);
+    return hipGetLastError();
 }
 
 template <typename KT, int D>
-static hipError_t attn_g(int G, dim3 grid, const AttnParams& ap, hipStream_t st) {
+static hipError_t attn_g(int G, const AttnParams& ap, int rows, int Hq, float* out, float* lse, hipStream_t st) {
     switch (G) {
-        case 1: launch_attn_t<KT, D, 1>(grid, ap, st); break;
-        case 2: launch_attn_t<KT, D, 2>(grid, ap, st); break;
-        case 4: launch_attn_t<KT, D, 4>(grid, ap, st); break;
-        case 8: launch_attn_t<KT, D, 8>(grid, ap, st); break;
-        case 16: launch_attn_t<KT, D, 16>(grid, ap, st); break;
+        case 1: return launch_attn_t<KT, D, 1>(ap, rows, Hq, out, lse, st);
+        case 2: return launch_attn_t<KT, D, 2>(ap, rows, Hq, out, lse, st);
+        case 4: return launch_attn_t<KT, D, 4>(ap, rows, Hq, out, lse, st);
+        case 8: return launch_attn_t<KT, D, 8>(ap, rows, Hq, out, lse, st);
+        case 16: return launch_attn_t<KT, D, 16>(ap, rows, Hq, out, lse, st);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st) {
@@ -483,22 +584,37 @@ hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st) {
     char* ws = a.ws;
     const int pairs = a.rows * g.Hkv;
     if (!a.dense) {
-        UnionParams up{};
-        up.ri = a.ri;
-        up.sel_blocks = a.sel_blocks;
-        up.n_sel = a.n_sel;
-        up.sel_cap = a.sel_cap;
-        up.items = reinterpret_cast<int2*>(ws + lay.aitems);
-        up.item_stride = g.nodes[0] + 2;
-        up.acnt = reinterpret_cast<int32_t*>(ws + lay.acnt);
-        up.cap = g.cap;
-        up.b = g.b;
-        up.Hq = g.Hq;
-        up.Hkv = g.Hkv;
-        up.G = g.G;
+        uint32_t* bm1 = reinterpret_cast<uint32_t*>(ws + lay.bitmap) + lay.bm_off[0];
+        const int64_t leaf_words = (g.nodes[0] + 32) / 32;
+        if (!a.bitmaps_ready) {
+            BitmapParams bp{a.sel_blocks, a.n_sel, a.sel_cap, bm1, lay.bm_words_total, leaf_words};
+            ProfScope ps("attn_bitmap", 0, st);
+            hipLaunchKernelGGL(attn_bitmap_kernel, dim3(a.rows * g.Hq), dim3(256), 0, st, bp);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        ItemsParams ip{};
+        ip.ri = a.ri;
+        ip.bm = bm1;
+        ip.stride = lay.bm_words_total;
+        ip.items = reinterpret_cast<int2*>(ws + lay.aitems);
+        ip.item_stride = g.nodes[0] + 2;
+        ip.acnt = reinterpret_cast<int32_t*>(ws + lay.acnt);
+        ip.cap = g.cap;
+        ip.lb = g.lb;
+        ip.Hq = g.Hq;
+        ip.Hkv = g.Hkv;
         {
-            ProfScope ps("attn_union", 0, st);
-            hipLaunchKernelGGL(attn_union_kernel, dim3(pairs), dim3(kUnionThreads), 0, st, up);
+            ProfScope ps("attn_items", 0, st);
+            const dim3 gi(pairs), bi(kItemsThreads);
+            switch (g.G) {
+                case 1: hipLaunchKernelGGL(attn_items_kernel<1>, gi, bi, 0, st, ip); break;
+                case 2: hipLaunchKernelGGL(attn_items_kernel<2>, gi, bi, 0, st, ip); break;
+                case 4: hipLaunchKernelGGL(attn_items_kernel<4>, gi, bi, 0, st, ip); break;
+                case 8: hipLaunchKernelGGL(attn_items_kernel<8>, gi, bi, 0, st, ip); break;
+                case 16: hipLaunchKernelGGL(attn_items_kernel<16>, gi, bi, 0, st, ip); break;
+                default: return hipErrorInvalidValue;
+            }
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -511,28 +627,30 @@ hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st) {
     ap.items = reinterpret_cast<const int2*>(ws + lay.aitems);
     ap.acnt = reinterpret_cast<const int32_t*>(ws + lay.acnt);
     ap.item_stride = g.nodes[0] + 2;
+    ap.plan = reinterpret_cast<int64_t*>(ws + lay.plan);
     ap.partial = reinterpret_cast<float*>(ws + lay.partial);
     ap.cap = g.cap;
     ap.b = g.b;
+    ap.lb = g.lb;
+    ap.lgpi = g.lb > 4 ? g.lb - 4 : 0;          // groups of kGroupTokens per chunk
     ap.Hq = g.Hq;
     ap.Hkv = g.Hkv;
-    ap.S = lay.splits;
+    ap.pairs = pairs;
+    ap.nwg = kAttnWorkgroups;
     ap.dense = a.dense ? 1 : 0;
-    ap.scale = g.scale;
-    const dim3 grid(lay.splits, pairs);
-    hipError_t e;
-    const bool bf = g.kv_dtype == ZHA_KV_BF16;
-    if (g.D == 128) e = bf ? attn_g<uint16_t, 128>(g.G, grid, ap, st) : attn_g<float, 128>(g.G, grid, ap, st);
-    else e = bf ? attn_g<uint16_t, 64>(g.G, grid, ap, st) : attn_g<float, 64>(g.G, grid, ap, st);
+    ap.qscale = g.scale * kLog2e;
+    {
+        ProfScope ps("attn_plan", 0, st);
+        hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, ap);
+    }
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    ProfScope ps("attend_combine", 0, st);
+    const bool bf = g.kv_dtype == ZHA_KV_BF16;
     if (g.D == 128)
-        hipLaunchKernelGGL(attend_combine_kernel<128>, dim3(a.rows * g.Hq), dim3(kCombineThreads), 0, st, ap, a.out,
-                           a.lse, g.G);
-    else
-        hipLaunchKernelGGL(attend_combine_kernel<64>, dim3(a.rows * g.Hq), dim3(kCombineThreads), 0, st, ap, a.out,
-                           a.lse, g.G);
-    return hipGetLastError();
+        return bf ? attn_g<uint16_t, 128>(g.G, ap, a.rows, g.Hq, a.out, a.lse, st)
+                  : attn_g<float, 128>(g.G, ap, a.rows, g.Hq, a.out, a.lse, st);
+    return bf ? attn_g<uint16_t, 64>(g.G, ap, a.rows, g.Hq, a.out, a.lse, st)
+              : attn_g<float, 64>(g.G, ap, a.rows, g.Hq, a.out, a.lse, st);
 }
 
 }  // namespace zha

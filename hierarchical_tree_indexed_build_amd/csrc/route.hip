@@ -9,22 +9,26 @@
 //   keep       = the smallest prefix in (score desc, node id asc) order whose
 //                softmax mass is >= top_p of the candidates' total.
 //
-// Two kernels per level, ordered by the kernel boundary alone: no device-scope
-// fences and no cross-workgroup atomics (on this part every XCD has its own L2,
-// and a device-scope release writes L2 back).
-//  * route_score_kernel - a workgroup owns kScoreParents parent slots of one
-//    (row, kv head). It ORs the group's kept bitmaps of level l+1 over its
-//    slots (plus the incomplete parent, whose complete children are the
-//    orphans) and scores each such parent's b children once for all g query
-//    heads: a summary row is read once per kv group. Scores land in a
-//    dense-by-node array per (row, query head).
-//  * route_cut_kernel - one workgroup per (row, query head). The candidates'
-//    scores are staged in LDS when they fit; masses exp(s - max) are held in
-//    2^-40 fixed point, so their sums are exact and independent of order; an
-//    MSB-first radix select over an order-preserving score key finds the
-//    boundary score; ties at the boundary go to the lower node ids; a stable
-//    compaction writes the kept ids in ascending order and the head's kept
-//    bitmap (built in LDS when it fits).
+// Kernels, ordered by kernel boundaries alone: no device-scope fences and no
+// cross-workgroup atomics (on this part every XCD has its own L2, and a
+// device-scope release writes L2 back).
+//  * route_upper_kernel - one workgroup per (row, query head) walks the small
+//    upper levels in one launch: candidates, scores and the cut stay in LDS
+//    from level to level.
+//  * per remaining level (the leaf level always):
+//    - route_score_kernel - a workgroup owns kScoreParents parent slots of one
+//      (row, kv head). It ORs the group's kept bitmaps of level l+1 over its
+//      slots (plus the incomplete parent, whose complete children are the
+//      orphans) and scores each such parent's b children once for all g query
+//      heads: a summary row is read once per kv group. Scores land in a
+//      dense-by-node array per (row, query head).
+//    - route_cut_kernel - one workgroup per (row, query head); the candidates'
+//      scores are staged in LDS when they fit.
+// The cut itself (both cut kernels): masses exp(s - max) are held in 2^-40
+// fixed point, so their sums are exact and independent of order; an MSB-first
+// radix select over an order-preserving score key finds the boundary score;
+// ties at the boundary go to the lower node ids; a stable compaction writes the
+// kept ids in ascending order and the head's kept bitmap.
 #include <algorithm>
 
 #include "zha_device.h"
@@ -144,7 +148,214 @@ __global__ __launch_bounds__(256) void route_score_kernel(ScoreParams p) {
 }
 
 // ----------------------------------------------------------------------------
-// cut
+// the cut: block primitives and the two phases shared by both cut kernels
+// ----------------------------------------------------------------------------
+constexpr int kCutThreads = 1024;
+constexpr int kCutWaves = kCutThreads / kWave;
+
+struct BlockScratch {
+    uint64_t hist[2][256];      // radix histograms, alternating between rounds
+    uint64_t red_u64[kCutWaves];
+    float red_f[kCutWaves];
+    uint32_t red_u32[kCutWaves];
+    uint64_t bcast_u64[2];
+    uint32_t bcast_u32[2];
+};
+
+// Block reductions: a DPP scan per wave (lane 63 holds the wave's result),
+// one LDS slot per wave, one barrier to publish and one to free the slots.
+__device__ __forceinline__ float block_max_f(float v, BlockScratch& bs) {
+    v = wave_scan_max_f(v);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 63) bs.red_f[w] = v;
+    __syncthreads();
+    float r = bs.red_f[0];
+#pragma unroll
+    for (int i = 1; i < kCutWaves; ++i) r = fmaxf(r, bs.red_f[i]);
+    __syncthreads();
+    return r;
+}
+
+// Sum of a u64 and max of a u32 over the block, in one round of barriers.
+__device__ __forceinline__ void block_sum_max(uint64_t& sum, uint32_t& mx, BlockScratch& bs) {
+    const uint64_t s = wave_scan_u64(sum);
+    const uint32_t m = wave_scan_max_u32(mx);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 63) {
+        bs.red_u64[w] = s;
+        bs.red_u32[w] = m;
+    }
+    __syncthreads();
+    uint64_t rs = 0;
+    uint32_t rm = 0;
+#pragma unroll
+    for (int i = 0; i < kCutWaves; ++i) {
+        rs += bs.red_u64[i];
+        rm = max(rm, bs.red_u32[i]);
+    }
+    __syncthreads();
+    sum = rs;
+    mx = rm;
+}
+
+// Exclusive prefix sum over the block in thread order; *total receives the sum.
+__device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, BlockScratch& bs, uint64_t* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint64_t inc = wave_scan_u64(v);
+    if (lane == 63) bs.red_u64[w] = inc;
+    __syncthreads();
+    uint64_t before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < kCutWaves; ++i) {
+        if (i < w) before += bs.red_u64[i];
+        all += bs.red_u64[i];
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - v;
+}
+
+// Where a cut ends: every candidate whose key is below kappa is kept, plus the
+// first need_ties (in candidate order) of those whose key equals kappa.
+struct CutBoundary {
+    bool take_all;
+    uint32_t kappa;
+    uint64_t need_ties;
+};
+
+// The boundary of the top-p cut over candidates 0..n-1 with scores score(k)
+// and maximum mx. Masses exp(s - mx) are 2^-40 fixed point; the total and
+// every partial sum are exact. An MSB-first radix select, 8 bits a round,
+// finds the key at which the mass of the keys before it first reaches
+// ceil(top_p * total). Rounds alternate between two histograms, so a round
+// needs two barriers: after the histogram, and after the digit is published.
+template <class ScoreAt>
+__device__ __forceinline__ CutBoundary cut_boundary(ScoreAt score, int64_t n, float mx, float top_p,
+                                                    BlockScratch& bs) {
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
+    CutBoundary cb{(top_p >= 1.0f) || n == 0, 0u, 0u};
+    if (cb.take_all) return cb;
+    uint64_t E = 0;
+    uint32_t kmax = 0;
+    for (int64_t k = tid; k < n; k += nt) {
+        const float s = score(k);
+        const uint64_t F = mass_fx(s, mx);
+        E += F;
+        if (F) kmax = max(kmax, desc_key(s));
+    }
+    for (int i = tid; i < 256; i += nt) bs.hist[0][i] = 0;      // published by the barriers below
+    block_sum_max(E, kmax, bs);
+    const uint32_t kmin = desc_key(mx);
+    uint64_t rem = static_cast<uint64_t>(ceil(static_cast<double>(top_p) * static_cast<double>(E)));
+    if (rem == 0) rem = 1;
+    int known = (kmin == kmax) ? 32 : __clz(static_cast<int>(kmin ^ kmax));
+    uint32_t prefix = kmin & top_bits_mask(known);
+    int cur = 0;
+    while (known < 32) {
+        const int nb = min(8, 32 - known);
+        const int shift = 32 - known - nb;
+        const uint32_t hmask = top_bits_mask(known);
+        uint64_t* hist = bs.hist[cur];
+        for (int64_t k = tid; k < n; k += nt) {
+            const float s = score(k);
+            const uint32_t key = desc_key(s);
+            if (((key ^ prefix) & hmask) != 0u) continue;
+            const uint64_t F = mass_fx(s, mx);
+            if (F) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[(key >> shift) & ((1u << nb) - 1u)]),
+                             static_cast<unsigned long long>(F));
+        }
+        for (int i = tid; i < 256; i += nt) bs.hist[cur ^ 1][i] = 0;   // the next round's histogram
+        __syncthreads();
+        if (wave == 0) {
+            // lanes own 4 consecutive digits; scan in digit order
+            uint64_t v[4], lsum = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[j] = hist[lane * 4 + j];
+                lsum += v[j];
+            }
+            const uint64_t inc = wave_scan_u64(lsum);
+            uint64_t c = inc - lsum;
+            int found = -1;
+            uint64_t before = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (found < 0 && v[j] != 0 && c + v[j] >= rem) {
+                    found = lane * 4 + j;
+                    before = c;
+                }
+                c += v[j];
+            }
+            const unsigned long long bal = __ballot(found >= 0);
+            // the bins hold the remaining mass (>= rem), so some lane finds the digit
+            const int first = bal ? __ffsll(static_cast<long long>(bal)) - 1 : 0;
+            if (lane == first) {
+                bs.bcast_u32[cur] = static_cast<uint32_t>(found >= 0 ? found : 0);
+                bs.bcast_u64[cur] = found >= 0 ? before : 0;
+            }
+        }
+        __syncthreads();
+        rem -= bs.bcast_u64[cur];
+        prefix |= bs.bcast_u32[cur] << shift;
+        known += nb;
+        cur ^= 1;
+    }
+    cb.kappa = prefix;
+    const uint64_t Fk = mass_fx(desc_key_to_float(prefix), mx);
+    cb.need_ties = Fk ? (rem + Fk - 1) / Fk : 0;
+    return cb;
+}
+
+// Stable compaction of the kept candidates: emit(pos, k) for each kept k, pos
+// its rank among the kept (ascending k). Threads own contiguous ranges of k.
+// Returns the number kept.
+template <class ScoreAt, class Emit>
+__device__ __forceinline__ int64_t cut_compact(ScoreAt score, int64_t n, const CutBoundary& cb, BlockScratch& bs,
+                                               Emit emit) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int64_t chunk = (n + nt - 1) / nt;
+    const int64_t k0 = imin(static_cast<int64_t>(tid) * chunk, n);
+    const int64_t k1 = imin(k0 + chunk, n);
+    uint32_t c_nt = 0, c_tie = 0;
+    if (!cb.take_all) {
+        for (int64_t k = k0; k < k1; ++k) {
+            const uint32_t key = desc_key(score(k));
+            c_nt += key < cb.kappa;
+            c_tie += key == cb.kappa;
+        }
+    } else {
+        c_nt = static_cast<uint32_t>(k1 - k0);
+    }
+    uint64_t tot;
+    const uint64_t pre = block_excl_scan_u64((static_cast<uint64_t>(c_tie) << 32) | c_nt, bs, &tot);
+    uint64_t nt_before = pre & 0xffffffffu, tie_before = pre >> 32;
+    const uint64_t tot_nt = tot & 0xffffffffu, tot_tie = tot >> 32;
+    const uint64_t ties_kept = tot_tie < cb.need_ties ? tot_tie : cb.need_ties;
+    for (int64_t k = k0; k < k1; ++k) {
+        int64_t pos;
+        if (cb.take_all) {
+            pos = k;
+        } else {
+            const uint32_t key = desc_key(score(k));
+            if (key < cb.kappa) {
+                pos = static_cast<int64_t>(nt_before + (tie_before < cb.need_ties ? tie_before : cb.need_ties));
+                ++nt_before;
+            } else if (key == cb.kappa) {
+                const bool keep = tie_before < cb.need_ties;
+                pos = static_cast<int64_t>(nt_before + tie_before);
+                ++tie_before;
+                if (!keep) continue;
+            } else {
+                continue;
+            }
+        }
+        emit(pos, k);
+    }
+    return static_cast<int64_t>(tot_nt + ties_kept);
+}
+
+// ----------------------------------------------------------------------------
+// per-level cut kernel (levels scored by route_score_kernel)
 // ----------------------------------------------------------------------------
 struct CutParams {
     RowInfo ri;
@@ -166,75 +377,14 @@ struct CutParams {
     float top_p;
 };
 
-constexpr int kCutThreads = 1024;
-constexpr int kCutWaves = kCutThreads / kWave;
 constexpr int kCutStage = 32768;      // candidate scores staged in LDS (128 KiB)
 constexpr int kCutBmWords = 4096;     // kept bitmap built in LDS (levels up to 131072 nodes)
 
 struct CutShared {
     float sc[kCutStage];
     uint32_t bm[kCutBmWords];
-    uint64_t hist[256];
-    uint64_t red_u64[kCutWaves];
-    float red_f[kCutWaves];
-    uint32_t red_u32[kCutWaves];
-    uint64_t bcast_u64;
-    uint32_t bcast_u32;
+    BlockScratch bs;
 };
-
-__device__ __forceinline__ float block_max_f(float v, CutShared& sh) {
-    v = group_max<kWave>(v);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) sh.red_f[w] = v;
-    __syncthreads();
-    float r = sh.red_f[0];
-#pragma unroll
-    for (int i = 1; i < kCutWaves; ++i) r = fmaxf(r, sh.red_f[i]);
-    __syncthreads();
-    return r;
-}
-
-__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, CutShared& sh) {
-    v = wave_sum_u64(v);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) sh.red_u64[w] = v;
-    __syncthreads();
-    uint64_t r = 0;
-#pragma unroll
-    for (int i = 0; i < kCutWaves; ++i) r += sh.red_u64[i];
-    __syncthreads();
-    return r;
-}
-
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, CutShared& sh) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64)));
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) sh.red_u32[w] = v;
-    __syncthreads();
-    uint32_t r = sh.red_u32[0];
-#pragma unroll
-    for (int i = 1; i < kCutWaves; ++i) r = max(r, sh.red_u32[i]);
-    __syncthreads();
-    return r;
-}
-
-// Exclusive prefix sum over the block in thread order; *total receives the sum.
-__device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, CutShared& sh, uint64_t* total) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const uint64_t inc = wave_incl_scan_u64(v, lane);
-    if (lane == 63) sh.red_u64[w] = inc;
-    __syncthreads();
-    uint64_t before = 0, all = 0;
-#pragma unroll
-    for (int i = 0; i < kCutWaves; ++i) {
-        if (i < w) before += sh.red_u64[i];
-        all += sh.red_u64[i];
-    }
-    __syncthreads();
-    *total = all;
-    return before + inc - v;
-}
 
 // The candidates of one (row, head) at one level, in ascending node order:
 // k < nkids are the children of the kept parents up[0..kc), then the orphans.
@@ -249,13 +399,13 @@ struct CutCands {
     }
 };
 
-// The cut proper. kStaged: every candidate score sits in sh.sc (read from HBM
-// once); otherwise each pass re-reads the scores from global memory. The two
-// variants are separate instantiations, so each only ever addresses one space.
+// kStaged: every candidate score sits in sh.sc (read from HBM once);
+// otherwise each pass re-reads the scores from global memory. The two
+// variants are separate instantiations, so each only addresses one space.
 template <bool kStaged>
-__device__ __forceinline__ void cut_body(const CutParams& p, CutShared& sh, const CutCands& cc, int64_t rh,
-                                         int64_t nc) {
-    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ void cut_level(const CutParams& p, CutShared& sh, const CutCands& cc, int64_t rh,
+                                          int64_t nc) {
+    const int tid = threadIdx.x, nt = blockDim.x;
     const bool leaf = (p.li == 0);
     const int64_t ncand = cc.ncand;
     auto score = [&](int64_t k) -> float {
@@ -264,7 +414,7 @@ __device__ __forceinline__ void cut_body(const CutParams& p, CutShared& sh, cons
     };
 
     // kept bitmap of this head at this level: the level below ORs the group's
-    // bitmaps to find the parents to score
+    // bitmaps to find the parents to score; the attention reads level 1
     uint32_t* bm = p.bitmap + rh * p.bm_words_total + p.bm_off;
     const int64_t words = (nc + 31) >> 5;
     const bool lds_bm = words <= kCutBmWords;
@@ -276,142 +426,58 @@ __device__ __forceinline__ void cut_body(const CutParams& p, CutShared& sh, cons
     }
 
     // ---- stage the scores, max ----
+    // kStageUnroll candidates per thread are in flight at once: their parent
+    // ids first, then their scores, so the two dependent loads of one
+    // candidate do not serialise the loop.
+    constexpr int kStageUnroll = 8;
     float mx = -INFINITY;
-    for (int64_t k = tid; k < ncand; k += nt) {
-        const float v = cc.sc[cc.node(k)];
-        if constexpr (kStaged) sh.sc[k] = v;
-        mx = fmaxf(mx, v);
-    }
-    mx = block_max_f(mx, sh);
-
-    // ---- fixed-point total mass; least significant key with mass ----
-    const bool take_all = (p.top_p >= 1.0f) || ncand == 0;
-    uint32_t kappa = 0;
-    uint64_t need_ties = 0;
-    if (!take_all) {
-        uint64_t E = 0;
-        uint32_t kmax = 0;
-        for (int64_t k = tid; k < ncand; k += nt) {
-            const float s = score(k);
-            const uint64_t F = mass_fx(s, mx);
-            E += F;
-            if (F) kmax = max(kmax, desc_key(s));
-        }
-        E = block_sum_u64(E, sh);
-        kmax = block_max_u32(kmax, sh);
-        const uint32_t kmin = desc_key(mx);
-        uint64_t rem = static_cast<uint64_t>(ceil(static_cast<double>(p.top_p) * static_cast<double>(E)));
-        if (rem == 0) rem = 1;
-        int known = (kmin == kmax) ? 32 : __clz(static_cast<int>(kmin ^ kmax));
-        uint32_t prefix = kmin & top_bits_mask(known);
-        // ---- radix select of the boundary key, 8 bits at a time ----
-        while (known < 32) {
-            const int nb = min(8, 32 - known);
-            const int shift = 32 - known - nb;
-            const uint32_t hmask = top_bits_mask(known);
-            for (int i = tid; i < 256; i += nt) sh.hist[i] = 0;
-            __syncthreads();
-            for (int64_t k = tid; k < ncand; k += nt) {
-                const float s = score(k);
-                const uint32_t key = desc_key(s);
-                if (((key ^ prefix) & hmask) != 0u) continue;
-                const uint64_t F = mass_fx(s, mx);
-                if (F) atomicAdd(reinterpret_cast<unsigned long long*>(&sh.hist[(key >> shift) & ((1u << nb) - 1u)]),
-                                 static_cast<unsigned long long>(F));
-            }
-            __syncthreads();
-            if (wave == 0) {
-                // lanes own 4 consecutive digits; scan in digit order
-                uint64_t v[4], lsum = 0;
+    for (int64_t kb = tid; kb < ncand; kb += static_cast<int64_t>(kStageUnroll) * nt) {
+        int64_t node[kStageUnroll];
+        float v[kStageUnroll];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    v[j] = sh.hist[lane * 4 + j];
-                    lsum += v[j];
-                }
-                const uint64_t inc = wave_incl_scan_u64(lsum, lane);
-                uint64_t c = inc - lsum;
-                int found = -1;
-                uint64_t before = 0;
+        for (int u = 0; u < kStageUnroll; ++u) {
+            const int64_t k = kb + static_cast<int64_t>(u) * nt;
+            node[u] = k < ncand ? cc.node(k) : -1;
+        }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (found < 0 && v[j] != 0 && c + v[j] >= rem) {
-                        found = lane * 4 + j;
-                        before = c;
-                    }
-                    c += v[j];
-                }
-                const unsigned long long bal = __ballot(found >= 0);
-                // the bins hold the remaining mass (>= rem), so some lane finds the digit
-                const int first = bal ? __ffsll(static_cast<long long>(bal)) - 1 : 0;
-                if (lane == first) {
-                    sh.bcast_u32 = static_cast<uint32_t>(found >= 0 ? found : 0);
-                    sh.bcast_u64 = found >= 0 ? before : 0;
-                }
+        for (int u = 0; u < kStageUnroll; ++u) v[u] = node[u] >= 0 ? cc.sc[node[u]] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kStageUnroll; ++u) {
+            const int64_t k = kb + static_cast<int64_t>(u) * nt;
+            if (k < ncand) {
+                if constexpr (kStaged) sh.sc[k] = v[u];
+                mx = fmaxf(mx, v[u]);
             }
-            __syncthreads();
-            rem -= sh.bcast_u64;
-            prefix |= sh.bcast_u32 << shift;
-            known += nb;
-            __syncthreads();
         }
-        kappa = prefix;
-        const uint64_t Fk = mass_fx(desc_key_to_float(kappa), mx);
-        need_ties = Fk ? (rem + Fk - 1) / Fk : 0;
     }
+    mx = block_max_f(mx, sh.bs);
 
-    // ---- stable selection: contiguous candidate ranges per thread ----
-    const int64_t chunk = (ncand + nt - 1) / nt;
-    const int64_t k0 = imin(static_cast<int64_t>(tid) * chunk, ncand);
-    const int64_t k1 = imin(k0 + chunk, ncand);
-    uint32_t c_nt = 0, c_tie = 0;
-    if (!take_all) {
-        for (int64_t k = k0; k < k1; ++k) {
-            const uint32_t key = desc_key(score(k));
-            c_nt += key < kappa;
-            c_tie += key == kappa;
-        }
-    } else {
-        c_nt = static_cast<uint32_t>(k1 - k0);
-    }
-    uint64_t tot;
-    const uint64_t pre = block_excl_scan_u64((static_cast<uint64_t>(c_tie) << 32) | c_nt, sh, &tot);
-    uint64_t nt_before = pre & 0xffffffffu, tie_before = pre >> 32;
-    const uint64_t tot_nt = tot & 0xffffffffu, tot_tie = tot >> 32;
-    const uint64_t ties_kept = tot_tie < need_ties ? tot_tie : need_ties;
-    const int64_t m = static_cast<int64_t>(tot_nt + ties_kept);
-
+    const CutBoundary cb = cut_boundary(score, ncand, mx, p.top_p, sh.bs);
     int32_t* kept_out = leaf ? nullptr : p.kept + rh * p.nodes_total + p.lvl_off;
     int32_t* sel_out = leaf ? p.sel_blocks + rh * p.sel_cap : nullptr;
     int32_t* lsel_out = p.level_sel ? p.level_sel + p.lsel_off + rh * p.nodes_l : nullptr;
-    for (int64_t k = k0; k < k1; ++k) {
-        const int64_t node = cc.node(k);
-        bool keep;
-        int64_t pos;
-        if (take_all) {
-            keep = true;
-            pos = k;
-        } else {
-            const uint32_t key = desc_key(score(k));
-            if (key < kappa) {
-                keep = true;
-                pos = static_cast<int64_t>(nt_before + (tie_before < need_ties ? tie_before : need_ties));
-                ++nt_before;
-            } else if (key == kappa) {
-                keep = tie_before < need_ties;
-                pos = static_cast<int64_t>(nt_before + tie_before);
-                ++tie_before;
-            } else {
-                keep = false;
-                pos = 0;
+    // a thread's candidates are contiguous, so its parent id changes every b of them:
+    // keep the last one instead of reloading it per candidate
+    int64_t last_pi = -1, last_par = 0;
+    const int64_t kid_mask = (int64_t(1) << cc.lb) - 1;
+    const int64_t m = cut_compact(score, ncand, cb, sh.bs, [&](int64_t pos, int64_t k) {
+        int64_t node;
+        if (k < cc.nkids) {
+            const int64_t pi = k >> cc.lb;
+            if (pi != last_pi) {
+                last_pi = pi;
+                last_par = cc.up[pi];
             }
+            node = (last_par << cc.lb) | (k & kid_mask);
+        } else {
+            node = (cc.nc_up << cc.lb) + (k - cc.nkids);
         }
-        if (!keep) continue;
         if (kept_out) kept_out[pos] = static_cast<int32_t>(node);
         if (sel_out && pos < p.sel_cap) sel_out[pos] = static_cast<int32_t>(node);
         if (lsel_out) lsel_out[pos] = static_cast<int32_t>(node);
         if (lds_bm) atomicOr(&sh.bm[node >> 5], 1u << (node & 31));
         else __hip_atomic_fetch_or(bm + (node >> 5), 1u << (node & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
+    });
     if (lds_bm) {
         __syncthreads();
         for (int64_t w = tid; w < words; w += nt) bm[w] = sh.bm[w];
@@ -448,12 +514,138 @@ __global__ __launch_bounds__(kCutThreads) void route_cut_kernel(CutParams p) {
     }
     cc.nkids = kc << p.lb;
     cc.ncand = cc.nkids + (nc - (cc.nc_up << p.lb));
-    if (cc.ncand <= kCutStage) cut_body<true>(p, sh, cc, rh, nc);
-    else cut_body<false>(p, sh, cc, rh, nc);
+    if (cc.ncand <= kCutStage) cut_level<true>(p, sh, cc, rh, nc);
+    else cut_level<false>(p, sh, cc, rh, nc);
 }
 
 // ----------------------------------------------------------------------------
-// launcher
+// fused traversal of the upper levels
+// One workgroup per (row, query head) walks every level from the top down to
+// level li_lo in one launch (every fused level has at most kUpperNodes nodes
+// per (sequence, kv head)). Per level: the candidate ids are built in LDS from
+// the kept nodes of the level above, each candidate's summary row is scored
+// against the head's query (16 waves, a row per LPR lanes), and the same
+// exact cut runs on the LDS-resident scores. The kept set stays in LDS for the
+// next level and is written out (kept list, count, bitmap) for the levels
+// below li_lo.
+// ----------------------------------------------------------------------------
+constexpr int kUpperNodes = 8192;
+
+struct UpperParams {
+    const float* q;            // [rows, Hq, D]
+    RowInfo ri;
+    const float* summaries;
+    int64_t sum_off[ZHA_MAX_LEVELS];
+    int64_t nodes[ZHA_MAX_LEVELS];
+    int64_t sel_off[ZHA_MAX_LEVELS];
+    int64_t bm_off[ZHA_MAX_LEVELS];
+    int64_t nodes_total;
+    int32_t* kept;             // ws kept lists
+    int32_t* kept_cnt;         // [rows, Hq, L]
+    uint32_t* bitmap;          // ws kept bitmaps
+    int64_t bm_words_total;
+    int32_t* level_stats;
+    int32_t* level_sel;
+    int64_t rows;
+    int64_t cap;
+    int b, lb, L, li_lo, Hq, Hkv, G, T;
+    float top_p, scale;
+};
+
+struct UpperShared {
+    float sc[kUpperNodes];
+    int32_t cid[kUpperNodes];          // candidate node ids, ascending
+    int32_t par[kUpperNodes];          // kept nodes of the level above, ascending
+    uint32_t bm[kUpperNodes / 32 + 1];
+    BlockScratch bs;
+};
+
+template <int D>
+__global__ __launch_bounds__(kCutThreads) void route_upper_kernel(UpperParams p) {
+    __shared__ UpperShared sh;
+    constexpr int DPL = 16;                    // dims per lane
+    constexpr int LPR = D / DPL;               // lanes per summary row
+    constexpr int RPP = kWave / LPR;           // rows per wave pass
+    constexpr int UNR = 2;                     // passes issued together (1024 threads: <= 128 VGPRs)
+    const int hq = blockIdx.x, row = blockIdx.y;
+    const int kv = hq / p.G, s = row / p.T;
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nw = nt / kWave;
+    const int sub = lane / LPR, part = lane % LPR;
+    const int N = clamp_visible(p.ri, row, p.cap);
+    const int64_t rh = static_cast<int64_t>(row) * p.Hq + hq;
+    float qv[DPL];
+    load_row<DPL>(p.q + rh * D + part * DPL, qv);
+
+    int64_t npar = 0;                          // kept nodes of the level above
+    for (int li = p.L - 1; li >= p.li_lo; --li) {
+        const bool top = (li == p.L - 1);
+        const int64_t nc = static_cast<int64_t>(N) >> (p.lb * (li + 1));
+        const int64_t nc_up = top ? 0 : (static_cast<int64_t>(N) >> (p.lb * (li + 2)));
+        const int64_t nkids = npar << p.lb;
+        const int64_t ncand = nkids + (nc - (nc_up << p.lb));   // <= nc <= nodes[li] <= kUpperNodes
+        for (int64_t k = tid; k < ncand; k += nt) {
+            sh.cid[k] = static_cast<int32_t>(k < nkids ? ((static_cast<int64_t>(sh.par[k >> p.lb]) << p.lb) |
+                                                          (k & (p.b - 1)))
+                                                       : (nc_up << p.lb) + (k - nkids));
+        }
+        const int64_t words = (nc + 31) >> 5;
+        for (int64_t w = tid; w < words; w += nt) sh.bm[w] = 0u;
+        __syncthreads();
+
+        // ---- score the candidates: a row per LPR lanes, RPP rows per wave pass ----
+        const float* summ = p.summaries + p.sum_off[li] + (static_cast<int64_t>(s) * p.Hkv + kv) * p.nodes[li] * D;
+        float mx = -INFINITY;
+        for (int64_t kb = static_cast<int64_t>(wave) * RPP * UNR; kb < ncand; kb += static_cast<int64_t>(nw) * RPP * UNR) {
+            float x[UNR][DPL];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int64_t k = imin(kb + u * RPP + sub, ncand - 1);   // a present row; extra results are dropped
+                load_row<DPL>(summ + static_cast<int64_t>(sh.cid[k]) * D + part * DPL, x[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                float t = 0.f;
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) t = fmaf(qv[e], x[u][e], t);
+                t = fast_group_sum<LPR>(t) * p.scale;
+                const int64_t k = kb + u * RPP + sub;
+                if (k < ncand) {
+                    mx = fmaxf(mx, t);
+                    if (part == 0) sh.sc[k] = t;
+                }
+            }
+        }
+        mx = block_max_f(mx, sh.bs);           // its barriers also publish sc[]
+
+        // ---- the cut ----
+        auto score = [&](int64_t k) -> float { return sh.sc[k]; };
+        const CutBoundary cb = cut_boundary(score, ncand, mx, p.top_p, sh.bs);
+        int32_t* kept_out = p.kept + rh * p.nodes_total + p.sel_off[li];
+        int32_t* lsel_out = p.level_sel ? p.level_sel + p.rows * p.Hq * p.sel_off[li] + rh * p.nodes[li] : nullptr;
+        const int64_t m = cut_compact(score, ncand, cb, sh.bs, [&](int64_t pos, int64_t k) {
+            const int32_t node = sh.cid[k];
+            sh.par[pos] = node;                 // parents of the next level (cid holds this level's ids)
+            kept_out[pos] = node;
+            if (lsel_out) lsel_out[pos] = node;
+            atomicOr(&sh.bm[node >> 5], 1u << (node & 31));
+        });
+        __syncthreads();
+        uint32_t* bm = p.bitmap + rh * p.bm_words_total + p.bm_off[li];
+        for (int64_t w = tid; w < words; w += nt) bm[w] = sh.bm[w];
+        if (tid == 0) {
+            p.kept_cnt[rh * p.L + li] = static_cast<int32_t>(m);
+            if (p.level_stats) {
+                p.level_stats[(rh * p.L + li) * 2 + 0] = static_cast<int32_t>(ncand);
+                p.level_stats[(rh * p.L + li) * 2 + 1] = static_cast<int32_t>(m);
+            }
+        }
+        npar = m;
+        __syncthreads();
+    }
+}
+
+// ----------------------------------------------------------------------------
+// launchers
 // ----------------------------------------------------------------------------
 template <int D, int G>
 static void launch_score_t(dim3 grid, const ScoreParams& sp, hipStream_t st) {
@@ -474,6 +666,15 @@ static hipError_t launch_score_g(int G, dim3 grid, const ScoreParams& sp, hipStr
     return hipGetLastError();
 }
 
+// Lowest level (0-based, >= 1) from which every level up to the top is handled
+// by the fused traversal; g.L when none is (the leaf level is never fused: its
+// scan needs the whole chip and the group's shared reads).
+static int upper_from(const Geo& g) {
+    int lo = g.L;
+    while (lo - 1 >= 1 && g.nodes[lo - 1] <= kUpperNodes) --lo;
+    return lo;
+}
+
 hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
     const WsLayout& lay = *a.lay;
     char* ws = a.ws;
@@ -483,8 +684,50 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(ws + lay.bitmap);
     uint32_t* status = reinterpret_cast<uint32_t*>(ws + lay.status);
     const int pairs = a.rows * g.Hkv;
+    const int li_lo = upper_from(g);
 
-    for (int li = g.L - 1; li >= 0; --li) {
+    if (li_lo < g.L) {
+        UpperParams up{};
+        up.q = a.q;
+        up.ri = a.ri;
+        up.summaries = a.summaries;
+        for (int l = 0; l < ZHA_MAX_LEVELS; ++l) {
+            up.sum_off[l] = g.sum_off[l];
+            up.nodes[l] = g.nodes[l];
+            up.sel_off[l] = g.sel_off[l];
+            up.bm_off[l] = static_cast<int64_t>(lay.bm_off[l]);
+        }
+        up.nodes_total = g.nodes_total;
+        up.kept = kept;
+        up.kept_cnt = kept_cnt;
+        up.bitmap = bitmap;
+        up.bm_words_total = lay.bm_words_total;
+        up.level_stats = a.level_stats;
+        up.level_sel = a.level_sel;
+        up.rows = a.rows;
+        up.cap = g.cap;
+        up.b = g.b;
+        up.lb = g.lb;
+        up.L = g.L;
+        up.li_lo = li_lo;
+        up.Hq = g.Hq;
+        up.Hkv = g.Hkv;
+        up.G = g.G;
+        up.T = a.ri.T;
+        up.top_p = a.top_p;
+        up.scale = g.scale;
+        {
+            ProfScope ps("route_upper", 0, st);
+            if (g.D == 128)
+                hipLaunchKernelGGL(route_upper_kernel<128>, dim3(g.Hq, a.rows), dim3(kCutThreads), 0, st, up);
+            else
+                hipLaunchKernelGGL(route_upper_kernel<64>, dim3(g.Hq, a.rows), dim3(kCutThreads), 0, st, up);
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+
+    for (int li = li_lo - 1; li >= 0; --li) {
         const bool top = (li == g.L - 1);
         ScoreParams sp{};
         sp.q = a.q;

@@ -84,11 +84,6 @@ zha_status make_geo(const zha_geom* in, Geo* g) {
     return ZHA_OK;
 }
 
-int splits_for(const Geo& g, int rows) {
-    const int pairs = rows * g.Hkv;
-    const int s = (2048 + pairs - 1) / pairs;
-    return s < 1 ? 1 : (s > kAttnSplitsMax ? kAttnSplitsMax : s);
-}
 
 WsLayout layout(const Geo& g, int rows) {
     WsLayout L{};
@@ -110,12 +105,10 @@ WsLayout layout(const Geo& g, int rows) {
     }
     L.bm_words_total = bw;
     L.bitmap = take(R * g.Hq * static_cast<size_t>(bw) * 4);
-    L.abm_words = g.nodes[0] / 32 + 1;
-    L.abm = take(R * g.Hq * static_cast<size_t>(L.abm_words) * 4);
     L.aitems = take(R * g.Hkv * static_cast<size_t>(g.nodes[0] + 2) * 8);
     L.acnt = take(R * g.Hkv * 4);
-    L.splits = splits_for(g, rows);
-    L.partial = take(R * g.Hq * static_cast<size_t>(L.splits) * (g.D + 2) * 4);
+    L.plan = take((R * g.Hkv + 1) * 8);
+    L.partial = take((static_cast<size_t>(kAttnWorkgroups) + R * g.Hkv) * g.G * (g.D + 2) * 4);
     L.total = off;
     return L;
 }
@@ -291,7 +284,7 @@ zha_status zha_route(const zha_geom* geom, const float* q, int32_t t, const int3
 static zha_status attend_impl(const Geo& g, const float* q, int32_t t, const int32_t* q_pos, const void* K,
                               const void* V, const int32_t* seq_lens, const int32_t* sel_blocks, const int32_t* n_sel,
                               int32_t sel_capacity, float* out, float* lse, void* ws, const WsLayout& L, int rows,
-                              bool dense, hipStream_t s) {
+                              bool dense, bool bitmaps_ready, hipStream_t s) {
     AttendArgs a{};
     a.q = q;
     a.ri = RowInfo{seq_lens, q_pos, t};
@@ -306,6 +299,7 @@ static zha_status attend_impl(const Geo& g, const float* q, int32_t t, const int
     a.ws = static_cast<char*>(ws);
     a.lay = &L;
     a.dense = dense;
+    a.bitmaps_ready = bitmaps_ready;
     const hipError_t e = launch_attend(g, a, s);
     if (e != hipSuccess) return hip_fail(e, "attend launch");
     return ZHA_OK;
@@ -325,7 +319,7 @@ zha_status zha_sparse_attend(const zha_geom* geom, const float* q, int32_t t, co
     const WsLayout L = layout(g, rows);
     if ((st = check_ws(ws, ws_bytes, L.total))) return st;
     return attend_impl(g, q, t, q_pos, K, V, seq_lens, sel_blocks, n_sel, sel_capacity, out, lse, ws, L, rows, false,
-                       static_cast<hipStream_t>(stream));
+                       false, static_cast<hipStream_t>(stream));
 }
 
 zha_status zha_attend(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos, const void* K,
@@ -346,7 +340,7 @@ zha_status zha_attend(const zha_geom* geom, const float* q, int32_t t, const int
                          level_sel, ws, L, rows, s)))
         return st;
     return attend_impl(g, q, t, q_pos, K, V, seq_lens, sel_blocks, n_sel, sel_capacity, out, lse, ws, L, rows, false,
-                       s);
+                       true, s);
 }
 
 zha_status zha_dense_attend(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos, const void* K,
@@ -362,7 +356,7 @@ zha_status zha_dense_attend(const zha_geom* geom, const float* q, int32_t t, con
     const WsLayout L = layout(g, rows);
     if ((st = check_ws(ws, ws_bytes, L.total))) return st;
     return attend_impl(g, q, t, q_pos, K, V, seq_lens, nullptr, nullptr, 1, out, lse, ws, L, rows, true,
-                       static_cast<hipStream_t>(stream));
+                       false, static_cast<hipStream_t>(stream));
 }
 
 zha_status zha_read_device_status(void* ws, void* stream, uint32_t* out, int32_t clear) {

@@ -157,6 +157,59 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v, int lane) {
     return v;
 }
 
+// Inclusive scans over the 64 lanes of a wave in lane order, built from DPP
+// row shifts (within rows of 16 lanes) and row broadcasts (lane 15 of a row to
+// the next row, lane 31 to rows 2 and 3): six VALU steps, no LDS traffic.
+// Lane 63 ends with the wave's total (or maximum).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_scan_add_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL, ROW_MASK, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), CTRL, ROW_MASK, 0xF, false);
+    return v + ((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ uint64_t wave_scan_u64(uint64_t v) {
+    v = dpp_scan_add_u64<0x111, 0xF>(v);   // row_shr:1
+    v = dpp_scan_add_u64<0x112, 0xF>(v);   // row_shr:2
+    v = dpp_scan_add_u64<0x114, 0xF>(v);   // row_shr:4
+    v = dpp_scan_add_u64<0x118, 0xF>(v);   // row_shr:8
+    v = dpp_scan_add_u64<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_scan_add_u64<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_scan_max_f(float v) {
+    const int t = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xF, false);
+    return fmaxf(v, __int_as_float(t));
+}
+__device__ __forceinline__ float wave_scan_max_f(float v) {
+    v = dpp_scan_max_f<0x111, 0xF>(v);
+    v = dpp_scan_max_f<0x112, 0xF>(v);
+    v = dpp_scan_max_f<0x114, 0xF>(v);
+    v = dpp_scan_max_f<0x118, 0xF>(v);
+    v = dpp_scan_max_f<0x142, 0xA>(v);
+    v = dpp_scan_max_f<0x143, 0xC>(v);
+    return v;
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_scan_max_u32(uint32_t v) {
+    const uint32_t t = __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, ROW_MASK, 0xF, false);
+    return v > t ? v : t;
+}
+__device__ __forceinline__ uint32_t wave_scan_max_u32(uint32_t v) {
+    v = dpp_scan_max_u32<0x111, 0xF>(v);
+    v = dpp_scan_max_u32<0x112, 0xF>(v);
+    v = dpp_scan_max_u32<0x114, 0xF>(v);
+    v = dpp_scan_max_u32<0x118, 0xF>(v);
+    v = dpp_scan_max_u32<0x142, 0xA>(v);
+    v = dpp_scan_max_u32<0x143, 0xC>(v);
+    return v;
+}
+__device__ __forceinline__ uint64_t lane63_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Order-preserving map of a float to uint32 that sorts DESCENDING scores first:
 // a < b as keys  <=>  score a > score b.
 __device__ __forceinline__ uint32_t desc_key(float s) {

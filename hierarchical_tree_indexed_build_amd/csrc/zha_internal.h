@@ -12,7 +12,7 @@ namespace zha {
 
 constexpr int kWave = 64;
 constexpr int kMaxGroup = 16;          // H_q / H_kv handled by one kernel group
-constexpr int kAttnSplitsMax = 256;    // split-K partitions per (row, kv head)
+constexpr int kAttnWorkgroups = 512;   // attention workgroups per launch (partial slots: this + pairs)
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
@@ -38,12 +38,10 @@ struct WsLayout {
     size_t bitmap;        // uint32 [rows, Hq, bm_words_total] kept bitmaps per level (a spare bit for index nodes[l])
     size_t bm_off[ZHA_MAX_LEVELS];    // word offset of each level inside a row-head bitmap
     int64_t bm_words_total;
-    size_t abm;           // uint32 [rows, Hq, abm_words] attention head bitmaps (leaf chunks + current chunk)
-    int64_t abm_words;
     size_t aitems;        // int2   [rows, Hkv, nodes[0] + 2] attention items (block, head mask)
     size_t acnt;          // int32  [rows, Hkv]
-    size_t partial;       // float  [rows, Hq, splits, D + 2] split-K partial states
-    int splits;
+    size_t plan;          // int64  [rows * Hkv + 1] exclusive prefix of attention groups per (row, kv head)
+    size_t partial;       // float  [kAttnWorkgroups + rows * Hkv, G, D + 2] split-K partial states
     size_t total;
 };
 
@@ -114,6 +112,7 @@ struct AttendArgs {
     char* ws;
     const WsLayout* lay;
     bool dense;
+    bool bitmaps_ready;       // the route already wrote the level-1 kept bitmaps
 };
 hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st);
 

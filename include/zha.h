@@ -159,7 +159,9 @@ ZHA_API zha_status zha_sparse_attend(const zha_geom* geom, const float* q, int32
                              const int32_t* sel_blocks, const int32_t* n_sel, int32_t sel_capacity,
                              float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* zha_route followed by zha_sparse_attend on one stream. */
+/* zha_route followed by zha_sparse_attend on one stream (identical results).
+ * One difference: if a kept list overflows sel_capacity (ZHA_DEV_SEL_OVERFLOW),
+ * the list is truncated but the attention still covers every kept chunk. */
 ZHA_API zha_status zha_attend(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos,
                       const void* K, const void* V, const float* summaries, const int32_t* seq_lens,
                       float top_p, int32_t sel_capacity, int32_t* sel_blocks, int32_t* n_sel,
@@ -181,7 +183,7 @@ ZHA_API zha_status zha_read_device_status(void* ws, void* stream, uint32_t* out,
  * §Latency Scaling, eqs. (3)-(4)). While active, every launch whose label
  * matches `label` is bracketed by two HIP events on its own stream. Labels:
  * build_level@l, append_fused, append_rows, advance_seq, route_score@l,
- * route_cut@l, attn_union, attend, attend_combine; a label without "@l"
+ * route_cut@l, attn_bitmap, attn_items, attend, attend_combine; a label without "@l"
  * matches every level. NULL stops recording. At most 8192 launches are kept
  * (later ones are counted as dropped). Host-side state shared by all threads:
  * for single-threaded benchmarks only. Creating the event pool is the only

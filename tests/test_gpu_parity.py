@@ -291,6 +291,35 @@ def test_selection_capacity_overflow_truncates():
     assert t.equal(sel[..., :50], sel_full[..., :50])
 
 
+def test_attend_covers_every_kept_chunk_when_the_list_overflows():
+    """zha_attend truncates an overflowing id list but still attends every kept chunk."""
+    t = torch()
+    w = _w("tiny", 0, None)
+    say("[attend overflow] tiny, sel_capacity 50")
+    st = Staged(w)
+    T = w.queries_per_step
+    q_pos = _qpos(st, T)
+    qn, q, sel_full, nsel_full, _, _, p = _route(st, T, q_pos)
+    assert int(nsel_full.max().item()) > 50
+    sel, nsel, _, _ = st.route_buffers(w.batch * T, 50)
+    out = t.zeros_like(q)
+    lse = t.zeros(q.shape[:3], dtype=t.float32, device="cuda")
+    Z.read_device_status(st.cache.ws, clear=True)
+    Z.attend(st.geom, q, q_pos, st.cache.K, st.cache.V, st.cache.summaries, st.cache.seq_lens, p, sel, nsel, out,
+             lse, st.cache.ws)
+    status = Z.read_device_status(st.cache.ws, clear=True)
+    assert status & Z.ZHA_DEV_SEL_OVERFLOW
+    assert t.equal(nsel, nsel_full)
+    o_np, l_np = out.cpu().numpy(), lse.cpu().numpy()
+    s_np, n_np = sel_full.cpu().numpy(), nsel_full.cpu().numpy()
+    for t_ in range(T):
+        N = int(q_pos[0, t_].item()) + 1
+        I = O.index_set(s_np[0, t_, 0, :n_np[0, t_, 0]], N, w.branching)
+        o, l = O.attend(qn[0, t_, 0], st.Kf[0, 0], st.Vf[0, 0], I, w.scale)
+        e = max(np.abs(o_np[0, t_, 0] - o).max(), abs(l_np[0, t_, 0] - l))
+        assert e <= attn_tol(w), (t_, e)
+
+
 def test_repeatable_bits():
     t = torch()
     w = _w("decode1m", 2, 1)
