@@ -117,13 +117,7 @@ __global__ __launch_bounds__(kItemsThreads) void attn_items_kernel(ItemsParams p
     uint64_t cnt = 0;
     for (int64_t wd = w0; wd < w1; ++wd) cnt += __popc(word(wd, heads));
     // block exclusive scan of the counts, in thread order
-    uint64_t inc = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t lo = __shfl_up(static_cast<uint32_t>(inc), o, 64);
-        const uint32_t hi = __shfl_up(static_cast<uint32_t>(inc >> 32), o, 64);
-        if (lane >= o) inc += (static_cast<uint64_t>(hi) << 32) | lo;
-    }
+    const uint64_t inc = wave_scan_u64(cnt);
     if (lane == 63) red[w] = inc;
     __syncthreads();
     uint64_t before = 0, total = 0;
@@ -209,13 +203,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnParams p) {
     for (int base = 0; base < p.pairs; base += nt) {
         const int pr = base + tid;
         const int64_t v = pr < p.pairs ? pair_groups(p, pr) : 0;
-        uint64_t inc = static_cast<uint64_t>(v);
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t lo = __shfl_up(static_cast<uint32_t>(inc), o, 64);
-            const uint32_t hi = __shfl_up(static_cast<uint32_t>(inc >> 32), o, 64);
-            if (lane >= o) inc += (static_cast<uint64_t>(hi) << 32) | lo;
-        }
+        const uint64_t inc = wave_scan_u64(static_cast<uint64_t>(v));
         if (lane == 63) red[w] = static_cast<int64_t>(inc);
         __syncthreads();
         int64_t before = 0, total = 0;

@@ -160,6 +160,10 @@ struct BlockScratch {
     uint32_t red_u32[kCutWaves];
     uint64_t bcast_u64[2];
     uint32_t bcast_u32[2];
+    uint32_t wkey[kWave];       // single-wave cut: keys, masses in rank order, prefix masses
+    uint64_t wmass[kWave];
+    uint64_t wpre[kWave];
+    int32_t wcount;
 };
 
 // Block reductions: a DPP scan per wave (lane 63 holds the wave's result),
@@ -304,6 +308,44 @@ __device__ __forceinline__ CutBoundary cut_boundary(ScoreAt score, int64_t n, fl
     const uint64_t Fk = mass_fx(desc_key_to_float(prefix), mx);
     cb.need_ties = Fk ? (rem + Fk - 1) / Fk : 0;
     return cb;
+}
+
+// The same cut for n <= 64 candidates, run by one wave with candidate k on
+// lane k and no block barriers: each lane ranks its candidate in (key asc,
+// index asc) order against the others' keys, the masses are laid out in rank
+// order and prefix-summed, and a candidate is kept when the mass ranked before
+// it is still below ceil(top_p * total). This keeps exactly the candidates the
+// boundary search keeps: all keys below the boundary key, and of the boundary
+// key's ties the first in index order. emit(pos, k) for every kept one, pos
+// ascending in k. Returns the number kept (on every lane).
+template <class ScoreAt, class Emit>
+__device__ __forceinline__ int wave_cut_small(ScoreAt score, int n, float top_p, BlockScratch& bs, Emit emit) {
+    const int lane = threadIdx.x & 63;
+    const bool valid = lane < n;
+    const float s = valid ? score(lane) : -INFINITY;
+    const float mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_scan_max_f(s)), 63));
+    const uint64_t F = valid ? mass_fx(s, mx) : 0;
+    const uint32_t key = desc_key(s);
+    const uint64_t E = lane63_u64(wave_scan_u64(F));
+    const bool take_all = (top_p >= 1.0f) || n == 0;
+    uint64_t rem = static_cast<uint64_t>(ceil(static_cast<double>(top_p) * static_cast<double>(E)));
+    if (rem == 0) rem = 1;
+    bs.wkey[lane] = key;
+    __builtin_amdgcn_wave_barrier();
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+        const uint32_t kj = bs.wkey[j];
+        rank += (kj < key) || (kj == key && j < lane);
+    }
+    if (valid) bs.wmass[rank] = F;
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t mj = lane < n ? bs.wmass[lane] : 0;
+    bs.wpre[lane] = wave_scan_u64(mj) - mj;
+    __builtin_amdgcn_wave_barrier();
+    const bool kept = valid && (take_all || bs.wpre[rank] < rem);
+    const unsigned long long bal = __ballot(kept);
+    if (kept) emit(static_cast<int64_t>(__popcll(bal & ((1ull << lane) - 1ull))), static_cast<int64_t>(lane));
+    return __popcll(bal);
 }
 
 // Stable compaction of the kept candidates: emit(pos, k) for each kept k, pos
@@ -452,7 +494,6 @@ __device__ __forceinline__ void cut_level(const CutParams& p, CutShared& sh, con
     }
     mx = block_max_f(mx, sh.bs);
 
-    const CutBoundary cb = cut_boundary(score, ncand, mx, p.top_p, sh.bs);
     int32_t* kept_out = leaf ? nullptr : p.kept + rh * p.nodes_total + p.lvl_off;
     int32_t* sel_out = leaf ? p.sel_blocks + rh * p.sel_cap : nullptr;
     int32_t* lsel_out = p.level_sel ? p.level_sel + p.lsel_off + rh * p.nodes_l : nullptr;
@@ -460,7 +501,7 @@ __device__ __forceinline__ void cut_level(const CutParams& p, CutShared& sh, con
     // keep the last one instead of reloading it per candidate
     int64_t last_pi = -1, last_par = 0;
     const int64_t kid_mask = (int64_t(1) << cc.lb) - 1;
-    const int64_t m = cut_compact(score, ncand, cb, sh.bs, [&](int64_t pos, int64_t k) {
+    auto emit = [&](int64_t pos, int64_t k) {
         int64_t node;
         if (k < cc.nkids) {
             const int64_t pi = k >> cc.lb;
@@ -477,7 +518,19 @@ __device__ __forceinline__ void cut_level(const CutParams& p, CutShared& sh, con
         if (lsel_out) lsel_out[pos] = static_cast<int32_t>(node);
         if (lds_bm) atomicOr(&sh.bm[node >> 5], 1u << (node & 31));
         else __hip_atomic_fetch_or(bm + (node >> 5), 1u << (node & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    });
+    };
+    int64_t m;
+    if (ncand <= kWave) {
+        if ((tid >> 6) == 0) {
+            const int mw = wave_cut_small(score, static_cast<int>(ncand), p.top_p, sh.bs, emit);
+            if (tid == 0) sh.bs.wcount = mw;
+        }
+        __syncthreads();
+        m = sh.bs.wcount;
+    } else {
+        const CutBoundary cb = cut_boundary(score, ncand, mx, p.top_p, sh.bs);
+        m = cut_compact(score, ncand, cb, sh.bs, emit);
+    }
     if (lds_bm) {
         __syncthreads();
         for (int64_t w = tid; w < words; w += nt) bm[w] = sh.bm[w];
@@ -615,21 +668,32 @@ __global__ __launch_bounds__(kCutThreads) void route_upper_kernel(UpperParams p)
                 }
             }
         }
-        mx = block_max_f(mx, sh.bs);           // its barriers also publish sc[]
-
         // ---- the cut ----
         auto score = [&](int64_t k) -> float { return sh.sc[k]; };
-        const CutBoundary cb = cut_boundary(score, ncand, mx, p.top_p, sh.bs);
         int32_t* kept_out = p.kept + rh * p.nodes_total + p.sel_off[li];
         int32_t* lsel_out = p.level_sel ? p.level_sel + p.rows * p.Hq * p.sel_off[li] + rh * p.nodes[li] : nullptr;
-        const int64_t m = cut_compact(score, ncand, cb, sh.bs, [&](int64_t pos, int64_t k) {
+        auto emit = [&](int64_t pos, int64_t k) {
             const int32_t node = sh.cid[k];
             sh.par[pos] = node;                 // parents of the next level (cid holds this level's ids)
             kept_out[pos] = node;
             if (lsel_out) lsel_out[pos] = node;
             atomicOr(&sh.bm[node >> 5], 1u << (node & 31));
-        });
-        __syncthreads();
+        };
+        int64_t m;
+        if (ncand <= kWave) {                  // one wave, no block steps
+            __syncthreads();                   // publishes sc[]
+            if (wave == 0) {
+                const int mw = wave_cut_small(score, static_cast<int>(ncand), p.top_p, sh.bs, emit);
+                if (lane == 0) sh.bs.wcount = mw;
+            }
+            __syncthreads();
+            m = sh.bs.wcount;
+        } else {
+            mx = block_max_f(mx, sh.bs);       // its barriers also publish sc[]
+            const CutBoundary cb = cut_boundary(score, ncand, mx, p.top_p, sh.bs);
+            m = cut_compact(score, ncand, cb, sh.bs, emit);
+            __syncthreads();
+        }
         uint32_t* bm = p.bitmap + rh * p.bm_words_total + p.bm_off[li];
         for (int64_t w = tid; w < words; w += nt) bm[w] = sh.bm[w];
         if (tid == 0) {
