@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the kernel's HBM traffic per launch from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) of --timed-only --copy-probe-mib M, then exit")
     return ap.parse_args()
 
 
@@ -252,6 +255,61 @@ def measured_traffic(kernel: str, workload: str):
     return int(rec["traffic_bytes_per_launch"])
 
 
+KERNEL_SYMBOLS = {"attend": "attend_kernel<", "route_score": "route_score_kernel<", "route_cut": "route_cut_kernel"}
+
+
+def _counter_rows(run_dir: str, counter: str):
+    """(dispatch id, kernel name, value) of every dispatch in a rocprofv3 --pmc csv run."""
+    import csv
+    paths = []
+    for dp, _, fs in os.walk(run_dir):
+        paths += [os.path.join(dp, f) for f in fs if f.endswith("counter_collection.csv")]
+    if len(paths) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {run_dir}, found {len(paths)}")
+    acc = {}
+    with open(paths[0]) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, v = acc.get(d, (r["Kernel_Name"], 0.0))
+            acc[d] = (name, v + float(r["Counter_Value"]))     # summed over agents/instances
+    return [(d, n, v) for d, (n, v) in sorted(acc.items())]
+
+
+def write_traffic(fetch_dir: str, write_dir: str, kernel: str, workload: str, probe_mib: int, steps: int):
+    """Turn two counter runs of `bench.py --timed-only --copy-probe-mib M` (FETCH_SIZE, then
+    WRITE_SIZE, both in KiB per dispatch) into HBM bytes per launch of `kernel`: each counter is
+    scaled by (copy size / its reading for the copy probe) and averaged over the last `steps`
+    launches, which are the timed ones."""
+    sym = KERNEL_SYMBOLS[kernel.split("@")[0]]
+    probe = probe_mib << 20
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter)
+        copies = [v for _, n, v in rows if "copyBuffer" in n]
+        if not copies:
+            raise SystemExit(f"{counter}: no copy kernel found in {d}")
+        factor = probe / (max(copies) * 1024.0)
+        vals = [v * 1024.0 * factor for _, n, v in rows if sym in n][-steps:]
+        if len(vals) < steps:
+            raise SystemExit(f"{counter}: {len(vals)} launches of {sym} in {d}, expected {steps}")
+        per[counter] = {"factor": round(factor, 4), "bytes_per_launch": sum(vals) / len(vals),
+                        "copy_probe_kib": max(copies)}
+    name = kernel.split("@")[0]
+    with open(os.path.join(ROOT, "hierarchical_tree_indexed_build_amd", "csrc", KERNEL_SOURCES[name]), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    rec = {"kernel": kernel, "workload": workload, "source_sha256": sha, "launches": steps,
+           "copy_probe_bytes": probe,
+           "fetch": per["FETCH_SIZE"], "write": per["WRITE_SIZE"],
+           "traffic_bytes_per_launch": int(round(per["FETCH_SIZE"]["bytes_per_launch"]
+                                                 + per["WRITE_SIZE"]["bytes_per_launch"]))}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 # ----------------------------------------------------------------------------
 def main():
     args = parse()
@@ -259,6 +317,11 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
               f"multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_from:
+        w = W.get_workload(args.workload)
+        write_traffic(*args.traffic_from, args.kernel, w.name, args.copy_probe_mib,
+                      args.steps if args.steps is not None else w.steps)
+        return
     import torch
     w = W.get_workload(args.workload)
     steps = args.steps if args.steps is not None else w.steps
