@@ -19,6 +19,9 @@
 //    slice of d; waves merge in LDS and write one (max, sum, acc[d]) partial
 //    per head and split.
 //  * attend_combine_kernel - per (row, head): LSE merge of the splits.
+// The attention's work plan is the prefix of the groups over the (row, kv
+// head) pairs: attn_plan_kernel writes it for more than 64 pairs; with fewer,
+// the attention and combine kernels take it from the pairs' counts themselves.
 #include <algorithm>
 
 #include "zha_device.h"
@@ -170,9 +173,10 @@ struct AttnParams {
     const int32_t* acnt;       // [pairs] items per pair (sparse)
     int64_t item_stride;
     int64_t* plan;             // [pairs + 1] exclusive prefix of groups per pair
-    float* partial;            // [nwg + pairs, G, D + 2]
+    float* partial;            // [nwg + pairs, G, D + 4]: max, sum, 2 pad, acc[D]
     int64_t cap;
     int b, lb, lgpi, Hq, Hkv, pairs, nwg, dense;
+    int wave_plan;             // pairs <= 64: kernels take the plan from the counts themselves
     float qscale;              // scale * log2(e)
 };
 
@@ -217,6 +221,51 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnParams p) {
     }
     if (tid == 0) p.plan[p.pairs] = carry;
 }
+
+// The group prefix over the pairs, as the attention and combine kernels see
+// it. With at most 64 pairs every wave builds it itself: lane pr loads pair
+// pr's group count and one wave scan gives plan[pr + 1] on lane pr, read back
+// with readlane (pr is uniform). Otherwise it is the plan kernel's output.
+struct PlanView {
+    const int64_t* plan;
+    uint64_t incl;             // wave plan: inclusive prefix on lane pr
+    int pairs;
+    bool wave;
+    __device__ __forceinline__ PlanView(const AttnParams& p) : plan(p.plan), incl(0), pairs(p.pairs), wave(p.wave_plan != 0) {
+        if (wave) {
+            const int lane = threadIdx.x & (kWave - 1);
+            incl = wave_scan_u64(lane < pairs ? static_cast<uint64_t>(pair_groups(p, lane)) : 0ull);
+        }
+    }
+    __device__ __forceinline__ int64_t at(int pr) const {     // plan[pr], 0 <= pr <= pairs
+        if (!wave) return plan[pr];
+        if (pr == 0) return 0;
+        const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(incl)), pr - 1));
+        const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(incl >> 32)), pr - 1));
+        return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+    }
+    __device__ __forceinline__ int64_t total() const { return at(pairs); }
+    // the last pair whose first group is at or before r (plan[pr] <= r)
+    __device__ __forceinline__ int first_pair(int64_t r) const {
+        if (wave) {
+            const int lane = threadIdx.x & (kWave - 1);
+            const int64_t excl = at_lane_excl();
+            const unsigned long long bal = __ballot(lane < pairs && excl <= r);
+            return __popcll(bal) - 1;                       // plan is nondecreasing: a prefix of lanes
+        }
+        int lo = 0, hi = pairs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (plan[mid] <= r) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    }
+    __device__ __forceinline__ int64_t at_lane_excl() const {  // plan[lane] on each lane (wave plan)
+        const uint64_t prev = __shfl_up(incl, 1);
+        return (threadIdx.x & (kWave - 1)) == 0 ? 0 : static_cast<int64_t>(prev);
+    }
+};
 
 template <typename KT, int D, int G>
 struct AttnCfg {
@@ -273,25 +322,20 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
     const int wg = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int part = lane % LPT, tsub = lane / LPT;
-    const int64_t total = p.plan[p.pairs];
+    const PlanView pv(p);
+    const int64_t total = pv.total();
     const int64_t chunk = attn_chunk(total, p.nwg);
     const int64_t r0 = static_cast<int64_t>(wg) * chunk;
     if (r0 >= total) return;
     const int64_t r1 = imin(r0 + chunk, total);
-    // first pair of the slice: the last pr with plan[pr] <= r0
-    int lo = 0, hi = p.pairs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (p.plan[mid] <= r0) lo = mid;
-        else hi = mid - 1;
-    }
+    const int lo = pv.first_pair(r0);          // first pair of the slice
     const int gpi = 1 << p.lgpi;
     const int tg = p.b >= kGroupTokens ? kGroupTokens : p.b;
 
     for (int pr = lo; pr < p.pairs; ++pr) {
-        const int64_t pg0 = p.plan[pr];
+        const int64_t pg0 = pv.at(pr);
         if (pg0 >= r1) break;
-        const int64_t ga = imax(r0, pg0) - pg0, gb = imin(r1, p.plan[pr + 1]) - pg0;   // this pair's groups here
+        const int64_t ga = imax(r0, pg0) - pg0, gb = imin(r1, pv.at(pr + 1)) - pg0;   // this pair's groups here
         if (ga >= gb) continue;                                  // a pair with no groups
         const int row = pr / p.Hkv, kv = pr % p.Hkv;
         const int s = row / p.ri.T;
@@ -445,20 +489,20 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
             }
         }
         __syncthreads();
-        float* pout = p.partial + static_cast<int64_t>(wg + pr) * G * (D + 2);
-        for (int idx = threadIdx.x; idx < G * (D + 2); idx += blockDim.x) {
-            const int h = idx / (D + 2), c = idx % (D + 2);
+        float* pout = p.partial + static_cast<int64_t>(wg + pr) * G * (D + 4);
+        for (int idx = threadIdx.x; idx < G * (D + 4); idx += blockDim.x) {
+            const int h = idx / (D + 4), c = idx % (D + 4);
             float M = -INFINITY;
 #pragma unroll
             for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
             float out = 0.f;
             if (c == 0) {
                 out = M;
-            } else {
+            } else if (c == 1 || c >= 4) {
 #pragma unroll
                 for (int w = 0; w < NW; ++w) {
                     const float f = (sm_m[w][h] == -INFINITY) ? 0.f : fast_exp2(sm_m[w][h] - M);
-                    out += f * (c == 1 ? sm_l[w][h] : sm_acc[w][h][c - 2]);
+                    out += f * (c == 1 ? sm_l[w][h] : sm_acc[w][h][c - 4]);
                 }
             }
             pout[idx] = out;
@@ -469,23 +513,31 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
 
 // ----------------------------------------------------------------------------
 // LSE merge of a pair's segments: one workgroup per (row, query head)
+// Thread (group, quad) merges every NGRP-th slot of the pair for four
+// dimensions: a slot's max, sum and float4 of the accumulator arrive in one
+// round of loads, kCombineUnroll slots at a time, into a private online LSE
+// state. The NGRP states then merge through LDS.
 // ----------------------------------------------------------------------------
-constexpr int kCombineThreads = 1024;   // 1024/D slot subsets per dimension: many loads in flight
-constexpr int kCombineChunk = 1024;     // slots staged in LDS at a time
+constexpr int kCombineThreads = 1024;
+constexpr int kCombineUnroll = 8;
 
 template <int D, int G>
 __global__ __launch_bounds__(kCombineThreads) void attend_combine_kernel(AttnParams p, float* out, float* lse) {
-    __shared__ float fs[kCombineChunk];
-    __shared__ float red[kCombineThreads / kWave];
-    __shared__ float part_acc[kCombineThreads];
+    constexpr int Q = D / 4;                        // float4 quads of a row
+    constexpr int NGRP = kCombineThreads / Q;       // slot groups
+    constexpr int U = kCombineUnroll;
+    constexpr int64_t SS = static_cast<int64_t>(G) * (D + 4);   // floats per slot
+    __shared__ float sm_m[NGRP], sm_l[NGRP];
+    __shared__ float4 sm_a[NGRP][Q];
     const int64_t rh = blockIdx.x;
     const int row = static_cast<int>(rh / p.Hq), hq = static_cast<int>(rh % p.Hq);
     const int kv = hq / G, h = hq % G;
     const int pr = row * p.Hkv + kv;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t total = p.plan[p.pairs];
+    const int tid = threadIdx.x, quad = tid % Q, grp = tid / Q;
+    const PlanView pv(p);
+    const int64_t total = pv.total();
     const int64_t chunk = attn_chunk(total, p.nwg);
-    const int64_t g0 = p.plan[pr], g1 = p.plan[pr + 1];
+    const int64_t g0 = pv.at(pr), g1 = pv.at(pr + 1);
     if (g0 >= g1) {                                              // nothing visible
         if (tid < D) out[rh * D + tid] = 0.f;
         if (tid == 0 && lse) lse[rh] = -INFINITY;
@@ -493,50 +545,71 @@ __global__ __launch_bounds__(kCombineThreads) void attend_combine_kernel(AttnPar
     }
     const int64_t w0 = g0 / chunk, w1 = (g1 - 1) / chunk;
     const int nslot = static_cast<int>(w1 - w0 + 1);
-    const float* pp = p.partial + ((w0 + pr) * G + h) * (D + 2);   // slot i at pp + i * G * (D + 2)
-    constexpr int64_t SS = static_cast<int64_t>(G) * (D + 2);
-    float M = -INFINITY;
-    for (int i = tid; i < nslot; i += kCombineThreads) M = fmaxf(M, pp[i * SS]);
-    M = group_max<kWave>(M);
-    if (lane == 0) red[wave] = M;
-    __syncthreads();
-    M = red[0];
+    const float* pp = p.partial + ((w0 + pr) * G + h) * (D + 4);   // slot i at pp + i * SS
+    float M = -INFINITY, L = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i0 = grp; i0 < nslot; i0 += NGRP * U) {
+        float mi[U], li[U];
+        float4 ai[U];
 #pragma unroll
-    for (int i = 1; i < kCombineThreads / kWave; ++i) M = fmaxf(M, red[i]);
-    __syncthreads();
-    constexpr int R = kCombineThreads / D;                      // slot subsets per dimension
-    const int dim = tid % D, sub = tid / D;
-    float a = 0.f, Lp = 0.f;
-    for (int c0 = 0; c0 < nslot; c0 += kCombineChunk) {
-        const int c1 = min(nslot, c0 + kCombineChunk);
-        for (int i = c0 + tid; i < c1; i += kCombineThreads) {
-            const float mi = pp[i * SS];
-            const float f = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M);
-            fs[i - c0] = f;
-            if (f != 0.f) Lp = fmaf(f, pp[i * SS + 1], Lp);
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * NGRP;
+            if (i < nslot) {
+                const float* sp = pp + i * SS;
+                mi[u] = sp[0];
+                li[u] = sp[1];
+                ai[u] = *reinterpret_cast<const float4*>(sp + 4 + 4 * quad);
+            } else {
+                mi[u] = -INFINITY;
+                li[u] = 0.f;
+                ai[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
-        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (mi[u] == -INFINITY) continue;
+            const float Mn = fmaxf(M, mi[u]);
+            const float fo = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+            const float fi = fast_exp2(mi[u] - Mn);
+            L = L * fo + li[u] * fi;
+            A.x = A.x * fo + ai[u].x * fi;
+            A.y = A.y * fo + ai[u].y * fi;
+            A.z = A.z * fo + ai[u].z * fi;
+            A.w = A.w * fo + ai[u].w * fi;
+            M = Mn;
+        }
+    }
+    if (quad == 0) {
+        sm_m[grp] = M;
+        sm_l[grp] = L;
+    }
+    sm_a[grp][quad] = A;
+    __syncthreads();
+    if (tid < Q) {
+        float Mx = -INFINITY;
 #pragma unroll 8
-        for (int i = c0 + sub; i < c1; i += R) {
-            const float f = fs[i - c0];
-            if (f != 0.f) a = fmaf(f, pp[i * SS + 2 + dim], a);
+        for (int g = 0; g < NGRP; ++g) Mx = fmaxf(Mx, sm_m[g]);
+        float Lt = 0.f;
+        float4 At = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+        for (int g = 0; g < NGRP; ++g) {
+            const float mg = sm_m[g];
+            const float f = (mg == -INFINITY) ? 0.f : fast_exp2(mg - Mx);
+            Lt += f * sm_l[g];
+            const float4 a = sm_a[g][tid];
+            At.x += f * a.x;
+            At.y += f * a.y;
+            At.z += f * a.z;
+            At.w += f * a.w;
         }
-        __syncthreads();
+        const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+        float* o = out + rh * D + 4 * tid;            // caller memory: no alignment assumed
+        o[0] = At.x * inv;
+        o[1] = At.y * inv;
+        o[2] = At.z * inv;
+        o[3] = At.w * inv;
+        if (tid == 0 && lse) lse[rh] = (Lt > 0.f) ? (Mx + __log2f(Lt)) * kLn2 : -INFINITY;
     }
-    Lp = group_sum<kWave>(Lp);
-    if (lane == 0) red[wave] = Lp;
-    part_acc[tid] = a;
-    __syncthreads();
-    float L = 0.f;
-#pragma unroll
-    for (int i = 0; i < kCombineThreads / kWave; ++i) L += red[i];
-    if (tid < D) {
-        float t = 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r) t += part_acc[r * D + tid];
-        out[rh * D + tid] = (L > 0.f) ? t / L : 0.f;
-    }
-    if (tid == 0 && lse) lse[rh] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ----------------------------------------------------------------------------
@@ -626,13 +699,16 @@ hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st) {
     ap.pairs = pairs;
     ap.nwg = kAttnWorkgroups;
     ap.dense = a.dense ? 1 : 0;
+    ap.wave_plan = pairs <= kWave ? 1 : 0;
     ap.qscale = g.scale * kLog2e;
-    {
-        ProfScope ps("attn_plan", 0, st);
-        hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, ap);
+    if (!ap.wave_plan) {
+        {
+            ProfScope ps("attn_plan", 0, st);
+            hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, ap);
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const bool bf = g.kv_dtype == ZHA_KV_BF16;
     if (g.D == 128)
         return bf ? attn_g<uint16_t, 128>(g.G, ap, a.rows, g.Hq, a.out, a.lse, st)

@@ -1,6 +1,7 @@
 // zha_abi.hip - the extern "C" entry points of libzha: argument validation,
 // size and offset arithmetic, workspace layout, and kernel sequencing on the
 // caller's stream. Every host-detectable error is returned before any launch.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -108,7 +109,27 @@ WsLayout layout(const Geo& g, int rows) {
     L.aitems = take(R * g.Hkv * static_cast<size_t>(g.nodes[0] + 2) * 8);
     L.acnt = take(R * g.Hkv * 4);
     L.plan = take((R * g.Hkv + 1) * 8);
-    L.partial = take((static_cast<size_t>(kAttnWorkgroups) + R * g.Hkv) * g.G * (g.D + 2) * 4);
+    L.partial = take((static_cast<size_t>(kAttnWorkgroups) + R * g.Hkv) * g.G * (g.D + 4) * 4);
+    // the split cut: candidates of a level are at most its node slots
+    const int64_t cand = g.nodes[0];
+    const int64_t slices = (cand + kSplitSlice - 1) / kSplitSlice;
+    L.split = R * g.Hq <= static_cast<size_t>(kSplitMaxPairs) && slices <= kSplitMaxSlices;
+    if (L.split) {
+        int64_t pm = 1;
+        for (int l = 0; l < g.L; ++l) {
+            const int64_t slots = (l == g.L - 1) ? (g.nodes[l] + g.b - 1) / g.b : g.nodes[l + 1] + 1;
+            pm = std::max<int64_t>(pm, (slots + kScoreParents - 1) / kScoreParents);
+        }
+        L.cand_stride = cand;
+        L.pmax_stride = pm;
+        L.slice_stride = slices;
+        L.cand_sc = take(R * g.Hq * static_cast<size_t>(cand) * 4);
+        L.cand_nd = take(R * g.Hq * static_cast<size_t>(cand) * 4);
+        L.pmax = take(R * g.Hq * static_cast<size_t>(pm) * 4);
+        L.chist = take(R * g.Hq * static_cast<size_t>(kCutBins) * 8);
+        L.cinfo = take(R * g.Hq * sizeof(SplitInfo));
+        L.cslice = take(R * g.Hq * static_cast<size_t>(slices) * 8);
+    }
     L.total = off;
     return L;
 }

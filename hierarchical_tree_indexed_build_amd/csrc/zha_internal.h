@@ -14,6 +14,12 @@ constexpr int kWave = 64;
 constexpr int kMaxGroup = 16;          // H_q / H_kv handled by one kernel group
 constexpr int kAttnWorkgroups = 512;   // attention workgroups per launch (partial slots: this + pairs)
 constexpr size_t kAlign = 256;
+constexpr int kScoreParents = 4;       // parent slots per scoring workgroup, one per wave
+constexpr int kCutBins = 2048;         // mass bins of a cut's first pass
+constexpr int kSplitSlice = 2048;      // candidates per workgroup of the split cut
+constexpr int kSplitSliceLog2 = 11;
+constexpr int kSplitMaxPairs = 128;    // (row, head) pairs up to which a level's cut is split over workgroups
+constexpr int kSplitMaxSlices = 1024;  // slices per (row, head) the split cut's boundary kernel can scan
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
@@ -41,8 +47,27 @@ struct WsLayout {
     size_t aitems;        // int2   [rows, Hkv, nodes[0] + 2] attention items (block, head mask)
     size_t acnt;          // int32  [rows, Hkv]
     size_t plan;          // int64  [rows * Hkv + 1] exclusive prefix of attention groups per (row, kv head)
-    size_t partial;       // float  [kAttnWorkgroups + rows * Hkv, G, D + 2] split-K partial states
+    size_t partial;       // float  [kAttnWorkgroups + rows * Hkv, G, D + 4] split-K partial states (max, sum, 2 pad, acc)
+    // split cut (rows * Hq <= kSplitMaxPairs and every level small enough); absent otherwise
+    bool split;
+    size_t cand_sc;       // float  [rows, Hq, cand_stride] a level's candidate scores in candidate order
+    size_t cand_nd;       // int32  [rows, Hq, cand_stride] their node ids
+    int64_t cand_stride;
+    size_t pmax;          // float  [rows, Hq, pmax_stride] per scoring workgroup maxima of a level
+    int64_t pmax_stride;
+    size_t chist;         // uint64 [rows, Hq, kCutBins] a level's mass per bin
+    size_t cinfo;         // SplitInfo [rows, Hq]
+    size_t cslice;        // uint64 [rows, Hq, slice_stride] (ties << 32 | below) before each slice
+    int64_t slice_stride;
     size_t total;
+};
+
+// A level's cut boundary as the split cut's boundary kernel leaves it.
+struct SplitInfo {
+    uint64_t need_ties;
+    uint32_t kappa;
+    int32_t take_all;
+    int64_t ncand;
 };
 
 // Parameters shared by every kernel that reads queries.

@@ -20,12 +20,15 @@ import pytest
 import hierarchical_tree_indexed_build_amd as Z
 import workloads as W
 from oracle import zha_oracle as O
-from tests.gpu_helpers import (Staged, attn_tol, check_sets, level_kept, say, summary_tol, torch)
+from tests.gpu_helpers import (Staged, attn_tol, check_sets, kv_tensor, level_kept, say, summary_tol, torch)
 
 pytestmark = pytest.mark.gpu
 
 # (workload, shrink, batch)
-CASES = [("tiny", 0, None), ("gqa128k", 2, 2), ("decode1m", 2, 1), ("decode16m", 2, 1), ("gqa128k", 1, 1)]
+# Few (row, head) pairs cut each level over many workgroups; batch 8 of
+# gqa128k (256 pairs) takes the one-workgroup-per-pair cut.
+CASES = [("tiny", 0, None), ("gqa128k", 2, 2), ("decode1m", 2, 1), ("decode16m", 2, 1), ("gqa128k", 1, 1),
+         ("gqa128k", 2, 8)]
 IDS = [f"{n}-s{s}" for n, s, _ in CASES]
 
 
@@ -115,6 +118,47 @@ def test_route_parity(case):
         for h in range(w.n_q_heads):
             n = c1[r, h]
             assert np.array_equal(s_np[r, h, :n], v1[r, h, :n])
+
+
+# Crafted key caches whose scores crowd the cut: every key equal (all scores
+# tie), two alternating chunk keys (two score values, many ties each), and a
+# shared key plus noise of a few sizes (narrow bands of distinct scores). They
+# reach each way the boundary search resolves the bin where the kept mass ends:
+# a one-wave ranking, a radix select over a short list, and one over all the
+# candidates of a crowded bin.
+DEGENERATE = [("equal", 0.0), ("two", 0.0), ("band", 1e-3), ("band", 1e-2), ("band", 3e-2)]
+
+
+# (workload, shrink, batch): b = 32 and b = 16 cut over many workgroups per
+# pair; batch 8 (256 pairs) cuts one workgroup per pair
+CROWDED_AT = [("decode1m", 1, 1), ("gqa128k", 1, 1), ("gqa128k", 1, 8)]
+
+
+@pytest.mark.parametrize("at", CROWDED_AT, ids=["decode1m-s1", "gqa128k-s1", "gqa128k-s1-b8"])
+@pytest.mark.parametrize("kind,noise", DEGENERATE, ids=[f"{k}-{e:g}" for k, e in DEGENERATE])
+def test_route_parity_crowded_scores(kind, noise, at):
+    t = torch()
+    w = _w(*at)
+    say(f"[route crowded] {kind} noise {noise:g} {w.name} batch {w.batch}")
+    st = Staged(w, build=False)
+    rng = np.random.default_rng(20261203)
+    B, H, C, D = st.K_np.shape
+    base = rng.standard_normal((B, H, 2, D)).astype(np.float32)
+    K = np.broadcast_to(base[:, :, :1, :], (B, H, C, D)).copy()
+    if kind == "two":
+        chunk = np.arange(C) // w.branching
+        K[:, :, chunk % 2 == 1, :] = base[:, :, 1:2, :]
+    if noise:
+        K += noise * rng.standard_normal(K.shape).astype(np.float32)
+    st.K_np = W.f32_to_bf16_bits(K)
+    st.Kf = W.as_f32(w, st.K_np)
+    st.cache.K.copy_(kv_tensor(w, st.K_np))
+    Z.build_tree(st.geom, st.cache.K, st.ref_q, st.cache.seq_lens, st.cache.summaries, st.cache.ws)
+    t.cuda.synchronize()
+    q_pos = _qpos(st, 1)
+    qn, q, sel, nsel, stats, lsel, p = _route(st, 1, q_pos)
+    flips = _teacher_forced(st, qn, q_pos.cpu().numpy(), stats, lsel, p, st.oracle_trees())
+    say(f"  margin-exempt differences: {flips}; kept leaves per head {nsel.cpu().numpy().reshape(-1)[:8]}")
 
 
 @pytest.mark.parametrize("case", CASES, ids=IDS)
