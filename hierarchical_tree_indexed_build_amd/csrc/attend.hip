@@ -69,10 +69,12 @@ __global__ __launch_bounds__(256) void attn_bitmap_kernel(BitmapParams p) {
 
 // ----------------------------------------------------------------------------
 // the group's attention items
-// One workgroup per (row, kv head): OR the g heads' level-1 bitmaps, add the
-// sink chunk and the current chunk, and compact the set bits in ascending
-// chunk order into (chunk, head mask) items with a block scan. Each thread
-// owns a contiguous run of bitmap words.
+// Workgroup = (segment of kItemsSegWords bitmap words, (row, kv head)). The
+// union of the g heads' level-1 bitmaps, plus the sink chunk and the current
+// chunk, is compacted in ascending chunk order into (chunk, head mask) items.
+// A segment's first item position is the popcount of the union before it,
+// which each workgroup takes itself from the (few) earlier words, so the
+// segments of a pair run in parallel. Each thread owns one word.
 // ----------------------------------------------------------------------------
 struct ItemsParams {
     RowInfo ri;
@@ -85,19 +87,25 @@ struct ItemsParams {
     int lb, Hq, Hkv;
 };
 
-constexpr int kItemsThreads = 1024;
+constexpr int kItemsThreads = 256;
+constexpr int kItemsSegWords = kItemsThreads;   // one word per thread
 
 template <int G>
 __global__ __launch_bounds__(kItemsThreads) void attn_items_kernel(ItemsParams p) {
-    __shared__ uint64_t red[kItemsThreads / kWave];
-    const int y = blockIdx.x;
+    constexpr int NW = kItemsThreads / kWave;
+    __shared__ uint64_t red[NW];
+    __shared__ uint64_t red2[NW];
+    const int seg = blockIdx.x, y = blockIdx.y;
     const int row = y / p.Hkv, kv = y % p.Hkv;
-    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int N = visible_clamped(p.ri, row, p.cap);
     const int64_t nc1 = static_cast<int64_t>(N) >> p.lb;                        // complete leaf chunks
     const int64_t nblk = N > 0 ? ((static_cast<int64_t>(N) - 1) >> p.lb) + 1 : 0;  // chunks incl. the current one
     const int64_t cur = nblk - 1;
     const int64_t words = (nblk + 31) >> 5;
+    const int64_t nseg = (words + kItemsSegWords - 1) / kItemsSegWords;
+    const int64_t last = nseg > 0 ? nseg - 1 : 0;      // the last segment writes the count
+    if (seg > last) return;
     const uint32_t* bm0 = p.bm + (static_cast<int64_t>(row) * p.Hq + static_cast<int64_t>(kv) * G) * p.stride;
     // word wd of the union: kept complete chunks of any head, the sink, the current chunk
     auto word = [&](int64_t wd, uint32_t (&heads)[G]) -> uint32_t {
@@ -113,37 +121,48 @@ __global__ __launch_bounds__(kItemsThreads) void attn_items_kernel(ItemsParams p
         if ((cur >> 5) == wd) u |= 1u << (cur & 31);
         return u;
     };
-    const int64_t per = (words + nt - 1) / nt;
-    const int64_t w0 = imin(static_cast<int64_t>(tid) * per, words);
-    const int64_t w1 = imin(w0 + per, words);
+    const int64_t w0 = static_cast<int64_t>(seg) * kItemsSegWords;
+    const int64_t wd = w0 + tid;
     uint32_t heads[G];
-    uint64_t cnt = 0;
-    for (int64_t wd = w0; wd < w1; ++wd) cnt += __popc(word(wd, heads));
-    // block exclusive scan of the counts, in thread order
+    const uint32_t mine = wd < words ? word(wd, heads) : 0u;
+    // items before the segment
+    uint64_t pre = 0;
+#pragma unroll 4
+    for (int64_t x = tid; x < w0; x += kItemsThreads) {
+        uint32_t hx[G];
+        pre += __popc(word(x, hx));
+    }
+    const uint64_t cnt = __popc(mine);
     const uint64_t inc = wave_scan_u64(cnt);
-    if (lane == 63) red[w] = inc;
+    const uint64_t pinc = wave_scan_u64(pre);
+    if (lane == 63) {
+        red[w] = inc;
+        red2[w] = pinc;
+    }
     __syncthreads();
     uint64_t before = 0, total = 0;
-    for (int i = 0; i < nt / kWave; ++i) {
-        if (i < w) before += red[i];
-        total += red[i];
-    }
-    int2* items = p.items + static_cast<int64_t>(y) * p.item_stride;
-    int64_t pos = static_cast<int64_t>(before + inc - cnt);
-    for (int64_t wd = w0; wd < w1; ++wd) {
-        uint32_t u = word(wd, heads);
-        while (u) {
-            const int bit = __ffs(static_cast<int>(u)) - 1;
-            u &= u - 1;
-            const int64_t chunk = (wd << 5) + bit;
-            uint32_t mask = 0;
 #pragma unroll
-            for (int h = 0; h < G; ++h) mask |= ((heads[h] >> bit) & 1u) << h;
-            if (chunk == cur) mask |= kAllHeads;
-            items[pos++] = make_int2(static_cast<int>(chunk), static_cast<int>(mask));
-        }
+    for (int i = 0; i < NW; ++i) {
+        if (i < w) before += red[i];
+        total += red[i] + red2[i];
     }
-    if (tid == 0) p.acnt[y] = static_cast<int32_t>(total);
+    uint64_t seg_before = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) seg_before += red2[i];
+    int2* items = p.items + static_cast<int64_t>(y) * p.item_stride;
+    int64_t pos = static_cast<int64_t>(seg_before + before + inc - cnt);
+    uint32_t u = mine;
+    while (u) {
+        const int bit = __ffs(static_cast<int>(u)) - 1;
+        u &= u - 1;
+        const int64_t chunk = (wd << 5) + bit;
+        uint32_t mask = 0;
+#pragma unroll
+        for (int h = 0; h < G; ++h) mask |= ((heads[h] >> bit) & 1u) << h;
+        if (chunk == cur) mask |= kAllHeads;
+        items[pos++] = make_int2(static_cast<int>(chunk), static_cast<int>(mask));
+    }
+    if (seg == last && tid == 0) p.acnt[y] = static_cast<int32_t>(total);
 }
 
 // ----------------------------------------------------------------------------
@@ -667,7 +686,10 @@ hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st) {
         ip.Hkv = g.Hkv;
         {
             ProfScope ps("attn_items", 0, st);
-            const dim3 gi(pairs), bi(kItemsThreads);
+            const int64_t iwords = (g.nodes[0] + 1 + 31) / 32;                  // chunks incl. the current one
+            const dim3 gi(static_cast<unsigned>(std::max<int64_t>(1, (iwords + kItemsSegWords - 1) / kItemsSegWords)),
+                          pairs),
+                bi(kItemsThreads);
             switch (g.G) {
                 case 1: hipLaunchKernelGGL(attn_items_kernel<1>, gi, bi, 0, st, ip); break;
                 case 2: hipLaunchKernelGGL(attn_items_kernel<2>, gi, bi, 0, st, ip); break;

@@ -16,17 +16,16 @@
 //    upper levels in one launch: candidates, scores and the cut stay in LDS
 //    from level to level.
 //  * per remaining level (the leaf level always):
-//    - route_score_kernel - a workgroup owns kScoreParents parent slots of one
+//    - route_score_kernel - a workgroup owns a run of up to 64 parent slots of one
 //      (row, kv head). It ORs the group's kept bitmaps of level l+1 over its
 //      slots (plus the incomplete parent, whose complete children are the
 //      orphans) and scores each such parent's b children once for all g query
 //      heads: a summary row is read once per kv group. Scores land in a
 //      dense-by-node array per (row, query head).
-//    - the cut: with few (row, head) pairs, route_split_hist_kernel,
-//      route_split_bound_kernel and route_split_emit_kernel spread each pair's
-//      cut over slices of its candidates; otherwise route_cut_kernel, one
-//      workgroup per (row, query head), with the scores staged in LDS when
-//      they fit.
+//    - the cut: with few (row, head) pairs, route_split_hist_kernel and
+//      route_split_emit_kernel spread each pair's cut over slices of its
+//      candidates; otherwise route_cut_kernel, one workgroup per (row, query
+//      head), with the scores staged in LDS when they fit.
 // The cut itself: masses exp(s - max) are held in 2^-40 fixed point, so their
 // sums are exact and independent of order. The masses are binned by the
 // score's distance below the max; the bin where the running mass reaches
@@ -66,17 +65,28 @@ struct ScoreParams {
     int64_t cap;
     int b, lb, li, L, Hq, Hkv, T;
     float scale;
-    // split cut of this level (null otherwise): each workgroup leaves the
-    // maximum of every head's candidates it scored, and workgroup 0 of a
-    // (row, kv head) clears the heads' mass bins
+    // split cut of this level (pmax null otherwise): every workgroup leaves the
+    // maximum of each head's own candidates it scored and writes their scores
+    // and ids in the head's candidate order; workgroup 0 of a (row, kv head)
+    // clears the heads' mass bins and this level's bitmaps
     float* pmax;               // [rows, Hq, pmax_stride], column blockIdx.x
     int64_t pmax_stride;
     unsigned long long* chist; // [rows, Hq, kCutBins]
+    uint32_t* bm_cur;          // this level's kept bitmaps (row-head stride bm_words_total)
+    const int32_t* rank_up;    // [rows, Hq, nodes_total]: a kept node's place in its head's kept list (level l+1)
+    int64_t lvl_off_up;
+    const int32_t* kept_cnt;   // [rows, Hq, L]
+    float* cand_sc;            // [rows, Hq, cand_stride]
+    int32_t* cand_nd;
+    int64_t cand_stride;
 };
 
-
+// Workgroup = a run of at most 64 parent slots of one (row, kv head), one
+// wave per active parent at a time. Every wave builds the run's masks itself
+// with ballots (lane = slot): the slots some head of the group kept, and for
+// each head the slots it takes candidates from.
 template <int D, int G>
-__global__ __launch_bounds__(256) void route_score_kernel(ScoreParams p) {
+__global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams p) {
     const int y = blockIdx.y;
     const int row = y / p.Hkv, kv = y % p.Hkv;
     const int s = row / p.T;
@@ -89,32 +99,33 @@ __global__ __launch_bounds__(256) void route_score_kernel(ScoreParams p) {
     // (scored when some head of the group kept them) and the incomplete parent
     // holding the orphans
     const int64_t slots = top ? ((nc + p.b - 1) >> p.lb) : (nc_up + (orphans > 0 ? 1 : 0));
-    const int64_t P0 = static_cast<int64_t>(blockIdx.x) * kScoreParents;
+    const int64_t per = (slots + gridDim.x - 1) / gridDim.x;          // <= 64 by the launch
+    const int64_t P0 = static_cast<int64_t>(blockIdx.x) * per;
+    const int64_t P1 = imin(P0 + per, slots);
     const int64_t rh0 = static_cast<int64_t>(row) * p.Hq + kv * G;      // the group's first (row, head)
-    if (p.chist && blockIdx.x == 0) {
+    const bool split = p.pmax != nullptr;
+    if (split && blockIdx.x == 0) {
         for (int i = threadIdx.x; i < G * kCutBins; i += blockDim.x) p.chist[rh0 * kCutBins + i] = 0ull;
+        const int64_t words = (nc + 31) >> 5;
+        for (int h = 0; h < G; ++h)
+            for (int64_t i = threadIdx.x; i < words; i += blockDim.x) p.bm_cur[(rh0 + h) * p.bm_words_total + i] = 0u;
     }
-    const int nact = P0 < slots ? static_cast<int>(imin(slots - P0, kScoreParents)) : 0;
-    uint32_t act = nact ? (1u << nact) - 1u : 0u;
-    uint32_t mine[G];                                        // parent slots each head takes candidates from
-    uint32_t orph = 0;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    const int64_t my_slot = P0 + lane;
+    const bool have = my_slot < P1;
+    const bool orph_l = !top && have && orphans > 0 && my_slot == nc_up;
+    uint64_t mine[G], act = 0;
 #pragma unroll
-    for (int h = 0; h < G; ++h) mine[h] = act;
-    if (!top && act) {
-        const uint32_t* bw = p.bm_up + rh0 * p.bm_words_total + (P0 >> 5);
-        uint32_t kept = 0;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            mine[h] = (bw[h * p.bm_words_total] >> (P0 & 31)) & ((1u << kScoreParents) - 1u);
-            kept |= mine[h];
-        }
-        orph = (orphans > 0 && nc_up >= P0 && nc_up < P0 + kScoreParents) ? (1u << (nc_up - P0)) : 0u;
-        act &= kept | orph;
-#pragma unroll
-        for (int h = 0; h < G; ++h) mine[h] |= orph;
+    for (int h = 0; h < G; ++h) {
+        bool k = have;
+        if (!top) k = orph_l || (have && ((p.bm_up[(rh0 + h) * p.bm_words_total + (my_slot >> 5)] >> (my_slot & 31)) & 1u));
+        mine[h] = __ballot(k);
+        act |= mine[h];
     }
     if (!act) {
-        if (p.pmax && threadIdx.x < G) p.pmax[(rh0 + threadIdx.x) * p.pmax_stride + blockIdx.x] = -INFINITY;
+        if (split && threadIdx.x < G) p.pmax[(rh0 + threadIdx.x) * p.pmax_stride + blockIdx.x] = -INFINITY;
         return;
     }
 
@@ -123,31 +134,42 @@ __global__ __launch_bounds__(256) void route_score_kernel(ScoreParams p) {
     constexpr int RPP = kWave / LPR;                         // rows per pass
     constexpr int UNR = 4;                                   // passes issued together
     static_assert(G <= LPR, "one lane per head writes the head's score");
-    const int lane = threadIdx.x & (kWave - 1);
     const int sub = lane / LPR, part = lane % LPR;
-    const int wave = threadIdx.x / kWave;
-    const int nw = blockDim.x / kWave;
 
     const float* summ = p.summ + (static_cast<int64_t>(s) * p.Hkv + kv) * p.nodes_l * D;
-    float* sc0 = p.scores + (static_cast<int64_t>(row) * p.Hq + kv * G) * p.nodes_total + p.lvl_off;
+    float* sc0 = p.scores + rh0 * p.nodes_total + p.lvl_off;
     float qv[G][DPL];
     float hmx[G];                                            // per head: max over its own candidates
 #pragma unroll
     for (int h = 0; h < G; ++h) hmx[h] = -INFINITY;
     bool have_q = false;
     int nth = 0;
-    for (uint32_t a = act; a; a &= a - 1, ++nth) {
+    for (uint64_t a = act; a; a &= a - 1, ++nth) {
         if (nth % nw != wave) continue;                      // parents dealt round-robin to the waves
         if (!have_q) {                                       // only waves with work read q
 #pragma unroll
             for (int h = 0; h < G; ++h)
-                load_row<DPL>(p.q + (static_cast<int64_t>(row) * p.Hq + kv * G + h) * D + part * DPL, qv[h]);
+                load_row<DPL>(p.q + (rh0 + h) * D + part * DPL, qv[h]);
             have_q = true;
         }
-        const int slot = __ffs(static_cast<int>(a)) - 1;
+        const int slot = __ffsll(static_cast<long long>(a)) - 1;
         const int64_t par = P0 + slot;
         const int64_t c0 = par << p.lb;
         const int64_t c1 = imin(c0 + p.b, nc);
+        // split: where this parent's children start in each head's candidate order
+        int64_t cbase[G];
+        if (split) {
+            const bool orph = !top && par == nc_up && orphans > 0;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                cbase[h] = -1;
+                if ((mine[h] >> slot) & 1ull) {
+                    if (top) cbase[h] = c0;
+                    else if (orph) cbase[h] = static_cast<int64_t>(p.kept_cnt[(rh0 + h) * p.L + p.li + 1]) << p.lb;
+                    else cbase[h] = static_cast<int64_t>(p.rank_up[(rh0 + h) * p.nodes_total + p.lvl_off_up + par]) << p.lb;
+                }
+            }
+        }
         for (int64_t cb = c0; cb < c1; cb += UNR * RPP) {
             float x[UNR][DPL];
 #pragma unroll
@@ -171,19 +193,25 @@ __global__ __launch_bounds__(256) void route_score_kernel(ScoreParams p) {
                     for (int h = 0; h < G; ++h) {
                         const float sv = acc[h] * p.scale;
                         if (part == h) sc0[static_cast<int64_t>(h) * p.nodes_total + c] = sv;
-                        if ((mine[h] >> slot) & 1u) hmx[h] = fmaxf(hmx[h], sv);
+                        if (split && cbase[h] >= 0) {
+                            hmx[h] = fmaxf(hmx[h], sv);
+                            if (part == h) {
+                                const int64_t at = (rh0 + h) * p.cand_stride + cbase[h] + (c - c0);
+                                p.cand_sc[at] = sv;
+                                p.cand_nd[at] = static_cast<int32_t>(c);
+                            }
+                        }
                     }
                 }
             }
         }
     }
-    if (p.pmax) {
-        __shared__ float red[G][4];
-        const int lane64 = threadIdx.x & 63;
+    if (split) {
+        __shared__ float red[G][kScoreThreads / kWave];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_scan_max_f(hmx[h])), 63));
-            if (lane64 == 0) red[h][wave] = m;
+            if (lane == 0) red[h][wave] = m;
         }
         __syncthreads();
         if (threadIdx.x < G) {
@@ -211,16 +239,53 @@ struct BlockScratch {
     uint32_t bcast_u32[2];
     uint32_t red_u32[kCutWaves];
     uint32_t list[kCutList];    // candidates of the boundary bin
+    float list_s[kCutList];     // and their scores
     uint32_t list_n;
-    uint32_t wkey[kWave];       // single-wave ranking: keys, candidate ids, masses in rank order, prefixes
-    uint32_t wk[kWave];
+    uint64_t wpk[kWave];        // single-wave ranking: (key, candidate) pairs, masses in rank order, prefixes
     uint64_t wmass[kWave];
     uint64_t wpre[kWave];
     int32_t wcount;
 };
 
+// The boundary bin's members resolved by one wave (m <= 64, member i on lane
+// i, candidate ids lk[] and scores ls[]): each lane ranks its member in (key,
+// candidate) order, the masses are laid out in rank order and prefix-summed,
+// and a member is kept while the mass ranked before it is below rem. Leaves
+// the largest kept key (the boundary key) in bs.bcast_u32[1] and the number
+// of kept members with that key in bs.bcast_u64[1].
+__device__ __forceinline__ void wave_resolve(const uint32_t* lk, const float* ls, int m, float mx, uint64_t rem,
+                                             BlockScratch& bs) {
+    const int lane = threadIdx.x & 63;
+    const bool valid = lane < m;
+    const uint32_t k = valid ? lk[lane] : 0u;
+    const float s = valid ? ls[lane] : 0.f;
+    const uint32_t key = valid ? desc_key(s) : 0xffffffffu;
+    const uint64_t F = valid ? mass_fx(s, mx) : 0;
+    const uint64_t pk = valid ? ((static_cast<uint64_t>(key) << 32) | k) : ~0ull;   // distinct per member
+    bs.wpk[lane] = pk;
+    __builtin_amdgcn_wave_barrier();
+    int rank = 0;
+#pragma unroll 8
+    for (int j = 0; j < kWave; ++j) rank += bs.wpk[j] < pk;
+    if (valid) bs.wmass[rank] = F;
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t mj = lane < m ? bs.wmass[lane] : 0;
+    bs.wpre[lane] = wave_scan_u64(mj) - mj;
+    __builtin_amdgcn_wave_barrier();
+    const bool kept = valid && bs.wpre[rank] < rem;
+    const uint32_t kap = static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(wave_scan_max_u32(kept ? key : 0u)), 63));
+    const uint64_t ties = __popcll(__ballot(kept && key == kap));
+    if (lane == 0) {
+        bs.bcast_u32[1] = kap;
+        bs.bcast_u64[1] = ties;
+    }
+}
+
 // Block reductions: a DPP scan per wave (lane 63 holds the wave's result),
 // one LDS slot per wave, one barrier to publish and one to free the slots.
+// NW: waves in the block (blockDim.x / 64).
+template <int NW = kCutWaves>
 __device__ __forceinline__ float block_max_f(float v, BlockScratch& bs) {
     v = wave_scan_max_f(v);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -228,11 +293,12 @@ __device__ __forceinline__ float block_max_f(float v, BlockScratch& bs) {
     __syncthreads();
     float r = bs.red_f[0];
 #pragma unroll
-    for (int i = 1; i < kCutWaves; ++i) r = fmaxf(r, bs.red_f[i]);
+    for (int i = 1; i < NW; ++i) r = fmaxf(r, bs.red_f[i]);
     __syncthreads();
     return r;
 }
 
+template <int NW = kCutWaves>
 __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, BlockScratch& bs) {
     v = wave_scan_u64(v);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -240,7 +306,7 @@ __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, BlockScratch& bs) 
     __syncthreads();
     uint64_t r = 0;
 #pragma unroll
-    for (int i = 0; i < kCutWaves; ++i) r += bs.red_u64[i];
+    for (int i = 0; i < NW; ++i) r += bs.red_u64[i];
     __syncthreads();
     return r;
 }
@@ -268,6 +334,7 @@ __device__ __forceinline__ void block_sum_max(uint64_t& sum, uint32_t& mx, Block
 }
 
 // Exclusive prefix sum over the block in thread order; *total receives the sum.
+template <int NW = kCutWaves>
 __device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, BlockScratch& bs, uint64_t* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const uint64_t inc = wave_scan_u64(v);
@@ -275,7 +342,7 @@ __device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, BlockScratch
     __syncthreads();
     uint64_t before = 0, all = 0;
 #pragma unroll
-    for (int i = 0; i < kCutWaves; ++i) {
+    for (int i = 0; i < NW; ++i) {
         if (i < w) before += bs.red_u64[i];
         all += bs.red_u64[i];
     }
@@ -512,41 +579,17 @@ __device__ __forceinline__ CutBoundary cut_boundary(ScoreAt score, int64_t n, fl
             if (lane == 0) base = atomicAdd(&bs.list_n, static_cast<uint32_t>(__popcll(bal)));
             base = static_cast<uint32_t>(__shfl(static_cast<int>(base), 0));
             const uint32_t pos = base + static_cast<uint32_t>(__popcll(bal & ((1ull << lane) - 1ull)));
-            if (mem && pos < kCutList) bs.list[pos] = static_cast<uint32_t>(k);
+            if (mem && pos < kCutList) {
+                bs.list[pos] = static_cast<uint32_t>(k);
+                bs.list_s[pos] = score(k);
+            }
         }
     }
     __syncthreads();
     const uint32_t m = bs.list_n;
 
     if (m <= kWave) {
-        if (wave == 0) {
-            const bool valid = lane < static_cast<int>(m);
-            const uint32_t k = valid ? bs.list[lane] : 0u;
-            const float s = valid ? score(k) : 0.f;
-            const uint32_t key = valid ? desc_key(s) : 0xffffffffu;
-            const uint64_t F = valid ? mass_fx(s, mx) : 0;
-            bs.wkey[lane] = key;
-            bs.wk[lane] = k;
-            __builtin_amdgcn_wave_barrier();
-            int rank = 0;
-            for (int j = 0; j < static_cast<int>(m); ++j) {
-                const uint32_t kj = bs.wkey[j], ij = bs.wk[j];
-                rank += (kj < key) || (kj == key && ij < k);
-            }
-            if (valid) bs.wmass[rank] = F;
-            __builtin_amdgcn_wave_barrier();
-            const uint64_t mj = lane < static_cast<int>(m) ? bs.wmass[lane] : 0;
-            bs.wpre[lane] = wave_scan_u64(mj) - mj;
-            __builtin_amdgcn_wave_barrier();
-            const bool kept = valid && bs.wpre[rank] < rem;
-            const uint32_t kap = static_cast<uint32_t>(
-                __builtin_amdgcn_readlane(static_cast<int>(wave_scan_max_u32(kept ? key : 0u)), 63));
-            const uint64_t ties = __popcll(__ballot(kept && key == kap));
-            if (lane == 0) {
-                bs.bcast_u32[1] = kap;
-                bs.bcast_u64[1] = ties;
-            }
-        }
+        if (wave == 0) wave_resolve(bs.list, bs.list_s, static_cast<int>(m), mx, rem, bs);
         __syncthreads();
         cb.kappa = bs.bcast_u32[1];
         cb.need_ties = bs.bcast_u64[1];
@@ -555,7 +598,7 @@ __device__ __forceinline__ CutBoundary cut_boundary(ScoreAt score, int64_t n, fl
     uint32_t kap;
     if (m <= kCutList) {
         kap = radix_kappa([&](int64_t e, uint32_t& key, uint64_t& F) {
-            const float s = score(static_cast<int64_t>(bs.list[e]));
+            const float s = bs.list_s[e];
             key = desc_key(s);
             F = mass_fx(s, mx);
             return true;
@@ -595,13 +638,11 @@ __device__ __forceinline__ int wave_cut_small(ScoreAt score, int n, float top_p,
     const bool take_all = (top_p >= 1.0f) || n == 0;
     uint64_t rem = static_cast<uint64_t>(ceil(static_cast<double>(top_p) * static_cast<double>(E)));
     if (rem == 0) rem = 1;
-    bs.wkey[lane] = key;
+    const uint64_t pk = valid ? ((static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(lane)) : ~0ull;
+    bs.wpk[lane] = pk;
     __builtin_amdgcn_wave_barrier();
     int rank = 0;
-    for (int j = 0; j < n; ++j) {
-        const uint32_t kj = bs.wkey[j];
-        rank += (kj < key) || (kj == key && j < lane);
-    }
+    for (int j = 0; j < n; ++j) rank += bs.wpk[j] < pk;
     if (valid) bs.wmass[rank] = F;
     __builtin_amdgcn_wave_barrier();
     const uint64_t mj = lane < n ? bs.wmass[lane] : 0;
@@ -872,17 +913,18 @@ __global__ __launch_bounds__(kCutThreads) void route_cut_kernel(CutParams p) {
 // the split cut: a level's cut spread over many workgroups per (row, head)
 // When few (row, head) pairs route at once, one workgroup per pair leaves most
 // of the chip idle while the largest candidate sets (tens of thousands) are
-// cut. The same cut then runs as three kernels over slices of kSplitSlice
-// candidates, ordered by kernel boundaries:
-//  * route_split_hist_kernel  (slice): the level max from the scoring
-//    workgroups' partial maxima; the slice's node ids and scores copied in
-//    candidate order; each mass added into the (row, head)'s global bins.
-//  * route_split_bound_kernel (row, head): the boundary bin from the bins, its
-//    members listed and resolved exactly (as in cut_boundary), and the count of
-//    kept candidates and of boundary ties before every slice.
-//  * route_split_emit_kernel  (slice): the kept ids written at their ranks and
-//    their bitmap bits set.
-// The kept set is the one cut_boundary and cut_compact produce.
+// cut. The same cut then runs over slices of kSplitSlice candidates, in two
+// kernels ordered by their boundary:
+//  * route_split_hist_kernel: the level max from the scoring workgroups'
+//    partial maxima; the slice's node ids and scores copied in candidate
+//    order and again grouped by bin, with each bin's start; its masses added
+//    into the (row, head)'s global bins.
+//  * route_split_emit_kernel: every slice finds the boundary bin from the
+//    global bins, gathers that bin's members from the slices' bin groups,
+//    resolves the boundary exactly (as cut_boundary does), counts the kept
+//    candidates of the earlier slices, and writes its own kept ids and bits.
+// The scoring kernel clears the bins and the level's bitmap beforehand. The
+// kept set is the one cut_boundary and cut_compact produce.
 // ----------------------------------------------------------------------------
 struct SplitParams {
     RowInfo ri;
@@ -905,12 +947,14 @@ struct SplitParams {
     const float* pmax;
     int pmax_n;                // scoring workgroups of the level
     int64_t pmax_stride;
-    float* cand_sc;
-    int32_t* cand_nd;
+    const float* cand_sc;      // [rows, Hq, cand_stride] scores in candidate order (from the scoring kernel)
+    const int32_t* cand_nd;    // node ids in candidate order
+    int32_t* rank;             // [rows, Hq, nodes_total] kept node -> its place in the kept list (levels >= 2)
+    uint32_t* srt_k;           // per slice, the slice's candidates grouped by bin: candidate index
+    float* srt_s;              //   and score
     int64_t cand_stride;
-    unsigned long long* chist;
-    SplitInfo* info;
-    unsigned long long* slice;
+    uint32_t* cum;             // [rows, Hq, slice_stride, kCutBins + 1] per slice: candidates in earlier bins
+    unsigned long long* chist; // [rows, Hq, kCutBins] masses per bin
     int64_t slice_stride;
 };
 
@@ -935,121 +979,152 @@ __device__ __forceinline__ CutCands split_cands(const SplitParams& p, int row, i
 }
 
 constexpr int kSplitThreads = 256;
+constexpr int kSplitWaves = kSplitThreads / kWave;
 constexpr int kSplitPer = kSplitSlice / kSplitThreads;       // candidates per thread
+constexpr int kBinsPerThread = kCutBins / kSplitThreads;
 
+// Slice workgroup: the level max; the slice's candidates grouped by bin (a
+// counting sort in LDS) with each bin's start; its masses added into the
+// (row, head)'s bins. The scoring kernel wrote the scores in candidate order.
 __global__ __launch_bounds__(kSplitThreads) void route_split_hist_kernel(SplitParams p) {
-    __shared__ unsigned long long bins[kCutBins];
-    __shared__ float red[kSplitThreads / kWave];
+    __shared__ unsigned long long mbin[kCutBins];
+    __shared__ uint32_t cbin[kCutBins];
+    __shared__ BlockScratch bs;
     const int sl = blockIdx.x, hq = blockIdx.y, row = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x;
     const int64_t rh = static_cast<int64_t>(row) * p.Hq + hq;
+    const int64_t k0 = static_cast<int64_t>(sl) << kSplitSliceLog2;
+    const int64_t cbase = rh * p.cand_stride;
+    // issued together: the candidate count, the scoring maxima, the slice's scores
     int64_t nc;
     const CutCands cc = split_cands(p, row, rh, &nc);
-    const int64_t k0 = static_cast<int64_t>(sl) << kSplitSliceLog2;
-    if (k0 >= cc.ncand) return;
     float mx = -INFINITY;
     for (int i = tid; i < p.pmax_n; i += kSplitThreads) mx = fmaxf(mx, p.pmax[rh * p.pmax_stride + i]);
-    int32_t nd[kSplitPer];
     float v[kSplitPer];
 #pragma unroll
     for (int u = 0; u < kSplitPer; ++u) {
         const int64_t k = k0 + tid + u * kSplitThreads;
-        nd[u] = k < cc.ncand ? static_cast<int32_t>(cc.node(k)) : -1;
+        v[u] = k < p.cand_stride ? p.cand_sc[cbase + k] : -INFINITY;
     }
+    if (k0 >= cc.ncand) return;
+    bool val[kSplitPer];
 #pragma unroll
-    for (int u = 0; u < kSplitPer; ++u) v[u] = nd[u] >= 0 ? cc.sc[nd[u]] : -INFINITY;
-    float* csc = p.cand_sc + rh * p.cand_stride;
-    int32_t* cnd = p.cand_nd + rh * p.cand_stride;
-#pragma unroll
-    for (int u = 0; u < kSplitPer; ++u) {
-        const int64_t k = k0 + tid + u * kSplitThreads;
-        if (nd[u] >= 0) {
-            csc[k] = v[u];
-            cnd[k] = nd[u];
-        }
+    for (int u = 0; u < kSplitPer; ++u) val[u] = k0 + tid + u * kSplitThreads < cc.ncand;
+    for (int i = tid; i < kCutBins; i += kSplitThreads) {
+        mbin[i] = 0ull;
+        cbin[i] = 0u;
     }
-    for (int i = tid; i < kCutBins; i += kSplitThreads) bins[i] = 0ull;
-    mx = wave_scan_max_f(mx);
-    if (lane == 63) red[w] = mx;
-    __syncthreads();                                  // also publishes the cleared bins
-    mx = red[0];
-#pragma unroll
-    for (int i = 1; i < kSplitThreads / kWave; ++i) mx = fmaxf(mx, red[i]);
+    mx = block_max_f<kSplitWaves>(mx, bs);            // its barriers also publish the cleared bins
     if (p.top_p >= 1.0f) return;                      // everything is kept: no bins needed
+    int bn[kSplitPer];
 #pragma unroll
     for (int u = 0; u < kSplitPer; ++u) {
-        if (nd[u] < 0) continue;
+        bn[u] = cut_bin(v[u], mx);
+        if (!val[u]) continue;
+        atomicAdd(&cbin[bn[u]], 1u);
         const uint64_t F = mass_fx(v[u], mx);
-        if (F) atomicAdd(&bins[cut_bin(v[u], mx)], static_cast<unsigned long long>(F));
+        if (F) atomicAdd(&mbin[bn[u]], static_cast<unsigned long long>(F));
     }
     __syncthreads();
+    // bin start offsets within the slice: thread t owns bins [t*BPT, t*BPT + BPT)
+    uint32_t c[kBinsPerThread], lsum = 0;
+#pragma unroll
+    for (int j = 0; j < kBinsPerThread; ++j) {
+        c[j] = cbin[tid * kBinsPerThread + j];
+        lsum += c[j];
+    }
+    uint64_t tot;
+    uint32_t run = static_cast<uint32_t>(block_excl_scan_u64<kSplitWaves>(lsum, bs, &tot));
+    uint32_t* cum = p.cum + (rh * p.slice_stride + sl) * (kCutBins + 1);
+#pragma unroll
+    for (int j = 0; j < kBinsPerThread; ++j) {
+        cum[tid * kBinsPerThread + j] = run;
+        cbin[tid * kBinsPerThread + j] = run;            // becomes the bin's write cursor
+        run += c[j];
+    }
+    if (tid == kSplitThreads - 1) cum[kCutBins] = run;
+    __syncthreads();
+    uint32_t* sk = p.srt_k + cbase + k0;
+    float* ss = p.srt_s + cbase + k0;
+#pragma unroll
+    for (int u = 0; u < kSplitPer; ++u) {
+        if (!val[u]) continue;
+        const uint32_t at = atomicAdd(&cbin[bn[u]], 1u);
+        sk[at] = static_cast<uint32_t>(k0 + tid + u * kSplitThreads);
+        ss[at] = v[u];
+    }
     unsigned long long* gb = p.chist + rh * kCutBins;
     for (int i = tid; i < kCutBins; i += kSplitThreads) {
-        const unsigned long long x = bins[i];
+        const unsigned long long x = mbin[i];
         if (x) atomicAdd(gb + i, x);                  // device scope: slices of a (row, head) sit on any XCD
     }
 }
 
-constexpr int kSplitBoundBatch = 16;                  // candidate scores per thread in flight
-
-struct SplitBoundShared {
-    uint32_t s_lt[kSplitMaxSlices];                   // per slice: candidates below the boundary key
-    uint32_t s_tie[kSplitMaxSlices];                  // per slice: candidates at the boundary key
+struct SplitEmitShared {
+    uint32_t s_lt[kSplitMaxSlices];                   // per slice: kept below the boundary key
+    uint32_t s_tie[kSplitMaxSlices];                  // per slice: at the boundary key
+    uint32_t s_mb[kSplitMaxSlices + 1];               // per slice: first member's place in the member order
+    uint32_t s_mo[kSplitMaxSlices];                   // per slice: members' offset in the slice's bin order
+    uint64_t wcnt[kSplitWaves];
     BlockScratch bs;
 };
 
-__global__ __launch_bounds__(kCutThreads) void route_split_bound_kernel(SplitParams p) {
-    __shared__ SplitBoundShared sh;
+// Slice workgroup: the level's boundary, worked out again by every slice of
+// the (row, head) from the bins and the boundary bin's members, then the
+// slice's kept ids at their ranks. Slice 0 also writes the level's counts.
+__global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitParams p) {
+    __shared__ SplitEmitShared sh;
     BlockScratch& bs = sh.bs;
-    const int hq = blockIdx.x, row = blockIdx.y;
-    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int BPW = kSplitSlice / kSplitThreads;           // 64-candidate blocks per wave
+    const int sl = blockIdx.x, hq = blockIdx.y, row = blockIdx.z;
+    const int tid = threadIdx.x, nt = kSplitThreads, lane = tid & 63, w = tid >> 6;
     const int64_t rh = static_cast<int64_t>(row) * p.Hq + hq;
+    const int64_t k0 = static_cast<int64_t>(sl) << kSplitSliceLog2;
+    const int64_t cbase = rh * p.cand_stride;
+    // issued together: the candidate count and this wave's blocks of the slice,
+    // [kw, kw + 64 * BPW) (entries past the count are never used)
     int64_t nc;
     const CutCands cc = split_cands(p, row, rh, &nc);
+    const int64_t kw = k0 + static_cast<int64_t>(w) * 64 * BPW;
+    float sv[BPW];
+    int32_t nd[BPW];
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+        const int64_t k = kw + j * 64 + lane;
+        sv[j] = k < p.cand_stride ? p.cand_sc[cbase + k] : 0.f;
+        nd[j] = k < p.cand_stride ? p.cand_nd[cbase + k] : 0;
+    }
     const int64_t ncand = cc.ncand;
     const int nsl = static_cast<int>((ncand + kSplitSlice - 1) >> kSplitSliceLog2);
-    const bool leaf = (p.li == 0);
-    // this level's bitmap starts empty; the emit kernel ORs the kept bits in
-    uint32_t* bm = p.bitmap + rh * p.bm_words_total + p.bm_off;
-    const int64_t words = (nc + 31) >> 5;
-    for (int64_t i = tid; i < words; i += nt) bm[i] = 0u;
+    if (sl >= nsl && sl != 0) return;
+    const bool take_all = (p.top_p >= 1.0f) || ncand == 0;
+    uint32_t kappa = 0u;
+    uint64_t need = 0;
     for (int i = tid; i < nsl; i += nt) {
         sh.s_lt[i] = 0u;
         sh.s_tie[i] = 0u;
     }
-    const bool take_all = (p.top_p >= 1.0f) || ncand == 0;
-    uint32_t kappa = 0u;
-    uint64_t need = 0;
-    const float* csc = p.cand_sc + rh * p.cand_stride;
     if (!take_all) {
-        // issued together: the bins, the scoring maxima, the first batch of candidate scores
-        constexpr int BPT = kCutBins / kCutThreads;
-        constexpr int U = kSplitBoundBatch;
         const unsigned long long* gb = p.chist + rh * kCutBins;
-        uint64_t v[BPT], lsum = 0;
+        uint64_t v[kBinsPerThread], lsum = 0;
 #pragma unroll
-        for (int j = 0; j < BPT; ++j) v[j] = gb[tid * BPT + j];
+        for (int j = 0; j < kBinsPerThread; ++j) v[j] = gb[tid * kBinsPerThread + j];
         float mx = -INFINITY;
         for (int i = tid; i < p.pmax_n; i += nt) mx = fmaxf(mx, p.pmax[rh * p.pmax_stride + i]);
-        float sb[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t k = tid + static_cast<int64_t>(u) * nt;
-            sb[u] = k < ncand ? csc[k] : 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < BPT; ++j) lsum += v[j];
-        mx = block_max_f(mx, bs);                     // its barriers also publish the cleared slice counts
+        for (int j = 0; j < kBinsPerThread; ++j) lsum += v[j];
+        mx = block_max_f<kSplitWaves>(mx, bs);
         if (tid == 0) bs.list_n = 0;
         for (int i = tid; i < 256; i += nt) bs.hist[0][i] = 0;
+        // the bin where the running mass first reaches ceil(top_p * total)
         uint64_t E;
-        uint64_t c = block_excl_scan_u64(lsum, bs, &E);
+        uint64_t c = block_excl_scan_u64<kSplitWaves>(lsum, bs, &E);
         uint64_t rem = static_cast<uint64_t>(ceil(static_cast<double>(p.top_p) * static_cast<double>(E)));
         if (rem == 0) rem = 1;
 #pragma unroll
-        for (int j = 0; j < BPT; ++j) {
+        for (int j = 0; j < kBinsPerThread; ++j) {
             if (v[j] != 0 && c < rem && c + v[j] >= rem) {
-                bs.bcast_u32[0] = static_cast<uint32_t>(tid * BPT + j);
+                bs.bcast_u32[0] = static_cast<uint32_t>(tid * kBinsPerThread + j);
                 bs.bcast_u64[0] = c;
             }
             c += v[j];
@@ -1057,114 +1132,95 @@ __global__ __launch_bounds__(kCutThreads) void route_split_bound_kernel(SplitPar
         __syncthreads();
         const int bstar = static_cast<int>(bs.bcast_u32[0]);
         rem -= bs.bcast_u64[0];
-        // one pass, U candidates per thread in flight: members of the boundary bin,
-        // and per slice the candidates in earlier bins
-        const int nc32 = static_cast<int>(ncand);         // a level holds fewer than 2^31 candidates
-        for (int kb = 0; kb < nc32; kb += U * nt) {
-            if (kb) {
+        // per slice: candidates in earlier bins (all kept) and the boundary bin's members
+        const uint32_t* cum = p.cum + rh * p.slice_stride * (kCutBins + 1);
+        constexpr int SPT = kSplitMaxSlices / kSplitThreads;   // slices per thread, contiguous
+        uint32_t mc[SPT], msum = 0;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int k = kb + tid + u * nt;
-                    sb[u] = k < nc32 ? csc[k] : 0.f;
-                }
+        for (int j = 0; j < SPT; ++j) {
+            const int s2 = tid * SPT + j;
+            mc[j] = 0u;
+            if (s2 < nsl) {
+                const uint32_t a = cum[static_cast<int64_t>(s2) * (kCutBins + 1) + bstar];
+                const uint32_t b = cum[static_cast<int64_t>(s2) * (kCutBins + 1) + bstar + 1];
+                sh.s_lt[s2] = a;
+                sh.s_mo[s2] = a;
+                mc[j] = b - a;
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int kw = kb + u * nt + (wave << 6);   // the wave's first candidate
-                const int k = kw + lane;
-                bool lt = false, mem = false;
-                if (k < nc32) {
-                    const int bn = cut_bin(sb[u], mx);
-                    lt = bn < bstar;
-                    mem = bn == bstar;                 // with any mass, so counts by key and by bin agree
-                }
-                const unsigned long long blt = __ballot(lt);
-                if (lane == 0 && blt) atomicAdd(&sh.s_lt[kw >> kSplitSliceLog2], static_cast<uint32_t>(__popcll(blt)));
-                const unsigned long long bal = __ballot(mem);
-                if (bal) {
-                    uint32_t base = 0;
-                    if (lane == 0) base = atomicAdd(&bs.list_n, static_cast<uint32_t>(__popcll(bal)));
-                    base = static_cast<uint32_t>(__shfl(static_cast<int>(base), 0));
-                    const uint32_t pos = base + static_cast<uint32_t>(__popcll(bal & ((1ull << lane) - 1ull)));
-                    if (mem && pos < kCutList) bs.list[pos] = static_cast<uint32_t>(k);
-                }
-            }
+            msum += mc[j];
         }
+        uint64_t mall;
+        uint32_t mb = static_cast<uint32_t>(block_excl_scan_u64<kSplitWaves>(msum, bs, &mall));
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            const int s2 = tid * SPT + j;
+            if (s2 < nsl) sh.s_mb[s2] = mb;
+            mb += mc[j];
+        }
+        if (tid == 0) sh.s_mb[nsl] = static_cast<uint32_t>(mall);
         __syncthreads();
-        const uint32_t m = bs.list_n;
-        auto score = [&](int64_t k) -> float { return csc[k]; };
-        if (m <= kWave) {
-            if (wave == 0) {
-                const bool valid = lane < static_cast<int>(m);
-                const uint32_t k = valid ? bs.list[lane] : 0u;
-                const float s = valid ? score(k) : 0.f;
-                const uint32_t key = valid ? desc_key(s) : 0xffffffffu;
-                const uint64_t F = valid ? mass_fx(s, mx) : 0;
-                bs.wkey[lane] = key;
-                bs.wk[lane] = k;
-                __builtin_amdgcn_wave_barrier();
-                int rank = 0;
-                for (int j = 0; j < static_cast<int>(m); ++j) {
-                    const uint32_t kj = bs.wkey[j], ij = bs.wk[j];
-                    rank += (kj < key) || (kj == key && ij < k);
-                }
-                if (valid) bs.wmass[rank] = F;
-                __builtin_amdgcn_wave_barrier();
-                const uint64_t mj = lane < static_cast<int>(m) ? bs.wmass[lane] : 0;
-                bs.wpre[lane] = wave_scan_u64(mj) - mj;
-                __builtin_amdgcn_wave_barrier();
-                const bool kept = valid && bs.wpre[rank] < rem;
-                const uint32_t kap = static_cast<uint32_t>(
-                    __builtin_amdgcn_readlane(static_cast<int>(wave_scan_max_u32(kept ? key : 0u)), 63));
-                const uint64_t ties = __popcll(__ballot(kept && key == kap));
-                if (lane == 0) {
-                    bs.bcast_u32[1] = kap;
-                    bs.bcast_u64[1] = ties;
-                }
+        const uint32_t m = static_cast<uint32_t>(mall);
+        // member e -> (candidate, score): its slice by binary search over the member offsets
+        auto member = [&](uint32_t e, uint32_t& k, float& s) {
+            int lo = 0, hi = nsl - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (sh.s_mb[mid] <= e) lo = mid;
+                else hi = mid - 1;
             }
+            const int64_t at = cbase + (static_cast<int64_t>(lo) << kSplitSliceLog2) + sh.s_mo[lo] + (e - sh.s_mb[lo]);
+            k = p.srt_k[at];
+            s = p.srt_s[at];
+        };
+        if (m <= kCutList) {
+            for (uint32_t e = tid; e < m; e += nt) {
+                uint32_t k;
+                float s;
+                member(e, k, s);
+                bs.list[e] = k;
+                bs.list_s[e] = s;
+            }
+            __syncthreads();
+        }
+        if (m <= kWave) {
+            if (w == 0) wave_resolve(bs.list, bs.list_s, static_cast<int>(m), mx, rem, bs);
             __syncthreads();
             kappa = bs.bcast_u32[1];
             need = bs.bcast_u64[1];
         } else {
             if (m <= kCutList) {
                 kappa = radix_kappa([&](int64_t e, uint32_t& key, uint64_t& F) {
-                    const float s = score(static_cast<int64_t>(bs.list[e]));
+                    const float s = bs.list_s[e];
                     key = desc_key(s);
                     F = mass_fx(s, mx);
                     return true;
                 }, m, rem, bs);
             } else {
-                kappa = radix_kappa([&](int64_t k, uint32_t& key, uint64_t& F) {
-                    const float s = score(k);
-                    if (cut_bin(s, mx) != bstar) return false;
+                kappa = radix_kappa([&](int64_t e, uint32_t& key, uint64_t& F) {
+                    uint32_t k;
+                    float s;
+                    member(static_cast<uint32_t>(e), k, s);
                     key = desc_key(s);
                     F = mass_fx(s, mx);
                     return true;
-                }, ncand, rem, bs);
+                }, m, rem, bs);
             }
             const uint64_t Fk = mass_fx(desc_key_to_float(kappa), mx);
             need = Fk ? (rem + Fk - 1) / Fk : 0;
         }
-        // the boundary bin's members below the boundary key, and its ties, per slice
-        if (m <= kCutList) {
-            for (uint32_t i = tid; i < m; i += nt) {
-                const uint32_t k = bs.list[i];
-                const uint32_t key = desc_key(score(k));
-                if (key < kappa) atomicAdd(&sh.s_lt[k >> kSplitSliceLog2], 1u);
-                else if (key == kappa) atomicAdd(&sh.s_tie[k >> kSplitSliceLog2], 1u);
+        // members below the boundary key, and the ties, per slice
+        for (uint32_t e = tid; e < m; e += nt) {
+            uint32_t k;
+            float s;
+            if (m <= kCutList) {
+                k = bs.list[e];
+                s = bs.list_s[e];
+            } else {
+                member(e, k, s);
             }
-        } else {                                       // a crowded bin: count every slice by key
-            for (int i = tid; i < nsl; i += nt) sh.s_lt[i] = 0u;
-            __syncthreads();
-            for (int64_t kb = 0; kb < ncand; kb += nt) {
-                const int64_t k = kb + tid;
-                const uint32_t key = k < ncand ? desc_key(csc[k]) : 0xffffffffu;
-                const unsigned long long blt = __ballot(k < ncand && key < kappa);
-                const unsigned long long bti = __ballot(k < ncand && key == kappa);
-                const int sidx = static_cast<int>((kb + (wave << 6)) >> kSplitSliceLog2);
-                if (lane == 0 && blt) atomicAdd(&sh.s_lt[sidx], __popcll(blt));
-                if (lane == 0 && bti) atomicAdd(&sh.s_tie[sidx], __popcll(bti));
-            }
+            const uint32_t key = desc_key(s);
+            if (key < kappa) atomicAdd(&sh.s_lt[k >> kSplitSliceLog2], 1u);
+            else if (key == kappa) atomicAdd(&sh.s_tie[k >> kSplitSliceLog2], 1u);
         }
     } else {
         for (int i = tid; i < nsl; i += nt) {
@@ -1173,20 +1229,18 @@ __global__ __launch_bounds__(kCutThreads) void route_split_bound_kernel(SplitPar
         }
     }
     __syncthreads();
-    // (ties << 32 | below) before each slice: one slice per thread, in slice order
-    const uint64_t mine = tid < nsl ? ((static_cast<uint64_t>(sh.s_tie[tid]) << 32) | sh.s_lt[tid]) : 0ull;
-    uint64_t all;
-    const uint64_t before = block_excl_scan_u64(mine, bs, &all);
-    if (tid < nsl) p.slice[rh * p.slice_stride + tid] = before;
+    // (ties << 32 | below) before this slice, and the totals
+    uint64_t mine = 0;
+    for (int i = tid; i < nsl; i += nt)
+        if (i < sl) mine += (static_cast<uint64_t>(sh.s_tie[i]) << 32) | sh.s_lt[i];
+    uint64_t mine_all = 0;
+    for (int i = tid; i < nsl; i += nt) mine_all += (static_cast<uint64_t>(sh.s_tie[i]) << 32) | sh.s_lt[i];
+    const uint64_t before_sl = block_sum_u64<kSplitWaves>(mine, bs);
+    const uint64_t all = block_sum_u64<kSplitWaves>(mine_all, bs);
     const uint64_t tot_lt = all & 0xffffffffu, tot_tie = all >> 32;
     const int64_t m_kept = static_cast<int64_t>(tot_lt + (tot_tie < need ? tot_tie : need));
-    if (tid == 0) {
-        SplitInfo si;
-        si.need_ties = need;
-        si.kappa = kappa;
-        si.take_all = take_all ? 1 : 0;
-        si.ncand = ncand;
-        p.info[rh] = si;
+    const bool leaf = (p.li == 0);
+    if (sl == 0 && tid == 0) {
         p.kept_cnt[rh * p.L + p.li] = static_cast<int32_t>(m_kept);
         if (leaf) {
             p.n_sel[rh] = static_cast<int32_t>(m_kept);
@@ -1197,42 +1251,19 @@ __global__ __launch_bounds__(kCutThreads) void route_split_bound_kernel(SplitPar
             p.level_stats[(rh * p.L + p.li) * 2 + 1] = static_cast<int32_t>(m_kept);
         }
     }
-}
-
-__global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitParams p) {
-    constexpr int NW = kSplitThreads / kWave;
-    constexpr int BPW = kSplitSlice / kSplitThreads;           // 64-candidate blocks per wave
-    __shared__ uint64_t wcnt[NW];
-    const int sl = blockIdx.x, hq = blockIdx.y, row = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int64_t rh = static_cast<int64_t>(row) * p.Hq + hq;
-    const SplitInfo si = p.info[rh];
-    const int64_t ncand = si.ncand;
-    const int64_t k0 = static_cast<int64_t>(sl) << kSplitSliceLog2;
-    if (k0 >= ncand) return;
-    const float* csc = p.cand_sc + rh * p.cand_stride;
-    const int32_t* cnd = p.cand_nd + rh * p.cand_stride;
-    // this wave's blocks: [kw, kw + 64 * BPW)
-    const int64_t kw = k0 + static_cast<int64_t>(w) * 64 * BPW;
-    float s[BPW];
-    int32_t nd[BPW];
-#pragma unroll
-    for (int j = 0; j < BPW; ++j) {
-        const int64_t k = kw + j * 64 + lane;
-        s[j] = k < ncand ? csc[k] : 0.f;
-        nd[j] = k < ncand ? cnd[k] : 0;
-    }
+    if (sl >= nsl) return;
+    // ---- the slice's kept ids ----
     auto classify = [&](int j, bool& lt, bool& tie) {
         const int64_t k = kw + j * 64 + lane;
         const bool valid = k < ncand;
-        if (si.take_all) {
+        if (take_all) {
             lt = valid;
             tie = false;
             return;
         }
-        const uint32_t key = desc_key(s[j]);
-        lt = valid && key < si.kappa;
-        tie = valid && key == si.kappa;
+        const uint32_t key = desc_key(sv[j]);
+        lt = valid && key < kappa;
+        tie = valid && key == kappa;
     };
     uint64_t c_lt = 0, c_tie = 0;
 #pragma unroll
@@ -1242,16 +1273,15 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitPa
         c_lt += __popcll(__ballot(lt));
         c_tie += __popcll(__ballot(tie));
     }
-    if (lane == 0) wcnt[w] = (c_tie << 32) | c_lt;
+    if (lane == 0) sh.wcnt[w] = (c_tie << 32) | c_lt;
     __syncthreads();
-    uint64_t before = p.slice[rh * p.slice_stride + sl];
+    uint64_t before = before_sl;
 #pragma unroll
-    for (int i = 0; i < NW; ++i)
-        if (i < w) before += wcnt[i];
+    for (int i = 0; i < kSplitWaves; ++i)
+        if (i < w) before += sh.wcnt[i];
     uint64_t lt_b = before & 0xffffffffu, tie_b = before >> 32;
-    const uint64_t need = si.need_ties;
-    const bool leaf = (p.li == 0);
     int32_t* kept_out = leaf ? nullptr : p.kept + rh * p.nodes_total + p.lvl_off;
+    int32_t* rank_out = leaf ? nullptr : p.rank + rh * p.nodes_total + p.lvl_off;
     int32_t* sel_out = leaf ? p.sel_blocks + rh * p.sel_cap : nullptr;
     int32_t* lsel_out = p.level_sel ? p.level_sel + p.lsel_off + rh * p.nodes_l : nullptr;
     uint32_t* bm = p.bitmap + rh * p.bm_words_total + p.bm_off;
@@ -1268,7 +1298,10 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitPa
         if (keep) {
             const int64_t pos = static_cast<int64_t>(my_lt + (lt ? (my_tie < need ? my_tie : need) : my_tie));
             const int32_t node = nd[j];
-            if (kept_out) kept_out[pos] = node;
+            if (kept_out) {
+                kept_out[pos] = node;
+                rank_out[node] = static_cast<int32_t>(pos);
+            }
             if (sel_out && pos < p.sel_cap) sel_out[pos] = node;
             if (lsel_out) lsel_out[pos] = node;
         }
@@ -1308,6 +1341,7 @@ struct UpperParams {
     int32_t* kept;             // ws kept lists
     int32_t* kept_cnt;         // [rows, Hq, L]
     uint32_t* bitmap;          // ws kept bitmaps
+    int32_t* rank;             // ws kept node -> place in its head's kept list (split cut only, else null)
     int64_t bm_words_total;
     int32_t* level_stats;
     int32_t* level_sel;
@@ -1384,10 +1418,12 @@ __global__ __launch_bounds__(kCutThreads) void route_upper_kernel(UpperParams p)
         auto score = [&](int64_t k) -> float { return sh.sc[k]; };
         int32_t* kept_out = p.kept + rh * p.nodes_total + p.sel_off[li];
         int32_t* lsel_out = p.level_sel ? p.level_sel + p.rows * p.Hq * p.sel_off[li] + rh * p.nodes[li] : nullptr;
+        int32_t* rank_out = p.rank ? p.rank + rh * p.nodes_total + p.sel_off[li] : nullptr;
         auto emit = [&](int64_t pos, int64_t k) {
             const int32_t node = sh.cid[k];
             sh.par[pos] = node;                 // parents of the next level (cid holds this level's ids)
             kept_out[pos] = node;
+            if (rank_out) rank_out[node] = static_cast<int32_t>(pos);
             if (lsel_out) lsel_out[pos] = node;
         };
         auto mark = [&](int64_t k, uint32_t bits) {
@@ -1429,7 +1465,7 @@ __global__ __launch_bounds__(kCutThreads) void route_upper_kernel(UpperParams p)
 template <int D, int G>
 static void launch_score_t(dim3 grid, const ScoreParams& sp, hipStream_t st) {
     ProfScope ps("route_score", sp.li + 1, st);
-    hipLaunchKernelGGL((route_score_kernel<D, G>), grid, dim3(256), 0, st, sp);
+    hipLaunchKernelGGL((route_score_kernel<D, G>), grid, dim3(kScoreThreads), 0, st, sp);
 }
 
 template <int D>
@@ -1480,6 +1516,7 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
         up.kept = kept;
         up.kept_cnt = kept_cnt;
         up.bitmap = bitmap;
+        up.rank = lay.split ? reinterpret_cast<int32_t*>(ws + lay.rank) : nullptr;
         up.bm_words_total = lay.bm_words_total;
         up.level_stats = a.level_stats;
         up.level_sel = a.level_sel;
@@ -1530,11 +1567,18 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
         // parent slots of the level: blocks of b nodes at the top; below, every
         // node of level l+1 plus the incomplete one
         const int64_t slots = top ? (g.nodes[li] + g.b - 1) / g.b : g.nodes[li + 1] + 1;
-        const int64_t gx = std::max<int64_t>(1, (slots + kScoreParents - 1) / kScoreParents);
+        const int64_t gx = score_groups(slots, pairs);
         if (lay.split) {
             sp.pmax = reinterpret_cast<float*>(ws + lay.pmax);
             sp.pmax_stride = lay.pmax_stride;
             sp.chist = reinterpret_cast<unsigned long long*>(ws + lay.chist);
+            sp.bm_cur = bitmap + lay.bm_off[li];
+            sp.rank_up = reinterpret_cast<const int32_t*>(ws + lay.rank);
+            sp.lvl_off_up = top ? 0 : g.sel_off[li + 1];
+            sp.kept_cnt = kept_cnt;
+            sp.cand_sc = reinterpret_cast<float*>(ws + lay.cand_sc);
+            sp.cand_nd = reinterpret_cast<int32_t*>(ws + lay.cand_nd);
+            sp.cand_stride = lay.cand_stride;
         }
         hipError_t e = (g.D == 128) ? launch_score_g<128>(g.G, dim3(static_cast<unsigned>(gx), pairs), sp, st)
                                     : launch_score_g<64>(g.G, dim3(static_cast<unsigned>(gx), pairs), sp, st);
@@ -1571,19 +1615,20 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
             xp.pmax = reinterpret_cast<const float*>(ws + lay.pmax);
             xp.pmax_n = static_cast<int>(gx);
             xp.pmax_stride = lay.pmax_stride;
-            xp.cand_sc = reinterpret_cast<float*>(ws + lay.cand_sc);
-            xp.cand_nd = reinterpret_cast<int32_t*>(ws + lay.cand_nd);
+            xp.cand_sc = reinterpret_cast<const float*>(ws + lay.cand_sc);
+            xp.cand_nd = reinterpret_cast<const int32_t*>(ws + lay.cand_nd);
+            xp.rank = reinterpret_cast<int32_t*>(ws + lay.rank);
+            xp.srt_k = reinterpret_cast<uint32_t*>(ws + lay.srt_k);
+            xp.srt_s = reinterpret_cast<float*>(ws + lay.srt_s);
             xp.cand_stride = lay.cand_stride;
+            xp.cum = reinterpret_cast<uint32_t*>(ws + lay.cum);
             xp.chist = reinterpret_cast<unsigned long long*>(ws + lay.chist);
-            xp.info = reinterpret_cast<SplitInfo*>(ws + lay.cinfo);
-            xp.slice = reinterpret_cast<unsigned long long*>(ws + lay.cslice);
             xp.slice_stride = lay.slice_stride;
             // candidates of a level are at most its node slots
             const unsigned nsl = static_cast<unsigned>((g.nodes[li] + kSplitSlice - 1) / kSplitSlice);
             {
                 ProfScope ps("route_cut", li + 1, st);
                 hipLaunchKernelGGL(route_split_hist_kernel, dim3(nsl, g.Hq, a.rows), dim3(kSplitThreads), 0, st, xp);
-                hipLaunchKernelGGL(route_split_bound_kernel, dim3(g.Hq, a.rows), dim3(kCutThreads), 0, st, xp);
                 hipLaunchKernelGGL(route_split_emit_kernel, dim3(nsl, g.Hq, a.rows), dim3(kSplitThreads), 0, st, xp);
             }
             e = hipGetLastError();

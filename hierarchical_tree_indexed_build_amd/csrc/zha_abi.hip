@@ -118,17 +118,19 @@ WsLayout layout(const Geo& g, int rows) {
         int64_t pm = 1;
         for (int l = 0; l < g.L; ++l) {
             const int64_t slots = (l == g.L - 1) ? (g.nodes[l] + g.b - 1) / g.b : g.nodes[l + 1] + 1;
-            pm = std::max<int64_t>(pm, (slots + kScoreParents - 1) / kScoreParents);
+            pm = std::max<int64_t>(pm, score_groups(slots, static_cast<int64_t>(R) * g.Hkv));
         }
         L.cand_stride = cand;
         L.pmax_stride = pm;
         L.slice_stride = slices;
+        L.rank = take(R * g.Hq * static_cast<size_t>(g.nodes_total) * 4);
         L.cand_sc = take(R * g.Hq * static_cast<size_t>(cand) * 4);
         L.cand_nd = take(R * g.Hq * static_cast<size_t>(cand) * 4);
+        L.srt_k = take(R * g.Hq * static_cast<size_t>(cand) * 4);
+        L.srt_s = take(R * g.Hq * static_cast<size_t>(cand) * 4);
         L.pmax = take(R * g.Hq * static_cast<size_t>(pm) * 4);
         L.chist = take(R * g.Hq * static_cast<size_t>(kCutBins) * 8);
-        L.cinfo = take(R * g.Hq * sizeof(SplitInfo));
-        L.cslice = take(R * g.Hq * static_cast<size_t>(slices) * 8);
+        L.cum = take(R * g.Hq * static_cast<size_t>(slices) * (kCutBins + 1) * 4);
     }
     L.total = off;
     return L;

@@ -14,7 +14,18 @@ constexpr int kWave = 64;
 constexpr int kMaxGroup = 16;          // H_q / H_kv handled by one kernel group
 constexpr int kAttnWorkgroups = 512;   // attention workgroups per launch (partial slots: this + pairs)
 constexpr size_t kAlign = 256;
-constexpr int kScoreParents = 4;       // parent slots per scoring workgroup, one per wave
+constexpr int kScoreThreads = 512;     // scoring workgroup: one wave per active parent at a time
+
+// Scoring workgroups per (row, kv head) for a level with `slots` parent slots:
+// about 512 in all over `pairs` (row, kv head) pairs, each a run of at most 64
+// slots (one wave's lanes build the run's masks).
+inline int64_t score_groups(int64_t slots, int64_t pairs) {
+    const int64_t target = (512 + pairs - 1) / (pairs > 0 ? pairs : 1);
+    int64_t w = target < slots ? target : slots;
+    const int64_t need = (slots + 63) / 64;
+    w = w > need ? w : need;
+    return w > 0 ? w : 1;
+}
 constexpr int kCutBins = 2048;         // mass bins of a cut's first pass
 constexpr int kSplitSlice = 2048;      // candidates per workgroup of the split cut
 constexpr int kSplitSliceLog2 = 11;
@@ -50,24 +61,18 @@ struct WsLayout {
     size_t partial;       // float  [kAttnWorkgroups + rows * Hkv, G, D + 4] split-K partial states (max, sum, 2 pad, acc)
     // split cut (rows * Hq <= kSplitMaxPairs and every level small enough); absent otherwise
     bool split;
+    size_t rank;          // int32  [rows, Hq, nodes_total] a kept node's place in its head's kept list
     size_t cand_sc;       // float  [rows, Hq, cand_stride] a level's candidate scores in candidate order
     size_t cand_nd;       // int32  [rows, Hq, cand_stride] their node ids
+    size_t srt_k;         // uint32 [rows, Hq, cand_stride] per slice, candidates grouped by bin
+    size_t srt_s;         // float  [rows, Hq, cand_stride] and their scores
     int64_t cand_stride;
     size_t pmax;          // float  [rows, Hq, pmax_stride] per scoring workgroup maxima of a level
     int64_t pmax_stride;
     size_t chist;         // uint64 [rows, Hq, kCutBins] a level's mass per bin
-    size_t cinfo;         // SplitInfo [rows, Hq]
-    size_t cslice;        // uint64 [rows, Hq, slice_stride] (ties << 32 | below) before each slice
+    size_t cum;           // uint32 [rows, Hq, slice_stride, kCutBins + 1] per slice, candidates before each bin
     int64_t slice_stride;
     size_t total;
-};
-
-// A level's cut boundary as the split cut's boundary kernel leaves it.
-struct SplitInfo {
-    uint64_t need_ties;
-    uint32_t kappa;
-    int32_t take_all;
-    int64_t ncand;
 };
 
 // Parameters shared by every kernel that reads queries.

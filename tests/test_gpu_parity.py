@@ -270,6 +270,24 @@ def test_causal_rows_and_short_prefixes():
         assert np.abs(o_np[0, t_, 0] - o).max() <= 1e-5, t_
 
 
+def test_route_levels_below_the_fused_levels():
+    """b = 2 puts a level of 16384 nodes above the leaves: it is scored and cut
+    on its own (split over slices for this one pair), and its kept ranks feed
+    the leaf level's scoring."""
+    w = W.get_workload("tiny")
+    w.n_tokens = 65536
+    w.capacity = 65536
+    w.branching = 2
+    w.n_levels = 5
+    w.top_p = 0.9
+    say("[route deep] tiny-like b=2 L=5 N=65536")
+    st = Staged(w)
+    q_pos = _qpos(st, w.queries_per_step)
+    qn, q, sel, nsel, stats, lsel, p = _route(st, w.queries_per_step, q_pos)
+    flips = _teacher_forced(st, qn, q_pos.cpu().numpy(), stats, lsel, p, st.oracle_trees())
+    say(f"  margin-exempt differences: {flips}")
+
+
 def test_append_bit_identical_to_build():
     t = torch()
     w = W.get_workload("decode1m", shrink=2)     # b = 32, L = 2, bf16, 8 kv heads
