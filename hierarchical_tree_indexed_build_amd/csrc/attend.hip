@@ -531,6 +531,262 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
 }
 
 // ----------------------------------------------------------------------------
+// split-K attention for bf16 caches with the scores on the matrix cores
+// Same work split, pipeline, partial slots and merge as attend_kernel; the
+// group's 16 x g score tile is one 16x16x32 bf16 MFMA per 32 dimensions:
+//   S^T[token][head] = sum_d K[token][d] * q[head][d],
+// A = the group's K rows (lane l: token l % 16, dims [(l/16) D/4, +D/4), read
+// straight from HBM as bf16), B = q (lane l: head l % 16, same dims; heads
+// >= g are zero). q is split into bf16 hi + lo parts, so q . k is exact to
+// about 2^-16 of |q| |k| (two MFMAs per slice). The result holds token
+// 4 (l/16) + r, head l % 16 in lane l, register r: the online softmax runs in
+// that layout, and the probabilities go through LDS to the value pass, which
+// stays on the VALU (lanes own 4 tokens x D/LPT dims as in attend_kernel).
+// ----------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t bf16_bits_rn(float x) {   // round to nearest even
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
+    using C = AttnCfg<uint16_t, D, G>;
+    constexpr int NW = 4;
+    constexpr int NP = C::NP, WPP = C::WPP, DPL = C::DPL, LPT = C::LPT, TPP = C::TPP;
+    constexpr int KW = D / 8;                    // 32-bit words of K per lane (D/4 bf16)
+    constexpr int NS = D / 32;                   // MFMA slices of 32 dimensions
+    static_assert(G <= 16 && kGroupTokens == 16, "16 x 16 score tile");
+    __shared__ float sm_m[NW][G], sm_l[NW][G];
+    __shared__ float sm_acc[NW][G][D];
+    __shared__ float sm_p[NW][kGroupTokens][G];   // a group's probabilities, token-major
+
+    const int wg = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int part = lane % LPT, tsub = lane / LPT;       // value-pass layout
+    const int mrow = lane & 15, mblk = lane >> 4;          // MFMA layout: token/head, dim block
+    const PlanView pv(p);
+    const int64_t total = pv.total();
+    const int64_t chunk = attn_chunk(total, p.nwg);
+    const int64_t r0 = static_cast<int64_t>(wg) * chunk;
+    if (r0 >= total) return;
+    const int64_t r1 = imin(r0 + chunk, total);
+    const int lo = pv.first_pair(r0);          // first pair of the slice
+    const int gpi = 1 << p.lgpi;
+    const int tg = p.b >= kGroupTokens ? kGroupTokens : p.b;
+
+    for (int pr = lo; pr < p.pairs; ++pr) {
+        const int64_t pg0 = pv.at(pr);
+        if (pg0 >= r1) break;
+        const int64_t ga = imax(r0, pg0) - pg0, gb = imin(r1, pv.at(pr + 1)) - pg0;   // this pair's groups here
+        if (ga >= gb) continue;                                  // a pair with no groups
+        const int row = pr / p.Hkv, kv = pr % p.Hkv;
+        const int s = row / p.ri.T;
+        const int N = visible_clamped(p.ri, row, p.cap);
+
+        // q of head mrow (zero beyond g), scaled, as bf16 hi + lo over this lane's dims
+        bf16x8_t qh[NS], ql[NS];
+        {
+            float qf[D / 4];
+            if (mrow < G) {
+                load_vec<D / 4>(p.q + (static_cast<int64_t>(row) * p.Hq + kv * G + mrow) * D + mblk * (D / 4), qf);
+            } else {
+#pragma unroll
+                for (int e = 0; e < D / 4; ++e) qf[e] = 0.f;
+            }
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float x = qf[sl * 8 + j] * p.qscale;
+                    const uint32_t hb = bf16_bits_rn(x);
+                    const float hi = __uint_as_float(hb << 16);
+                    const uint32_t lb = bf16_bits_rn(x - hi);
+                    qh[sl][j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hb));
+                    ql[sl][j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lb));
+                }
+        }
+        const uint16_t* Kr = static_cast<const uint16_t*>(p.K) + (static_cast<int64_t>(s) * p.Hkv + kv) * p.cap * D + mblk * (D / 4);
+        const uint16_t* Vb = static_cast<const uint16_t*>(p.V) + (static_cast<int64_t>(s) * p.Hkv + kv) * p.cap * D + part * DPL;
+        const int2* items = p.items + static_cast<int64_t>(pr) * p.item_stride;
+
+        // softmax state: in the MFMA layout (head mrow) m and this lane's share of l;
+        // the accumulators in the value-pass layout
+        float m = -INFINITY, l = 0.f;
+        float acc[G][DPL];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+
+        int64_t batch_k0 = -1;
+        int2 batch = make_int2(0, 0);
+        auto item_of = [&](int64_t g) -> int2 {
+            const int64_t it = g >> p.lgpi;
+            if (p.dense) return make_int2(static_cast<int>(it), static_cast<int>(kAllHeads));
+            const int64_t k = (g - ga - wave) / NW;                 // this wave's k-th group
+            if (batch_k0 < 0 || k >= batch_k0 + kWave) {
+                batch_k0 = k;
+                const int64_t gl = g + static_cast<int64_t>(lane) * NW;
+                batch = gl < gb ? items[gl >> p.lgpi] : make_int2(0, 0);
+            }
+            const int src = static_cast<int>(k - batch_k0);
+            return make_int2(__builtin_amdgcn_readlane(batch.x, src), __builtin_amdgcn_readlane(batch.y, src));
+        };
+        auto first_token = [&](int64_t g, int2 e) -> int64_t {
+            return (static_cast<int64_t>(e.x) << p.lb) + (g & (gpi - 1)) * kGroupTokens;
+        };
+        auto issue = [&](int64_t t0, uint32_t (&kb)[KW], uint32_t (&vb)[NP][WPP]) {
+            {
+                const int j = min(mrow, tg - 1);
+                const int64_t t = imin(t0 + j, N - 1);        // always a present row
+                load_words<KW>(Kr + t * D, kb);
+            }
+#pragma unroll
+            for (int ps = 0; ps < NP; ++ps) {
+                const int j = min(ps * TPP + tsub, tg - 1);
+                const int64_t t = imin(t0 + j, N - 1);
+                load_words<WPP>(Vb + t * D, vb[ps]);
+            }
+        };
+        auto consume = [&](int64_t t0, uint32_t mask, const uint32_t (&kb)[KW], const uint32_t (&vb)[NP][WPP]) {
+            // scores: 16 tokens x 16 heads
+            f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl) {
+                bf16x8_t a;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t w = kb[sl * 4 + j];
+                    a[2 * j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w & 0xffffu));
+                    a[2 * j + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w >> 16));
+                }
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[sl], sc, 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[sl], sc, 0, 0, 0);
+            }
+            // online softmax of head mrow over tokens 4 * mblk + r
+            const bool hv = mrow < G;
+            const bool hm = hv && ((mask & kAllHeads) || ((mask >> mrow) & 1u));
+            float sv[4], gm = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 4 * mblk + r;
+                const int64_t t = t0 + j;
+                const bool ok = hv && (j < tg) && (t < N) && (hm || t == 0);
+                sv[r] = ok ? sc[r] : -INFINITY;
+                gm = fmaxf(gm, sv[r]);
+            }
+            gm = fmaxf(gm, __shfl_xor(gm, 16));
+            gm = fmaxf(gm, __shfl_xor(gm, 32));
+            const float mn = fmaxf(m, gm);
+            const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);   // 0 while nothing was seen
+            float ps_sum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pr_ = (mn == -INFINITY) ? 0.f : fast_exp2(sv[r] - mn);   // 0 when masked
+                ps_sum += pr_;
+                if (hv) sm_p[wave][4 * mblk + r][mrow] = pr_;
+            }
+            l = l * alpha + ps_sum;
+            m = mn;
+            __builtin_amdgcn_wave_barrier();
+            // value pass: rescale, then accumulate p * v for the lane's tokens
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) acc[h][e] *= ah;
+            }
+#pragma unroll
+            for (int ps = 0; ps < NP; ++ps) {
+                float v[DPL];
+                widen<uint16_t, DPL, WPP>(vb[ps], v);
+                const float* pp = &sm_p[wave][ps * TPP + tsub][0];
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float ph = pp[h];
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
+                }
+            }
+            __builtin_amdgcn_wave_barrier();                       // sm_p is rewritten by the next group
+        };
+
+        uint32_t kA[KW], vA[NP][WPP], kB[KW], vB[NP][WPP];
+        int64_t g = ga + wave;
+        if (g < gb) {
+            int2 e0 = item_of(g);                                          // chunk of group g
+            int2 e1 = (g + NW < gb) ? item_of(g + NW) : make_int2(0, 0);   // chunk of group g + NW
+            issue(first_token(g, e0), kA, vA);
+            for (;;) {
+                int64_t gn = g + NW;
+                int2 e2 = make_int2(0, 0);
+                if (gn < gb) {
+                    issue(first_token(gn, e1), kB, vB);
+                    if (gn + NW < gb) e2 = item_of(gn + NW);
+                }
+                consume(first_token(g, e0), static_cast<uint32_t>(e0.y), kA, vA);
+                if (gn >= gb) break;
+                g = gn;
+                e0 = e1;
+                e1 = e2;
+                gn = g + NW;
+                e2 = make_int2(0, 0);
+                if (gn < gb) {
+                    issue(first_token(gn, e1), kA, vA);
+                    if (gn + NW < gb) e2 = item_of(gn + NW);
+                }
+                consume(first_token(g, e0), static_cast<uint32_t>(e0.y), kB, vB);
+                if (gn >= gb) break;
+                g = gn;
+                e0 = e1;
+                e1 = e2;
+            }
+        }
+
+        // ---- merge: the four dim blocks' shares of l, the token slots of the
+        // accumulators, then the waves ----
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (lane < G) {
+            sm_m[wave][lane] = m;
+            sm_l[wave][lane] = l;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[h][e] = strided_sum<LPT>(acc[h][e]);
+            if (lane < LPT) {
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) sm_acc[wave][h][part * DPL + e] = acc[h][e];
+            }
+        }
+        __syncthreads();
+        float* pout = p.partial + static_cast<int64_t>(wg + pr) * G * (D + 4);
+        for (int idx = threadIdx.x; idx < G * (D + 4); idx += blockDim.x) {
+            const int h = idx / (D + 4), c = idx % (D + 4);
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+            float out = 0.f;
+            if (c == 0) {
+                out = M;
+            } else if (c == 1 || c >= 4) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const float f = (sm_m[w][h] == -INFINITY) ? 0.f : fast_exp2(sm_m[w][h] - M);
+                    out += f * (c == 1 ? sm_l[w][h] : sm_acc[w][h][c - 4]);
+                }
+            }
+            pout[idx] = out;
+        }
+        __syncthreads();                                         // sm_* are reused by the next segment
+    }
+}
+
+// ----------------------------------------------------------------------------
 // LSE merge of a pair's segments: one workgroup per (row, query head)
 // Thread (group, quad) merges every NGRP-th slot of the pair for four
 // dimensions: a slot's max, sum and float4 of the accumulator arrive in one
@@ -638,7 +894,10 @@ template <typename KT, int D, int G>
 static hipError_t launch_attn_t(const AttnParams& ap, int rows, int Hq, float* out, float* lse, hipStream_t st) {
     {
         ProfScope ps("attend", 0, st);
-        hipLaunchKernelGGL((attend_kernel<KT, D, G>), dim3(ap.nwg), dim3(256), 0, st, ap);
+        if constexpr (sizeof(KT) == 2)       // bf16 cache: scores on the matrix cores
+            hipLaunchKernelGGL((attend_mfma_kernel<D, G>), dim3(ap.nwg), dim3(256), 0, st, ap);
+        else
+            hipLaunchKernelGGL((attend_kernel<KT, D, G>), dim3(ap.nwg), dim3(256), 0, st, ap);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

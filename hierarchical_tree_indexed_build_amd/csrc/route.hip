@@ -16,7 +16,7 @@
 //    upper levels in one launch: candidates, scores and the cut stay in LDS
 //    from level to level.
 //  * per remaining level (the leaf level always):
-//    - route_score_kernel - a workgroup owns a run of up to 64 parent slots of one
+//    - route_score_kernel - a workgroup owns up to 64 interleaved parent slots of one
 //      (row, kv head). It ORs the group's kept bitmaps of level l+1 over its
 //      slots (plus the incomplete parent, whose complete children are the
 //      orphans) and scores each such parent's b children once for all g query
@@ -69,7 +69,7 @@ struct ScoreParams {
     // maximum of each head's own candidates it scored and writes their scores
     // and ids in the head's candidate order; workgroup 0 of a (row, kv head)
     // clears the heads' mass bins and this level's bitmaps
-    float* pmax;               // [rows, Hq, pmax_stride], column blockIdx.x
+    float* pmax;               // [rows, Hq, pmax_stride], column = the workgroup's run (blockIdx.x)
     int64_t pmax_stride;
     unsigned long long* chist; // [rows, Hq, kCutBins]
     uint32_t* bm_cur;          // this level's kept bitmaps (row-head stride bm_words_total)
@@ -81,13 +81,14 @@ struct ScoreParams {
     int64_t cand_stride;
 };
 
-// Workgroup = a run of at most 64 parent slots of one (row, kv head), one
-// wave per active parent at a time. Every wave builds the run's masks itself
-// with ballots (lane = slot): the slots some head of the group kept, and for
-// each head the slots it takes candidates from.
+// Workgroup = at most 64 parent slots of one (row, kv head), taken every
+// gridDim.x-th, one wave per active parent at a time. Every wave builds the
+// slots' masks itself with ballots (lane = slot): the slots some head of the
+// group kept, and for each head the slots it takes candidates from.
 template <int D, int G>
 __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams p) {
     const int y = blockIdx.y;
+    const int run = blockIdx.x;
     const int row = y / p.Hkv, kv = y % p.Hkv;
     const int s = row / p.T;
     const int N = clamp_visible(p.ri, row, p.cap);
@@ -99,12 +100,14 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
     // (scored when some head of the group kept them) and the incomplete parent
     // holding the orphans
     const int64_t slots = top ? ((nc + p.b - 1) >> p.lb) : (nc_up + (orphans > 0 ? 1 : 0));
-    const int64_t per = (slots + gridDim.x - 1) / gridDim.x;          // <= 64 by the launch
-    const int64_t P0 = static_cast<int64_t>(blockIdx.x) * per;
-    const int64_t P1 = imin(P0 + per, slots);
+    // slots are dealt to the workgroups round-robin (slot = run + i * W,
+    // i < per <= 64 by the launch), so the runs of kept parents a cut leaves
+    // are spread evenly over the workgroups
+    const int64_t W = gridDim.x;
+    const int64_t per = (slots + W - 1) / W;
     const int64_t rh0 = static_cast<int64_t>(row) * p.Hq + kv * G;      // the group's first (row, head)
     const bool split = p.pmax != nullptr;
-    if (split && blockIdx.x == 0) {
+    if (split && run == 0) {
         for (int i = threadIdx.x; i < G * kCutBins; i += blockDim.x) p.chist[rh0 * kCutBins + i] = 0ull;
         const int64_t words = (nc + 31) >> 5;
         for (int h = 0; h < G; ++h)
@@ -113,8 +116,8 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int nw = blockDim.x / kWave;
-    const int64_t my_slot = P0 + lane;
-    const bool have = my_slot < P1;
+    const int64_t my_slot = run + static_cast<int64_t>(lane) * W;
+    const bool have = lane < per && my_slot < slots;
     const bool orph_l = !top && have && orphans > 0 && my_slot == nc_up;
     uint64_t mine[G], act = 0;
 #pragma unroll
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
         act |= mine[h];
     }
     if (!act) {
-        if (split && threadIdx.x < G) p.pmax[(rh0 + threadIdx.x) * p.pmax_stride + blockIdx.x] = -INFINITY;
+        if (split && threadIdx.x < G) p.pmax[(rh0 + threadIdx.x) * p.pmax_stride + run] = -INFINITY;
         return;
     }
 
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
             have_q = true;
         }
         const int slot = __ffsll(static_cast<long long>(a)) - 1;
-        const int64_t par = P0 + slot;
+        const int64_t par = run + static_cast<int64_t>(slot) * W;
         const int64_t c0 = par << p.lb;
         const int64_t c1 = imin(c0 + p.b, nc);
         // split: where this parent's children start in each head's candidate order
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
         if (threadIdx.x < G) {
             float m = red[threadIdx.x][0];
             for (int w = 1; w < nw; ++w) m = fmaxf(m, red[threadIdx.x][w]);
-            p.pmax[(rh0 + threadIdx.x) * p.pmax_stride + blockIdx.x] = m;
+            p.pmax[(rh0 + threadIdx.x) * p.pmax_stride + run] = m;
         }
     }
 }
@@ -280,6 +283,25 @@ __device__ __forceinline__ void wave_resolve(const uint32_t* lk, const float* ls
         bs.bcast_u32[1] = kap;
         bs.bcast_u64[1] = ties;
     }
+}
+
+// LDS histogram updates from a whole wave (every lane calls, `active` or
+// not). Lanes that share an index with at least 7 others are combined first
+// and updated by one lane: many candidates of a cut can fall in one bin, and
+// LDS atomics on one address serialise. The remaining lanes update directly.
+__device__ __forceinline__ void wave_add_u64(unsigned long long* base, int idx, uint64_t v, bool active) {
+    const int lane = threadIdx.x & 63;
+    unsigned long long pend = __ballot(active);
+    for (int it = 0; it < 4 && pend; ++it) {
+        const int leader = __ffsll(static_cast<long long>(pend)) - 1;
+        const int li = __builtin_amdgcn_readlane(idx, leader);
+        const unsigned long long grp = __ballot(active && idx == li) & pend;
+        if (__popcll(grp) < 8) break;
+        const uint64_t sum = lane63_u64(wave_scan_u64(((grp >> lane) & 1ull) ? v : 0ull));
+        if (lane == leader) atomicAdd(base + li, static_cast<unsigned long long>(sum));
+        pend &= ~grp;
+    }
+    if ((pend >> lane) & 1ull) atomicAdd(base + idx, static_cast<unsigned long long>(v));
 }
 
 // Block reductions: a DPP scan per wave (lane 63 holds the wave's result),
@@ -530,13 +552,16 @@ __device__ __forceinline__ CutBoundary cut_boundary(ScoreAt score, int64_t n, fl
     for (int i = tid; i < kCutBins; i += nt) bins[i] = 0;
     __syncthreads();
     uint64_t E = 0;
-    for (int64_t k = tid; k < n; k += nt) {
-        const float s = score(k);
-        const uint64_t F = mass_fx(s, mx);
-        if (F) {
-            E += F;
-            atomicAdd(reinterpret_cast<unsigned long long*>(&bins[cut_bin(s, mx)]), static_cast<unsigned long long>(F));
+    for (int64_t kb = 0; kb < n; kb += nt) {                  // uniform trip count: whole waves update
+        const int64_t k = kb + tid;
+        float s = 0.f;
+        uint64_t F = 0;
+        if (k < n) {
+            s = score(k);
+            F = mass_fx(s, mx);
         }
+        E += F;
+        wave_add_u64(reinterpret_cast<unsigned long long*>(bins), cut_bin(s, mx), F, F != 0);
     }
     if (tid == 0) bs.list_n = 0;
     for (int i = tid; i < 256; i += nt) bs.hist[0][i] = 0;
@@ -642,6 +667,7 @@ __device__ __forceinline__ int wave_cut_small(ScoreAt score, int n, float top_p,
     bs.wpk[lane] = pk;
     __builtin_amdgcn_wave_barrier();
     int rank = 0;
+#pragma unroll 4
     for (int j = 0; j < n; ++j) rank += bs.wpk[j] < pk;
     if (valid) bs.wmass[rank] = F;
     __builtin_amdgcn_wave_barrier();
@@ -1394,7 +1420,8 @@ __global__ __launch_bounds__(kCutThreads) void route_upper_kernel(UpperParams p)
         // ---- score the candidates: a row per LPR lanes, RPP rows per wave pass ----
         const float* summ = p.summaries + p.sum_off[li] + (static_cast<int64_t>(s) * p.Hkv + kv) * p.nodes[li] * D;
         float mx = -INFINITY;
-        for (int64_t kb = static_cast<int64_t>(wave) * RPP * UNR; kb < ncand; kb += static_cast<int64_t>(nw) * RPP * UNR) {
+        // a lone candidate carries the whole mass and is kept unscored
+        for (int64_t kb = static_cast<int64_t>(wave) * RPP * UNR; ncand > 1 && kb < ncand; kb += static_cast<int64_t>(nw) * RPP * UNR) {
             float x[UNR][DPL];
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
@@ -1431,7 +1458,14 @@ __global__ __launch_bounds__(kCutThreads) void route_upper_kernel(UpperParams p)
             atomicOr(&sh.bm[node >> 5], bits << (node & 31));
         };
         int64_t m;
-        if (ncand <= kWave) {                  // one wave, no block steps
+        if (ncand == 1) {
+            if (tid == 0) {
+                emit(0, 0);
+                mark(0, 1u);
+            }
+            __syncthreads();
+            m = 1;
+        } else if (ncand <= kWave) {           // one wave, no block steps
             __syncthreads();                   // publishes sc[]
             if (wave == 0) {
                 const int mw = wave_cut_small(score, static_cast<int>(ncand), p.top_p, sh.bs,

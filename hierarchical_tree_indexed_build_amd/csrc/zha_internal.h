@@ -17,8 +17,8 @@ constexpr size_t kAlign = 256;
 constexpr int kScoreThreads = 512;     // scoring workgroup: one wave per active parent at a time
 
 // Scoring workgroups per (row, kv head) for a level with `slots` parent slots:
-// about 512 in all over `pairs` (row, kv head) pairs, each a run of at most 64
-// slots (one wave's lanes build the run's masks).
+// about 512 in all over `pairs` (row, kv head) pairs, each with at most 64
+// slots (one wave's lanes build their masks).
 inline int64_t score_groups(int64_t slots, int64_t pairs) {
     const int64_t target = (512 + pairs - 1) / (pairs > 0 ? pairs : 1);
     int64_t w = target < slots ? target : slots;

@@ -28,7 +28,7 @@ pytestmark = pytest.mark.gpu
 # Few (row, head) pairs cut each level over many workgroups; batch 8 of
 # gqa128k (256 pairs) takes the one-workgroup-per-pair cut.
 CASES = [("tiny", 0, None), ("gqa128k", 2, 2), ("decode1m", 2, 1), ("decode16m", 2, 1), ("gqa128k", 1, 1),
-         ("gqa128k", 2, 8)]
+         ("gqa128k", 2, 8), ("gqa128k", 0, 1)]
 IDS = [f"{n}-s{s}" for n, s, _ in CASES]
 
 
@@ -130,11 +130,12 @@ DEGENERATE = [("equal", 0.0), ("two", 0.0), ("band", 1e-3), ("band", 1e-2), ("ba
 
 
 # (workload, shrink, batch): b = 32 and b = 16 cut over many workgroups per
-# pair; batch 8 (256 pairs) cuts one workgroup per pair
-CROWDED_AT = [("decode1m", 1, 1), ("gqa128k", 1, 1), ("gqa128k", 1, 8)]
+# pair; batch 8 (256 pairs) cuts one workgroup per pair; the full gqa128k
+# tree has an upper level of about 500 candidates, cut by one wave
+CROWDED_AT = [("decode1m", 1, 1), ("gqa128k", 1, 1), ("gqa128k", 1, 8), ("gqa128k", 0, 1)]
 
 
-@pytest.mark.parametrize("at", CROWDED_AT, ids=["decode1m-s1", "gqa128k-s1", "gqa128k-s1-b8"])
+@pytest.mark.parametrize("at", CROWDED_AT, ids=["decode1m-s1", "gqa128k-s1", "gqa128k-s1-b8", "gqa128k"])
 @pytest.mark.parametrize("kind,noise", DEGENERATE, ids=[f"{k}-{e:g}" for k, e in DEGENERATE])
 def test_route_parity_crowded_scores(kind, noise, at):
     t = torch()
