@@ -255,7 +255,8 @@ def measured_traffic(kernel: str, workload: str):
     return int(rec["traffic_bytes_per_launch"])
 
 
-KERNEL_SYMBOLS = {"attend": "attend_kernel<", "route_score": "route_score_kernel<", "route_cut": "route_cut_kernel"}
+KERNEL_SYMBOLS = {"attend": ("attend_kernel<", "attend_mfma_kernel<"), "route_score": ("route_score_kernel<",),
+                  "route_cut": ("route_cut_kernel", "route_split_hist_kernel", "route_split_emit_kernel")}
 
 
 def _counter_rows(run_dir: str, counter: str):
@@ -291,7 +292,7 @@ def write_traffic(fetch_dir: str, write_dir: str, kernel: str, workload: str, pr
         if not copies:
             raise SystemExit(f"{counter}: no copy kernel found in {d}")
         factor = probe / (max(copies) * 1024.0)
-        vals = [v * 1024.0 * factor for _, n, v in rows if sym in n][-steps:]
+        vals = [v * 1024.0 * factor for _, n, v in rows if any(x in n for x in sym)][-steps:]
         if len(vals) < steps:
             raise SystemExit(f"{counter}: {len(vals)} launches of {sym} in {d}, expected {steps}")
         per[counter] = {"factor": round(factor, 4), "bytes_per_launch": sum(vals) / len(vals),
