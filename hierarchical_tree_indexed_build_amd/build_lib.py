@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libzha.so")
-SOURCES = ["zha_abi.hip", "build.hip", "route.hip", "attend.hip"]
+SOURCES = ["zha_abi.hip", "build.hip", "route.hip", "route_dense.hip", "attend.hip"]
 ARCH = os.environ.get("ZHA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -41,14 +41,6 @@
 
 namespace zha {
 
-__device__ __forceinline__ int clamp_visible(const RowInfo& ri, int row, int64_t cap) {
-    const int s = row / ri.T;
-    int n = row_visible(ri, row);
-    const int lim = static_cast<int>(imin(ri.seq_lens[s], cap));
-    n = n < 0 ? 0 : n;
-    return n > lim ? lim : n;
-}
-
 // ----------------------------------------------------------------------------
 // scoring
 // ----------------------------------------------------------------------------
@@ -1524,6 +1516,46 @@ static int upper_from(const Geo& g) {
     return lo;
 }
 
+// One workgroup per (row, query head) cuts level li from the dense-by-node
+// scores.
+static hipError_t launch_cut(const Geo& g, const RouteArgs& a, int li, hipStream_t st) {
+    const WsLayout& lay = *a.lay;
+    char* ws = a.ws;
+    const bool top = (li == g.L - 1);
+    CutParams cp{};
+    cp.ri = a.ri;
+    cp.scores = reinterpret_cast<float*>(ws + lay.scores);
+    cp.nodes_total = g.nodes_total;
+    cp.lvl_off = g.sel_off[li];
+    cp.lvl_off_up = top ? 0 : g.sel_off[li + 1];
+    cp.kept = reinterpret_cast<int32_t*>(ws + lay.kept);
+    cp.kept_cnt = reinterpret_cast<int32_t*>(ws + lay.kept_cnt);
+    cp.bitmap = reinterpret_cast<uint32_t*>(ws + lay.bitmap);
+    cp.bm_words_total = lay.bm_words_total;
+    cp.bm_off = static_cast<int64_t>(lay.bm_off[li]);
+    cp.sel_blocks = a.sel_blocks;
+    cp.n_sel = a.n_sel;
+    cp.sel_cap = a.sel_cap;
+    cp.level_stats = a.level_stats;
+    cp.level_sel = a.level_sel;
+    cp.lsel_off = static_cast<int64_t>(a.rows) * g.Hq * g.sel_off[li];
+    cp.nodes_l = g.nodes[li];
+    cp.status = reinterpret_cast<uint32_t*>(ws + lay.status);
+    cp.cap = g.cap;
+    cp.b = g.b;
+    cp.lb = g.lb;
+    cp.li = li;
+    cp.L = g.L;
+    cp.Hq = g.Hq;
+    cp.T = a.ri.T;
+    cp.top_p = a.top_p;
+    {
+        ProfScope ps("route_cut", li + 1, st);
+        hipLaunchKernelGGL(route_cut_kernel, dim3(g.Hq, a.rows), dim3(kCutThreads), 0, st, cp);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
     const WsLayout& lay = *a.lay;
     char* ws = a.ws;
@@ -1533,6 +1565,15 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(ws + lay.bitmap);
     uint32_t* status = reinterpret_cast<uint32_t*>(ws + lay.status);
     const int pairs = a.rows * g.Hkv;
+
+    // many rows per sequence: every level's scores on the matrix cores at
+    // once, then the levels' cuts from the top
+    if (a.ri.T >= kDenseMinRows && dense_scores_fit(g, a.ri.T)) {
+        hipError_t e = launch_dense_scores(g, a.ri, a.q, a.summaries, scores, 0, g.L - 1, st);
+        for (int li = g.L - 1; e == hipSuccess && li >= 0; --li) e = launch_cut(g, a, li, st);
+        return e;
+    }
+
     const int li_lo = upper_from(g);
 
     if (li_lo < g.L) {
@@ -1670,38 +1711,7 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
             continue;
         }
 
-        CutParams cp{};
-        cp.ri = a.ri;
-        cp.scores = scores;
-        cp.nodes_total = g.nodes_total;
-        cp.lvl_off = g.sel_off[li];
-        cp.lvl_off_up = top ? 0 : g.sel_off[li + 1];
-        cp.kept = kept;
-        cp.kept_cnt = kept_cnt;
-        cp.bitmap = bitmap;
-        cp.bm_words_total = lay.bm_words_total;
-        cp.bm_off = static_cast<int64_t>(lay.bm_off[li]);
-        cp.sel_blocks = a.sel_blocks;
-        cp.n_sel = a.n_sel;
-        cp.sel_cap = a.sel_cap;
-        cp.level_stats = a.level_stats;
-        cp.level_sel = a.level_sel;
-        cp.lsel_off = static_cast<int64_t>(a.rows) * g.Hq * g.sel_off[li];
-        cp.nodes_l = g.nodes[li];
-        cp.status = status;
-        cp.cap = g.cap;
-        cp.b = g.b;
-        cp.lb = g.lb;
-        cp.li = li;
-        cp.L = g.L;
-        cp.Hq = g.Hq;
-        cp.T = a.ri.T;
-        cp.top_p = a.top_p;
-        {
-            ProfScope ps("route_cut", li + 1, st);
-            hipLaunchKernelGGL(route_cut_kernel, dim3(g.Hq, a.rows), dim3(kCutThreads), 0, st, cp);
-        }
-        e = hipGetLastError();
+        e = launch_cut(g, a, li, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

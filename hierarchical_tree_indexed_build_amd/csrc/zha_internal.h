@@ -88,6 +88,15 @@ __host__ __device__ inline int row_visible(const RowInfo& ri, int row) {
     return pos + 1;
 }
 
+// Tokens a row sees, clamped to its sequence's length and the capacity.
+__device__ __forceinline__ int clamp_visible(const RowInfo& ri, int row, int64_t cap) {
+    const int s = row / ri.T;
+    const int n = row_visible(ri, row);
+    const int64_t len = ri.seq_lens[s];
+    const int lim = static_cast<int>(len < cap ? len : cap);
+    return n < 0 ? 0 : (n > lim ? lim : n);
+}
+
 // Opt-in kernel timing (zha_profile_start): brackets a launch with two events
 // when `label` (optionally "label@level") matches the active target.
 class ProfScope {
@@ -127,6 +136,13 @@ struct RouteArgs {
     const WsLayout* lay;
 };
 hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st);
+
+// Rows per sequence from which every level is scored densely on the matrix
+// cores (route_dense.hip) instead of by gathering the kept parents' children.
+constexpr int kDenseMinRows = 64;
+bool dense_scores_fit(const Geo& g, int T);
+hipError_t launch_dense_scores(const Geo& g, const RowInfo& ri, const float* q, const float* summaries,
+                               float* scores, int li_lo, int li_hi, hipStream_t st);
 
 struct AttendArgs {
     const float* q;

@@ -1,0 +1,112 @@
+"""Chunked causal prefill on the GPU against the oracle.
+
+A chunk of new tokens is appended to a built cache (the tree grows by every
+node the chunk completes), then every row of the chunk is routed and attended
+at once, each row seeing the tokens up to its own position. With this many
+rows per sequence every level's node scores come from one contraction per
+(sequence, kv head) on the fp32 matrix cores; the cuts read them per
+(row, head).
+
+Checks, on sampled rows (every head): each level's kept set against the
+oracle's cut of the same candidates (teacher forcing, margin exemptions as in
+the decode tests), the candidate counts, and the attention output over the
+GPU's own index set within the bf16 tolerance.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import hierarchical_tree_indexed_build_amd as Z
+import workloads as W
+from oracle import zha_oracle as O
+from tests.gpu_helpers import Staged, attn_tol, check_sets, kv_tensor, say, torch
+
+pytestmark = pytest.mark.gpu
+
+# (workload, shrink, chunk): shrink 1 is a 16384-token cache + 512-row chunk
+# (16 row tiles per kv head, 9 node tiles at level 1, the last one ragged);
+# shrink 2 with 200 rows has a ragged row tile; shrink 0 is the full
+# 262144-token cache + 8192-row chunk.
+PREFILL = [("prefill256k", 2, 200), ("prefill256k", 1, None), ("prefill256k", 0, None)]
+
+
+def _sample_rows(T, k):
+    rows = set(range(0, T, max(1, T // k)))
+    rows.update({0, 1, T // 2, T - 2, T - 1})
+    return sorted(r for r in rows if 0 <= r < T)
+
+
+def _run_prefill(w, sel_cap):
+    t = torch()
+    n0, T = w.n_tokens, w.prefill_chunk
+    st = Staged(w, max_t=T)
+    kn, vn = W.prefill_chunk_kv(w)
+    Z.append(st.geom, st.cache.K, st.cache.V, kv_tensor(w, kn), kv_tensor(w, vn), st.cache.seq_lens, st.ref_q,
+             st.cache.summaries, st.cache.ws)
+    qn, q = st.queries(0, rows=T)
+    q_pos = (n0 + t.arange(T, dtype=t.int32, device="cuda")).view(1, T).repeat(w.batch, 1).contiguous()
+    sizes = Z.query_sizes(st.geom, T)
+    sel = t.full((w.batch, T, w.n_q_heads, sel_cap), -1, dtype=t.int32, device="cuda")
+    nsel = t.zeros((w.batch, T, w.n_q_heads), dtype=t.int32, device="cuda")
+    stats = t.zeros((w.batch, T, w.n_q_heads, w.n_levels, 2), dtype=t.int32, device="cuda")
+    lsel = t.full((sizes.level_sel_bytes // 4,), -1, dtype=t.int32, device="cuda")
+    out = t.zeros_like(q)
+    lse = t.zeros(q.shape[:3], dtype=t.float32, device="cuda")
+    Z.attend(st.geom, q, q_pos, st.cache.K, st.cache.V, st.cache.summaries, st.cache.seq_lens, w.top_p, sel, nsel,
+             out, lse, st.cache.ws, level_stats=stats, level_sel=lsel)
+    t.cuda.synchronize()
+    assert int(st.cache.seq_lens[0].item()) == n0 + T
+    Kf = np.concatenate([st.Kf[:, :, :n0], W.as_f32(w, kn)], axis=2)
+    Vf = np.concatenate([st.Vf[:, :, :n0], W.as_f32(w, vn)], axis=2)
+    return st, qn, q_pos, sel, nsel, stats, lsel, out, lse, Kf, Vf
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=[f"{n}-s{s}" + (f"-c{c}" if c else "") for n, s, c in PREFILL])
+def test_prefill_chunk_parity(case):
+    name, shrink, chunk = case
+    w = W.get_workload(name, shrink=shrink, chunk=chunk)
+    T = w.prefill_chunk
+    say(f"[prefill] {w.name}: {w.n_tokens} cached tokens + {T}-row causal chunk, L={w.n_levels}")
+    full = shrink == 0
+    sel_cap = 4096 if full else None
+    st, qn, q_pos, sel, nsel, stats, lsel, out, lse, Kf, Vf = _run_prefill(
+        w, sel_cap if sel_cap else (w.capacity // w.branching))
+    assert Z.read_device_status(st.cache.ws, clear=True) & ~Z.ZHA_DEV_SEL_OVERFLOW == 0
+    rows = _sample_rows(T, 12 if full else 48)
+    say(f"  checking rows {rows[:6]}... ({len(rows)} rows x {w.n_q_heads} heads)")
+    trees = O.build_all(Kf, st.R, [w.n_tokens + T] * w.batch, w.branching)
+    g = st.geom
+    ridx = torch().tensor(rows, dtype=torch().int64, device="cuda")
+    # per level: kept ids of the sampled rows only (the full buffers are large)
+    kept = {}
+    for level in range(1, w.n_levels + 1):
+        v = Z.level_sel_view(lsel, st.sizes, g, w.batch * T, level)
+        kept[level] = v.view(w.batch, T, w.n_q_heads, -1).index_select(1, ridx).cpu().numpy()
+    st_np = stats.index_select(1, ridx).cpu().numpy()
+    o_np = out.index_select(1, ridx).cpu().numpy()
+    l_np = lse.index_select(1, ridx).cpu().numpy()
+    tol = attn_tol(w)
+    flips = 0
+    worst = 0.0
+    for s in range(w.batch):
+        for i, t_ in enumerate(rows):
+            N = w.n_tokens + t_ + 1
+            for hq in range(w.n_q_heads):
+                kv = hq // w.group
+                parents = None
+                for level in range(w.n_levels, 0, -1):
+                    cand, cnt = st_np[s, i, hq, level - 1]
+                    gpu_ids = kept[level][s, i, hq, :cnt]
+                    cut = O.route_level(qn[s, t_, hq], trees[s][kv][level - 1], level, parents, N, w.branching,
+                                        w.n_levels, w.top_p, w.scale)
+                    assert cand == len(cut.ids), (s, t_, hq, level, cand, len(cut.ids))
+                    assert np.all(np.diff(gpu_ids) > 0), "kept ids must be ascending"
+                    flips += check_sets(gpu_ids, cut, w.top_p, f"row {t_} head {hq} level {level}")
+                    parents = gpu_ids
+                I = O.index_set(parents, N, w.branching)
+                o, l = O.attend(qn[s, t_, hq], Kf[s, kv], Vf[s, kv], I, w.scale)
+                e = max(np.abs(o_np[s, i, hq] - o).max(), abs(l_np[s, i, hq] - l))
+                worst = max(worst, e)
+                assert e <= tol, (s, t_, hq, e)
+    say(f"  margin-exempt differences: {flips}; worst |gpu - oracle| attention {worst:.3g} (tol {tol})")
