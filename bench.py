@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="decode1m", choices=["decode1m", "gqa128k", "decode16m"])
+    ap.add_argument("--workload", default="decode1m", choices=["decode1m", "gqa128k", "decode16m", "prefill256k"])
     ap.add_argument("--kernel", default="attend", help="kernel label timed live for the roofline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="copy a buffer of this many MiB once before the timed steps (calibrates byte counters)")
@@ -312,6 +312,163 @@ def write_traffic(fetch_dir: str, write_dir: str, kernel: str, workload: str, pr
 
 
 # ----------------------------------------------------------------------------
+# chunked prefill: append a causal chunk, then route and attend all its rows
+# ----------------------------------------------------------------------------
+FP32_MFMA_PEAK = 157.3e12   # MI355X dense fp32 matrix FLOP/s
+PREFILL_METRIC = "ZHA chunked-prefill rows/sec at 256K-token KV (8192-row causal chunk)"
+
+
+def prefill_main(args, w):
+    """One step = seq_lens reset to the cache length, zha_append of the chunk
+    (summarising every node it completes), zha_attend of its T causal rows.
+    Re-appending the same chunk at the same place rewrites identical bits, so
+    every step does the same work."""
+    import torch
+    steps = args.steps if args.steps is not None else 5
+    warm = min(args.warmup, 2)
+    T, n0 = w.prefill_chunk, w.n_tokens
+    log(f"[bench] workload {w.name}: {w.description}; steps {steps}, warmup {warm}")
+    geom = Z.make_geom(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.branching, w.n_levels, w.capacity,
+                       w.kv_dtype)
+    c = Z.Cache(geom, T)
+    kdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    K_host, V_host = W.kv_cache(w)
+    c.K.copy_(torch.from_numpy(K_host).view(kdt))
+    c.V.copy_(torch.from_numpy(V_host).view(kdt))
+    kn, vn = W.prefill_chunk_kv(w)
+    k_new = torch.from_numpy(kn).view(kdt).cuda()
+    v_new = torch.from_numpy(vn).view(kdt).cuda()
+    ref_q = torch.from_numpy(W.ref_queries(w)).cuda()
+    q_host = W.queries(w, 0, rows=T)
+    q = torch.from_numpy(q_host).cuda()
+    q_pos = (n0 + torch.arange(T, dtype=torch.int32, device="cuda")).view(1, T).repeat(w.batch, 1).contiguous()
+    lens0 = torch.full((w.batch,), n0, dtype=torch.int32, device="cuda")
+    c.seq_lens.copy_(lens0)
+    Z.build_tree(geom, c.K, ref_q, c.seq_lens, c.summaries, c.ws)
+    sel_cap = 4096
+    sel = torch.zeros((w.batch, T, w.n_q_heads, sel_cap), dtype=torch.int32, device="cuda")
+    nsel = torch.zeros((w.batch, T, w.n_q_heads), dtype=torch.int32, device="cuda")
+    out = torch.zeros((w.batch, T, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((w.batch, T, w.n_q_heads), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(level_stats=None):
+        c.seq_lens.copy_(lens0)
+        Z.append(geom, c.K, c.V, k_new, v_new, c.seq_lens, ref_q, c.summaries, c.ws)
+        Z.attend(geom, q, q_pos, c.K, c.V, c.summaries, c.seq_lens, w.top_p, sel, nsel, out, lse, c.ws,
+                 level_stats=level_stats)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    if Z.read_device_status(c.ws, clear=True) & ~Z.ZHA_DEV_SEL_OVERFLOW:
+        raise RuntimeError("device status raised during warmup")
+    kernel = "route_dense" if args.kernel == "attend" else args.kernel
+    Z.profile_start(kernel)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms, k_launch, _ = Z.profile_collect()
+    Z.profile_start(None)
+    if args.timed_only:
+        print(json.dumps({"workload": w.name, "steps": steps, "warmup": warm, "ms_per_step": wall * 1e3 / steps,
+                          "kernel": kernel, "kernel_avg_us": k_ms / max(1, k_launch) * 1e3,
+                          "launches": k_launch}), flush=True)
+        return
+    # per-step time of each kernel family, one family per pass
+    fam_ms = {}
+    for fam in ("append_rows", "build_level", "advance_seq", "route_dense", "route_cut", "attn_items", "attn_plan",
+                "attend", "attend_combine"):
+        Z.profile_start(fam)
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        ms, _, _ = Z.profile_collect()
+        fam_ms[fam] = round(ms / 2, 4)
+    Z.profile_start(None)
+    stats = torch.zeros((w.batch, T, w.n_q_heads, w.n_levels, 2), dtype=torch.int32, device="cuda")
+    step(level_stats=stats)
+    torch.cuda.synchronize()
+    st = stats.cpu().numpy()
+
+    # algorithmic work of the dense scores: every node each row sees, for each of its heads
+    d, g, bb = w.head_dim, w.group, w.branching
+    Nv = n0 + 1 + np.arange(T, dtype=np.int64)
+    seen = sum(int((Nv // bb ** l).sum()) for l in range(1, w.n_levels + 1))
+    flops = 2.0 * d * seen * w.batch * w.n_q_heads
+    k_avg_s = (k_ms / 1e3) / max(1, k_launch)
+    achieved = flops / k_avg_s if (kernel == "route_dense" and k_avg_s > 0) else 0.0
+
+    cpu = None
+    if not args.no_cpu:
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f}s")
+        cpu = prefill_cpu_baseline(w, c, q_host, K_host, V_host, kn, vn, args.cpu_seconds)
+    ms_step = wall * 1e3 / steps
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": round(w.batch * T * steps / wall, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_tokens": n0, "chunk": T, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": d, "branching": bb, "levels": w.n_levels,
+                   "top_p": w.top_p, "kv_cache": w.kv_dtype},
+        "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": FP32_MFMA_PEAK / 1e12,
+                     "unit": "TFLOP/s", "frac": round(achieved / FP32_MFMA_PEAK, 4), "traffic": None,
+                     "kernel": kernel, "flops_per_launch": flops, "avg_launch_us": round(k_avg_s * 1e6, 3),
+                     "launches": k_launch},
+        "cpu_baseline": cpu,
+        "ms_by_kernel_family": fam_ms,
+        "candidates_per_row_head": [round(float(st[..., l, 0].mean()), 1) for l in range(w.n_levels)],
+        "kept_per_row_head": [round(float(st[..., l, 1].mean()), 2) for l in range(w.n_levels)],
+    }
+    print(json.dumps(res), flush=True)
+
+
+def prefill_cpu_baseline(w, c, q_host, K_host, V_host, kn, vn, budget_s):
+    """The oracle routes and attends the chunk's rows in order (every head),
+    against the GPU-built tree copied to the host, until the budget is spent."""
+    from threadpoolctl import threadpool_limits
+    from oracle import zha_oracle as O
+    T, n0 = w.prefill_chunk, w.n_tokens
+    N = n0 + T
+    summ = c.summaries.cpu().numpy()
+    sizes = c.sizes
+    trees = [[[summ[sizes.level_offset[l - 1] + (s * w.n_kv_heads + h) * sizes.level_nodes[l - 1] * w.head_dim:]
+               [:(N // w.branching ** l) * w.head_dim].reshape(-1, w.head_dim)
+               for l in range(1, w.n_levels + 1)] for h in range(w.n_kv_heads)] for s in range(w.batch)]
+    Kf = np.concatenate([W.as_f32(w, K_host[:, :, :n0]), W.as_f32(w, kn)], axis=2)
+    Vf = np.concatenate([W.as_f32(w, V_host[:, :, :n0]), W.as_f32(w, vn)], axis=2)
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < budget_s and done < T:
+            n = n0 + done + 1
+            for s in range(w.batch):
+                for hq in range(w.n_q_heads):
+                    kv = hq // w.group
+                    r = O.route(q_host[s, done, hq], trees[s][kv], n, w.branching, w.top_p)
+                    I = O.index_set(r.selected[0], n, w.branching)
+                    O.attend(q_host[s, done, hq], Kf[s, kv], Vf[s, kv], I)
+            done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(done * w.batch / el, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"the chunk's first {done} rows x {w.batch} sequence(s) x {w.n_q_heads} heads (route + "
+                      f"exact attention per head, NumPy fp64, one BLAS thread) against the GPU-built tree, "
+                      f"{el:.1f}s"}
+
+
+# ----------------------------------------------------------------------------
 def main():
     args = parse()
     if args.gpus != 1:
@@ -325,6 +482,9 @@ def main():
         return
     import torch
     w = W.get_workload(args.workload)
+    if w.prefill_chunk:
+        prefill_main(args, w)
+        return
     steps = args.steps if args.steps is not None else w.steps
     warm = args.warmup
     log(f"[bench] workload {w.name}: {w.description}; steps {steps}, warmup {warm}")

@@ -13,15 +13,16 @@
 //    add chunk 0 (sink) and the current chunk, and compact them into one
 //    ascending list of (chunk, head mask) items; K/V of a chunk are then read
 //    once for the whole GQA group.
-//  * attend_kernel      - split-K flash decoding. Workgroup = (split, row, kv
-//    head); each wave streams 16-token groups of its split through a two-stage
+//  * attend_kernel      - split-K flash decoding. Workgroup = one share of a
+//    (row, kv head) pair's groups; each wave streams 16-token groups of it through a two-stage
 //    register pipeline with an online softmax for all g heads; lanes own a
 //    slice of d; waves merge in LDS and write one (max, sum, acc[d]) partial
 //    per head and split.
 //  * attend_combine_kernel - per (row, head): LSE merge of the splits.
-// The attention's work plan is the prefix of the groups over the (row, kv
-// head) pairs: attn_plan_kernel writes it for more than 64 pairs; with fewer,
-// the attention and combine kernels take it from the pairs' counts themselves.
+// The attention's work plan is the prefix of the groups and of the workgroup
+// shares over the (row, kv head) pairs: attn_plan_kernel writes it for more
+// than 64 pairs; with fewer, the attention and combine kernels take it from
+// the pairs' counts themselves.
 #include <algorithm>
 
 #include "zha_device.h"
@@ -168,14 +169,14 @@ __global__ __launch_bounds__(kItemsThreads) void attn_items_kernel(ItemsParams p
 // ----------------------------------------------------------------------------
 // split-K attention, balanced over the whole chip
 // Work unit: a group of kGroupTokens tokens of one item (chunk) of one (row,
-// kv head) pair. attn_plan_kernel takes the exclusive prefix of the groups
-// over the pairs; attend_kernel then gives each of its nwg workgroups an equal
-// slice of that global range, whatever pairs it spans: a heavy pair is spread
-// over many workgroups and light pairs share one. A workgroup writes one
-// partial state per pair segment of its slice, at slot (workgroup + pair),
-// which is unique because consecutive segments belong to consecutive pairs.
-// Scores are kept in log2 units (q is pre-scaled by scale * log2(e)), so
-// every exponential is one native exp2.
+// kv head) pair. Each pair's groups are cut into shares of the same size
+// (attn_chunk), one workgroup per share: a heavy pair is spread over many
+// workgroups, and no workgroup spans two pairs, so each one loads a single
+// q, starts a single pipeline and writes a single partial state, at slot
+// = its workgroup index. attn_plan_kernel writes the prefixes of the groups
+// and of the shares over the pairs (or the kernels build them, for at most
+// 64 pairs). Scores are kept in log2 units (q is pre-scaled by
+// scale * log2(e)), so every exponential is one native exp2.
 // ----------------------------------------------------------------------------
 constexpr int kGroupTokens = 16;          // tokens a wave handles per pipeline stage
 
@@ -191,16 +192,24 @@ struct AttnParams {
     const int2* items;         // [pairs, item_stride] (sparse)
     const int32_t* acnt;       // [pairs] items per pair (sparse)
     int64_t item_stride;
-    int64_t* plan;             // [pairs + 1] exclusive prefix of groups per pair
-    float* partial;            // [nwg + pairs, G, D + 4]: max, sum, 2 pad, acc[D]
+    int64_t* plan;             // [2 (pairs + 1)] exclusive prefixes of groups, then of workgroup shares, per pair
+    float* partial;            // [nwg + pairs, G, D + 4] by workgroup: max, sum, 2 pad, acc[D]
     int64_t cap;
     int b, lb, lgpi, Hq, Hkv, pairs, nwg, dense;
     int wave_plan;             // pairs <= 64: kernels take the plan from the counts themselves
     float qscale;              // scale * log2(e)
 };
 
-__device__ __forceinline__ int64_t attn_chunk(int64_t total, int nwg) {
-    const int64_t c = (total + nwg - 1) / nwg;
+// Each (row, kv head) pair's groups are cut into workgroup shares of `chunk`
+// groups (a pair's last share may be shorter), so no workgroup spans two
+// pairs: one q load, one online-softmax state and one partial per workgroup.
+// With fewer pairs than workgroups, chunk is large enough that every pair's
+// shares fit in nwg workgroups together: sum ceil(n / chunk) <= total / chunk
+// + pairs <= nwg.
+__device__ __forceinline__ int64_t attn_chunk(int64_t total, int nwg, int pairs) {
+    const int64_t avail = static_cast<int64_t>(nwg) - pairs;
+    const int64_t d = avail > 0 ? avail : nwg;
+    const int64_t c = (total + d - 1) / d;
     return c < kMinChunk ? kMinChunk : c;
 }
 
@@ -239,50 +248,84 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnParams p) {
         __syncthreads();
     }
     if (tid == 0) p.plan[p.pairs] = carry;
+    // second pass: the prefix of the pairs' workgroup shares
+    const int64_t chunk = attn_chunk(carry, p.nwg, p.pairs);
+    int64_t* wplan = p.plan + p.pairs + 1;
+    carry = 0;
+    for (int base = 0; base < p.pairs; base += nt) {
+        const int pr = base + tid;
+        const int64_t v = pr < p.pairs ? (pair_groups(p, pr) + chunk - 1) / chunk : 0;
+        const uint64_t inc = wave_scan_u64(static_cast<uint64_t>(v));
+        if (lane == 63) red[w] = static_cast<int64_t>(inc);
+        __syncthreads();
+        int64_t before = 0, total = 0;
+        for (int i = 0; i < nt / kWave; ++i) {
+            if (i < w) before += red[i];
+            total += red[i];
+        }
+        if (pr < p.pairs) wplan[pr] = carry + before + static_cast<int64_t>(inc) - v;
+        carry += total;
+        __syncthreads();
+    }
+    if (tid == 0) wplan[p.pairs] = carry;
 }
 
-// The group prefix over the pairs, as the attention and combine kernels see
-// it. With at most 64 pairs every wave builds it itself: lane pr loads pair
-// pr's group count and one wave scan gives plan[pr + 1] on lane pr, read back
-// with readlane (pr is uniform). Otherwise it is the plan kernel's output.
+// The work plan as the attention and combine kernels see it: the prefix of
+// the groups over the pairs, and the prefix of their workgroup shares. With at
+// most 64 pairs every wave builds both itself: lane pr loads pair pr's group
+// count and wave scans give the prefixes on lane pr, read back with readlane
+// (pr is uniform). Otherwise they are the plan kernel's output.
 struct PlanView {
-    const int64_t* plan;
-    uint64_t incl;             // wave plan: inclusive prefix on lane pr
+    const int64_t* plan;       // [pairs + 1] group prefix, then [pairs + 1] workgroup prefix
+    uint64_t incl;             // wave plan: inclusive group prefix on lane pr
+    uint64_t wincl;            // wave plan: inclusive workgroup prefix on lane pr
+    int64_t chunk;             // groups per workgroup share
     int pairs;
     bool wave;
-    __device__ __forceinline__ PlanView(const AttnParams& p) : plan(p.plan), incl(0), pairs(p.pairs), wave(p.wave_plan != 0) {
+    __device__ __forceinline__ PlanView(const AttnParams& p)
+        : plan(p.plan), incl(0), wincl(0), chunk(0), pairs(p.pairs), wave(p.wave_plan != 0) {
         if (wave) {
             const int lane = threadIdx.x & (kWave - 1);
-            incl = wave_scan_u64(lane < pairs ? static_cast<uint64_t>(pair_groups(p, lane)) : 0ull);
+            const int64_t n = lane < pairs ? pair_groups(p, lane) : 0;
+            incl = wave_scan_u64(static_cast<uint64_t>(n));
+            chunk = attn_chunk(at(pairs), p.nwg, pairs);
+            wincl = wave_scan_u64(static_cast<uint64_t>((n + chunk - 1) / chunk));
+        } else {
+            chunk = attn_chunk(plan[pairs], p.nwg, pairs);
         }
     }
-    __device__ __forceinline__ int64_t at(int pr) const {     // plan[pr], 0 <= pr <= pairs
-        if (!wave) return plan[pr];
-        if (pr == 0) return 0;
-        const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(incl)), pr - 1));
-        const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(incl >> 32)), pr - 1));
+    static __device__ __forceinline__ int64_t lane_read(uint64_t v, int l) {
+        const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l));
+        const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), l));
         return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
     }
+    __device__ __forceinline__ int64_t at(int pr) const {     // first group of pair pr, 0 <= pr <= pairs
+        if (!wave) return plan[pr];
+        return pr == 0 ? 0 : lane_read(incl, pr - 1);
+    }
+    __device__ __forceinline__ int64_t wat(int pr) const {    // first workgroup of pair pr, 0 <= pr <= pairs
+        if (!wave) return plan[pairs + 1 + pr];
+        return pr == 0 ? 0 : lane_read(wincl, pr - 1);
+    }
     __device__ __forceinline__ int64_t total() const { return at(pairs); }
-    // the last pair whose first group is at or before r (plan[pr] <= r)
-    __device__ __forceinline__ int first_pair(int64_t r) const {
+    // the pair whose shares include workgroup w, or -1 past the last share
+    __device__ __forceinline__ int pair_of_wg(int64_t w) const {
+        if (w >= wat(pairs)) return -1;
         if (wave) {
             const int lane = threadIdx.x & (kWave - 1);
-            const int64_t excl = at_lane_excl();
-            const unsigned long long bal = __ballot(lane < pairs && excl <= r);
-            return __popcll(bal) - 1;                       // plan is nondecreasing: a prefix of lanes
+            const uint64_t prev = __shfl_up(wincl, 1);
+            const int64_t excl = lane == 0 ? 0 : static_cast<int64_t>(prev);
+            const unsigned long long bal = __ballot(lane < pairs && excl <= w);
+            return __popcll(bal) - 1;                       // a prefix of lanes; the last one owns w
         }
+        const int64_t* wp = plan + pairs + 1;
         int lo = 0, hi = pairs - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (plan[mid] <= r) lo = mid;
+            if (wp[mid] <= w) lo = mid;
             else hi = mid - 1;
         }
         return lo;
-    }
-    __device__ __forceinline__ int64_t at_lane_excl() const {  // plan[lane] on each lane (wave plan)
-        const uint64_t prev = __shfl_up(incl, 1);
-        return (threadIdx.x & (kWave - 1)) == 0 ? 0 : static_cast<int64_t>(prev);
     }
 };
 
@@ -342,20 +385,14 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int part = lane % LPT, tsub = lane / LPT;
     const PlanView pv(p);
-    const int64_t total = pv.total();
-    const int64_t chunk = attn_chunk(total, p.nwg);
-    const int64_t r0 = static_cast<int64_t>(wg) * chunk;
-    if (r0 >= total) return;
-    const int64_t r1 = imin(r0 + chunk, total);
-    const int lo = pv.first_pair(r0);          // first pair of the slice
+    const int pr = pv.pair_of_wg(wg);           // the one pair this workgroup works on
+    if (pr < 0) return;
     const int gpi = 1 << p.lgpi;
     const int tg = p.b >= kGroupTokens ? kGroupTokens : p.b;
 
-    for (int pr = lo; pr < p.pairs; ++pr) {
-        const int64_t pg0 = pv.at(pr);
-        if (pg0 >= r1) break;
-        const int64_t ga = imax(r0, pg0) - pg0, gb = imin(r1, pv.at(pr + 1)) - pg0;   // this pair's groups here
-        if (ga >= gb) continue;                                  // a pair with no groups
+    {
+        // this workgroup's share of the pair's groups
+        const int64_t ga = (wg - pv.wat(pr)) * pv.chunk, gb = imin(ga + pv.chunk, pv.at(pr + 1) - pv.at(pr));
         const int row = pr / p.Hkv, kv = pr % p.Hkv;
         const int s = row / p.ri.T;
         const int N = visible_clamped(p.ri, row, p.cap);
@@ -508,7 +545,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
             }
         }
         __syncthreads();
-        float* pout = p.partial + static_cast<int64_t>(wg + pr) * G * (D + 4);
+        float* pout = p.partial + static_cast<int64_t>(wg) * G * (D + 4);
         for (int idx = threadIdx.x; idx < G * (D + 4); idx += blockDim.x) {
             const int h = idx / (D + 4), c = idx % (D + 4);
             float M = -INFINITY;
@@ -526,7 +563,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
             }
             pout[idx] = out;
         }
-        __syncthreads();                                         // sm_* are reused by the next segment
     }
 }
 
@@ -568,34 +604,29 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
     const int part = lane % LPT, tsub = lane / LPT;       // value-pass layout
     const int mrow = lane & 15, mblk = lane >> 4;          // MFMA layout: token/head, dim block
     const PlanView pv(p);
-    const int64_t total = pv.total();
-    const int64_t chunk = attn_chunk(total, p.nwg);
-    const int64_t r0 = static_cast<int64_t>(wg) * chunk;
-    if (r0 >= total) return;
-    const int64_t r1 = imin(r0 + chunk, total);
-    const int lo = pv.first_pair(r0);          // first pair of the slice
+    const int pr = pv.pair_of_wg(wg);           // the one pair this workgroup works on
+    if (pr < 0) return;
     const int gpi = 1 << p.lgpi;
     const int tg = p.b >= kGroupTokens ? kGroupTokens : p.b;
 
-    for (int pr = lo; pr < p.pairs; ++pr) {
-        const int64_t pg0 = pv.at(pr);
-        if (pg0 >= r1) break;
-        const int64_t ga = imax(r0, pg0) - pg0, gb = imin(r1, pv.at(pr + 1)) - pg0;   // this pair's groups here
-        if (ga >= gb) continue;                                  // a pair with no groups
+    {
+        // this workgroup's share of the pair's groups
+        const int64_t ga = (wg - pv.wat(pr)) * pv.chunk, gb = imin(ga + pv.chunk, pv.at(pr + 1) - pv.at(pr));
         const int row = pr / p.Hkv, kv = pr % p.Hkv;
         const int s = row / p.ri.T;
         const int N = visible_clamped(p.ri, row, p.cap);
 
-        // q of head mrow (zero beyond g), scaled, as bf16 hi + lo over this lane's dims
+        // q of head mrow (zero beyond g): its load is issued here, its split into
+        // scaled bf16 hi + lo parts waits until the first K/V rows are in flight
         bf16x8_t qh[NS], ql[NS];
-        {
-            float qf[D / 4];
-            if (mrow < G) {
-                load_vec<D / 4>(p.q + (static_cast<int64_t>(row) * p.Hq + kv * G + mrow) * D + mblk * (D / 4), qf);
-            } else {
+        float qf[D / 4];
+        if (mrow < G) {
+            load_vec<D / 4>(p.q + (static_cast<int64_t>(row) * p.Hq + kv * G + mrow) * D + mblk * (D / 4), qf);
+        } else {
 #pragma unroll
-                for (int e = 0; e < D / 4; ++e) qf[e] = 0.f;
-            }
+            for (int e = 0; e < D / 4; ++e) qf[e] = 0.f;
+        }
+        auto split_q = [&]() {
 #pragma unroll
             for (int sl = 0; sl < NS; ++sl)
 #pragma unroll
@@ -607,7 +638,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
                     qh[sl][j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hb));
                     ql[sl][j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lb));
                 }
-        }
+        };
         const uint16_t* Kr = static_cast<const uint16_t*>(p.K) + (static_cast<int64_t>(s) * p.Hkv + kv) * p.cap * D + mblk * (D / 4);
         const uint16_t* Vb = static_cast<const uint16_t*>(p.V) + (static_cast<int64_t>(s) * p.Hkv + kv) * p.cap * D + part * DPL;
         const int2* items = p.items + static_cast<int64_t>(pr) * p.item_stride;
@@ -720,6 +751,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
             int2 e0 = item_of(g);                                          // chunk of group g
             int2 e1 = (g + NW < gb) ? item_of(g + NW) : make_int2(0, 0);   // chunk of group g + NW
             issue(first_token(g, e0), kA, vA);
+            split_q();
             for (;;) {
                 int64_t gn = g + NW;
                 int2 e2 = make_int2(0, 0);
@@ -764,7 +796,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
             }
         }
         __syncthreads();
-        float* pout = p.partial + static_cast<int64_t>(wg + pr) * G * (D + 4);
+        float* pout = p.partial + static_cast<int64_t>(wg) * G * (D + 4);
         for (int idx = threadIdx.x; idx < G * (D + 4); idx += blockDim.x) {
             const int h = idx / (D + 4), c = idx % (D + 4);
             float M = -INFINITY;
@@ -782,7 +814,6 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
             }
             pout[idx] = out;
         }
-        __syncthreads();                                         // sm_* are reused by the next segment
     }
 }
 
@@ -810,17 +841,14 @@ __global__ __launch_bounds__(kCombineThreads) void attend_combine_kernel(AttnPar
     const int pr = row * p.Hkv + kv;
     const int tid = threadIdx.x, quad = tid % Q, grp = tid / Q;
     const PlanView pv(p);
-    const int64_t total = pv.total();
-    const int64_t chunk = attn_chunk(total, p.nwg);
-    const int64_t g0 = pv.at(pr), g1 = pv.at(pr + 1);
-    if (g0 >= g1) {                                              // nothing visible
+    const int64_t w0 = pv.wat(pr), w1 = pv.wat(pr + 1);       // the pair's workgroups = its slots
+    if (w0 >= w1) {                                              // nothing visible
         if (tid < D) out[rh * D + tid] = 0.f;
         if (tid == 0 && lse) lse[rh] = -INFINITY;
         return;
     }
-    const int64_t w0 = g0 / chunk, w1 = (g1 - 1) / chunk;
-    const int nslot = static_cast<int>(w1 - w0 + 1);
-    const float* pp = p.partial + ((w0 + pr) * G + h) * (D + 4);   // slot i at pp + i * SS
+    const int nslot = static_cast<int>(w1 - w0);
+    const float* pp = p.partial + (w0 * G + h) * (D + 4);       // slot i at pp + i * SS
     float M = -INFINITY, L = 0.f;
     float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int i0 = grp; i0 < nslot; i0 += NGRP * U) {
@@ -895,9 +923,9 @@ static hipError_t launch_attn_t(const AttnParams& ap, int rows, int Hq, float* o
     {
         ProfScope ps("attend", 0, st);
         if constexpr (sizeof(KT) == 2)       // bf16 cache: scores on the matrix cores
-            hipLaunchKernelGGL((attend_mfma_kernel<D, G>), dim3(ap.nwg), dim3(256), 0, st, ap);
+            hipLaunchKernelGGL((attend_mfma_kernel<D, G>), dim3(ap.nwg + ap.pairs), dim3(256), 0, st, ap);
         else
-            hipLaunchKernelGGL((attend_kernel<KT, D, G>), dim3(ap.nwg), dim3(256), 0, st, ap);
+            hipLaunchKernelGGL((attend_kernel<KT, D, G>), dim3(ap.nwg + ap.pairs), dim3(256), 0, st, ap);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

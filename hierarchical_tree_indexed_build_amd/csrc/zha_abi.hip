@@ -108,7 +108,7 @@ WsLayout layout(const Geo& g, int rows) {
     L.bitmap = take(R * g.Hq * static_cast<size_t>(bw) * 4);
     L.aitems = take(R * g.Hkv * static_cast<size_t>(g.nodes[0] + 2) * 8);
     L.acnt = take(R * g.Hkv * 4);
-    L.plan = take((R * g.Hkv + 1) * 8);
+    L.plan = take(2 * (R * g.Hkv + 1) * 8);
     L.partial = take((static_cast<size_t>(kAttnWorkgroups) + R * g.Hkv) * g.G * (g.D + 4) * 4);
     // the split cut: candidates of a level are at most its node slots
     const int64_t cand = g.nodes[0];

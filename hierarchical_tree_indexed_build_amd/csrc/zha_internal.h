@@ -12,7 +12,7 @@ namespace zha {
 
 constexpr int kWave = 64;
 constexpr int kMaxGroup = 16;          // H_q / H_kv handled by one kernel group
-constexpr int kAttnWorkgroups = 512;   // attention workgroups per launch (partial slots: this + pairs)
+constexpr int kAttnWorkgroups = 512;   // attention workgroups when pairs are few (launch and partial slots: this + pairs)
 constexpr size_t kAlign = 256;
 constexpr int kScoreThreads = 512;     // scoring workgroup: one wave per active parent at a time
 
@@ -57,8 +57,8 @@ struct WsLayout {
     int64_t bm_words_total;
     size_t aitems;        // int2   [rows, Hkv, nodes[0] + 2] attention items (block, head mask)
     size_t acnt;          // int32  [rows, Hkv]
-    size_t plan;          // int64  [rows * Hkv + 1] exclusive prefix of attention groups per (row, kv head)
-    size_t partial;       // float  [kAttnWorkgroups + rows * Hkv, G, D + 4] split-K partial states (max, sum, 2 pad, acc)
+    size_t plan;          // int64  [2, rows * Hkv + 1] exclusive prefixes of attention groups and workgroup shares per (row, kv head)
+    size_t partial;       // float  [kAttnWorkgroups + rows * Hkv, G, D + 4] split-K partial state per workgroup (max, sum, 2 pad, acc)
     // split cut (rows * Hq <= kSplitMaxPairs and every level small enough); absent otherwise
     bool split;
     size_t rank;          // int32  [rows, Hq, nodes_total] a kept node's place in its head's kept list
