@@ -326,6 +326,7 @@ __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, BlockScratch& bs) 
 }
 
 // Sum of a u64 and max of a u32 over the block, in one round of barriers.
+template <int NW = kCutWaves>
 __device__ __forceinline__ void block_sum_max(uint64_t& sum, uint32_t& mx, BlockScratch& bs) {
     const uint64_t s = wave_scan_u64(sum);
     const uint32_t m = wave_scan_max_u32(mx);
@@ -338,7 +339,7 @@ __device__ __forceinline__ void block_sum_max(uint64_t& sum, uint32_t& mx, Block
     uint64_t rs = 0;
     uint32_t rm = 0;
 #pragma unroll
-    for (int i = 0; i < kCutWaves; ++i) {
+    for (int i = 0; i < NW; ++i) {
         rs += bs.red_u64[i];
         rm = max(rm, bs.red_u32[i]);
     }
@@ -446,7 +447,7 @@ __device__ __forceinline__ uint32_t radix_kappa(Entry entry, int64_t cnt, uint64
 // finds the key at which the mass of the keys before it first reaches
 // ceil(top_p * total). Rounds alternate between two histograms, so a round
 // needs two barriers: after the histogram, and after the digit is published.
-template <class ScoreAt>
+template <int NW = kCutWaves, class ScoreAt>
 __device__ __forceinline__ CutBoundary cut_boundary_radix(ScoreAt score, int64_t n, float mx, float top_p,
                                                     BlockScratch& bs) {
     const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
@@ -461,7 +462,7 @@ __device__ __forceinline__ CutBoundary cut_boundary_radix(ScoreAt score, int64_t
         if (F) kmax = max(kmax, desc_key(s));
     }
     for (int i = tid; i < 256; i += nt) bs.hist[0][i] = 0;      // published by the barriers below
-    block_sum_max(E, kmax, bs);
+    block_sum_max<NW>(E, kmax, bs);
     const uint32_t kmin = desc_key(mx);
     uint64_t rem = static_cast<uint64_t>(ceil(static_cast<double>(top_p) * static_cast<double>(E)));
     if (rem == 0) rem = 1;
@@ -473,13 +474,18 @@ __device__ __forceinline__ CutBoundary cut_boundary_radix(ScoreAt score, int64_t
         const int shift = 32 - known - nb;
         const uint32_t hmask = top_bits_mask(known);
         uint64_t* hist = bs.hist[cur];
-        for (int64_t k = tid; k < n; k += nt) {
-            const float s = score(k);
-            const uint32_t key = desc_key(s);
-            if (((key ^ prefix) & hmask) != 0u) continue;
-            const uint64_t F = mass_fx(s, mx);
-            if (F) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[(key >> shift) & ((1u << nb) - 1u)]),
-                             static_cast<unsigned long long>(F));
+        for (int64_t kb = 0; kb < n; kb += nt) {                  // uniform trip count: whole waves update
+            const int64_t k = kb + tid;
+            uint32_t key = 0;
+            uint64_t F = 0;
+            if (k < n) {
+                const float s = score(k);
+                key = desc_key(s);
+                if (((key ^ prefix) & hmask) == 0u) F = mass_fx(s, mx);
+            }
+            // the first rounds put most candidates in one digit: combine them per wave
+            wave_add_u64(reinterpret_cast<unsigned long long*>(hist), static_cast<int>((key >> shift) & ((1u << nb) - 1u)),
+                         F, F != 0);
         }
         for (int i = tid; i < 256; i += nt) bs.hist[cur ^ 1][i] = 0;   // the next round's histogram
         __syncthreads();
@@ -679,12 +685,12 @@ __device__ __forceinline__ int wave_cut_small(ScoreAt score, int n, float top_p,
 // aligned run of (1 << run_lg) <= 32 candidates starting at k that keeps any,
 // bit i set when k + i is kept (a run maps to consecutive node ids inside one
 // bitmap word). Returns the number kept.
-template <class ScoreAt, class Emit, class Mark>
+template <int NW = kCutWaves, class ScoreAt, class Emit, class Mark>
 __device__ __forceinline__ int64_t cut_compact(ScoreAt score, int64_t n, const CutBoundary& cb, int run_lg,
                                                BlockScratch& bs, Emit emit, Mark mark) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t nblk = (n + 63) >> 6;
-    const int64_t per = (nblk + kCutWaves - 1) / kCutWaves;
+    const int64_t per = (nblk + NW - 1) / NW;
     const int64_t b0 = imin(static_cast<int64_t>(w) * per, nblk), b1 = imin(b0 + per, nblk);
     const unsigned long long below = (1ull << lane) - 1ull;
     auto classify = [&](int64_t k, bool& lt, bool& tie) {
@@ -709,7 +715,7 @@ __device__ __forceinline__ int64_t cut_compact(ScoreAt score, int64_t n, const C
     __syncthreads();
     uint64_t before = 0, all = 0;
 #pragma unroll
-    for (int i = 0; i < kCutWaves; ++i) {
+    for (int i = 0; i < NW; ++i) {
         const uint64_t x = bs.wcnt[i];
         if (i < w) before += x;
         all += x;
@@ -1340,12 +1346,15 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitPa
 // level li_lo in one launch (every fused level has at most kUpperNodes nodes
 // per (sequence, kv head)). Per level: the candidate ids are built in LDS from
 // the kept nodes of the level above, each candidate's summary row is scored
-// against the head's query (16 waves, a row per LPR lanes), and the same
+// against the head's query (8 waves, a row per LPR lanes, 4 passes of rows in
+// flight per wave), and the same
 // exact cut runs on the LDS-resident scores. The kept set stays in LDS for the
 // next level and is written out (kept list, count, bitmap) for the levels
 // below li_lo.
 // ----------------------------------------------------------------------------
 constexpr int kUpperNodes = 8192;
+constexpr int kUpperThreads = 512;     // 8 waves: rows in flight for the scoring, cheap barriers for the cut
+constexpr int kUpperWaves = kUpperThreads / kWave;
 
 struct UpperParams {
     const float* q;            // [rows, Hq, D]
@@ -1378,15 +1387,16 @@ struct UpperShared {
 };
 
 template <int D>
-__global__ __launch_bounds__(kCutThreads) void route_upper_kernel(UpperParams p) {
+__global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams p) {
     __shared__ UpperShared sh;
+    constexpr int NW = kUpperWaves;
     constexpr int DPL = 16;                    // dims per lane
     constexpr int LPR = D / DPL;               // lanes per summary row
     constexpr int RPP = kWave / LPR;           // rows per wave pass
-    constexpr int UNR = 2;                     // passes issued together (1024 threads: <= 128 VGPRs)
+    constexpr int UNR = 4;                     // passes issued together: 4 * RPP rows in flight per wave
     const int hq = blockIdx.x, row = blockIdx.y;
     const int kv = hq / p.G, s = row / p.T;
-    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nw = nt / kWave;
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nw = NW;
     const int sub = lane / LPR, part = lane % LPR;
     const int N = clamp_visible(p.ri, row, p.cap);
     const int64_t rh = static_cast<int64_t>(row) * p.Hq + hq;
@@ -1467,9 +1477,9 @@ __global__ __launch_bounds__(kCutThreads) void route_upper_kernel(UpperParams p)
             __syncthreads();
             m = sh.bs.wcount;
         } else {
-            mx = block_max_f(mx, sh.bs);       // its barriers also publish sc[]
-            const CutBoundary cb = cut_boundary_radix(score, ncand, mx, p.top_p, sh.bs);
-            m = cut_compact(score, ncand, cb, p.lb < 5 ? p.lb : 5, sh.bs, emit, mark);
+            mx = block_max_f<NW>(mx, sh.bs);   // its barriers also publish sc[]
+            const CutBoundary cb = cut_boundary_radix<NW>(score, ncand, mx, p.top_p, sh.bs);
+            m = cut_compact<NW>(score, ncand, cb, p.lb < 5 ? p.lb : 5, sh.bs, emit, mark);
         }
         uint32_t* bm = p.bitmap + rh * p.bm_words_total + p.bm_off[li];
         for (int64_t w = tid; w < words; w += nt) bm[w] = sh.bm[w];
@@ -1610,9 +1620,9 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
         {
             ProfScope ps("route_upper", 0, st);
             if (g.D == 128)
-                hipLaunchKernelGGL(route_upper_kernel<128>, dim3(g.Hq, a.rows), dim3(kCutThreads), 0, st, up);
+                hipLaunchKernelGGL(route_upper_kernel<128>, dim3(g.Hq, a.rows), dim3(kUpperThreads), 0, st, up);
             else
-                hipLaunchKernelGGL(route_upper_kernel<64>, dim3(g.Hq, a.rows), dim3(kCutThreads), 0, st, up);
+                hipLaunchKernelGGL(route_upper_kernel<64>, dim3(g.Hq, a.rows), dim3(kUpperThreads), 0, st, up);
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
