@@ -248,8 +248,9 @@ struct BlockScratch {
 // and a member is kept while the mass ranked before it is below rem. Leaves
 // the largest kept key (the boundary key) in bs.bcast_u32[1] and the number
 // of kept members with that key in bs.bcast_u64[1].
+template <class Scratch>
 __device__ __forceinline__ void wave_resolve(const uint32_t* lk, const float* ls, int m, float mx, uint64_t rem,
-                                             BlockScratch& bs) {
+                                             Scratch& bs) {
     const int lane = threadIdx.x & 63;
     const bool valid = lane < m;
     const uint32_t k = valid ? lk[lane] : 0u;
@@ -649,8 +650,8 @@ __device__ __forceinline__ CutBoundary cut_boundary(ScoreAt score, int64_t n, fl
 // boundary search keeps: all keys below the boundary key, and of the boundary
 // key's ties the first in index order. emit(pos, k) for every kept one, pos
 // ascending in k. Returns the number kept (on every lane).
-template <class ScoreAt, class Emit>
-__device__ __forceinline__ int wave_cut_small(ScoreAt score, int n, float top_p, BlockScratch& bs, Emit emit) {
+template <class ScoreAt, class Emit, class Scratch>
+__device__ __forceinline__ int wave_cut_small(ScoreAt score, int n, float top_p, Scratch& bs, Emit emit) {
     const int lane = threadIdx.x & 63;
     const bool valid = lane < n;
     const float s = valid ? score(lane) : -INFINITY;
@@ -766,6 +767,7 @@ struct CutParams {
     int64_t cap;
     int b, lb, li, L, Hq, T;
     float top_p;
+    int64_t pairs;             // rows * Hq (the one-wave-per-pair kernel)
 };
 
 constexpr int kCutStage = 32768;      // candidate scores staged in LDS (128 KiB)
@@ -931,6 +933,263 @@ __global__ __launch_bounds__(kCutThreads) void route_cut_kernel(CutParams p) {
     cc.ncand = cc.nkids + (nc - (cc.nc_up << p.lb));
     if (cc.ncand <= kCutStage && kc <= kCutUpStage) cut_level<true>(p, sh, cc, rh, nc);
     else cut_level<false>(p, sh, cc, rh, nc);
+}
+
+// ----------------------------------------------------------------------------
+// one wave per (row, head): a level's cut for many pairs at once
+// When thousands of (row, head) pairs route together (the rows of a prefill
+// chunk), a workgroup per pair spends most of its time starting up and
+// synchronising. Here each wave cuts one pair's level on its own, with its
+// candidates' scores in its own 8 KiB of LDS and no block barriers:
+//  1. the candidates' maximum; their 2^-40 fixed-point masses, summed in total
+//     and per bin of the score's distance below the maximum (kWaveBins bins);
+//  2. a scan of the bins finds the bin where the running mass reaches
+//     ceil(top_p * total); its members, if at most 64, are ranked exactly by
+//     wave_resolve, else an MSB-first radix select over their keys pins the
+//     boundary key and the ties it needs;
+//  3. a stable ballot compaction writes the kept ids in ascending order and
+//     the kept bitmap.
+// The kept set is the one cut_boundary and cut_compact produce.
+// ----------------------------------------------------------------------------
+constexpr int kWaveCutThreads = 256;
+constexpr int kWaveCutWaves = kWaveCutThreads / kWave;
+constexpr int kWaveBins = 256;
+constexpr float kWaveBinScale = 256.0f / 28.0f;
+constexpr int kWaveStage = 2048;        // candidate scores staged per wave: levels of up to 2048 nodes
+constexpr int kWaveBmWords = kWaveStage / 32 + 1;          // the level's kept bitmap, in LDS
+
+struct WaveScratch {
+    uint64_t wpk[kWave];       // wave_resolve / wave_cut_small ranking
+    uint64_t wmass[kWave];
+    uint64_t wpre[kWave];
+    uint64_t bcast_u64[2];
+    uint32_t bcast_u32[2];
+    uint64_t bins[kWaveBins];  // mass per bin, then per radix digit
+    uint32_t list[kWave];      // members of the boundary bin
+    float list_s[kWave];
+    uint32_t bm[kWaveBmWords];
+    float sc[kWaveStage];      // the candidates' scores, in candidate order
+};
+
+__device__ __forceinline__ int wave_bin(float s, float mx) {
+    const float d = (mx - s) * kWaveBinScale;
+    return d < static_cast<float>(kWaveBins - 1) ? static_cast<int>(d) : kWaveBins - 1;
+}
+
+__device__ __forceinline__ int64_t lane_read_u64(uint64_t v, int l) {
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), l));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// The digit (lane-owned runs of 4 in order) at which the running mass of
+// hist[0..256) first reaches rem; *before receives the mass of the earlier
+// digits. hist holds at least rem in total.
+__device__ __forceinline__ int wave_find_digit(const uint64_t* hist, uint64_t rem, uint64_t* before) {
+    const int lane = threadIdx.x & 63;
+    uint64_t v[4], lsum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[j] = hist[lane * 4 + j];
+        lsum += v[j];
+    }
+    const uint64_t inc = wave_scan_u64(lsum);
+    uint64_t c = inc - lsum;
+    int found = -1;
+    uint64_t bf = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (found < 0 && v[j] != 0 && c + v[j] >= rem) {
+            found = lane * 4 + j;
+            bf = c;
+        }
+        c += v[j];
+    }
+    const unsigned long long bal = __ballot(found >= 0);
+    const int first = bal ? __ffsll(static_cast<long long>(bal)) - 1 : 0;
+    *before = static_cast<uint64_t>(lane_read_u64(bf, first));
+    return __builtin_amdgcn_readlane(found, first);
+}
+
+// The candidates' scores are staged in the wave's LDS (a level of at most
+// kWaveStage nodes), so every pass after the load runs on LDS.
+__global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutParams p) {
+    __shared__ WaveScratch wsh[kWaveCutWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t rh = static_cast<int64_t>(blockIdx.x) * kWaveCutWaves + wave;
+    if (rh >= p.pairs) return;                       // the whole wave: nothing below syncs the block
+    WaveScratch& ws = wsh[wave];
+    const int row = static_cast<int>(rh / p.Hq);
+    const int N = clamp_visible(p.ri, row, p.cap);
+    const int64_t nc = static_cast<int64_t>(N) >> (p.lb * (p.li + 1));
+    CutCands cc;
+    cc.sc = p.scores + rh * p.nodes_total + p.lvl_off;
+    cc.lb = p.lb;
+    cc.up = nullptr;
+    cc.nc_up = 0;
+    int64_t kc = 0;
+    if (p.li != p.L - 1) {
+        cc.nc_up = static_cast<int64_t>(N) >> (p.lb * (p.li + 2));
+        kc = p.kept_cnt[rh * p.L + p.li + 1];
+        cc.up = p.kept + rh * p.nodes_total + p.lvl_off_up;
+    }
+    cc.nkids = kc << p.lb;
+    cc.ncand = cc.nkids + (nc - (cc.nc_up << p.lb));
+    const int n = static_cast<int>(cc.ncand);        // <= nodes of the level <= kWaveStage
+    const bool leaf = (p.li == 0);
+
+    int32_t* kept_out = leaf ? nullptr : p.kept + rh * p.nodes_total + p.lvl_off;
+    int32_t* sel_out = leaf ? p.sel_blocks + rh * p.sel_cap : nullptr;
+    int32_t* lsel_out = p.level_sel ? p.level_sel + p.lsel_off + rh * p.nodes_l : nullptr;
+    uint32_t* bm = p.bitmap + rh * p.bm_words_total + p.bm_off;
+    const int64_t words = (nc + 31) >> 5;            // <= kWaveBmWords
+    for (int64_t w = lane; w < words; w += kWave) ws.bm[w] = 0u;
+    __builtin_amdgcn_wave_barrier();
+    auto emit = [&](int64_t pos, int64_t k) {
+        const int32_t node = static_cast<int32_t>(cc.node(k));
+        if (kept_out) kept_out[pos] = node;
+        if (sel_out && pos < p.sel_cap) sel_out[pos] = node;
+        if (lsel_out) lsel_out[pos] = node;
+    };
+    auto mark = [&](int64_t k, uint32_t bits) {
+        const int64_t node = cc.node(k);
+        atomicOr(&ws.bm[node >> 5], bits << (node & 31));
+    };
+
+    int64_t m;
+    if (n <= kWave) {
+        m = wave_cut_small([&](int64_t k) -> float { return cc.sc[cc.node(k)]; }, n, p.top_p, ws,
+                           [&](int64_t pos, int64_t k) { emit(pos, k); mark(k, 1u); });
+    } else {
+        // every candidate's score into LDS, kStageU loads in flight per lane; the maximum
+        constexpr int kStageU = 8;
+        float mx = -INFINITY;
+        for (int kb = 0; kb < n; kb += kStageU * kWave) {
+            float v[kStageU];
+#pragma unroll
+            for (int u = 0; u < kStageU; ++u) {
+                const int k = kb + u * kWave + lane;
+                v[u] = k < n ? cc.sc[cc.node(k)] : -INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < kStageU; ++u) {
+                const int k = kb + u * kWave + lane;
+                if (k < n) ws.sc[k] = v[u];
+                mx = fmaxf(mx, v[u]);
+            }
+        }
+        mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_scan_max_f(mx)), 63));
+        __builtin_amdgcn_wave_barrier();
+        const int nblk = (n + kWave - 1) / kWave;
+        const bool take_all = p.top_p >= 1.0f;
+        uint32_t kappa = 0;
+        uint64_t need = 0;
+        if (!take_all) {
+            for (int i = lane; i < kWaveBins; i += kWave) ws.bins[i] = 0;
+            __builtin_amdgcn_wave_barrier();
+            uint64_t E = 0;
+            for (int r = 0; r < nblk; ++r) {                         // whole-wave updates
+                const int k = lane + r * kWave;
+                const float sv = k < n ? ws.sc[k] : mx;
+                const uint64_t F = k < n ? mass_fx(sv, mx) : 0;
+                E += F;
+                wave_add_u64(reinterpret_cast<unsigned long long*>(ws.bins), wave_bin(sv, mx), F, F != 0);
+            }
+            E = lane63_u64(wave_scan_u64(E));
+            uint64_t rem = static_cast<uint64_t>(ceil(static_cast<double>(p.top_p) * static_cast<double>(E)));
+            if (rem == 0) rem = 1;
+            __builtin_amdgcn_wave_barrier();
+            // 2. the boundary bin and its members
+            uint64_t before;
+            const int bstar = wave_find_digit(ws.bins, rem, &before);
+            rem -= before;
+            uint32_t nm = 0;
+            for (int r = 0; r < nblk; ++r) {
+                const int k = lane + r * kWave;
+                const float sv = k < n ? ws.sc[k] : mx;
+                const bool mem = k < n && wave_bin(sv, mx) == bstar && mass_fx(sv, mx) != 0;
+                const unsigned long long bal = __ballot(mem);
+                const uint32_t pos = nm + static_cast<uint32_t>(__popcll(bal & ((1ull << lane) - 1ull)));
+                if (mem && pos < kWave) {
+                    ws.list[pos] = static_cast<uint32_t>(k);
+                    ws.list_s[pos] = sv;
+                }
+                nm += static_cast<uint32_t>(__popcll(bal));
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (nm <= kWave) {
+                wave_resolve(ws.list, ws.list_s, static_cast<int>(nm), mx, rem, ws);
+                __builtin_amdgcn_wave_barrier();
+                kappa = ws.bcast_u32[1];
+                need = ws.bcast_u64[1];
+            } else {
+                // a crowded bin: radix select over its members' keys, 8 bits a round
+                uint32_t prefix = 0;
+                for (int known = 0; known < 32; known += 8) {
+                    const int shift = 24 - known;
+                    const uint32_t hmask = known ? ~0u << (32 - known) : 0u;
+                    for (int i = lane; i < kWaveBins; i += kWave) ws.bins[i] = 0;
+                    __builtin_amdgcn_wave_barrier();
+                    for (int r = 0; r < nblk; ++r) {
+                        const int k = lane + r * kWave;
+                        const float sv = k < n ? ws.sc[k] : mx;
+                        const uint32_t key = desc_key(sv);
+                        const bool in = k < n && wave_bin(sv, mx) == bstar && ((key ^ prefix) & hmask) == 0u;
+                        const uint64_t F = in ? mass_fx(sv, mx) : 0;
+                        wave_add_u64(reinterpret_cast<unsigned long long*>(ws.bins), static_cast<int>((key >> shift) & 255u),
+                                     F, F != 0);
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                    uint64_t bd;
+                    const int d = wave_find_digit(ws.bins, rem, &bd);
+                    rem -= bd;
+                    prefix |= static_cast<uint32_t>(d) << shift;
+                    __builtin_amdgcn_wave_barrier();
+                }
+                kappa = prefix;
+                const uint64_t Fk = mass_fx(desc_key_to_float(kappa), mx);
+                need = Fk ? (rem + Fk - 1) / Fk : 0;
+            }
+        }
+        // 3. stable compaction, 64 candidates (one register slot) at a time
+        const int run_lg = p.lb < 5 ? p.lb : 5;
+        const int run = 1 << run_lg;
+        const unsigned long long run_mask = (1ull << run) - 1ull;
+        const unsigned long long below = (1ull << lane) - 1ull;
+        uint64_t lt_b = 0, tie_b = 0;
+        for (int r = 0; r < nblk; ++r) {
+            const int64_t k = lane + r * kWave;
+            const bool valid = k < n;
+            const uint32_t key = valid ? desc_key(ws.sc[k]) : 0u;
+            const bool lt = valid && (take_all || key < kappa);
+            const bool tie = valid && !take_all && key == kappa;
+            const unsigned long long blt = __ballot(lt), btie = __ballot(tie);
+            const uint64_t my_lt = lt_b + __popcll(blt & below), my_tie = tie_b + __popcll(btie & below);
+            const bool keep = lt || (tie && my_tie < need);
+            if (keep) emit(static_cast<int64_t>(my_lt + (lt ? (my_tie < need ? my_tie : need) : my_tie)), k);
+            const unsigned long long bkeep = __ballot(keep);
+            if ((lane & (run - 1)) == 0) {
+                const uint32_t bits = static_cast<uint32_t>((bkeep >> lane) & run_mask);
+                if (bits) mark(k, bits);
+            }
+            lt_b += __popcll(blt);
+            tie_b += __popcll(btie);
+        }
+        m = static_cast<int64_t>(lt_b + (tie_b < need ? tie_b : need));
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int64_t w = lane; w < words; w += kWave) bm[w] = ws.bm[w];
+    if (lane == 0) {
+        p.kept_cnt[rh * p.L + p.li] = static_cast<int32_t>(m);
+        if (leaf) {
+            p.n_sel[rh] = static_cast<int32_t>(m);
+            if (m > p.sel_cap) atomicOr(p.status, ZHA_DEV_SEL_OVERFLOW);
+        }
+        if (p.level_stats) {
+            p.level_stats[(rh * p.L + p.li) * 2 + 0] = static_cast<int32_t>(n);
+            p.level_stats[(rh * p.L + p.li) * 2 + 1] = static_cast<int32_t>(m);
+        }
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -1526,9 +1785,9 @@ static int upper_from(const Geo& g) {
     return lo;
 }
 
-// One workgroup per (row, query head) cuts level li from the dense-by-node
-// scores.
-static hipError_t launch_cut(const Geo& g, const RouteArgs& a, int li, hipStream_t st) {
+// Level li's cut from the dense-by-node scores: one workgroup per (row, query
+// head), or one wave per pair (wave = true) when the pairs are many.
+static hipError_t launch_cut(const Geo& g, const RouteArgs& a, int li, hipStream_t st, bool wave = false) {
     const WsLayout& lay = *a.lay;
     char* ws = a.ws;
     const bool top = (li == g.L - 1);
@@ -1559,9 +1818,14 @@ static hipError_t launch_cut(const Geo& g, const RouteArgs& a, int li, hipStream
     cp.Hq = g.Hq;
     cp.T = a.ri.T;
     cp.top_p = a.top_p;
+    cp.pairs = static_cast<int64_t>(a.rows) * g.Hq;
     {
         ProfScope ps("route_cut", li + 1, st);
-        hipLaunchKernelGGL(route_cut_kernel, dim3(g.Hq, a.rows), dim3(kCutThreads), 0, st, cp);
+        if (wave) {
+            hipLaunchKernelGGL(route_wave_cut_kernel, dim3(static_cast<unsigned>((cp.pairs + kWaveCutWaves - 1) / kWaveCutWaves)),
+                               dim3(kWaveCutThreads), 0, st, cp);
+        } else
+            hipLaunchKernelGGL(route_cut_kernel, dim3(g.Hq, a.rows), dim3(kCutThreads), 0, st, cp);
     }
     return hipGetLastError();
 }
@@ -1580,7 +1844,9 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
     // once, then the levels' cuts from the top
     if (a.ri.T >= kDenseMinRows && dense_scores_fit(g, a.ri.T)) {
         hipError_t e = launch_dense_scores(g, a.ri, a.q, a.summaries, scores, 0, g.L - 1, st);
-        for (int li = g.L - 1; e == hipSuccess && li >= 0; --li) e = launch_cut(g, a, li, st);
+        // one wave per pair while a level's candidates fit a wave's LDS
+        for (int li = g.L - 1; e == hipSuccess && li >= 0; --li)
+            e = launch_cut(g, a, li, st, g.nodes[li] <= kWaveStage);
         return e;
     }
 

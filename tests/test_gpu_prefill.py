@@ -20,7 +20,7 @@ import pytest
 import hierarchical_tree_indexed_build_amd as Z
 import workloads as W
 from oracle import zha_oracle as O
-from tests.gpu_helpers import Staged, attn_tol, check_sets, kv_tensor, say, torch
+from tests.gpu_helpers import Staged, attn_tol, check_sets, kv_tensor, level_kept, say, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -110,3 +110,52 @@ def test_prefill_chunk_parity(case):
                 worst = max(worst, e)
                 assert e <= tol, (s, t_, hq, e)
     say(f"  margin-exempt differences: {flips}; worst |gpu - oracle| attention {worst:.3g} (tol {tol})")
+
+
+# crowded scores through the one-wave-per-pair cut: identical keys (every
+# score equal: one bin, ties broken by node id) and keys within a narrow band
+# (crowded bins resolved by radix select)
+CROWDED = [("equal", 0.0), ("band", 1e-3), ("band", 3e-2)]
+
+
+@pytest.mark.parametrize("kind,noise", CROWDED, ids=[f"{k}-{e:g}" for k, e in CROWDED])
+def test_many_rows_crowded_scores(kind, noise):
+    t = torch()
+    w = W.get_workload("gqa128k", shrink=1, batch=1)
+    T = 64
+    say(f"[many rows crowded] {kind} noise {noise:g}: {w.n_tokens} tokens, {T} causal rows")
+    st = Staged(w, max_t=T, build=False)
+    rng = np.random.default_rng(20261204)
+    B, H, C, D = st.K_np.shape
+    base = rng.standard_normal((B, H, 1, D)).astype(np.float32)
+    K = np.broadcast_to(base, (B, H, C, D)).copy()
+    if noise:
+        K += noise * rng.standard_normal(K.shape).astype(np.float32)
+    st.K_np = W.f32_to_bf16_bits(K)
+    st.Kf = W.as_f32(w, st.K_np)
+    st.cache.K.copy_(kv_tensor(w, st.K_np))
+    Z.build_tree(st.geom, st.cache.K, st.ref_q, st.cache.seq_lens, st.cache.summaries, st.cache.ws)
+    qn, q = st.queries(0, rows=T)
+    q_pos = (w.n_tokens - T + t.arange(T, dtype=t.int32, device="cuda")).view(1, T).contiguous()
+    sel, nsel, stats, lsel = st.route_buffers(T)
+    Z.route(st.geom, q, q_pos, st.cache.summaries, st.cache.seq_lens, w.top_p, sel, nsel, st.cache.ws,
+            level_stats=stats, level_sel=lsel)
+    t.cuda.synchronize()
+    trees = st.oracle_trees()
+    kept = {level: level_kept(st, lsel, stats, T, level) for level in range(1, w.n_levels + 1)}
+    flips = 0
+    for t_ in range(T):
+        N = w.n_tokens - T + t_ + 1
+        for hq in range(w.n_q_heads):
+            kv = hq // w.group
+            parents = None
+            for level in range(w.n_levels, 0, -1):
+                v, cnt, cand = kept[level]
+                gpu_ids = v[t_, hq, :cnt[t_, hq]]
+                cut = O.route_level(qn[0, t_, hq], trees[0][kv][level - 1], level, parents, N, w.branching,
+                                    w.n_levels, w.top_p, w.scale)
+                assert cand[t_, hq] == len(cut.ids), (t_, hq, level, cand[t_, hq], len(cut.ids))
+                assert np.all(np.diff(gpu_ids) > 0), "kept ids must be ascending"
+                flips += check_sets(gpu_ids, cut, w.top_p, f"row {t_} head {hq} level {level}")
+                parents = gpu_ids
+    say(f"  margin-exempt differences: {flips}")
