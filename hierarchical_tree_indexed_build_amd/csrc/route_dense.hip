@@ -42,7 +42,7 @@ struct DenseParams {
     float* scores;             // [rows, Hq, nodes_total] by node id, level offsets sc_off
     int64_t nodes_total;
     int64_t cap;
-    int Hq, Hkv, G, lb, nlev;
+    int Hq, Hkv, G, lgG, lb, nlev;   // G = 1 << lgG <= 16
     int64_t mrows;             // T * G: contraction rows per (sequence, kv head)
     float scale;
     int li[ZHA_MAX_LEVELS];            // level (0-based) of each handled entry
@@ -61,8 +61,8 @@ struct DenseShared {
 // Contraction row r of (sequence s, kv head kv) is query head kv*G + r % G of
 // the sequence's row r / G.
 __device__ __forceinline__ int64_t dense_rh(const DenseParams& p, int s, int kv, int64_t r) {
-    const int64_t row = static_cast<int64_t>(s) * p.ri.T + r / p.G;
-    return row * p.Hq + static_cast<int64_t>(kv) * p.G + r % p.G;
+    const int64_t row = static_cast<int64_t>(s) * p.ri.T + (r >> p.lgG);
+    return row * p.Hq + (static_cast<int64_t>(kv) << p.lgG) + (r & (p.G - 1));
 }
 
 template <int D>
@@ -91,28 +91,27 @@ __global__ __launch_bounds__(kDenseThreads) void route_dense_score_kernel(DenseP
     const int64_t ncols = imin(static_cast<int64_t>(sh.vis_max) >> (p.lb * (li + 1)), p.nodes[e]);
     if (n0 >= ncols) return;                           // uniform: every thread read the same vis_max
 
-    // staging: 128 rows x 32 dims per operand = 1024 float4, four per thread
+    // staging: 128 rows x 32 dims per operand = 1024 float4, four per thread:
+    // rows tr + 32u (u < 4) at dims [4 c4, 4 c4 + 4) of the chunk. Row tr + 32u
+    // of Q is query row tr + 32u of the same head (32 is a multiple of G), so
+    // the four A rows are one pointer apart by a fixed stride.
     constexpr int kPer = kDenseTM * kDenseTK / 4 / kDenseThreads;
-    const float* a_src[kPer];
-    const float* b_src[kPer];
-    int st_off[kPer];
-    const float* summ = p.summaries + p.sum_off[e] + (static_cast<int64_t>(s) * p.Hkv + kv) * p.nodes[e] * D;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-        const int idx = tid + u * kDenseThreads;
-        const int r = idx / (kDenseTK / 4), c4 = idx % (kDenseTK / 4);
-        st_off[u] = r * kDenseLd + c4 * 4;
-        const int64_t mr = m0 + r, nr = n0 + r;
-        a_src[u] = mr < p.mrows ? p.q + dense_rh(p, s, kv, mr) * D + c4 * 4 : nullptr;
-        b_src[u] = nr < ncols ? summ + nr * D + c4 * 4 : nullptr;
-    }
+    constexpr int kRowStep = kDenseThreads / (kDenseTK / 4);      // 32 rows between a thread's rows
+    const int tr = tid / (kDenseTK / 4), c4 = tid % (kDenseTK / 4);
+    const int st0 = tr * kDenseLd + c4 * 4;
+    const int64_t mr0 = m0 + tr, nr0 = n0 + tr;
+    const int na = static_cast<int>(imax(0, imin(kPer, (p.mrows - mr0 + kRowStep - 1) / kRowStep)));
+    const int nb = static_cast<int>(imax(0, imin(kPer, (ncols - nr0 + kRowStep - 1) / kRowStep)));
+    const float* a0 = p.q + (na ? dense_rh(p, s, kv, mr0) : 0) * D + c4 * 4;
+    const int64_t a_step = (static_cast<int64_t>(kRowStep) >> p.lgG) * p.Hq * D;
+    const float* b0 = p.summaries + p.sum_off[e] + ((static_cast<int64_t>(s) * p.Hkv + kv) * p.nodes[e] + nr0) * D + c4 * 4;
     f32x4_t ra[kPer], rb[kPer];
     auto fetch = [&](int c) {
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            ra[u] = a_src[u] ? *reinterpret_cast<const f32x4_t*>(a_src[u] + c * kDenseTK) : z;
-            rb[u] = b_src[u] ? *reinterpret_cast<const f32x4_t*>(b_src[u] + c * kDenseTK) : z;
+            ra[u] = u < na ? *reinterpret_cast<const f32x4_t*>(a0 + u * a_step + c * kDenseTK) : z;
+            rb[u] = u < nb ? *reinterpret_cast<const f32x4_t*>(b0 + static_cast<int64_t>(u) * kRowStep * D + c * kDenseTK) : z;
         }
     };
     fetch(0);
@@ -131,8 +130,8 @@ __global__ __launch_bounds__(kDenseThreads) void route_dense_score_kernel(DenseP
         if (c) __syncthreads();                        // the previous chunk's products are done
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
-            *reinterpret_cast<f32x4_t*>(sa + st_off[u]) = ra[u];
-            *reinterpret_cast<f32x4_t*>(sb + st_off[u]) = rb[u];
+            *reinterpret_cast<f32x4_t*>(sa + st0 + u * kRowStep * kDenseLd) = ra[u];
+            *reinterpret_cast<f32x4_t*>(sb + st0 + u * kRowStep * kDenseLd) = rb[u];
         }
         __syncthreads();
         if (c + 1 < kChunks) fetch(c + 1);
@@ -193,6 +192,8 @@ hipError_t launch_dense_scores(const Geo& g, const RowInfo& ri, const float* q, 
     p.Hq = g.Hq;
     p.Hkv = g.Hkv;
     p.G = g.G;
+    p.lgG = 0;
+    while ((1 << p.lgG) < g.G) ++p.lgG;
     p.lb = g.lb;
     p.mrows = static_cast<int64_t>(ri.T) * g.G;
     p.scale = g.scale;
