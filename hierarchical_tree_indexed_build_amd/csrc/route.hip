@@ -1591,7 +1591,11 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitPa
         const unsigned long long bkeep = __ballot(keep);
         if ((lane & (run - 1)) == 0) {
             const uint32_t bits = static_cast<uint32_t>((bkeep >> lane) & run_mask);
-            if (bits)   // a run's nodes are consecutive and share one word; runs of other slices may share it too
+            // a run's nodes are consecutive and share one word. With b >= 32 a run is
+            // a whole, aligned word that no other run touches: a plain store. With
+            // smaller b, runs of other slices may share the word.
+            if (bits && run == 32) bm[nd[j] >> 5] = bits;
+            else if (bits)
                 __hip_atomic_fetch_or(bm + (nd[j] >> 5), bits << (nd[j] & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         lt_b += __popcll(blt);
