@@ -73,10 +73,12 @@ struct ScoreParams {
     int64_t cand_stride;
 };
 
-// Workgroup = at most 64 parent slots of one (row, kv head), taken every
-// gridDim.x-th, one wave per active parent at a time. Every wave builds the
-// slots' masks itself with ballots (lane = slot): the slots some head of the
-// group kept, and for each head the slots it takes candidates from.
+// Workgroup = one wave = at most 64 parent slots of one (row, kv head), taken
+// every gridDim.x-th, its active parents one at a time. The wave builds the
+// slots' masks with ballots (lane = slot): the slots some head of the group
+// kept, and for each head the slots it takes candidates from. About 2048
+// waves in all, what the chip holds at once at this kernel's register use,
+// so a heavy pair's parents are spread as wide as the chip allows.
 template <int D, int G>
 __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams p) {
     const int y = blockIdx.y;
@@ -99,11 +101,13 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
     const int64_t per = (slots + W - 1) / W;
     const int64_t rh0 = static_cast<int64_t>(row) * p.Hq + kv * G;      // the group's first (row, head)
     const bool split = p.pmax != nullptr;
-    if (split && run == 0) {
-        for (int i = threadIdx.x; i < G * kCutBins; i += blockDim.x) p.chist[rh0 * kCutBins + i] = 0ull;
+    if (split) {
+        // the runs of the pair clear its heads' bins and this level's bitmaps between them
+        const int64_t stride = W * blockDim.x, first = static_cast<int64_t>(run) * blockDim.x + threadIdx.x;
+        for (int64_t i = first; i < G * kCutBins; i += stride) p.chist[rh0 * kCutBins + i] = 0ull;
         const int64_t words = (nc + 31) >> 5;
-        for (int h = 0; h < G; ++h)
-            for (int64_t i = threadIdx.x; i < words; i += blockDim.x) p.bm_cur[(rh0 + h) * p.bm_words_total + i] = 0u;
+        for (int64_t i = first; i < G * words; i += stride)
+            p.bm_cur[(rh0 + i / words) * p.bm_words_total + i % words] = 0u;
     }
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;

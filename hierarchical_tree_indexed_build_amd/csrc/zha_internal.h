@@ -14,13 +14,14 @@ constexpr int kWave = 64;
 constexpr int kMaxGroup = 16;          // H_q / H_kv handled by one kernel group
 constexpr int kAttnWorkgroups = 512;   // attention workgroups when pairs are few (launch and partial slots: this + pairs)
 constexpr size_t kAlign = 256;
-constexpr int kScoreThreads = 512;     // scoring workgroup: one wave per active parent at a time
+constexpr int kScoreThreads = 64;      // scoring workgroup: one wave, its active parents one at a time
+constexpr int kScoreWaves = 2048;      // scoring waves per launch: what the chip holds at once
 
 // Scoring workgroups per (row, kv head) for a level with `slots` parent slots:
-// about 512 in all over `pairs` (row, kv head) pairs, each with at most 64
-// slots (one wave's lanes build their masks).
+// about kScoreWaves in all over `pairs` (row, kv head) pairs, each with at
+// most 64 slots (the wave's lanes build their masks).
 inline int64_t score_groups(int64_t slots, int64_t pairs) {
-    const int64_t target = (512 + pairs - 1) / (pairs > 0 ? pairs : 1);
+    const int64_t target = (kScoreWaves + pairs - 1) / (pairs > 0 ? pairs : 1);
     int64_t w = target < slots ? target : slots;
     const int64_t need = (slots + 63) / 64;
     w = w > need ? w : need;
