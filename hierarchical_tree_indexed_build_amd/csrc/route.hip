@@ -458,9 +458,28 @@ __device__ __forceinline__ CutBoundary cut_boundary_radix(ScoreAt score, int64_t
     const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
     CutBoundary cb{(top_p >= 1.0f) || n == 0, 0u, 0u};
     if (cb.take_all) return cb;
+    // the first kRadixCache candidates of each thread keep their key and mass in
+    // registers for every round; any beyond them are recomputed per round
+    constexpr int kRadixCache = 4;
+    uint32_t ck[kRadixCache];
+    uint64_t cF[kRadixCache];
     uint64_t E = 0;
     uint32_t kmax = 0;
-    for (int64_t k = tid; k < n; k += nt) {
+#pragma unroll
+    for (int j = 0; j < kRadixCache; ++j) {
+        const int64_t k = tid + static_cast<int64_t>(j) * nt;
+        ck[j] = 0u;
+        cF[j] = 0;
+        if (k < n) {
+            const float s = score(k);
+            ck[j] = desc_key(s);
+            cF[j] = mass_fx(s, mx);
+            E += cF[j];
+            if (cF[j]) kmax = max(kmax, ck[j]);
+        }
+    }
+    const int64_t cached = static_cast<int64_t>(kRadixCache) * nt;
+    for (int64_t k = cached + tid; k < n; k += nt) {
         const float s = score(k);
         const uint64_t F = mass_fx(s, mx);
         E += F;
@@ -479,7 +498,14 @@ __device__ __forceinline__ CutBoundary cut_boundary_radix(ScoreAt score, int64_t
         const int shift = 32 - known - nb;
         const uint32_t hmask = top_bits_mask(known);
         uint64_t* hist = bs.hist[cur];
-        for (int64_t kb = 0; kb < n; kb += nt) {                  // uniform trip count: whole waves update
+        // the first rounds put most candidates in one digit: wave_add_u64 combines them per wave
+#pragma unroll
+        for (int j = 0; j < kRadixCache; ++j) {                  // whole waves update
+            const uint64_t F = ((ck[j] ^ prefix) & hmask) == 0u ? cF[j] : 0;
+            wave_add_u64(reinterpret_cast<unsigned long long*>(hist), static_cast<int>((ck[j] >> shift) & ((1u << nb) - 1u)),
+                         F, F != 0);
+        }
+        for (int64_t kb = cached; kb < n; kb += nt) {             // uniform trip count
             const int64_t k = kb + tid;
             uint32_t key = 0;
             uint64_t F = 0;
@@ -488,7 +514,6 @@ __device__ __forceinline__ CutBoundary cut_boundary_radix(ScoreAt score, int64_t
                 key = desc_key(s);
                 if (((key ^ prefix) & hmask) == 0u) F = mass_fx(s, mx);
             }
-            // the first rounds put most candidates in one digit: combine them per wave
             wave_add_u64(reinterpret_cast<unsigned long long*>(hist), static_cast<int>((key >> shift) & ((1u << nb) - 1u)),
                          F, F != 0);
         }
