@@ -571,7 +571,7 @@ __device__ __forceinline__ CutBoundary cut_boundary_radix(ScoreAt score, int64_t
 //     is below what rem still needs; a longer list goes through a radix select.
 // The result is the same key and tie count as a radix select over all the
 // candidates: bins only narrow the search.
-template <class ScoreAt>
+template <int NW = kCutWaves, class ScoreAt>
 __device__ __forceinline__ CutBoundary cut_boundary(ScoreAt score, int64_t n, float mx, float top_p,
                                                     uint64_t* bins, BlockScratch& bs) {
     const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
@@ -593,11 +593,11 @@ __device__ __forceinline__ CutBoundary cut_boundary(ScoreAt score, int64_t n, fl
     }
     if (tid == 0) bs.list_n = 0;
     for (int i = tid; i < 256; i += nt) bs.hist[0][i] = 0;
-    E = block_sum_u64(E, bs);                       // its barriers also publish the bins
+    E = block_sum_u64<NW>(E, bs);                   // its barriers also publish the bins
     uint64_t rem = static_cast<uint64_t>(ceil(static_cast<double>(top_p) * static_cast<double>(E)));
     if (rem == 0) rem = 1;
 
-    constexpr int BPT = kCutBins / kCutThreads;     // bins per thread, in bin order
+    constexpr int BPT = kCutBins / (NW * kWave);    // bins per thread, in bin order
     uint64_t v[BPT], lsum = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
@@ -605,7 +605,7 @@ __device__ __forceinline__ CutBoundary cut_boundary(ScoreAt score, int64_t n, fl
         lsum += v[j];
     }
     uint64_t tot;
-    uint64_t c = block_excl_scan_u64(lsum, bs, &tot);
+    uint64_t c = block_excl_scan_u64<NW>(lsum, bs, &tot);
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
         if (v[j] != 0 && c < rem && c + v[j] >= rem) {  // exactly one bin crosses rem (tot >= rem)
@@ -1675,6 +1675,7 @@ struct UpperShared {
     int32_t cid[kUpperNodes];          // candidate node ids, ascending
     int32_t par[kUpperNodes];          // kept nodes of the level above, ascending
     uint32_t bm[kUpperNodes / 32 + 1];
+    uint64_t bins[kCutBins];           // mass bins of the boundary search
     BlockScratch bs;
 };
 
@@ -1770,7 +1771,7 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
             m = sh.bs.wcount;
         } else {
             mx = block_max_f<NW>(mx, sh.bs);   // its barriers also publish sc[]
-            const CutBoundary cb = cut_boundary_radix<NW>(score, ncand, mx, p.top_p, sh.bs);
+            const CutBoundary cb = cut_boundary<NW>(score, ncand, mx, p.top_p, sh.bins, sh.bs);
             m = cut_compact<NW>(score, ncand, cb, p.lb < 5 ? p.lb : 5, sh.bs, emit, mark);
         }
         uint32_t* bm = p.bitmap + rh * p.bm_words_total + p.bm_off[li];
