@@ -198,6 +198,8 @@ struct AttnParams {
     int b, lb, lgpi, Hq, Hkv, pairs, nwg, dense;
     int wave_plan;             // pairs <= 64: kernels take the plan from the counts themselves
     float qscale;              // scale * log2(e)
+    float* out;                // [rows, Hq, D]: written here for a pair of one share, else by the combine
+    float* lse;                // [rows, Hq] or null
 };
 
 // Each (row, kv head) pair's groups are cut into workgroup shares of `chunk`
@@ -545,23 +547,43 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
             }
         }
         __syncthreads();
-        float* pout = p.partial + static_cast<int64_t>(wg) * G * (D + 4);
-        for (int idx = threadIdx.x; idx < G * (D + 4); idx += blockDim.x) {
-            const int h = idx / (D + 4), c = idx % (D + 4);
-            float M = -INFINITY;
+        if (pv.wat(pr + 1) - pv.wat(pr) == 1) {
+            // the pair's only share: normalise here (the combine skips the pair)
+            const int64_t rh0 = static_cast<int64_t>(row) * p.Hq + kv * G;
+            for (int idx = threadIdx.x; idx < G * (D + 1); idx += blockDim.x) {
+                const int h = idx / (D + 1), c = idx % (D + 1);
+                float M = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
-            float out = 0.f;
-            if (c == 0) {
-                out = M;
-            } else if (c == 1 || c >= 4) {
+                for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+                float L = 0.f, A = 0.f;
 #pragma unroll
                 for (int w = 0; w < NW; ++w) {
                     const float f = (sm_m[w][h] == -INFINITY) ? 0.f : fast_exp2(sm_m[w][h] - M);
-                    out += f * (c == 1 ? sm_l[w][h] : sm_acc[w][h][c - 4]);
+                    L += f * sm_l[w][h];
+                    if (c < D) A += f * sm_acc[w][h][c];
                 }
+                if (c < D) p.out[(rh0 + h) * D + c] = A * (L > 0.f ? 1.f / L : 0.f);
+                else if (p.lse) p.lse[rh0 + h] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
             }
-            pout[idx] = out;
+        } else {
+            float* pout = p.partial + static_cast<int64_t>(wg) * G * (D + 4);
+            for (int idx = threadIdx.x; idx < G * (D + 4); idx += blockDim.x) {
+                const int h = idx / (D + 4), c = idx % (D + 4);
+                float M = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+                float out = 0.f;
+                if (c == 0) {
+                    out = M;
+                } else if (c == 1 || c >= 4) {
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) {
+                        const float f = (sm_m[w][h] == -INFINITY) ? 0.f : fast_exp2(sm_m[w][h] - M);
+                        out += f * (c == 1 ? sm_l[w][h] : sm_acc[w][h][c - 4]);
+                    }
+                }
+                pout[idx] = out;
+            }
         }
     }
 }
@@ -796,23 +818,43 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
             }
         }
         __syncthreads();
-        float* pout = p.partial + static_cast<int64_t>(wg) * G * (D + 4);
-        for (int idx = threadIdx.x; idx < G * (D + 4); idx += blockDim.x) {
-            const int h = idx / (D + 4), c = idx % (D + 4);
-            float M = -INFINITY;
+        if (pv.wat(pr + 1) - pv.wat(pr) == 1) {
+            // the pair's only share: normalise here (the combine skips the pair)
+            const int64_t rh0 = static_cast<int64_t>(row) * p.Hq + kv * G;
+            for (int idx = threadIdx.x; idx < G * (D + 1); idx += blockDim.x) {
+                const int h = idx / (D + 1), c = idx % (D + 1);
+                float M = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
-            float out = 0.f;
-            if (c == 0) {
-                out = M;
-            } else if (c == 1 || c >= 4) {
+                for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+                float L = 0.f, A = 0.f;
 #pragma unroll
                 for (int w = 0; w < NW; ++w) {
                     const float f = (sm_m[w][h] == -INFINITY) ? 0.f : fast_exp2(sm_m[w][h] - M);
-                    out += f * (c == 1 ? sm_l[w][h] : sm_acc[w][h][c - 4]);
+                    L += f * sm_l[w][h];
+                    if (c < D) A += f * sm_acc[w][h][c];
                 }
+                if (c < D) p.out[(rh0 + h) * D + c] = A * (L > 0.f ? 1.f / L : 0.f);
+                else if (p.lse) p.lse[rh0 + h] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
             }
-            pout[idx] = out;
+        } else {
+            float* pout = p.partial + static_cast<int64_t>(wg) * G * (D + 4);
+            for (int idx = threadIdx.x; idx < G * (D + 4); idx += blockDim.x) {
+                const int h = idx / (D + 4), c = idx % (D + 4);
+                float M = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+                float out = 0.f;
+                if (c == 0) {
+                    out = M;
+                } else if (c == 1 || c >= 4) {
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) {
+                        const float f = (sm_m[w][h] == -INFINITY) ? 0.f : fast_exp2(sm_m[w][h] - M);
+                        out += f * (c == 1 ? sm_l[w][h] : sm_acc[w][h][c - 4]);
+                    }
+                }
+                pout[idx] = out;
+            }
         }
     }
 }
@@ -847,6 +889,7 @@ __global__ __launch_bounds__(kCombineThreads) void attend_combine_kernel(AttnPar
         if (tid == 0 && lse) lse[rh] = -INFINITY;
         return;
     }
+    if (w1 - w0 == 1) return;                                    // its one workgroup wrote the output
     const int nslot = static_cast<int>(w1 - w0);
     const float* pp = p.partial + (w0 * G + h) * (D + 4);       // slot i at pp + i * SS
     float M = -INFINITY, L = 0.f;
@@ -1010,6 +1053,8 @@ hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st) {
     ap.dense = a.dense ? 1 : 0;
     ap.wave_plan = pairs <= kWave ? 1 : 0;
     ap.qscale = g.scale * kLog2e;
+    ap.out = a.out;
+    ap.lse = a.lse;
     if (!ap.wave_plan) {
         {
             ProfScope ps("attn_plan", 0, st);
