@@ -803,15 +803,18 @@ constexpr int kCutStage = 32768;      // candidate scores staged in LDS (128 KiB
 constexpr int kCutUpStage = 2048;     // kept parents staged in LDS with them
 constexpr int kCutBmWords = 4096;     // kept bitmap built in LDS (levels up to 131072 nodes)
 
-struct CutShared {
-    float sc[kCutStage];
-    int32_t up[kCutUpStage];
+template <int kStage, int kUpStage, int kBmWords>
+struct CutSharedT {
+    static constexpr int stage = kStage, up_stage = kUpStage, bm_words = kBmWords;
+    float sc[kStage];
+    int32_t up[kUpStage];
     union {
         uint64_t bins[kCutBins];      // the cut's first pass
-        uint32_t bm[kCutBmWords];     // then the kept bitmap
+        uint32_t bm[kBmWords];        // then the kept bitmap
     };
     BlockScratch bs;
 };
+using CutShared = CutSharedT<kCutStage, kCutUpStage, kCutBmWords>;
 
 // The candidates of one (row, head) at one level, in ascending node order:
 // k < nkids are the children of the kept parents up[0..kc), then the orphans.
@@ -829,8 +832,8 @@ struct CutCands {
 // kStaged: the candidates' scores and parents sit in LDS (read from HBM
 // once); otherwise each pass re-reads them from global memory. The two
 // variants are separate instantiations, so each only addresses one space.
-template <bool kStaged>
-__device__ __forceinline__ void cut_level(const CutParams& p, CutShared& sh, CutCands cc, int64_t rh,
+template <bool kStaged, int NW, class Sh>
+__device__ __forceinline__ void cut_level(const CutParams& p, Sh& sh, CutCands cc, int64_t rh,
                                           int64_t nc) {
     const int tid = threadIdx.x, nt = blockDim.x;
     const bool leaf = (p.li == 0);
@@ -847,8 +850,8 @@ __device__ __forceinline__ void cut_level(const CutParams& p, CutShared& sh, Cut
         for (int64_t i = tid; i < kc; i += nt) sh.up[i] = cc.up[i];
         __syncthreads();
         cc.up = sh.up;
-        // every candidate of the thread in flight at once: at most kCutStage / kCutThreads
-        constexpr int U = kCutStage / kCutThreads;
+        // every candidate of the thread in flight at once: at most stage / threads
+        constexpr int U = Sh::stage / (NW * kWave);
         float v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -887,7 +890,7 @@ __device__ __forceinline__ void cut_level(const CutParams& p, CutShared& sh, Cut
     // bitmaps to find the parents to score; the attention reads level 1
     uint32_t* bm = p.bitmap + rh * p.bm_words_total + p.bm_off;
     const int64_t words = (nc + 31) >> 5;
-    const bool lds_bm = words <= kCutBmWords;
+    const bool lds_bm = words <= Sh::bm_words;
     auto emit = [&](int64_t pos, int64_t k) {
         const int32_t node = static_cast<int32_t>(cc.node(k));
         if (kept_out) kept_out[pos] = node;
@@ -919,10 +922,10 @@ __device__ __forceinline__ void cut_level(const CutParams& p, CutShared& sh, Cut
         __syncthreads();
         m = sh.bs.wcount;
     } else {
-        mx = block_max_f(mx, sh.bs);                      // its barriers also publish the staged scores
-        const CutBoundary cb = cut_boundary(score, ncand, mx, p.top_p, sh.bins, sh.bs);
+        mx = block_max_f<NW>(mx, sh.bs);                  // its barriers also publish the staged scores
+        const CutBoundary cb = cut_boundary<NW>(score, ncand, mx, p.top_p, sh.bins, sh.bs);
         clear_bm();                                        // published by the compaction's first barrier
-        m = cut_compact(score, ncand, cb, cc.lb < 5 ? cc.lb : 5, sh.bs, emit, mark);
+        m = cut_compact<NW>(score, ncand, cb, cc.lb < 5 ? cc.lb : 5, sh.bs, emit, mark);
     }
     if (lds_bm) {
         __syncthreads();
@@ -941,8 +944,9 @@ __device__ __forceinline__ void cut_level(const CutParams& p, CutShared& sh, Cut
     }
 }
 
-__global__ __launch_bounds__(kCutThreads) void route_cut_kernel(CutParams p) {
-    __shared__ CutShared sh;
+template <int NW, class Sh>
+__global__ __launch_bounds__(NW * kWave) void route_cut_kernel(CutParams p) {
+    __shared__ Sh sh;
     const int hq = blockIdx.x, row = blockIdx.y;
     const int N = clamp_visible(p.ri, row, p.cap);
     const int64_t nc = static_cast<int64_t>(N) >> (p.lb * (p.li + 1));
@@ -960,8 +964,8 @@ __global__ __launch_bounds__(kCutThreads) void route_cut_kernel(CutParams p) {
     }
     cc.nkids = kc << p.lb;
     cc.ncand = cc.nkids + (nc - (cc.nc_up << p.lb));
-    if (cc.ncand <= kCutStage && kc <= kCutUpStage) cut_level<true>(p, sh, cc, rh, nc);
-    else cut_level<false>(p, sh, cc, rh, nc);
+    if (cc.ncand <= Sh::stage && kc <= Sh::up_stage) cut_level<true, NW>(p, sh, cc, rh, nc);
+    else cut_level<false, NW>(p, sh, cc, rh, nc);
 }
 
 // ----------------------------------------------------------------------------
@@ -988,6 +992,8 @@ constexpr int kWaveStage = 2048;        // candidate scores staged per wave: lev
 constexpr int kWaveBmWords = kWaveStage / 32 + 1;          // the level's kept bitmap, in LDS
 
 struct WaveScratch {
+    static constexpr bool staged = true;
+    static constexpr int bm_words = kWaveBmWords;
     uint64_t wpk[kWave];       // wave_resolve / wave_cut_small ranking
     uint64_t wmass[kWave];
     uint64_t wpre[kWave];
@@ -1040,14 +1046,35 @@ __device__ __forceinline__ int wave_find_digit(const uint64_t* hist, uint64_t re
     return __builtin_amdgcn_readlane(found, first);
 }
 
-// The candidates' scores are staged in the wave's LDS (a level of at most
-// kWaveStage nodes), so every pass after the load runs on LDS.
+// WS::staged: the candidates' scores are staged in the wave's LDS (a level
+// of at most kWaveStage nodes), so every pass after the load runs on LDS.
+// Otherwise every pass re-reads them from global memory, kPassU blocks of 64
+// in flight per lane; that variant keeps only the small scratch in LDS, so
+// many more waves share a compute unit.
+constexpr int kPassU = 8;
+
+struct WaveScratchU {           // the unstaged variant's scratch
+    static constexpr bool staged = false;
+    static constexpr int bm_words = 576;     // levels of up to 18432 nodes keep the bitmap in LDS
+    uint64_t wpk[kWave];
+    uint64_t wmass[kWave];
+    uint64_t wpre[kWave];
+    uint64_t bcast_u64[2];
+    uint32_t bcast_u32[2];
+    uint64_t bins[kWaveBins];
+    uint32_t list[kWave];
+    float list_s[kWave];
+    uint32_t bm[bm_words];
+};
+
+template <class WS>
 __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutParams p) {
-    __shared__ WaveScratch wsh[kWaveCutWaves];
+    constexpr bool kStaged = WS::staged;
+    __shared__ WS wsh[kWaveCutWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t rh = static_cast<int64_t>(blockIdx.x) * kWaveCutWaves + wave;
     if (rh >= p.pairs) return;                       // the whole wave: nothing below syncs the block
-    WaveScratch& ws = wsh[wave];
+    WS& ws = wsh[wave];
     const int row = static_cast<int>(rh / p.Hq);
     const int N = clamp_visible(p.ri, row, p.cap);
     const int64_t nc = static_cast<int64_t>(N) >> (p.lb * (p.li + 1));
@@ -1064,15 +1091,21 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
     }
     cc.nkids = kc << p.lb;
     cc.ncand = cc.nkids + (nc - (cc.nc_up << p.lb));
-    const int n = static_cast<int>(cc.ncand);        // <= nodes of the level <= kWaveStage
+    const int n = static_cast<int>(cc.ncand);        // staged: <= nodes of the level <= kWaveStage
     const bool leaf = (p.li == 0);
 
     int32_t* kept_out = leaf ? nullptr : p.kept + rh * p.nodes_total + p.lvl_off;
     int32_t* sel_out = leaf ? p.sel_blocks + rh * p.sel_cap : nullptr;
     int32_t* lsel_out = p.level_sel ? p.level_sel + p.lsel_off + rh * p.nodes_l : nullptr;
     uint32_t* bm = p.bitmap + rh * p.bm_words_total + p.bm_off;
-    const int64_t words = (nc + 31) >> 5;            // <= kWaveBmWords
-    for (int64_t w = lane; w < words; w += kWave) ws.bm[w] = 0u;
+    const int64_t words = (nc + 31) >> 5;
+    const bool lds_bm = words <= WS::bm_words;       // always, staged
+    if (lds_bm) {
+        for (int64_t w = lane; w < words; w += kWave) ws.bm[w] = 0u;
+    } else {
+        for (int64_t w = lane; w < words; w += kWave) bm[w] = 0u;
+        __threadfence_block();
+    }
     __builtin_amdgcn_wave_barrier();
     auto emit = [&](int64_t pos, int64_t k) {
         const int32_t node = static_cast<int32_t>(cc.node(k));
@@ -1082,7 +1115,8 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
     };
     auto mark = [&](int64_t k, uint32_t bits) {
         const int64_t node = cc.node(k);
-        atomicOr(&ws.bm[node >> 5], bits << (node & 31));
+        if (lds_bm) atomicOr(&ws.bm[node >> 5], bits << (node & 31));
+        else __hip_atomic_fetch_or(bm + (node >> 5), bits << (node & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
     };
 
     int64_t m;
@@ -1090,40 +1124,71 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
         m = wave_cut_small([&](int64_t k) -> float { return cc.sc[cc.node(k)]; }, n, p.top_p, ws,
                            [&](int64_t pos, int64_t k) { emit(pos, k); mark(k, 1u); });
     } else {
-        // every candidate's score into LDS, kStageU loads in flight per lane; the maximum
-        constexpr int kStageU = 8;
+        const int nblk = (n + kWave - 1) / kWave;
+        // blocks r0 .. r0 + kPassU - 1 of the candidates (block r holds k = 64 r + lane)
+        auto fetch_global = [&](int r0, float (&v)[kPassU]) {
+            int64_t nd[kPassU];
+#pragma unroll
+            for (int u = 0; u < kPassU; ++u) {
+                const int k = lane + (r0 + u) * kWave;
+                nd[u] = k < n ? cc.node(k) : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < kPassU; ++u) v[u] = nd[u] >= 0 ? cc.sc[nd[u]] : 0.f;
+        };
+        auto pass = [&](auto&& body) {             // body(r, score): whole waves, blocks in order
+            for (int r0 = 0; r0 < nblk; r0 += kPassU) {
+                float v[kPassU];
+                if constexpr (kStaged) {
+#pragma unroll
+                    for (int u = 0; u < kPassU; ++u) {
+                        const int k = lane + (r0 + u) * kWave;
+                        v[u] = k < n ? ws.sc[k] : 0.f;
+                    }
+                } else {
+                    fetch_global(r0, v);
+                }
+#pragma unroll
+                for (int u = 0; u < kPassU; ++u)
+                    if (r0 + u < nblk) body(r0 + u, v[u]);
+            }
+        };
+        // the maximum (staged: while the scores go to LDS)
         float mx = -INFINITY;
-        for (int kb = 0; kb < n; kb += kStageU * kWave) {
-            float v[kStageU];
+        if constexpr (kStaged) {
+            for (int r0 = 0; r0 < nblk; r0 += kPassU) {
+                float v[kPassU];
+                fetch_global(r0, v);
 #pragma unroll
-            for (int u = 0; u < kStageU; ++u) {
-                const int k = kb + u * kWave + lane;
-                v[u] = k < n ? cc.sc[cc.node(k)] : -INFINITY;
+                for (int u = 0; u < kPassU; ++u) {
+                    const int k = lane + (r0 + u) * kWave;
+                    if (k < n) {
+                        ws.sc[k] = v[u];
+                        mx = fmaxf(mx, v[u]);
+                    }
+                }
             }
-#pragma unroll
-            for (int u = 0; u < kStageU; ++u) {
-                const int k = kb + u * kWave + lane;
-                if (k < n) ws.sc[k] = v[u];
-                mx = fmaxf(mx, v[u]);
-            }
+        } else {
+            pass([&](int r, float sv) {
+                if (lane + r * kWave < n) mx = fmaxf(mx, sv);
+            });
         }
         mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_scan_max_f(mx)), 63));
         __builtin_amdgcn_wave_barrier();
-        const int nblk = (n + kWave - 1) / kWave;
         const bool take_all = p.top_p >= 1.0f;
         uint32_t kappa = 0;
         uint64_t need = 0;
         if (!take_all) {
+            // 1. masses, in total and per bin
             for (int i = lane; i < kWaveBins; i += kWave) ws.bins[i] = 0;
             __builtin_amdgcn_wave_barrier();
             uint64_t E = 0;
-            for (int r = 0; r < nblk; ++r) {                         // whole-wave updates
-                const int k = lane + r * kWave;
-                const float sv = k < n ? ws.sc[k] : mx;
-                const uint64_t F = k < n ? mass_fx(sv, mx) : 0;
+            pass([&](int r, float sv) {
+                const bool valid = lane + r * kWave < n;
+                const uint64_t F = valid ? mass_fx(sv, mx) : 0;
                 E += F;
-                wave_add_u64(reinterpret_cast<unsigned long long*>(ws.bins), wave_bin(sv, mx), F, F != 0);
-            }
+                wave_add_u64(reinterpret_cast<unsigned long long*>(ws.bins), valid ? wave_bin(sv, mx) : 0, F, F != 0);
+            });
             E = lane63_u64(wave_scan_u64(E));
             uint64_t rem = static_cast<uint64_t>(ceil(static_cast<double>(p.top_p) * static_cast<double>(E)));
             if (rem == 0) rem = 1;
@@ -1133,9 +1198,8 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
             const int bstar = wave_find_digit(ws.bins, rem, &before);
             rem -= before;
             uint32_t nm = 0;
-            for (int r = 0; r < nblk; ++r) {
+            pass([&](int r, float sv) {
                 const int k = lane + r * kWave;
-                const float sv = k < n ? ws.sc[k] : mx;
                 const bool mem = k < n && wave_bin(sv, mx) == bstar && mass_fx(sv, mx) != 0;
                 const unsigned long long bal = __ballot(mem);
                 const uint32_t pos = nm + static_cast<uint32_t>(__popcll(bal & ((1ull << lane) - 1ull)));
@@ -1144,7 +1208,7 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
                     ws.list_s[pos] = sv;
                 }
                 nm += static_cast<uint32_t>(__popcll(bal));
-            }
+            });
             __builtin_amdgcn_wave_barrier();
             if (nm <= kWave) {
                 wave_resolve(ws.list, ws.list_s, static_cast<int>(nm), mx, rem, ws);
@@ -1159,15 +1223,14 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
                     const uint32_t hmask = known ? ~0u << (32 - known) : 0u;
                     for (int i = lane; i < kWaveBins; i += kWave) ws.bins[i] = 0;
                     __builtin_amdgcn_wave_barrier();
-                    for (int r = 0; r < nblk; ++r) {
-                        const int k = lane + r * kWave;
-                        const float sv = k < n ? ws.sc[k] : mx;
+                    pass([&](int r, float sv) {
                         const uint32_t key = desc_key(sv);
-                        const bool in = k < n && wave_bin(sv, mx) == bstar && ((key ^ prefix) & hmask) == 0u;
+                        const bool in = lane + r * kWave < n && wave_bin(sv, mx) == bstar &&
+                                        ((key ^ prefix) & hmask) == 0u;
                         const uint64_t F = in ? mass_fx(sv, mx) : 0;
                         wave_add_u64(reinterpret_cast<unsigned long long*>(ws.bins), static_cast<int>((key >> shift) & 255u),
                                      F, F != 0);
-                    }
+                    });
                     __builtin_amdgcn_wave_barrier();
                     uint64_t bd;
                     const int d = wave_find_digit(ws.bins, rem, &bd);
@@ -1180,16 +1243,16 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
                 need = Fk ? (rem + Fk - 1) / Fk : 0;
             }
         }
-        // 3. stable compaction, 64 candidates (one register slot) at a time
+        // 3. stable compaction, 64 candidates (one block) at a time
         const int run_lg = p.lb < 5 ? p.lb : 5;
         const int run = 1 << run_lg;
         const unsigned long long run_mask = (1ull << run) - 1ull;
         const unsigned long long below = (1ull << lane) - 1ull;
         uint64_t lt_b = 0, tie_b = 0;
-        for (int r = 0; r < nblk; ++r) {
+        pass([&](int r, float sv) {
             const int64_t k = lane + r * kWave;
             const bool valid = k < n;
-            const uint32_t key = valid ? desc_key(ws.sc[k]) : 0u;
+            const uint32_t key = valid ? desc_key(sv) : 0u;
             const bool lt = valid && (take_all || key < kappa);
             const bool tie = valid && !take_all && key == kappa;
             const unsigned long long blt = __ballot(lt), btie = __ballot(tie);
@@ -1203,11 +1266,13 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
             }
             lt_b += __popcll(blt);
             tie_b += __popcll(btie);
-        }
+        });
         m = static_cast<int64_t>(lt_b + (tie_b < need ? tie_b : need));
     }
-    __builtin_amdgcn_wave_barrier();
-    for (int64_t w = lane; w < words; w += kWave) bm[w] = ws.bm[w];
+    if (lds_bm) {
+        __builtin_amdgcn_wave_barrier();
+        for (int64_t w = lane; w < words; w += kWave) bm[w] = ws.bm[w];
+    }
     if (lane == 0) {
         p.kept_cnt[rh * p.L + p.li] = static_cast<int32_t>(m);
         if (leaf) {
@@ -1820,8 +1885,11 @@ static int upper_from(const Geo& g) {
 }
 
 // Level li's cut from the dense-by-node scores: one workgroup per (row, query
-// head), or one wave per pair (wave = true) when the pairs are many.
-static hipError_t launch_cut(const Geo& g, const RouteArgs& a, int li, hipStream_t st, bool wave = false) {
+// head), or one wave per pair when the pairs are many (many = true): with the
+// candidates staged in the wave's LDS when the level fits (wave = true), else
+// re-read from global memory in every pass.
+static hipError_t launch_cut(const Geo& g, const RouteArgs& a, int li, hipStream_t st, bool wave = false,
+                             bool many = false) {
     const WsLayout& lay = *a.lay;
     char* ws = a.ws;
     const bool top = (li == g.L - 1);
@@ -1855,11 +1923,14 @@ static hipError_t launch_cut(const Geo& g, const RouteArgs& a, int li, hipStream
     cp.pairs = static_cast<int64_t>(a.rows) * g.Hq;
     {
         ProfScope ps("route_cut", li + 1, st);
+        const dim3 wgrid(static_cast<unsigned>((cp.pairs + kWaveCutWaves - 1) / kWaveCutWaves));
         if (wave) {
-            hipLaunchKernelGGL(route_wave_cut_kernel, dim3(static_cast<unsigned>((cp.pairs + kWaveCutWaves - 1) / kWaveCutWaves)),
-                               dim3(kWaveCutThreads), 0, st, cp);
-        } else
-            hipLaunchKernelGGL(route_cut_kernel, dim3(g.Hq, a.rows), dim3(kCutThreads), 0, st, cp);
+            hipLaunchKernelGGL(route_wave_cut_kernel<WaveScratch>, wgrid, dim3(kWaveCutThreads), 0, st, cp);
+        } else if (many) {
+            hipLaunchKernelGGL(route_wave_cut_kernel<WaveScratchU>, wgrid, dim3(kWaveCutThreads), 0, st, cp);
+        } else {
+            hipLaunchKernelGGL((route_cut_kernel<kCutWaves, CutShared>), dim3(g.Hq, a.rows), dim3(kCutThreads), 0, st, cp);
+        }
     }
     return hipGetLastError();
 }
@@ -1880,7 +1951,7 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
         hipError_t e = launch_dense_scores(g, a.ri, a.q, a.summaries, scores, 0, g.L - 1, st);
         // one wave per pair while a level's candidates fit a wave's LDS
         for (int li = g.L - 1; e == hipSuccess && li >= 0; --li)
-            e = launch_cut(g, a, li, st, g.nodes[li] <= kWaveStage);
+            e = launch_cut(g, a, li, st, g.nodes[li] <= kWaveStage, true);
         return e;
     }
 
