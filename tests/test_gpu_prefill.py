@@ -159,3 +159,45 @@ def test_many_rows_crowded_scores(kind, noise):
                 flips += check_sets(gpu_ids, cut, w.top_p, f"row {t_} head {hq} level {level}")
                 parents = gpu_ids
     say(f"  margin-exempt differences: {flips}")
+
+
+def test_many_rows_deep_levels():
+    """b = 2 puts levels of 32768 and 16384 nodes under 64 causal rows: the
+    one-wave cut re-reads their scores from global memory, and the larger
+    one keeps its kept bitmap in global memory."""
+    t = torch()
+    w = W.get_workload("tiny")
+    w.n_tokens = 65536
+    w.capacity = 65536
+    w.branching = 2
+    w.n_levels = 5
+    w.top_p = 0.9
+    T = 64
+    say(f"[many rows deep] b=2 L=5 N=65536, {T} causal rows")
+    st = Staged(w, max_t=T)
+    qn, q = st.queries(0, rows=T)
+    q_pos = (w.n_tokens - T + t.arange(T, dtype=t.int32, device="cuda")).view(1, T).contiguous()
+    sel, nsel, stats, lsel = st.route_buffers(T)
+    Z.route(st.geom, q, q_pos, st.cache.summaries, st.cache.seq_lens, w.top_p, sel, nsel, st.cache.ws,
+            level_stats=stats, level_sel=lsel)
+    t.cuda.synchronize()
+    trees = st.oracle_trees()
+    kept = {level: level_kept(st, lsel, stats, T, level) for level in range(1, w.n_levels + 1)}
+    flips = 0
+    for t_ in range(T):
+        N = w.n_tokens - T + t_ + 1
+        parents = None
+        for level in range(w.n_levels, 0, -1):
+            v, cnt, cand = kept[level]
+            gpu_ids = v[t_, 0, :cnt[t_, 0]]
+            cut = O.route_level(qn[0, t_, 0], trees[0][0][level - 1], level, parents, N, w.branching,
+                                w.n_levels, w.top_p, w.scale)
+            assert cand[t_, 0] == len(cut.ids), (t_, level, cand[t_, 0], len(cut.ids))
+            assert np.all(np.diff(gpu_ids) > 0), "kept ids must be ascending"
+            flips += check_sets(gpu_ids, cut, w.top_p, f"row {t_} level {level}")
+            parents = gpu_ids
+        # the leaf level's kept ids also arrive as sel_blocks / n_sel
+        n1 = int(nsel[0, t_, 0].item())
+        assert n1 == len(parents)
+        assert np.array_equal(np.sort(sel[0, t_, 0, :n1].cpu().numpy()), parents)
+    say(f"  margin-exempt differences: {flips}")
