@@ -867,7 +867,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
 // state. The NGRP states then merge through LDS.
 // ----------------------------------------------------------------------------
 constexpr int kCombineThreads = 1024;
-constexpr int kCombineUnroll = 8;
+constexpr int kCombineUnroll = 16;
 
 template <int D, int G>
 __global__ __launch_bounds__(kCombineThreads) void attend_combine_kernel(AttnParams p, float* out, float* lse) {
