@@ -61,8 +61,14 @@ struct ScoreParams {
     // maximum of each head's own candidates it scored and writes their scores
     // and ids in the head's candidate order; workgroup 0 of a (row, kv head)
     // clears the heads' mass bins and this level's bitmaps
-    float* pmax;               // [rows, Hq, pmax_stride], column = the workgroup's run (blockIdx.x)
+    float* pmax;               // [rows, Hq, pmax_stride], column = the workgroup's run within its pair
     int64_t pmax_stride;
+    int32_t* pruns;            // [rows, Hq]: runs (workgroups) of the head's pair
+    // waves dealt by parent counts (ScoreShape): the 1-D grid's size, 0 for a
+    // grid of runs x pairs; the pairs, and the waves each gets at least
+    int64_t bal_waves;
+    int pairs;
+    int64_t bal_need;
     unsigned long long* chist; // [rows, Hq, kCutBins]
     uint32_t* bm_cur;          // this level's kept bitmaps (row-head stride bm_words_total)
     const int32_t* rank_up;    // [rows, Hq, nodes_total]: a kept node's place in its head's kept list (level l+1)
@@ -73,19 +79,94 @@ struct ScoreParams {
     int64_t cand_stride;
 };
 
+// The pair and run of this scoring wave when the waves are dealt by parent
+// counts: lane l < pairs weighs pair l by the parents its heads kept at the
+// level above (all its slots at the top), and pair l owns waves
+// [end(l-1), end(l)) with end(l) = need (l+1) + extra * (weights of pairs
+// 0..l) / (all weights), extra = the waves beyond need per pair. Every wave
+// derives the same split from the same counts.
+// Tokens a row sees (clamp_visible) with its two loads issued together.
+__device__ __forceinline__ int score_visible(const RowInfo& ri, int row, int64_t cap) {
+    const int s = row / ri.T, t = row % ri.T;
+    const int len = ri.seq_lens[s];
+    const int pos = ri.q_pos ? ri.q_pos[row] : len - ri.T + t;
+    const int n = pos + 1;
+    const int lim = static_cast<int>(len < cap ? len : cap);
+    return n < 0 ? 0 : (n > lim ? lim : n);
+}
+
+template <int G>
+__device__ __forceinline__ void score_deal(const ScoreParams& p, int* y_out, int* run_out, int64_t* w_out,
+                                           int* n_out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const bool top = (p.li == p.L - 1);
+    uint64_t wgt = 0;
+    int nl = 0;
+    if (lane < p.pairs) {
+        // one round of loads, every address valid whatever the level: the
+        // row's length and position, and its heads' kept counts
+        const int row = lane / p.Hkv, kv = lane % p.Hkv;
+        const int sq = row / p.ri.T, t = row % p.ri.T;
+        const int32_t* pp = p.ri.q_pos ? p.ri.q_pos + row : p.ri.seq_lens + sq;
+        const int len = p.ri.seq_lens[sq];
+        const int pv = *pp;
+        const int64_t r0 = static_cast<int64_t>(row) * p.Hq + kv * G;
+        const int lup = p.li + 1 < p.L ? p.li + 1 : p.L - 1;
+        int32_t kcs[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) kcs[h] = p.kept_cnt[(r0 + h) * p.L + lup];
+        __asm__ volatile("" ::: "memory");               // not sunk into the branch below
+        const int n = (p.ri.q_pos ? pv : len - p.ri.T + t) + 1;
+        const int lim = static_cast<int>(len < p.cap ? len : p.cap);
+        nl = n < 0 ? 0 : (n > lim ? lim : n);
+        if (top) {
+            wgt = static_cast<uint64_t>((((static_cast<int64_t>(nl) >> (p.lb * (p.li + 1))) + p.b - 1) >> p.lb));
+        } else {
+#pragma unroll
+            for (int h = 0; h < G; ++h) wgt += static_cast<uint64_t>(kcs[h]);
+            wgt += 1;                                    // the incomplete parent
+        }
+    }
+    const uint64_t cum = wave_scan_u64(wgt);
+    const uint64_t tot = static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(
+                             static_cast<int>(static_cast<uint32_t>(cum)), p.pairs - 1))) |
+                         (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(
+                              static_cast<int>(static_cast<uint32_t>(cum >> 32)), p.pairs - 1))) << 32);
+    const int64_t extra = p.bal_waves - p.bal_need * p.pairs;
+    const int64_t share = tot ? static_cast<int64_t>(static_cast<uint64_t>(extra) * cum / tot)
+                              : extra * (lane + 1) / p.pairs;
+    const int end = static_cast<int>(p.bal_need * (lane + 1) + share);
+    const int gw = blockIdx.x;
+    const int y = __popcll(__ballot(lane < p.pairs && end <= gw));
+    const int start = y ? __builtin_amdgcn_readlane(end, y - 1) : 0;
+    *y_out = y;
+    *run_out = gw - start;
+    *w_out = __builtin_amdgcn_readlane(end, y) - start;
+    *n_out = __builtin_amdgcn_readlane(nl, y);
+}
+
 // Workgroup = one wave = at most 64 parent slots of one (row, kv head), taken
-// every gridDim.x-th, its active parents one at a time. The wave builds the
-// slots' masks with ballots (lane = slot): the slots some head of the group
-// kept, and for each head the slots it takes candidates from. About 2048
-// waves in all, what the chip holds at once at this kernel's register use,
+// every W-th of the pair's W waves, its active parents one at a time. The
+// wave builds the slots' masks with ballots (lane = slot): the slots some head
+// of the group kept, and for each head the slots it takes candidates from.
+// About 2048 waves in all, what the chip holds at once at this kernel's
+// register use; with few pairs they are dealt by parent counts (score_deal),
 // so a heavy pair's parents are spread as wide as the chip allows.
 template <int D, int G>
 __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams p) {
-    const int y = blockIdx.y;
-    const int run = blockIdx.x;
+    static_assert(kScoreThreads == kWave, "a scoring workgroup is one wave");
+    int y, run, N;
+    int64_t W;
+    if (p.bal_waves) {
+        score_deal<G>(p, &y, &run, &W, &N);
+    } else {
+        y = blockIdx.y;
+        run = blockIdx.x;
+        W = gridDim.x;
+        N = score_visible(p.ri, y / p.Hkv, p.cap);
+    }
     const int row = y / p.Hkv, kv = y % p.Hkv;
     const int s = row / p.T;
-    const int N = clamp_visible(p.ri, row, p.cap);
     const bool top = (p.li == p.L - 1);
     const int64_t nc = static_cast<int64_t>(N) >> (p.lb * (p.li + 1));
     const int64_t nc_up = top ? 0 : (static_cast<int64_t>(N) >> (p.lb * (p.li + 2)));
@@ -97,10 +178,10 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
     // slots are dealt to the workgroups round-robin (slot = run + i * W,
     // i < per <= 64 by the launch), so the runs of kept parents a cut leaves
     // are spread evenly over the workgroups
-    const int64_t W = gridDim.x;
     const int64_t per = (slots + W - 1) / W;
     const int64_t rh0 = static_cast<int64_t>(row) * p.Hq + kv * G;      // the group's first (row, head)
     const bool split = p.pmax != nullptr;
+    if (split && run == 0 && threadIdx.x < G) p.pruns[rh0 + threadIdx.x] = static_cast<int32_t>(W);
     if (split) {
         // the runs of the pair clear its heads' bins and this level's bitmaps between them
         const int64_t stride = W * blockDim.x, first = static_cast<int64_t>(run) * blockDim.x + threadIdx.x;
@@ -110,16 +191,42 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
             p.bm_cur[(rh0 + i / words) * p.bm_words_total + i % words] = 0u;
     }
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int nw = blockDim.x / kWave;
+    constexpr int DPL = (G <= 4) ? 16 : (G == 8 ? 8 : 4);   // dims per lane
+    constexpr int LPR = D / DPL;                             // lanes per summary row
+    constexpr int RPP = kWave / LPR;                         // rows per pass
+    constexpr int UNR = 4;                                   // passes issued together
+    static_assert(G <= LPR, "one lane per head writes the head's score");
+    const int sub = lane / LPR, part = lane % LPR;
+
+    // one round of loads: the heads' queries, the slots' kept bits at the
+    // level above (a slot past the end reads slot 0's word and is dropped),
+    // and the heads' kept counts there (the incomplete parent's children
+    // follow the kept parents' in a head's candidate order)
+    float qv[G][DPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h) load_row<DPL>(p.q + (rh0 + h) * D + part * DPL, qv[h]);
     const int64_t my_slot = run + static_cast<int64_t>(lane) * W;
     const bool have = lane < per && my_slot < slots;
     const bool orph_l = !top && have && orphans > 0 && my_slot == nc_up;
+    const int64_t ms = have ? my_slot : 0;
+    // every load below reads a valid address whatever the level, so that
+    // none sits behind a branch (which would wait for it there)
+    uint32_t word[G];
+    int32_t kc[G];
+    const int64_t wi = top ? 0 : (ms >> 5);
+    const int lup = p.li + 1 < p.L ? p.li + 1 : p.L - 1;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        word[h] = p.bm_up[(rh0 + h) * p.bm_words_total + wi];
+        kc[h] = p.kept_cnt[(rh0 + h) * p.L + lup];
+    }
+    // keeps the query loads here, in flight with the bit loads, rather than
+    // sunk past the mask test to where q is first used
+    __asm__ volatile("" ::: "memory");
     uint64_t mine[G], act = 0;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        bool k = have;
-        if (!top) k = orph_l || (have && ((p.bm_up[(rh0 + h) * p.bm_words_total + (my_slot >> 5)] >> (my_slot & 31)) & 1u));
+        const bool k = top ? have : (orph_l || (have && ((word[h] >> (ms & 31)) & 1u)));
         mine[h] = __ballot(k);
         act |= mine[h];
     }
@@ -128,54 +235,47 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
         return;
     }
 
-    constexpr int DPL = (G <= 4) ? 16 : (G == 8 ? 8 : 4);   // dims per lane
-    constexpr int LPR = D / DPL;                             // lanes per summary row
-    constexpr int RPP = kWave / LPR;                         // rows per pass
-    constexpr int UNR = 4;                                   // passes issued together
-    static_assert(G <= LPR, "one lane per head writes the head's score");
-    const int sub = lane / LPR, part = lane % LPR;
-
     const float* summ = p.summ + (static_cast<int64_t>(s) * p.Hkv + kv) * p.nodes_l * D;
     float* sc0 = p.scores + rh0 * p.nodes_total + p.lvl_off;
-    float qv[G][DPL];
     float hmx[G];                                            // per head: max over its own candidates
 #pragma unroll
     for (int h = 0; h < G; ++h) hmx[h] = -INFINITY;
-    bool have_q = false;
-    int nth = 0;
-    for (uint64_t a = act; a; a &= a - 1, ++nth) {
-        if (nth % nw != wave) continue;                      // parents dealt round-robin to the waves
-        if (!have_q) {                                       // only waves with work read q
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-                load_row<DPL>(p.q + (rh0 + h) * D + part * DPL, qv[h]);
-            have_q = true;
-        }
+    for (uint64_t a = act; a; a &= a - 1) {
         const int slot = __ffsll(static_cast<long long>(a)) - 1;
         const int64_t par = run + static_cast<int64_t>(slot) * W;
         const int64_t c0 = par << p.lb;
         const int64_t c1 = imin(c0 + p.b, nc);
-        // split: where this parent's children start in each head's candidate order
-        int64_t cbase[G];
-        if (split) {
-            const bool orph = !top && par == nc_up && orphans > 0;
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                cbase[h] = -1;
-                if ((mine[h] >> slot) & 1ull) {
-                    if (top) cbase[h] = c0;
-                    else if (orph) cbase[h] = static_cast<int64_t>(p.kept_cnt[(rh0 + h) * p.L + p.li + 1]) << p.lb;
-                    else cbase[h] = static_cast<int64_t>(p.rank_up[(rh0 + h) * p.nodes_total + p.lvl_off_up + par]) << p.lb;
-                }
-            }
-        }
-        for (int64_t cb = c0; cb < c1; cb += UNR * RPP) {
-            float x[UNR][DPL];
+        float x[UNR][DPL];
+        auto load_pass = [&](int64_t cb) {
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
                 const int64_t c = imin(cb + u * RPP + sub, c1 - 1);   // a present row; extra results are dropped
                 load_row<DPL>(summ + c * D + part * DPL, x[u]);
             }
+        };
+        load_pass(c0);
+        // split: where this parent's children start in each head's candidate
+        // order. The ranks are read together with the first summaries (without
+        // the split, and for the incomplete parent past the ranked ones, from
+        // a valid stand-in address, unused).
+        const bool orph = !top && par == nc_up && orphans > 0;
+        const int64_t pr = (top || nc_up == 0) ? 0 : imin(par, nc_up - 1);
+        const int32_t* rp = split ? p.rank_up + rh0 * p.nodes_total + p.lvl_off_up + pr : p.kept_cnt;
+        const int64_t rstride = split ? p.nodes_total : 0;
+        int32_t rk[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) rk[h] = rp[h * rstride];
+        int64_t cbase[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            cbase[h] = -1;
+            if (split && ((mine[h] >> slot) & 1ull)) {
+                if (top) cbase[h] = c0;
+                else if (orph) cbase[h] = static_cast<int64_t>(kc[h]) << p.lb;
+                else cbase[h] = static_cast<int64_t>(rk[h]) << p.lb;
+            }
+        }
+        for (int64_t cb = c0;;) {
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
                 const int64_t c = cb + u * RPP + sub;
@@ -203,21 +303,19 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
                     }
                 }
             }
+            cb += UNR * RPP;
+            if (cb >= c1) break;
+            load_pass(cb);
         }
     }
     if (split) {
-        __shared__ float red[G][kScoreThreads / kWave];
+        float m = -INFINITY;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_scan_max_f(hmx[h])), 63));
-            if (lane == 0) red[h][wave] = m;
+            const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_scan_max_f(hmx[h])), 63));
+            if (lane == h) m = mh;
         }
-        __syncthreads();
-        if (threadIdx.x < G) {
-            float m = red[threadIdx.x][0];
-            for (int w = 1; w < nw; ++w) m = fmaxf(m, red[threadIdx.x][w]);
-            p.pmax[(rh0 + threadIdx.x) * p.pmax_stride + run] = m;
-        }
+        if (lane < G) p.pmax[(rh0 + lane) * p.pmax_stride + run] = m;
     }
 }
 
@@ -1322,7 +1420,7 @@ struct SplitParams {
     int b, lb, li, L, Hq, T;
     float top_p;
     const float* pmax;
-    int pmax_n;                // scoring workgroups of the level
+    const int32_t* pruns;      // [rows, Hq]: the scoring runs of the head's pair (columns of pmax)
     int64_t pmax_stride;
     const float* cand_sc;      // [rows, Hq, cand_stride] scores in candidate order (from the scoring kernel)
     const int32_t* cand_nd;    // node ids in candidate order
@@ -1376,7 +1474,8 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_hist_kernel(SplitPa
     int64_t nc;
     const CutCands cc = split_cands(p, row, rh, &nc);
     float mx = -INFINITY;
-    for (int i = tid; i < p.pmax_n; i += kSplitThreads) mx = fmaxf(mx, p.pmax[rh * p.pmax_stride + i]);
+    const int pmax_n = p.pruns[rh];
+    for (int i = tid; i < pmax_n; i += kSplitThreads) mx = fmaxf(mx, p.pmax[rh * p.pmax_stride + i]);
     float v[kSplitPer];
 #pragma unroll
     for (int u = 0; u < kSplitPer; ++u) {
@@ -1487,7 +1586,8 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitPa
 #pragma unroll
         for (int j = 0; j < kBinsPerThread; ++j) v[j] = gb[tid * kBinsPerThread + j];
         float mx = -INFINITY;
-        for (int i = tid; i < p.pmax_n; i += nt) mx = fmaxf(mx, p.pmax[rh * p.pmax_stride + i]);
+        const int pmax_n = p.pruns[rh];
+        for (int i = tid; i < pmax_n; i += nt) mx = fmaxf(mx, p.pmax[rh * p.pmax_stride + i]);
 #pragma unroll
         for (int j = 0; j < kBinsPerThread; ++j) lsum += v[j];
         mx = block_max_f<kSplitWaves>(mx, bs);
@@ -2023,21 +2123,27 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
         // parent slots of the level: blocks of b nodes at the top; below, every
         // node of level l+1 plus the incomplete one
         const int64_t slots = top ? (g.nodes[li] + g.b - 1) / g.b : g.nodes[li + 1] + 1;
-        const int64_t gx = score_groups(slots, pairs);
+        const ScoreShape shp = score_shape(slots, pairs);
+        sp.kept_cnt = kept_cnt;
+        sp.pairs = static_cast<int>(pairs);
+        sp.bal_waves = shp.balanced ? shp.waves : 0;
+        sp.bal_need = shp.need;
+        const dim3 sgrid = shp.balanced ? dim3(static_cast<unsigned>(shp.waves), 1)
+                                        : dim3(static_cast<unsigned>(shp.waves), static_cast<unsigned>(pairs));
         if (lay.split) {
             sp.pmax = reinterpret_cast<float*>(ws + lay.pmax);
             sp.pmax_stride = lay.pmax_stride;
+            sp.pruns = reinterpret_cast<int32_t*>(ws + lay.pruns);
             sp.chist = reinterpret_cast<unsigned long long*>(ws + lay.chist);
             sp.bm_cur = bitmap + lay.bm_off[li];
             sp.rank_up = reinterpret_cast<const int32_t*>(ws + lay.rank);
             sp.lvl_off_up = top ? 0 : g.sel_off[li + 1];
-            sp.kept_cnt = kept_cnt;
             sp.cand_sc = reinterpret_cast<float*>(ws + lay.cand_sc);
             sp.cand_nd = reinterpret_cast<int32_t*>(ws + lay.cand_nd);
             sp.cand_stride = lay.cand_stride;
         }
-        hipError_t e = (g.D == 128) ? launch_score_g<128>(g.G, dim3(static_cast<unsigned>(gx), pairs), sp, st)
-                                    : launch_score_g<64>(g.G, dim3(static_cast<unsigned>(gx), pairs), sp, st);
+        hipError_t e = (g.D == 128) ? launch_score_g<128>(g.G, sgrid, sp, st)
+                                    : launch_score_g<64>(g.G, sgrid, sp, st);
         if (e != hipSuccess) return e;
 
         if (lay.split) {
@@ -2069,7 +2175,7 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
             xp.T = a.ri.T;
             xp.top_p = a.top_p;
             xp.pmax = reinterpret_cast<const float*>(ws + lay.pmax);
-            xp.pmax_n = static_cast<int>(gx);
+            xp.pruns = reinterpret_cast<const int32_t*>(ws + lay.pruns);
             xp.pmax_stride = lay.pmax_stride;
             xp.cand_sc = reinterpret_cast<const float*>(ws + lay.cand_sc);
             xp.cand_nd = reinterpret_cast<const int32_t*>(ws + lay.cand_nd);

@@ -118,7 +118,7 @@ WsLayout layout(const Geo& g, int rows) {
         int64_t pm = 1;
         for (int l = 0; l < g.L; ++l) {
             const int64_t slots = (l == g.L - 1) ? (g.nodes[l] + g.b - 1) / g.b : g.nodes[l + 1] + 1;
-            pm = std::max<int64_t>(pm, score_groups(slots, static_cast<int64_t>(R) * g.Hkv));
+            pm = std::max<int64_t>(pm, score_shape(slots, static_cast<int64_t>(R) * g.Hkv).max_runs);
         }
         L.cand_stride = cand;
         L.pmax_stride = pm;
@@ -129,6 +129,7 @@ WsLayout layout(const Geo& g, int rows) {
         L.srt_k = take(R * g.Hq * static_cast<size_t>(cand) * 4);
         L.srt_s = take(R * g.Hq * static_cast<size_t>(cand) * 4);
         L.pmax = take(R * g.Hq * static_cast<size_t>(pm) * 4);
+        L.pruns = take(R * g.Hq * 4);
         L.chist = take(R * g.Hq * static_cast<size_t>(kCutBins) * 8);
         L.cum = take(R * g.Hq * static_cast<size_t>(slices) * (kCutBins + 1) * 4);
     }

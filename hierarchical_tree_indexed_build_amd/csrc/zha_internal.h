@@ -27,6 +27,34 @@ inline int64_t score_groups(int64_t slots, int64_t pairs) {
     w = w > need ? w : need;
     return w > 0 ? w : 1;
 }
+
+// Launch shape of a level's scoring. With at most 64 (row, kv head) pairs the
+// waves are dealt out in the kernel by each pair's parent count (the kept
+// counts of the level above), `need` at least per pair so that no wave holds
+// more than 64 slots: the heavy pairs, whose parents would otherwise queue up
+// one after another in a few waves, get most of the chip. With more pairs
+// every pair gets score_groups waves (a grid of runs x pairs).
+struct ScoreShape {
+    bool balanced;
+    int64_t waves;      // balanced: the 1-D grid; otherwise runs per pair
+    int64_t need;       // balanced: waves every pair gets at least
+    int64_t max_runs;   // most waves one pair can get (columns of the split cut's maxima)
+};
+inline ScoreShape score_shape(int64_t slots, int64_t pairs) {
+    ScoreShape s{};
+    if (pairs <= 64) {
+        s.balanced = true;
+        s.need = slots > 0 ? (slots + 63) / 64 : 1;
+        s.waves = kScoreWaves > 2 * s.need * pairs ? kScoreWaves : 2 * s.need * pairs;
+        s.max_runs = s.waves - (pairs - 1) * s.need;
+    } else {
+        s.balanced = false;
+        s.waves = score_groups(slots, pairs);
+        s.need = s.waves;
+        s.max_runs = s.waves;
+    }
+    return s;
+}
 constexpr int kCutBins = 2048;         // mass bins of a cut's first pass
 constexpr int kSplitSlice = 2048;      // candidates per workgroup of the split cut
 constexpr int kSplitSliceLog2 = 11;
@@ -70,6 +98,7 @@ struct WsLayout {
     int64_t cand_stride;
     size_t pmax;          // float  [rows, Hq, pmax_stride] per scoring workgroup maxima of a level
     int64_t pmax_stride;
+    size_t pruns;         // int32  [rows, Hq] scoring workgroups of the head's (row, kv head) pair
     size_t chist;         // uint64 [rows, Hq, kCutBins] a level's mass per bin
     size_t cum;           // uint32 [rows, Hq, slice_stride, kCutBins + 1] per slice, candidates before each bin
     int64_t slice_stride;
