@@ -171,14 +171,6 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
     const int64_t nc = static_cast<int64_t>(N) >> (p.lb * (p.li + 1));
     const int64_t nc_up = top ? 0 : (static_cast<int64_t>(N) >> (p.lb * (p.li + 2)));
     const int64_t orphans = nc - (nc_up << p.lb);
-    // parent slots: at the top, blocks of b nodes; below, the complete parents
-    // (scored when some head of the group kept them) and the incomplete parent
-    // holding the orphans
-    const int64_t slots = top ? ((nc + p.b - 1) >> p.lb) : (nc_up + (orphans > 0 ? 1 : 0));
-    // slots are dealt to the workgroups round-robin (slot = run + i * W,
-    // i < per <= 64 by the launch), so the runs of kept parents a cut leaves
-    // are spread evenly over the workgroups
-    const int64_t per = (slots + W - 1) / W;
     const int64_t rh0 = static_cast<int64_t>(row) * p.Hq + kv * G;      // the group's first (row, head)
     const bool split = p.pmax != nullptr;
     if (split && run == 0 && threadIdx.x < G) p.pruns[rh0 + threadIdx.x] = static_cast<int32_t>(W);
@@ -198,78 +190,86 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
     static_assert(G <= LPR, "one lane per head writes the head's score");
     const int sub = lane / LPR, part = lane % LPR;
 
-    // one round of loads: the heads' queries, the slots' kept bits at the
-    // level above (a slot past the end reads slot 0's word and is dropped),
-    // and the heads' kept counts there (the incomplete parent's children
-    // follow the kept parents' in a head's candidate order)
+    // The pair's active parents, in node order: at the top every block of b
+    // nodes; below, the complete parents some head of the group kept at the
+    // level above, then the incomplete parent holding the orphans (taken by
+    // every head). The wave takes active parents run, run + W, run + 2W, ...,
+    // so a pair's parents spread evenly over its waves however the cut
+    // clustered them. Below the top the wave finds them from the union of
+    // the heads' kept bits, kWpl words a lane per pass.
+    constexpr int kWpl = 8;
+    const int64_t nwords = top ? 0 : (nc_up + 31) >> 5;
+    // first round of loads, every address valid whatever the level: the
+    // heads' queries, the first pass's kept bits, and the heads' kept counts
+    // at the level above (the incomplete parent's children follow the kept
+    // parents' in a head's candidate order)
     float qv[G][DPL];
 #pragma unroll
     for (int h = 0; h < G; ++h) load_row<DPL>(p.q + (rh0 + h) * D + part * DPL, qv[h]);
-    const int64_t my_slot = run + static_cast<int64_t>(lane) * W;
-    const bool have = lane < per && my_slot < slots;
-    const bool orph_l = !top && have && orphans > 0 && my_slot == nc_up;
-    const int64_t ms = have ? my_slot : 0;
-    // every load below reads a valid address whatever the level, so that
-    // none sits behind a branch (which would wait for it there)
-    uint32_t word[G];
-    int32_t kc[G];
-    const int64_t wi = top ? 0 : (ms >> 5);
     const int lup = p.li + 1 < p.L ? p.li + 1 : p.L - 1;
+    int32_t kc[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        word[h] = p.bm_up[(rh0 + h) * p.bm_words_total + wi];
-        kc[h] = p.kept_cnt[(rh0 + h) * p.L + lup];
-    }
-    // keeps the query loads here, in flight with the bit loads, rather than
-    // sunk past the mask test to where q is first used
-    __asm__ volatile("" ::: "memory");
-    uint64_t mine[G], act = 0;
+    for (int h = 0; h < G; ++h) kc[h] = p.kept_cnt[(rh0 + h) * p.L + lup];
+    uint32_t u[kWpl];
+    auto load_union = [&](int64_t w0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const bool k = top ? have : (orph_l || (have && ((word[h] >> (ms & 31)) & 1u)));
-        mine[h] = __ballot(k);
-        act |= mine[h];
-    }
-    if (!act) {
-        if (split && threadIdx.x < G) p.pmax[(rh0 + threadIdx.x) * p.pmax_stride + run] = -INFINITY;
-        return;
-    }
+        for (int k = 0; k < kWpl; ++k) {
+            const int64_t wd = w0 + static_cast<int64_t>(lane) * kWpl + k;
+            const int64_t wc = wd < nwords ? wd : 0;
+            uint32_t x = 0;
+#pragma unroll
+            for (int h = 0; h < G; ++h) x |= p.bm_up[(rh0 + h) * p.bm_words_total + wc];
+            // only bits of complete parents count
+            const int64_t lo = wd << 5;
+            const uint32_t valid = wd >= nwords ? 0u : (nc_up - lo >= 32 ? ~0u : ((1u << (nc_up - lo)) - 1u));
+            u[k] = x & valid;
+        }
+    };
+    load_union(0);
+    __asm__ volatile("" ::: "memory");      // keeps the loads above here, in one round
 
     const float* summ = p.summ + (static_cast<int64_t>(s) * p.Hkv + kv) * p.nodes_l * D;
     float* sc0 = p.scores + rh0 * p.nodes_total + p.lvl_off;
     float hmx[G];                                            // per head: max over its own candidates
 #pragma unroll
     for (int h = 0; h < G; ++h) hmx[h] = -INFINITY;
-    for (uint64_t a = act; a; a &= a - 1) {
-        const int slot = __ffsll(static_cast<long long>(a)) - 1;
-        const int64_t par = run + static_cast<int64_t>(slot) * W;
+    // scores parent par's children for all G heads; the heads of `hm` (bit h)
+    // take them as candidates (read with the summaries when the split cut
+    // needs them: all heads for the incomplete parent and at the top)
+    auto score_parent = [&](int64_t par, bool every) {
         const int64_t c0 = par << p.lb;
         const int64_t c1 = imin(c0 + p.b, nc);
         float x[UNR][DPL];
         auto load_pass = [&](int64_t cb) {
 #pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                const int64_t c = imin(cb + u * RPP + sub, c1 - 1);   // a present row; extra results are dropped
-                load_row<DPL>(summ + c * D + part * DPL, x[u]);
+            for (int u2 = 0; u2 < UNR; ++u2) {
+                const int64_t c = imin(cb + u2 * RPP + sub, c1 - 1);   // a present row; extra results are dropped
+                load_row<DPL>(summ + c * D + part * DPL, x[u2]);
             }
         };
         load_pass(c0);
-        // split: where this parent's children start in each head's candidate
-        // order. The ranks are read together with the first summaries (without
+        // split: which heads took the parent and where its children start in
+        // each head's candidate order, read with the first summaries (without
         // the split, and for the incomplete parent past the ranked ones, from
-        // a valid stand-in address, unused).
-        const bool orph = !top && par == nc_up && orphans > 0;
+        // valid stand-in addresses, unused)
+        const bool orph = !top && par == nc_up;
         const int64_t pr = (top || nc_up == 0) ? 0 : imin(par, nc_up - 1);
         const int32_t* rp = split ? p.rank_up + rh0 * p.nodes_total + p.lvl_off_up + pr : p.kept_cnt;
         const int64_t rstride = split ? p.nodes_total : 0;
+        const uint32_t* bp = split ? p.bm_up + rh0 * p.bm_words_total + (pr >> 5) : p.bm_up;
+        const int64_t bstride = split ? p.bm_words_total : 0;
         int32_t rk[G];
+        uint32_t bw[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) rk[h] = rp[h * rstride];
+        for (int h = 0; h < G; ++h) {
+            rk[h] = rp[h * rstride];
+            bw[h] = bp[h * bstride];
+        }
         int64_t cbase[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             cbase[h] = -1;
-            if (split && ((mine[h] >> slot) & 1ull)) {
+            if (split && (every || ((bw[h] >> (pr & 31)) & 1u))) {
                 if (top) cbase[h] = c0;
                 else if (orph) cbase[h] = static_cast<int64_t>(kc[h]) << p.lb;
                 else cbase[h] = static_cast<int64_t>(rk[h]) << p.lb;
@@ -277,14 +277,14 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
         }
         for (int64_t cb = c0;;) {
 #pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                const int64_t c = cb + u * RPP + sub;
+            for (int u2 = 0; u2 < UNR; ++u2) {
+                const int64_t c = cb + u2 * RPP + sub;
                 float acc[G];
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     float t = 0.f;
 #pragma unroll
-                    for (int e = 0; e < DPL; ++e) t = fmaf(qv[h][e], x[u][e], t);
+                    for (int e = 0; e < DPL; ++e) t = fmaf(qv[h][e], x[u2][e], t);
                     acc[h] = fast_group_sum<LPR>(t);
                 }
                 if (c < c1) {
@@ -307,6 +307,48 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
             if (cb >= c1) break;
             load_pass(cb);
         }
+    };
+
+    int64_t j = run;                       // the next active parent this wave takes
+    if (top) {
+        const int64_t blocks = (nc + p.b - 1) >> p.lb;
+        for (; j < blocks; j += W) score_parent(j, true);
+    } else {
+        int64_t base = 0;                  // active parents before this pass
+        for (int64_t w0 = 0; w0 < nwords; w0 += static_cast<int64_t>(kWave) * kWpl) {
+            if (w0) load_union(w0);
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int k = 0; k < kWpl; ++k) cnt += __popc(u[k]);
+            const uint64_t incl = wave_scan_u64(cnt);
+            const int64_t pass_n = static_cast<int64_t>(lane63_u64(incl));
+            for (; j < base + pass_n; j += W) {
+                // the lane whose words hold active parent j, then the word and the bit
+                const uint64_t rel = static_cast<uint64_t>(j - base);
+                const int L = __popcll(__ballot(incl <= rel));
+                const uint64_t before = L ? static_cast<uint64_t>(
+                    static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(incl)), L - 1))) : 0;
+                uint32_t r = static_cast<uint32_t>(rel - before);
+                int64_t par = -1;
+#pragma unroll
+                for (int k = 0; k < kWpl; ++k) {
+                    uint32_t xw = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u[k]), L));
+                    const uint32_t c = static_cast<uint32_t>(__popc(xw));
+                    if (par < 0) {
+                        if (r < c) {
+                            for (uint32_t i = 0; i < r; ++i) xw &= xw - 1u;
+                            par = ((w0 + static_cast<int64_t>(L) * kWpl + k) << 5) + __builtin_ctz(xw);
+                        } else {
+                            r -= c;
+                        }
+                    }
+                }
+                score_parent(par, false);
+            }
+            base += pass_n;
+        }
+        // the incomplete parent is active parent `base`
+        if (orphans > 0 && j == base) score_parent(nc_up, true);
     }
     if (split) {
         float m = -INFINITY;
