@@ -178,13 +178,20 @@ __global__ __launch_bounds__(1024) void append_fused_kernel(FusedParams p) {
         const int64_t dst0 = (bh * p.cap + len) * row_bytes;
         const int64_t src0 = bh * p.t_new * row_bytes;
         for (int64_t o = lane * 16; o < nbytes; o += kWave * 16) {
-            *reinterpret_cast<uint4*>(p.K + dst0 + o) = *reinterpret_cast<const uint4*>(p.kn + src0 + o);
-            *reinterpret_cast<uint4*>(p.V + dst0 + o) = *reinterpret_cast<const uint4*>(p.vn + src0 + o);
+            // both loads before either store (the compiler cannot tell the
+            // new rows from the cache apart)
+            const uint4 kx = *reinterpret_cast<const uint4*>(p.kn + src0 + o);
+            const uint4 vx = *reinterpret_cast<const uint4*>(p.vn + src0 + o);
+            *reinterpret_cast<uint4*>(p.K + dst0 + o) = kx;
+            *reinterpret_cast<uint4*>(p.V + dst0 + o) = vx;
         }
-        __threadfence();
         for (int l = 0; l < p.L; ++l) {
             const int64_t lo = len / p.span[l], hi = (len + p.t_new) / p.span[l];
             if (lo >= hi) break;      // nothing completes here, so nothing above either
+            // what the wave wrote last (the new rows, or the level below's
+            // summaries) is read back next, by other lanes; a step that
+            // completes no node needs no fence
+            __threadfence();
             float* lvl = p.summaries + p.sum_off[l];
             const float* r = p.ref_q + (static_cast<int64_t>(l) * p.Hkv + h) * D;
             for (int64_t i = lo; i < hi; ++i) {
@@ -197,7 +204,6 @@ __global__ __launch_bounds__(1024) void append_fused_kernel(FusedParams p) {
                     reduce_node_wave<float, B, D>(ch, r, p.scale, o, lane);
                 }
             }
-            __threadfence();
         }
     }
     __syncthreads();
