@@ -74,8 +74,11 @@ __global__ __launch_bounds__(256) void attn_bitmap_kernel(BitmapParams p) {
 // union of the g heads' level-1 bitmaps, plus the sink chunk and the current
 // chunk, is compacted in ascending chunk order into (chunk, head mask) items.
 // A segment's first item position is the popcount of the union before it,
-// which each workgroup takes itself from the (few) earlier words, so the
-// segments of a pair run in parallel. Each thread owns one word.
+// which each workgroup takes itself from the (few) earlier words, all its
+// threads counting, so the segments of a pair run in parallel. The first
+// wave owns the segment's words, one a lane: a segment is one wave's worth
+// of scattered item stores, so a dense stretch of kept chunks spreads over
+// many compute units.
 // ----------------------------------------------------------------------------
 struct ItemsParams {
     RowInfo ri;
@@ -89,7 +92,7 @@ struct ItemsParams {
 };
 
 constexpr int kItemsThreads = 256;
-constexpr int kItemsSegWords = kItemsThreads;   // one word per thread
+constexpr int kItemsSegWords = kWave;           // one word per lane of the first wave
 
 template <int G>
 __global__ __launch_bounds__(kItemsThreads) void attn_items_kernel(ItemsParams p) {
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(kItemsThreads) void attn_items_kernel(ItemsParams p
     const int64_t w0 = static_cast<int64_t>(seg) * kItemsSegWords;
     const int64_t wd = w0 + tid;
     uint32_t heads[G];
-    const uint32_t mine = wd < words ? word(wd, heads) : 0u;
+    const uint32_t mine = (tid < kItemsSegWords && wd < words) ? word(wd, heads) : 0u;
     // items before the segment
     uint64_t pre = 0;
 #pragma unroll 4
