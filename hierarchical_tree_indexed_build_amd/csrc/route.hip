@@ -1904,17 +1904,43 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
     load_row<DPL>(p.q + rh * D + part * DPL, qv);
 
     int64_t npar = 0;                          // kept nodes of the level above
+    int32_t par0 = -1;                         // their one id when a lone candidate was kept (not in LDS)
     for (int li = p.L - 1; li >= p.li_lo; --li) {
         const bool top = (li == p.L - 1);
         const int64_t nc = static_cast<int64_t>(N) >> (p.lb * (li + 1));
         const int64_t nc_up = top ? 0 : (static_cast<int64_t>(N) >> (p.lb * (li + 2)));
         const int64_t nkids = npar << p.lb;
         const int64_t ncand = nkids + (nc - (nc_up << p.lb));   // <= nc <= nodes[li] <= kUpperNodes
+        if (ncand == 1) {
+            // A lone candidate carries the whole mass and is kept unscored, with
+            // no block step. With b >= 2 a kept parent brings b candidates, so
+            // the lone one is the level's first node past the complete parents'
+            // children (at the top: node 0).
+            const int32_t node = static_cast<int32_t>(nc_up << p.lb);
+            uint32_t* bmg = p.bitmap + rh * p.bm_words_total + p.bm_off[li];
+            const int64_t words = (nc + 31) >> 5;
+            for (int64_t w = tid; w < words; w += nt) bmg[w] = (w == (node >> 5)) ? (1u << (node & 31)) : 0u;
+            if (tid == 0) {
+                p.kept[rh * p.nodes_total + p.sel_off[li]] = node;
+                if (p.rank) p.rank[rh * p.nodes_total + p.sel_off[li] + node] = 0;
+                if (p.level_sel) p.level_sel[p.rows * p.Hq * p.sel_off[li] + rh * p.nodes[li]] = node;
+                p.kept_cnt[rh * p.L + li] = 1;
+                if (p.level_stats) {
+                    p.level_stats[(rh * p.L + li) * 2 + 0] = 1;
+                    p.level_stats[(rh * p.L + li) * 2 + 1] = 1;
+                }
+            }
+            npar = 1;
+            par0 = node;
+            continue;
+        }
         for (int64_t k = tid; k < ncand; k += nt) {
-            sh.cid[k] = static_cast<int32_t>(k < nkids ? ((static_cast<int64_t>(sh.par[k >> p.lb]) << p.lb) |
-                                                          (k & (p.b - 1)))
+            const int64_t pk = k >> p.lb;
+            const int32_t par = par0 >= 0 ? par0 : sh.par[pk];
+            sh.cid[k] = static_cast<int32_t>(k < nkids ? ((static_cast<int64_t>(par) << p.lb) | (k & (p.b - 1)))
                                                        : (nc_up << p.lb) + (k - nkids));
         }
+        par0 = -1;
         const int64_t words = (nc + 31) >> 5;
         for (int64_t w = tid; w < words; w += nt) sh.bm[w] = 0u;
         __syncthreads();
@@ -1922,8 +1948,7 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
         // ---- score the candidates: a row per LPR lanes, RPP rows per wave pass ----
         const float* summ = p.summaries + p.sum_off[li] + (static_cast<int64_t>(s) * p.Hkv + kv) * p.nodes[li] * D;
         float mx = -INFINITY;
-        // a lone candidate carries the whole mass and is kept unscored
-        for (int64_t kb = static_cast<int64_t>(wave) * RPP * UNR; ncand > 1 && kb < ncand; kb += static_cast<int64_t>(nw) * RPP * UNR) {
+        for (int64_t kb = static_cast<int64_t>(wave) * RPP * UNR; kb < ncand; kb += static_cast<int64_t>(nw) * RPP * UNR) {
             float x[UNR][DPL];
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
@@ -1960,14 +1985,7 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
             atomicOr(&sh.bm[node >> 5], bits << (node & 31));
         };
         int64_t m;
-        if (ncand == 1) {
-            if (tid == 0) {
-                emit(0, 0);
-                mark(0, 1u);
-            }
-            __syncthreads();
-            m = 1;
-        } else if (ncand <= kWave) {           // one wave, no block steps
+        if (ncand <= kWave) {                  // one wave, no block steps
             __syncthreads();                   // publishes sc[]
             if (wave == 0) {
                 const int mw = wave_cut_small(score, static_cast<int>(ncand), p.top_p, sh.bs,
