@@ -1475,6 +1475,32 @@ struct SplitParams {
     int64_t slice_stride;
 };
 
+// This thread's share of the maximum over a head's scoring maxima (columns
+// [0, pruns[rh]) of its pmax row). When the row stride allows, every column
+// is loaded at once, in the same round as the count (columns past it hold
+// stale values and are masked), rather than after it.
+template <int NT>
+__device__ __forceinline__ float split_pmax(const SplitParams& p, int64_t rh, int tid) {
+    constexpr int kSpec = 8;
+    const float* col = p.pmax + rh * p.pmax_stride;
+    const int n = p.pruns[rh];
+    float mx = -INFINITY;
+    if (p.pmax_stride <= static_cast<int64_t>(kSpec) * NT) {
+        float v[kSpec];
+#pragma unroll
+        for (int j = 0; j < kSpec; ++j) {
+            const int64_t i = tid + static_cast<int64_t>(j) * NT;
+            v[j] = col[i < p.pmax_stride ? i : 0];
+        }
+#pragma unroll
+        for (int j = 0; j < kSpec; ++j)
+            if (tid + j * NT < n) mx = fmaxf(mx, v[j]);
+        return mx;
+    }
+    for (int i = tid; i < n; i += NT) mx = fmaxf(mx, col[i]);
+    return mx;
+}
+
 __device__ __forceinline__ CutCands split_cands(const SplitParams& p, int row, int64_t rh, int64_t* nc_out) {
     const int N = clamp_visible(p.ri, row, p.cap);
     const int64_t nc = static_cast<int64_t>(N) >> (p.lb * (p.li + 1));
@@ -1515,9 +1541,7 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_hist_kernel(SplitPa
     // issued together: the candidate count, the scoring maxima, the slice's scores
     int64_t nc;
     const CutCands cc = split_cands(p, row, rh, &nc);
-    float mx = -INFINITY;
-    const int pmax_n = p.pruns[rh];
-    for (int i = tid; i < pmax_n; i += kSplitThreads) mx = fmaxf(mx, p.pmax[rh * p.pmax_stride + i]);
+    float mx = split_pmax<kSplitThreads>(p, rh, tid);
     float v[kSplitPer];
 #pragma unroll
     for (int u = 0; u < kSplitPer; ++u) {
@@ -1627,9 +1651,7 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitPa
         uint64_t v[kBinsPerThread], lsum = 0;
 #pragma unroll
         for (int j = 0; j < kBinsPerThread; ++j) v[j] = gb[tid * kBinsPerThread + j];
-        float mx = -INFINITY;
-        const int pmax_n = p.pruns[rh];
-        for (int i = tid; i < pmax_n; i += nt) mx = fmaxf(mx, p.pmax[rh * p.pmax_stride + i]);
+        float mx = split_pmax<kSplitThreads>(p, rh, tid);
 #pragma unroll
         for (int j = 0; j < kBinsPerThread; ++j) lsum += v[j];
         mx = block_max_f<kSplitWaves>(mx, bs);
