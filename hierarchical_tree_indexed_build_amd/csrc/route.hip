@@ -1502,7 +1502,12 @@ __device__ __forceinline__ float split_pmax(const SplitParams& p, int64_t rh, in
 }
 
 __device__ __forceinline__ CutCands split_cands(const SplitParams& p, int row, int64_t rh, int64_t* nc_out) {
+    // one round of loads, every address valid whatever the level: the row's
+    // length and position, and the head's kept count at the level above
+    const bool top = (p.li == p.L - 1);
     const int N = clamp_visible(p.ri, row, p.cap);
+    const int32_t kc_up = p.kept_cnt[rh * p.L + (top ? p.li : p.li + 1)];
+    __asm__ volatile("" ::: "memory");         // issued here, not sunk into the branches below
     const int64_t nc = static_cast<int64_t>(N) >> (p.lb * (p.li + 1));
     CutCands cc;
     cc.sc = p.scores + rh * p.nodes_total + p.lvl_off;
@@ -1510,9 +1515,9 @@ __device__ __forceinline__ CutCands split_cands(const SplitParams& p, int row, i
     cc.up = nullptr;
     cc.nc_up = 0;
     int64_t kc = 0;
-    if (p.li != p.L - 1) {
+    if (!top) {
         cc.nc_up = static_cast<int64_t>(N) >> (p.lb * (p.li + 2));
-        kc = p.kept_cnt[rh * p.L + p.li + 1];
+        kc = kc_up;
         cc.up = p.kept + rh * p.nodes_total + p.lvl_off_up;
     }
     cc.nkids = kc << p.lb;
@@ -1636,6 +1641,13 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitPa
         sv[j] = k < p.cand_stride ? p.cand_sc[cbase + k] : 0.f;
         nd[j] = k < p.cand_stride ? p.cand_nd[cbase + k] : 0;
     }
+    // and, in the same round, the head's mass bins and scoring maxima (read
+    // whether or not the cut needs them)
+    const unsigned long long* gb = p.chist + rh * kCutBins;
+    uint64_t v[kBinsPerThread], lsum = 0;
+#pragma unroll
+    for (int j = 0; j < kBinsPerThread; ++j) v[j] = gb[tid * kBinsPerThread + j];
+    float mx = split_pmax<kSplitThreads>(p, rh, tid);
     const int64_t ncand = cc.ncand;
     const int nsl = static_cast<int>((ncand + kSplitSlice - 1) >> kSplitSliceLog2);
     if (sl >= nsl && sl != 0) return;
@@ -1647,11 +1659,6 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitPa
         sh.s_tie[i] = 0u;
     }
     if (!take_all) {
-        const unsigned long long* gb = p.chist + rh * kCutBins;
-        uint64_t v[kBinsPerThread], lsum = 0;
-#pragma unroll
-        for (int j = 0; j < kBinsPerThread; ++j) v[j] = gb[tid * kBinsPerThread + j];
-        float mx = split_pmax<kSplitThreads>(p, rh, tid);
 #pragma unroll
         for (int j = 0; j < kBinsPerThread; ++j) lsum += v[j];
         mx = block_max_f<kSplitWaves>(mx, bs);

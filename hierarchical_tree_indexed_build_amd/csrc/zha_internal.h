@@ -118,11 +118,13 @@ __host__ __device__ inline int row_visible(const RowInfo& ri, int row) {
     return pos + 1;
 }
 
-// Tokens a row sees, clamped to its sequence's length and the capacity.
+// Tokens a row sees, clamped to its sequence's length and the capacity. Its
+// two loads (length, and position or again the length) go out together.
 __device__ __forceinline__ int clamp_visible(const RowInfo& ri, int row, int64_t cap) {
-    const int s = row / ri.T;
-    const int n = row_visible(ri, row);
-    const int64_t len = ri.seq_lens[s];
+    const int s = row / ri.T, t = row % ri.T;
+    const int len = ri.seq_lens[s];
+    const int pv = *(ri.q_pos ? ri.q_pos + row : ri.seq_lens + s);
+    const int n = (ri.q_pos ? pv : len - ri.T + t) + 1;
     const int lim = static_cast<int>(len < cap ? len : cap);
     return n < 0 ? 0 : (n > lim ? lim : n);
 }
