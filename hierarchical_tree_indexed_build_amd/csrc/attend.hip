@@ -70,15 +70,18 @@ __global__ __launch_bounds__(256) void attn_bitmap_kernel(BitmapParams p) {
 
 // ----------------------------------------------------------------------------
 // the group's attention items
-// Workgroup = (segment of kItemsSegWords bitmap words, (row, kv head)). The
+// Workgroup = (segment of seg_words bitmap words, (row, kv head)). The
 // union of the g heads' level-1 bitmaps, plus the sink chunk and the current
 // chunk, is compacted in ascending chunk order into (chunk, head mask) items.
 // A segment's first item position is the popcount of the union before it,
 // which each workgroup takes itself from the (few) earlier words, all its
-// threads counting, so the segments of a pair run in parallel. The first
-// wave owns the segment's words, one a lane: a segment is one wave's worth
-// of scattered item stores, so a dense stretch of kept chunks spreads over
-// many compute units.
+// threads counting, so the segments of a pair run in parallel. A thread owns
+// one word of the segment. With few pairs a segment is 64 words, owned by
+// the first wave: one wave's worth of scattered item stores, so a dense
+// stretch of kept chunks spreads over many compute units. With many pairs
+// (the rows of a prefill chunk) the chip is full anyway and a segment is
+// 256 words, one per thread, so that fewer workgroups re-count the words
+// before theirs.
 // ----------------------------------------------------------------------------
 struct ItemsParams {
     RowInfo ri;
@@ -89,10 +92,12 @@ struct ItemsParams {
     int32_t* acnt;             // [rows, Hkv]
     int64_t cap;
     int lb, Hq, Hkv;
+    int seg_words;             // words per segment: kItemsSegFew or kItemsThreads
 };
 
 constexpr int kItemsThreads = 256;
-constexpr int kItemsSegWords = kWave;           // one word per lane of the first wave
+constexpr int kItemsSegFew = kWave;             // with few pairs: one word per lane of the first wave
+constexpr int kItemsFewPairs = 64;
 
 template <int G>
 __global__ __launch_bounds__(kItemsThreads) void attn_items_kernel(ItemsParams p) {
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(kItemsThreads) void attn_items_kernel(ItemsParams p
     const int64_t nblk = N > 0 ? ((static_cast<int64_t>(N) - 1) >> p.lb) + 1 : 0;  // chunks incl. the current one
     const int64_t cur = nblk - 1;
     const int64_t words = (nblk + 31) >> 5;
-    const int64_t nseg = (words + kItemsSegWords - 1) / kItemsSegWords;
+    const int64_t nseg = (words + p.seg_words - 1) / p.seg_words;
     const int64_t last = nseg > 0 ? nseg - 1 : 0;      // the last segment writes the count
     if (seg > last) return;
     const uint32_t* bm0 = p.bm + (static_cast<int64_t>(row) * p.Hq + static_cast<int64_t>(kv) * G) * p.stride;
@@ -125,10 +130,10 @@ __global__ __launch_bounds__(kItemsThreads) void attn_items_kernel(ItemsParams p
         if ((cur >> 5) == wd) u |= 1u << (cur & 31);
         return u;
     };
-    const int64_t w0 = static_cast<int64_t>(seg) * kItemsSegWords;
+    const int64_t w0 = static_cast<int64_t>(seg) * p.seg_words;
     const int64_t wd = w0 + tid;
     uint32_t heads[G];
-    const uint32_t mine = (tid < kItemsSegWords && wd < words) ? word(wd, heads) : 0u;
+    const uint32_t mine = (tid < p.seg_words && wd < words) ? word(wd, heads) : 0u;
     // items before the segment
     uint64_t pre = 0;
 #pragma unroll 4
@@ -1017,10 +1022,11 @@ hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st) {
         ip.lb = g.lb;
         ip.Hq = g.Hq;
         ip.Hkv = g.Hkv;
+        ip.seg_words = pairs <= kItemsFewPairs ? kItemsSegFew : kItemsThreads;
         {
             ProfScope ps("attn_items", 0, st);
             const int64_t iwords = (g.nodes[0] + 1 + 31) / 32;                  // chunks incl. the current one
-            const dim3 gi(static_cast<unsigned>(std::max<int64_t>(1, (iwords + kItemsSegWords - 1) / kItemsSegWords)),
+            const dim3 gi(static_cast<unsigned>(std::max<int64_t>(1, (iwords + ip.seg_words - 1) / ip.seg_words)),
                           pairs),
                 bi(kItemsThreads);
             switch (g.G) {
