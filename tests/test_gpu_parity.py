@@ -26,10 +26,12 @@ pytestmark = pytest.mark.gpu
 
 # (workload, shrink, batch)
 # Few (row, head) pairs cut each level over many workgroups; batch 8 of
-# gqa128k (256 pairs) takes the one-workgroup-per-pair cut.
+# gqa128k (256 pairs) takes the one-workgroup-per-pair cut. Up to 64 (row,
+# kv head) pairs deal the scoring waves by kept counts; batch 16 (128 such
+# pairs) takes the even grid of runs x pairs.
 CASES = [("tiny", 0, None), ("gqa128k", 2, 2), ("decode1m", 2, 1), ("decode16m", 2, 1), ("gqa128k", 1, 1),
-         ("gqa128k", 2, 8), ("gqa128k", 0, 1)]
-IDS = [f"{n}-s{s}" for n, s, _ in CASES]
+         ("gqa128k", 2, 8), ("gqa128k", 2, 16), ("gqa128k", 0, 1)]
+IDS = [f"{n}-s{s}" + (f"-b{b}" if b else "") for n, s, b in CASES]
 
 
 def _w(name, shrink, batch):
