@@ -9,9 +9,11 @@
 //   keep       = the smallest prefix in (score desc, node id asc) order whose
 //                softmax mass is >= top_p of the candidates' total.
 //
-// Kernels, ordered by kernel boundaries alone: no device-scope fences and no
-// cross-workgroup atomics (on this part every XCD has its own L2, and a
-// device-scope release writes L2 back).
+// Kernels, ordered by kernel boundaries alone: no device-scope fences (on this
+// part every XCD has its own L2, and a device-scope release writes L2 back).
+// The one cross-workgroup atomic is the split cut's u64 add into a pair's
+// mass bins (route_split_hist_kernel): integer sums are exact in any order,
+// and only the next kernel reads them.
 //  * route_upper_kernel - one workgroup per (row, query head) walks the small
 //    upper levels in one launch: candidates, scores and the cut stay in LDS
 //    from level to level.

@@ -321,27 +321,3 @@ def build_all(K: np.ndarray, R: np.ndarray, seq_lens: Sequence[int], b: int, sca
     """trees[s][h] for K [B, H_kv, N_cap, d] (fp32 values) and R [L, H_kv, d]."""
     B, H = K.shape[:2]
     return [[build_tree(K[s, h, :int(seq_lens[s])], R[:, h], b, scale) for h in range(H)] for s in range(B)]
-
-
-def decode_all(q: np.ndarray, q_pos: np.ndarray, K: np.ndarray, V: np.ndarray, trees, b: int, p: float,
-               scale=None, dense: bool = False):
-    """Route and attend every (sequence, row, query head): returns dict of arrays/lists."""
-    B, T, Hq, d = q.shape
-    Hkv = K.shape[1]
-    g = Hq // Hkv
-    out = np.zeros((B, T, Hq, d))
-    lse = np.zeros((B, T, Hq))
-    routes = [[[None] * Hq for _ in range(T)] for _ in range(B)]
-    for s in range(B):
-        for t in range(T):
-            n = int(q_pos[s, t]) + 1
-            for h in range(Hq):
-                kv = h // g
-                if dense:
-                    idx = np.arange(n)
-                else:
-                    r = route(q[s, t, h], trees[s][kv], n, b, p, scale)
-                    routes[s][t][h] = r
-                    idx = index_set(r.selected[0], n, b)
-                out[s, t, h], lse[s, t, h] = attend(q[s, t, h], K[s, kv], V[s, kv], idx, scale)
-    return {"out": out, "lse": lse, "routes": routes}

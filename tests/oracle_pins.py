@@ -207,6 +207,40 @@ def pin_cut_bruteforce(orc):
     assert checked > 300
 
 
+def pin_cut_exemptions(orc):
+    """The margin rule's exempt sets on hand-worked cases (golden file); then, on
+    random cuts with many exact ties, the oracle's set (which only pairs the
+    candidates nearest the boundary) equals a pass over every pair."""
+    for c in _load("exemption_cases.json")["cases"]:
+        s = np.array([_parse_score(x) for x in c["scores"]])
+        r = orc.topp_cut(np.array(c["ids"]), s, c["p"])
+        got = [int(x) for x in orc.cut_exemptions(r, c["p"])]
+        assert got == c["exempt"], (c["name"], got, c["exempt"])
+    rng = np.random.default_rng(22)
+    for _ in range(200):
+        n = int(rng.integers(2, 30))
+        s = np.round(rng.standard_normal(n) * 0.5, 3)
+        ids = rng.permutation(1000)[:n]
+        p = float(rng.choice([0.3, 0.6, 0.9, 0.95]))
+        r = orc.topp_cut(ids, s, p)
+        ex = set(int(x) for x in orc.cut_exemptions(r, p))
+        w = np.exp(s - s.max())
+        w = w / w.sum()
+        order = np.lexsort((ids, -s))
+        before = np.concatenate([[0.0], np.cumsum(w[order])])
+        rank = {int(ids[j]): k for k, j in enumerate(order)}
+        kept = set(int(x) for x in r.selected)
+        pos = {int(i): j for j, i in enumerate(ids)}
+        want = set()
+        for i in map(int, ids):
+            if abs(before[rank[i]] - p) < 1e-5:
+                want.add(i)
+            for o in map(int, ids):
+                if (i in kept) != (o in kept) and s[pos[i]] != s[pos[o]] and abs(w[pos[i]] - w[pos[o]]) < 1e-5:
+                    want.add(i)
+        assert ex == want, (sorted(ex), sorted(want))
+
+
 def pin_cut_uniform(orc):
     for n in [1, 2, 3, 7, 16, 100, 240, 257]:
         for p in [0.1, 0.33, 0.5, 0.91, 0.95, 0.999]:
@@ -401,7 +435,7 @@ def pin_split_merge(orc):
 
 ALL_PINS = [
     pin_geometry, pin_summary_sdpa, pin_summary_closed_forms, pin_incremental_equals_batch,
-    pin_cut_golden, pin_cut_bruteforce, pin_cut_uniform,
+    pin_cut_golden, pin_cut_bruteforce, pin_cut_exemptions, pin_cut_uniform,
     pin_route_golden, pin_route_dense_mask, pin_causal_prefix,
     pin_attend_sdpa, pin_p1_dense, pin_eq1_identity, pin_split_merge,
 ]

@@ -38,6 +38,17 @@ MUTANTS = {
     "attend-unnormalised": ("return (e @ v) / l, mx + math.log(l)", "return (e @ v) / e.max(), mx + math.log(l)"),
     "lse-no-max": ("return (e @ v) / l, mx + math.log(l)", "return (e @ v) / l, math.log(l)"),
     "span-off": ("return b ** level", "return b ** (level + 1)"),
+    "exempt-all": ("return np.array(sorted(ex), dtype=np.int64)",
+                   "return np.array(sorted(int(i) for i in cut.ids), dtype=np.int64)"),
+    "exempt-none": ("return np.array(sorted(ex), dtype=np.int64)", "return np.array([], dtype=np.int64)"),
+    "exempt-ties": ("diff = cut.scores64[cand_out] != cut.scores64[x]",
+                    "diff = cut.scores64[cand_out] == cut.scores64[cand_out]"),
+    "exempt-same-side": ("cand_out = outside[wo > lo_in - margin]", "cand_out = inside[wi > lo_in - margin]"),
+    "exempt-prefix-after": ("if abs(cut.prefix[k] - p) < margin:", "if abs(cut.prefix[k + 1] - p) < margin:"),
+    "exempt-margin-wide": ("margin: float = 1e-5", "margin: float = 1e-4"),
+    "exempt-no-rule-i": ("ex.add(int(cut.ids[cut.order[k]]))", "pass"),
+    "exempt-one-sided": ("                for y in cand_out[close & diff]:\n                    ex.add(int(cut.ids[y]))\n",
+                         ""),
 }
 
 
