@@ -77,17 +77,9 @@ class Bench:
         self.sizes = self.c.sizes
         t0 = time.time()
         kdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
-        self.K_host = np.zeros((w.batch, w.n_kv_heads, w.capacity, w.head_dim),
-                               np.uint16 if w.kv_dtype == "bf16" else np.float32)
-        self.V_host = np.zeros_like(self.K_host)
-        for s in range(w.batch):
-            lay = W.cluster_layout(w, s)
-            for h in range(w.n_kv_heads):
-                k, v = W.kv_chunk(w, s, h, 0, w.n_tokens, lay)
-                self.K_host[s, h, :w.n_tokens] = k
-                self.V_host[s, h, :w.n_tokens] = v
-                self.c.K[s, h, :w.n_tokens].copy_(torch.from_numpy(k).view(kdt))
-                self.c.V[s, h, :w.n_tokens].copy_(torch.from_numpy(v).view(kdt))
+        self.K_host, self.V_host = W.kv_cache(w)
+        self.c.K.copy_(torch.from_numpy(self.K_host).view(kdt))
+        self.c.V.copy_(torch.from_numpy(self.V_host).view(kdt))
         log(f"[bench] generated and uploaded the {w.n_tokens}-token cache in {time.time() - t0:.1f}s")
         self.R = W.ref_queries(w)
         self.ref_q = torch.from_numpy(self.R).cuda()

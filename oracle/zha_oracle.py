@@ -86,17 +86,28 @@ def pool_children(children: np.ndarray, r: np.ndarray, b: int, scale: float) -> 
     return s.astype(F32)
 
 
-def build_tree(K: np.ndarray, R: np.ndarray, b: int, scale: Optional[float] = None) -> List[np.ndarray]:
+def build_tree(K: np.ndarray, R: np.ndarray, b: int, scale: Optional[float] = None,
+               slab: Optional[int] = None) -> List[np.ndarray]:
     """All levels for one (sequence, kv head).
 
     K: (N, d) keys of the visible tokens. R: (L, d) reference queries of this kv
     head. Returns [X_1, ..., X_L] with X_l of shape (floor(N / b^l), d), fp32.
+    With ``slab`` (a multiple of b), level 1 is pooled ``slab`` keys at a time,
+    which bounds the fp64 copy of K for very long caches; a leaf never spans
+    two slabs, so the nodes are the same.
     """
     d = K.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     levels = []
-    X = np.asarray(K, dtype=F64)
-    for l in range(R.shape[0]):
+    if slab is None or R.shape[0] == 0:
+        X = np.asarray(K, dtype=F64)
+    else:
+        assert slab % b == 0, "a slab must hold whole leaf chunks"
+        n1 = K.shape[0] // b
+        X = np.concatenate([pool_children(K[t0:min(t0 + slab, n1 * b)], R[0], b, scale)
+                            for t0 in range(0, n1 * b, slab)] or [np.zeros((0, d), F32)])
+        levels.append(X)
+    for l in range(len(levels), R.shape[0]):
         X = pool_children(X, R[l], b, scale)
         levels.append(X)
     return levels
@@ -317,7 +328,7 @@ def realised_mass(q, K, n_visible, idx, scale=None) -> float:
 # ----------------------------------------------------------------------------
 # Whole-batch helpers (GQA: query head h uses kv head h // (H_q / H_kv))
 # ----------------------------------------------------------------------------
-def build_all(K: np.ndarray, R: np.ndarray, seq_lens: Sequence[int], b: int, scale=None):
+def build_all(K: np.ndarray, R: np.ndarray, seq_lens: Sequence[int], b: int, scale=None, slab=None):
     """trees[s][h] for K [B, H_kv, N_cap, d] (fp32 values) and R [L, H_kv, d]."""
     B, H = K.shape[:2]
-    return [[build_tree(K[s, h, :int(seq_lens[s])], R[:, h], b, scale) for h in range(H)] for s in range(B)]
+    return [[build_tree(K[s, h, :int(seq_lens[s])], R[:, h], b, scale, slab) for h in range(H)] for s in range(B)]

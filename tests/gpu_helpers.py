@@ -63,10 +63,10 @@ class Staged:
     def gpu_level(self, level):
         return self.cache.level(level).cpu().numpy()
 
-    def oracle_trees(self, n_tokens=None):
+    def oracle_trees(self, n_tokens=None, slab=None):
         w = self.w
         lens = [w.n_tokens if n_tokens is None else n_tokens] * w.batch
-        return O.build_all(self.Kf, self.R, lens, w.branching)
+        return O.build_all(self.Kf, self.R, lens, w.branching, slab=slab)
 
     def route_buffers(self, rows, sel_cap=None):
         t = torch()
@@ -123,3 +123,75 @@ def check_sets(gpu_ids, cut, p, where=""):
 
 def attn_tol(w):
     return 1e-5 if w.kv_dtype == "fp32" else 2e-3
+
+
+def teacher_forced(st, qn, qpos_np, stats, lsel, p, trees, pairs=None):
+    """Check every level's kept set of each (row, query head), teacher-forced: the
+    oracle cuts the candidates of the GPU's own kept parents. Candidate counts
+    must be exact, kept ids ascending, and the sets equal up to the margin
+    exemptions. ``pairs`` (a list of (sequence, query head)) restricts the check
+    to a sample. Returns the number of exempt differences."""
+    w = st.w
+    rows = qn.shape[0] * qn.shape[1]
+    kept = {l: level_kept(st, lsel, stats, rows, l) for l in range(1, w.n_levels + 1)}
+    todo = pairs if pairs is not None else [(s, h) for s in range(w.batch) for h in range(w.n_q_heads)]
+    flips = 0
+    for s, hq in todo:
+        for t_ in range(qn.shape[1]):
+            r = s * qn.shape[1] + t_
+            N = int(qpos_np[s, t_]) + 1
+            kv = hq // w.group
+            tree = trees[s][kv]
+            parents = None
+            for level in range(w.n_levels, 0, -1):
+                v, cnt, cand = kept[level]
+                gpu_ids = v[r, hq, :cnt[r, hq]]
+                cut = O.route_level(qn[s, t_, hq], tree[level - 1], level, parents, N, w.branching,
+                                    w.n_levels, p, w.scale)
+                assert cand[r, hq] == len(cut.ids), (s, t_, hq, level, cand[r, hq], len(cut.ids))
+                assert np.all(np.diff(gpu_ids) > 0), "kept ids must be ascending"
+                flips += check_sets(gpu_ids, cut, p, f"row {r} head {hq} level {level}")
+                parents = gpu_ids
+    return flips
+
+
+def check_tree(st, trees, n_tokens, pairs=None):
+    """GPU summaries of every level against the oracle's tree (summary_tol per level)."""
+    w = st.w
+    worst = 0.0
+    todo = pairs if pairs is not None else [(s, h) for s in range(w.batch) for h in range(w.n_kv_heads)]
+    for level in range(1, w.n_levels + 1):
+        gpu = st.gpu_level(level)
+        for s, h in todo:
+            ref = trees[s][h][level - 1]
+            n = ref.shape[0]
+            assert n == n_tokens // w.branching ** level
+            if n == 0:
+                continue
+            children = st.Kf[s, h, :n_tokens] if level == 1 else trees[s][h][level - 2]
+            tol = summary_tol(children.astype(np.float64), st.R[level - 1, h].astype(np.float64), w.scale)
+            err = np.abs(gpu[s, h, :n].astype(np.float64) - ref).max()
+            assert err <= tol, (level, s, h, err, tol)
+            worst = max(worst, err / tol)
+    return worst
+
+
+def check_attention(st, qn, qpos_np, out, lse, sel, nsel, pairs=None):
+    """GPU attention of each (row, head) against the oracle over the GPU's own index set."""
+    w = st.w
+    o_np, l_np = out.cpu().numpy(), lse.cpu().numpy()
+    s_np, n_np = sel.cpu().numpy(), nsel.cpu().numpy()
+    tol = attn_tol(w)
+    worst = 0.0
+    todo = pairs if pairs is not None else [(s, h) for s in range(w.batch) for h in range(w.n_q_heads)]
+    for s, hq in todo:
+        for t_ in range(qn.shape[1]):
+            N = int(qpos_np[s, t_]) + 1
+            kv = hq // w.group
+            I = O.index_set(s_np[s, t_, hq, :n_np[s, t_, hq]], N, w.branching)
+            o, l = O.attend(qn[s, t_, hq], st.Kf[s, kv], st.Vf[s, kv], I, w.scale)
+            e = max(np.abs(o_np[s, t_, hq] - o).max(), abs(l_np[s, t_, hq] - l))
+            worst = max(worst, e)
+            assert e <= tol, (s, t_, hq, e)
+    return worst
+

@@ -143,8 +143,10 @@ def pin_incremental_equals_batch(orc):
         R = rng.standard_normal((L, 8)).astype(np.float32)
         t1 = orc.build_tree(K, R, b)
         t2 = orc.build_tree_incremental(K, R, b)
-        for a, c in zip(t1, t2):
+        t3 = orc.build_tree(K, R, b, slab=3 * b)      # level 1 pooled a few leaves at a time
+        for a, c, e in zip(t1, t2, t3):
             assert a.shape == c.shape and np.array_equal(a, c), (b, L, n)
+            assert a.shape == e.shape and np.array_equal(a, e), (b, L, n)
 
 
 # ----------------------------------------------------------------------------

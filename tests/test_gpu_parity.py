@@ -20,7 +20,7 @@ import pytest
 import hierarchical_tree_indexed_build_amd as Z
 import workloads as W
 from oracle import zha_oracle as O
-from tests.gpu_helpers import (Staged, attn_tol, check_sets, kv_tensor, level_kept, say, summary_tol, torch)
+from tests.gpu_helpers import (Staged, attn_tol, kv_tensor, level_kept, say, summary_tol, teacher_forced, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,31 +77,6 @@ def _route(st, rows_per_seq, q_pos, top_p=None, sel_cap=None, step=0):
     return qn, q, sel, nsel, stats, lsel, p
 
 
-def _teacher_forced(st, qn, qpos_np, stats, lsel, p, trees):
-    w = st.w
-    rows = qn.shape[0] * qn.shape[1]
-    kept = {l: level_kept(st, lsel, stats, rows, l) for l in range(1, w.n_levels + 1)}
-    flips = 0
-    for s in range(w.batch):
-        for t_ in range(qn.shape[1]):
-            r = s * qn.shape[1] + t_
-            N = int(qpos_np[s, t_]) + 1
-            for hq in range(w.n_q_heads):
-                kv = hq // w.group
-                tree = trees[s][kv]
-                parents = None
-                for level in range(w.n_levels, 0, -1):
-                    v, cnt, cand = kept[level]
-                    gpu_ids = v[r, hq, :cnt[r, hq]]
-                    cut = O.route_level(qn[s, t_, hq], tree[level - 1], level, parents, N, w.branching,
-                                        w.n_levels, p, w.scale)
-                    assert cand[r, hq] == len(cut.ids), (s, t_, hq, level, cand[r, hq], len(cut.ids))
-                    assert np.all(np.diff(gpu_ids) > 0), "kept ids must be ascending"
-                    flips += check_sets(gpu_ids, cut, p, f"row {r} head {hq} level {level}")
-                    parents = gpu_ids
-    return flips
-
-
 @pytest.mark.parametrize("case", CASES, ids=IDS)
 def test_route_parity(case):
     w = _w(*case)
@@ -110,7 +85,7 @@ def test_route_parity(case):
     T = w.queries_per_step
     q_pos = _qpos(st, T)
     qn, q, sel, nsel, stats, lsel, p = _route(st, T, q_pos)
-    flips = _teacher_forced(st, qn, q_pos.cpu().numpy(), stats, lsel, p, st.oracle_trees())
+    flips = teacher_forced(st, qn, q_pos.cpu().numpy(), stats, lsel, p, st.oracle_trees())
     say(f"  margin-exempt differences: {flips}")
     # level-1 outputs agree with the level_sel copy
     v1, c1, _ = level_kept(st, lsel, stats, w.batch * T, 1)
@@ -160,7 +135,7 @@ def test_route_parity_crowded_scores(kind, noise, at):
     t.cuda.synchronize()
     q_pos = _qpos(st, 1)
     qn, q, sel, nsel, stats, lsel, p = _route(st, 1, q_pos)
-    flips = _teacher_forced(st, qn, q_pos.cpu().numpy(), stats, lsel, p, st.oracle_trees())
+    flips = teacher_forced(st, qn, q_pos.cpu().numpy(), stats, lsel, p, st.oracle_trees())
     say(f"  margin-exempt differences: {flips}; kept leaves per head {nsel.cpu().numpy().reshape(-1)[:8]}")
 
 
@@ -261,7 +236,7 @@ def test_causal_rows_and_short_prefixes():
     q_pos = t.arange(300, dtype=t.int32, device="cuda").view(1, 300)
     qn, q, sel, nsel, stats, lsel, p = _route(st, 300, q_pos)
     trees = st.oracle_trees()
-    _teacher_forced(st, qn, q_pos.cpu().numpy(), stats, lsel, p, trees)
+    teacher_forced(st, qn, q_pos.cpu().numpy(), stats, lsel, p, trees)
     out = t.zeros_like(q)
     lse = t.zeros(q.shape[:3], dtype=t.float32, device="cuda")
     Z.sparse_attend(st.geom, q, q_pos, st.cache.K, st.cache.V, st.cache.seq_lens, sel, nsel, out, lse, st.cache.ws)
@@ -287,39 +262,77 @@ def test_route_levels_below_the_fused_levels():
     st = Staged(w)
     q_pos = _qpos(st, w.queries_per_step)
     qn, q, sel, nsel, stats, lsel, p = _route(st, w.queries_per_step, q_pos)
-    flips = _teacher_forced(st, qn, q_pos.cpu().numpy(), stats, lsel, p, st.oracle_trees())
+    flips = teacher_forced(st, qn, q_pos.cpu().numpy(), stats, lsel, p, st.oracle_trees())
     say(f"  margin-exempt differences: {flips}")
 
 
-def test_append_bit_identical_to_build():
+def _append_case(name, shrink, n0, capacity, singles, chunk):
+    """`singles` one-token appends, then one append of `chunk` tokens, against host data:
+    the cache rows must be the appended tokens' bits; every level must match the
+    oracle's incremental build on the host keys; and a fresh build over the host
+    cache must give the same summary bits as the appends."""
     t = torch()
-    w = W.get_workload("decode1m", shrink=2)     # b = 32, L = 2, bf16, 8 kv heads
-    w.capacity = 1400
-    n0 = 1000
-    say("[append] decode1m shrink 2: 60 single-token appends, then a 200-token chunk")
+    w = W.get_workload(name, shrink=shrink)
+    w.capacity = capacity
+    say(f"[append] {w.name} {w.kv_dtype} b={w.branching} L={w.n_levels}: {singles} single-token appends "
+        f"from {n0}, then {chunk} tokens")
     st = Staged(w, n_tokens=n0)
-    for step in range(60):
+    K_host, V_host = st.K_np.copy(), st.V_np.copy()
+    n = n0
+    for step in range(singles):
         kn, vn = W.appended_tokens(w, step, 1)
-        kt, vt = (t.from_numpy(x).view(t.bfloat16).cuda() for x in (kn, vn))
-        Z.append(st.geom, st.cache.K, st.cache.V, kt, vt, st.cache.seq_lens, st.ref_q, st.cache.summaries,
-                 st.cache.ws)
-    kn, vn = W.appended_tokens(w, 999, 200)
-    kt, vt = (t.from_numpy(x).view(t.bfloat16).cuda() for x in (kn, vn))
-    Z.append(st.geom, st.cache.K, st.cache.V, kt, vt, st.cache.seq_lens, st.ref_q, st.cache.summaries, st.cache.ws)
+        K_host[:, :, n:n + 1], V_host[:, :, n:n + 1] = kn, vn
+        Z.append(st.geom, st.cache.K, st.cache.V, kv_tensor(w, kn), kv_tensor(w, vn), st.cache.seq_lens, st.ref_q,
+                 st.cache.summaries, st.cache.ws)
+        n += 1
+    if chunk:
+        kn, vn = W.appended_tokens(w, 999, chunk)
+        K_host[:, :, n:n + chunk], V_host[:, :, n:n + chunk] = kn, vn
+        Z.append(st.geom, st.cache.K, st.cache.V, kv_tensor(w, kn), kv_tensor(w, vn), st.cache.seq_lens, st.ref_q,
+                 st.cache.summaries, st.cache.ws)
+        n += chunk
     t.cuda.synchronize()
-    assert int(st.cache.seq_lens[0].item()) == n0 + 260
     assert Z.read_device_status(st.cache.ws) == 0
-    # the appended rows landed where they should
-    assert t.equal(st.cache.K[:, :, n0 + 60:n0 + 260], kt)
+    assert np.all(st.cache.seq_lens.cpu().numpy() == n)
+    bits = t.uint16 if w.kv_dtype == "bf16" else t.float32
+    assert np.array_equal(st.cache.K.view(bits).cpu().numpy()[:, :, :n], K_host[:, :, :n])
+    assert np.array_equal(st.cache.V.view(bits).cpu().numpy()[:, :, :n], V_host[:, :, :n])
+    # the oracle grows its tree one token at a time from the host keys
+    Kf = W.as_f32(w, K_host)
+    for level in range(1, w.n_levels + 1):
+        gpu = st.gpu_level(level)
+        for s in range(w.batch):
+            for h in range(w.n_kv_heads):
+                ref = O.build_tree_incremental(Kf[s, h, :n], st.R[:, h], w.branching)
+                m = n // w.branching ** level
+                assert ref[level - 1].shape[0] == m
+                if m == 0:
+                    continue
+                children = Kf[s, h, :n] if level == 1 else ref[level - 2]
+                tol = summary_tol(children.astype(np.float64), st.R[level - 1, h].astype(np.float64), w.scale)
+                err = np.abs(gpu[s, h, :m].astype(np.float64) - ref[level - 1]).max()
+                assert err <= tol, (level, s, h, err, tol)
+    # a build over the host cache: the same bits
     ref = Z.Cache(st.geom, 1)
-    ref.K.copy_(st.cache.K)
-    ref.seq_lens.copy_(st.cache.seq_lens)
+    ref.K.copy_(kv_tensor(w, K_host))
+    ref.seq_lens.fill_(n)
     Z.build_tree(st.geom, ref.K, st.ref_q, ref.seq_lens, ref.summaries, ref.ws)
     t.cuda.synchronize()
     for level in range(1, w.n_levels + 1):
-        a, b = st.cache.level(level), ref.level(level)
-        n = (n0 + 260) // w.branching ** level
-        assert t.equal(a[:, :, :n], b[:, :, :n]), level
+        m = n // w.branching ** level
+        assert t.equal(st.cache.level(level)[:, :, :m], ref.level(level)[:, :, :m]), level
+
+
+def test_append_matches_host_tokens_bf16():
+    """The decode path's fused single-token append (b = 32, bf16, 8 kv heads),
+    crossing leaf boundaries, then the multi-token path."""
+    _append_case("decode1m", 2, 1000, 1400, 60, 200)
+
+
+def test_append_matches_host_tokens_fp32_cascade():
+    """fp32 cache, b = 16, L = 3: single-token appends from 4000 to 4100 complete
+    leaves, level-2 nodes and, at 4096, the top node, all in the fused kernel."""
+    _append_case("tiny", 0, 4000, 4200, 100, 0)
 
 
 def test_append_past_capacity_writes_nothing():

@@ -33,6 +33,8 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, List, Optional, Tuple
 
 import numpy as np
@@ -268,15 +270,40 @@ def kv_chunk(w: Workload, seq: int, kv: int, t0: int, t1: int, layout=None) -> T
             _to_kv_dtype(w, values_f32(w, seq, kv, t0, t1)))
 
 
-def kv_cache(w: Workload) -> Tuple[np.ndarray, np.ndarray]:
-    """Whole initial cache [B, H_kv, capacity, d]; rows past n_tokens are zero."""
+def host_threads() -> int:
+    """Threads for host-side generation: the cores this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def kv_cache(w: Workload, threads: Optional[int] = None, slab: int = 1 << 20) -> Tuple[np.ndarray, np.ndarray]:
+    """Whole initial cache [B, H_kv, capacity, d]; rows past n_tokens are zero.
+
+    Slabs of ``slab`` tokens of every (sequence, kv head) are drawn on a thread
+    pool (NumPy's generators release the GIL); each slab seeds its own streams,
+    so the bits do not depend on the slab size or the thread count.
+    """
     dt = np.uint16 if w.kv_dtype == "bf16" else np.float32
     K = np.zeros((w.batch, w.n_kv_heads, w.capacity, w.head_dim), dtype=dt)
     V = np.zeros_like(K)
-    for s in range(w.batch):
-        lay = cluster_layout(w, s) if w.cluster_mode != "needles" else None
-        for h in range(w.n_kv_heads):
-            K[s, h, :w.n_tokens], V[s, h, :w.n_tokens] = kv_chunk(w, s, h, 0, w.n_tokens, lay)
+    lays = [cluster_layout(w, s) if w.cluster_mode != "needles" else None for s in range(w.batch)]
+    tasks = [(s, h, t0, min(t0 + slab, w.n_tokens)) for s in range(w.batch) for h in range(w.n_kv_heads)
+             for t0 in range(0, w.n_tokens, slab)]
+
+    def fill(task):
+        s, h, t0, t1 = task
+        K[s, h, t0:t1], V[s, h, t0:t1] = kv_chunk(w, s, h, t0, t1, lays[s])
+
+    n = host_threads() if threads is None else max(1, threads)
+    if n == 1 or len(tasks) == 1:
+        for task in tasks:
+            fill(task)
+    else:
+        with ThreadPoolExecutor(n) as ex:
+            list(ex.map(fill, tasks))
     return K, V
 
 
