@@ -23,7 +23,7 @@ ZHA_KV_BF16, ZHA_KV_F32 = 0, 1
 ZHA_MAX_LEVELS = 8
 
 EXPORTED = ("zha_query_sizes", "zha_build_tree", "zha_append", "zha_route", "zha_sparse_attend", "zha_attend",
-            "zha_dense_attend", "zha_read_device_status", "zha_profile_start", "zha_profile_collect",
+            "zha_attend_noalloc", "zha_dense_attend", "zha_read_device_status", "zha_profile_start", "zha_profile_collect",
             "zha_status_string", "zha_last_error")
 
 
@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
             "zha_route": [GP, _P, i32, _P, _P, _P, f32, i32, _P, _P, _P, _P, _P, sz, _P],
             "zha_sparse_attend": [GP, _P, i32, _P, _P, _P, _P, _P, _P, i32, _P, _P, _P, sz, _P],
             "zha_attend": [GP, _P, i32, _P, _P, _P, _P, _P, f32, i32, _P, _P, _P, _P, _P, _P, _P, sz, _P],
+            "zha_attend_noalloc": [GP, _P, i32, _P, _P, _P, _P, _P, f32, i32, _P, _P, _P, _P, _P, _P, _P, _P],
             "zha_dense_attend": [GP, _P, i32, _P, _P, _P, _P, _P, _P, _P, sz, _P],
             "zha_read_device_status": [_P, _P, ctypes.POINTER(ctypes.c_uint32), i32],
         }
@@ -158,6 +159,16 @@ def attend(geom, q, q_pos, K, V, summaries, seq_lens, top_p, sel_blocks, n_sel, 
                             _ptr(seq_lens), float(top_p), sel_blocks.shape[-1], _ptr(sel_blocks), _ptr(n_sel),
                             _ptr(level_stats), _ptr(level_sel), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws),
                             _stream(stream)), "zha_attend")
+
+
+def attend_noalloc(geom, q, q_pos, K, V, summaries, seq_lens, top_p, sel_blocks, n_sel, out, lse, level_stats=None,
+                   level_sel=None, dev_status=None, stream=None):
+    """zha_attend with the library's static scratch instead of a workspace (no allocation)."""
+    t = q.shape[1]
+    _check(lib().zha_attend_noalloc(ctypes.byref(geom), _ptr(q), t, _ptr(q_pos), _ptr(K), _ptr(V), _ptr(summaries),
+                                    _ptr(seq_lens), float(top_p), sel_blocks.shape[-1], _ptr(sel_blocks), _ptr(n_sel),
+                                    _ptr(level_stats), _ptr(level_sel), _ptr(out), _ptr(lse), _ptr(dev_status),
+                                    _stream(stream)), "zha_attend_noalloc")
 
 
 def dense_attend(geom, q, q_pos, K, V, seq_lens, out, lse, ws, stream=None):

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -162,6 +163,32 @@ struct Profiler {
 };
 Profiler g_prof;
 constexpr int kProfSlots = 8192;
+
+// ---- the static scratch of zha_attend_noalloc ----
+// Device memory the library owns, for callers that cannot allocate. Each GPU
+// the library runs on holds its own copy until the process ends. In host code
+// `scratch` names a host-side stand-in, never the device memory: its device
+// address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    void* ptr = nullptr;       // device address of this device's scratch
+    bool cleared = false;      // the whole array was zeroed once (its first call)
+};
+ScratchSlot g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Clears `words` 32-bit words (a fill kernel rather than a memset, so that the
+// call stays valid under stream capture).
+__global__ void zero_words_kernel(uint32_t* p, size_t words) {
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        p[i] = 0u;
+}
+
+__global__ void copy_word_kernel(const uint32_t* src, uint32_t* dst) { *dst = *src; }
 
 bool prof_matches(const char* label, int level) {
     if (g_prof.target.empty()) return false;
@@ -365,6 +392,61 @@ zha_status zha_attend(const zha_geom* geom, const float* q, int32_t t, const int
         return st;
     return attend_impl(g, q, t, q_pos, K, V, seq_lens, sel_blocks, n_sel, sel_capacity, out, lse, ws, L, rows, false,
                        true, s);
+}
+
+zha_status zha_attend_noalloc(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos, const void* K,
+                              const void* V, const float* summaries, const int32_t* seq_lens, float top_p,
+                              int32_t sel_capacity, int32_t* sel_blocks, int32_t* n_sel, int32_t* level_stats,
+                              int32_t* level_sel, float* out, float* lse, uint32_t* dev_status, void* stream) {
+    Geo g;
+    zha_status st = make_geo(geom, &g);
+    if (st) return st;
+    if ((st = check_route_args(q, summaries, seq_lens, top_p, sel_capacity, sel_blocks, n_sel))) return st;
+    if (!K || !V || !out || !lse) return fail(ZHA_ERR_NULL, "K, V, out and lse are required");
+    int rows;
+    if ((st = check_rows(g, t, &rows))) return st;
+    const WsLayout L = layout(g, rows);
+    if (L.total > kScratchBytes)
+        return fail(ZHA_ERR_WORKSPACE,
+                    "this call needs %zu bytes of scratch; the static scratch holds %zu: use zha_attend with a "
+                    "workspace",
+                    L.total, kScratchBytes);
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "current device");
+    if (dev < 0 || dev >= kMaxDevices) return fail(ZHA_ERR_UNSUPPORTED, "device %d is past the %d the scratch table holds", dev, kMaxDevices);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    bool first = false;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ScratchSlot& slot = g_scratch[dev];
+        if (!slot.ptr) {
+            void* ptr = nullptr;
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_fail(e, "scratch address");
+            if (!ptr) return fail(ZHA_ERR_HIP, "scratch address is NULL");
+            slot.ptr = ptr;
+        }
+        ws = slot.ptr;
+        first = !slot.cleared;
+        slot.cleared = true;
+    }
+    // the status word starts every call at zero; the whole array once, on its first call
+    const size_t words = first ? kScratchBytes / 4 : 1;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(first ? 1024 : 1), dim3(256), 0, s, static_cast<uint32_t*>(ws), words);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "scratch clear launch");
+    if ((st = route_impl(g, q, t, q_pos, summaries, seq_lens, top_p, sel_capacity, sel_blocks, n_sel, level_stats,
+                         level_sel, ws, L, rows, s)))
+        return st;
+    if ((st = attend_impl(g, q, t, q_pos, K, V, seq_lens, sel_blocks, n_sel, sel_capacity, out, lse, ws, L, rows,
+                          false, true, s)))
+        return st;
+    if (dev_status) {
+        hipLaunchKernelGGL(copy_word_kernel, dim3(1), dim3(1), 0, s, static_cast<const uint32_t*>(ws), dev_status);
+        if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "status copy launch");
+    }
+    return ZHA_OK;
 }
 
 zha_status zha_dense_attend(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos, const void* K,

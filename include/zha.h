@@ -32,7 +32,8 @@
  * Conventions for every function:
  *  - All tensor pointers are DEVICE pointers, owned by the caller, and must
  *    stay valid until the work enqueued on `stream` has finished. The library
- *    never allocates or frees memory and keeps no pointer after returning.
+ *    never allocates or frees memory and keeps no pointer after returning; the
+ *    one memory it owns is the static scratch of zha_attend_noalloc.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
  *    work is enqueued asynchronously on it; no call synchronises except
  *    zha_read_device_status.
@@ -167,6 +168,24 @@ ZHA_API zha_status zha_attend(const zha_geom* geom, const float* q, int32_t t, c
                       float top_p, int32_t sel_capacity, int32_t* sel_blocks, int32_t* n_sel,
                       int32_t* level_stats, int32_t* level_sel, float* out, float* lse,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* zha_attend for callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * kernels and results, with no workspace argument. Its scratch is a static
+ * 64 MiB array inside the library, one per GPU the library runs on, held until
+ * the process ends; the call allocates and frees nothing. A call whose layout
+ * needs more (zha_query_sizes(geom, t).workspace_bytes > 64 MiB) returns
+ * ZHA_ERR_WORKSPACE before anything is enqueued. The first call on a device
+ * zeroes the whole array; every call zeroes its status word. dev_status
+ * (nullable, a device pointer) receives the call's ZHA_DEV_* bits, written
+ * after its last kernel on `stream`. Every call on one GPU shares that GPU's
+ * array and it keeps the last call's contents: calls that overlap on one GPU
+ * (concurrent streams or threads) race and must be serialised by the caller. */
+ZHA_API zha_status zha_attend_noalloc(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos,
+                              const void* K, const void* V, const float* summaries, const int32_t* seq_lens,
+                              float top_p, int32_t sel_capacity, int32_t* sel_blocks, int32_t* n_sel,
+                              int32_t* level_stats, int32_t* level_sel, float* out, float* lse,
+                              uint32_t* dev_status, void* stream);
 
 /* Dense baseline: exact attention of each row over all tokens it sees
  * [The Quadratic Bottleneck: decode re-reads the whole cache per token]. */
