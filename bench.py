@@ -52,6 +52,9 @@ def parse():
                     help="run the warmup and timed steps only (for profiler runs), print a short line")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed run")
+    ap.add_argument("--cold", action="store_true",
+                    help="with --timed-only: read a 512 MiB buffer before every timed step (counter runs of "
+                         "the cache-flushed steps)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the kernel's HBM traffic per launch from two rocprofv3 --pmc runs "
@@ -63,36 +66,31 @@ def parse():
 # staging
 # ----------------------------------------------------------------------------
 class Bench:
-    def __init__(self, w, steps, warmup):
+    def __init__(self, w, steps, warmup, K_host, V_host, q_host, kv_new):
         import torch
         self.t = torch
         self.w = w
         self.steps, self.warmup = steps, warmup
-        total = steps + warmup
-        if w.append_per_step:
-            w.capacity = w.n_tokens + total * w.append_per_step
         self.geom = Z.make_geom(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.branching, w.n_levels,
                                 w.capacity, w.kv_dtype)
         self.c = Z.Cache(self.geom, 1)
         self.sizes = self.c.sizes
         t0 = time.time()
         kdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
-        self.K_host, self.V_host = W.kv_cache(w)
+        self.K_host, self.V_host = K_host, V_host
         self.c.K.copy_(torch.from_numpy(self.K_host).view(kdt))
         self.c.V.copy_(torch.from_numpy(self.V_host).view(kdt))
-        log(f"[bench] generated and uploaded the {w.n_tokens}-token cache in {time.time() - t0:.1f}s")
+        log(f"[bench] uploaded the {w.n_tokens}-token cache in {time.time() - t0:.1f}s")
         self.R = W.ref_queries(w)
         self.ref_q = torch.from_numpy(self.R).cuda()
         self.c.seq_lens.fill_(w.n_tokens)
         # per-step inputs, resident in HBM before any timing
-        qs = np.stack([W.queries(w, i) for i in range(total)])             # [S, B, 1, Hq, d]
-        self.q = torch.from_numpy(qs).cuda()
-        self.q_host = qs
+        self.q = torch.from_numpy(q_host).cuda()                          # [S, B, 1, Hq, d]
+        self.q_host = q_host
         if w.append_per_step:
-            kv = [W.appended_tokens(w, i) for i in range(total)]
-            self.k_new = torch.stack([torch.from_numpy(k).view(kdt) for k, _ in kv]).cuda()
-            self.v_new = torch.stack([torch.from_numpy(v).view(kdt) for _, v in kv]).cuda()
-            self.kv_host = kv
+            self.k_new = torch.stack([torch.from_numpy(k).view(kdt) for k, _ in kv_new]).cuda()
+            self.v_new = torch.stack([torch.from_numpy(v).view(kdt) for _, v in kv_new]).cuda()
+            self.kv_host = kv_new
         n1 = self.sizes.level_nodes[0]
         self.sel = torch.zeros((w.batch, 1, w.n_q_heads, n1), dtype=torch.int32, device="cuda")
         self.nsel = torch.zeros((w.batch, 1, w.n_q_heads), dtype=torch.int32, device="cuda")
@@ -178,55 +176,106 @@ def step_bytes(b: Bench, stats, lsel, sel, nsel, N):
 # ----------------------------------------------------------------------------
 # CPU oracle baseline
 # ----------------------------------------------------------------------------
-def cpu_baseline(b: Bench, budget_s: float):
-    """Time the oracle's per-query work (route + attend, every head) on host cores.
+_CPU = {}     # the oracle leg's inputs, set before its worker processes fork (they inherit it)
 
-    The oracle routes against the tree the GPU built (copied to the host): the
-    tree is built once per cache, the metric counts per-query work. Sampled
-    queries are the timed steps' queries, in order, until the budget is spent.
-    """
-    from threadpoolctl import threadpool_limits
+
+def cpu_workers() -> int:
+    """Worker processes for the oracle leg: the cores this process may run on,
+    at most 16 (one GPU's share of a host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _oracle_query(task):
+    """One (step, sequence, query head) through the oracle: route, then exact
+    attention over the index set. Runs in a worker with one BLAS thread."""
     from oracle import zha_oracle as O
-    w, t = b.w, b.t
-    N = int(b.c.seq_lens[0].item())
-    summ = b.c.summaries.cpu().numpy()
-    trees = []
-    for s in range(w.batch):
-        per = []
-        for h in range(w.n_kv_heads):
-            lv = []
-            for level in range(1, w.n_levels + 1):
-                n = N // w.branching ** level
-                off = b.sizes.level_offset[level - 1]
-                rows = b.sizes.level_nodes[level - 1]
-                base = off + (s * w.n_kv_heads + h) * rows * w.head_dim
-                lv.append(summ[base:base + n * w.head_dim].reshape(n, w.head_dim))
-            per.append(lv)
-        trees.append(per)
-    Kh, Vh = b.K_host, b.V_host
-    if w.append_per_step:
-        for i, (k, v) in enumerate(b.kv_host):
-            Kh[:, :, w.n_tokens + i] = k[:, :, 0]
-            Vh[:, :, w.n_tokens + i] = v[:, :, 0]
-    Kf = [[W.as_f32(w, Kh[s, h, :N]) for h in range(w.n_kv_heads)] for s in range(w.batch)]
-    Vf = [[W.as_f32(w, Vh[s, h, :N]) for h in range(w.n_kv_heads)] for s in range(w.batch)]
-    done = 0
+    step, s, hq = task
+    d = _CPU
+    w = d["w"]
+    kv = hq // w.group
+    N = d["N"][step]
+    q = d["q"][step][s, 0, hq]
+    r = O.route(q, d["trees"][s][kv], N, w.branching, d["top_p"])
+    I = O.index_set(r.selected[0], N, w.branching)
+    o, lse = O.attend(q, d["Kf"][s][kv], d["Vf"][s][kv], I)
+    return step, s, hq, r.selected[0].astype(np.int32), o, lse
+
+
+def _one_blas_thread():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+
+
+def cpu_baseline(w, K_host, V_host, q_host, kv_new, first_step, last_step, budget_s):
+    """The oracle's per-query work (route + exact attention of every head) timed on
+    the host's cores before the GPU is touched: a process pool (fork) with one
+    BLAS thread per worker, one decode step's queries per round, steps
+    first_step, first_step + 1, ... until about budget_s seconds have passed.
+    The oracle builds its own tree from the host keys (not timed: it is built
+    once per cache). Returns the record and the outputs per (step, s, hq)."""
+    import multiprocessing as mp
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import zha_oracle as O
+    app = w.append_per_step
+    n_last = w.n_tokens + (last_step + 1) * app
+    Kh, Vh = K_host, V_host
+    if app:
+        Kh, Vh = K_host.copy(), V_host.copy()
+        for i, (k, v) in enumerate(kv_new[:last_step + 1]):
+            Kh[:, :, w.n_tokens + i * app:w.n_tokens + (i + 1) * app] = k
+            Vh[:, :, w.n_tokens + i * app:w.n_tokens + (i + 1) * app] = v
+    Kf = [[W.as_f32(w, Kh[s, h, :n_last]) for h in range(w.n_kv_heads)] for s in range(w.batch)]
+    Vf = [[W.as_f32(w, Vh[s, h, :n_last]) for h in range(w.n_kv_heads)] for s in range(w.batch)]
+    R = W.ref_queries(w)
     t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while time.perf_counter() - t0 < budget_s and done < b.q_host.shape[0]:
-            q = b.q_host[done]
-            for s in range(w.batch):
-                for hq in range(w.n_q_heads):
-                    kv = hq // w.group
-                    r = O.route(q[s, 0, hq], trees[s][kv], N, w.branching, w.top_p)
-                    I = O.index_set(r.selected[0], N, w.branching)
-                    O.attend(q[s, 0, hq], Kf[s][kv], Vf[s][kv], I)
+    with ThreadPoolExecutor(W.host_threads()) as ex:
+        flat = list(ex.map(lambda sh: O.build_tree(Kf[sh[0]][sh[1]], R[:, sh[1]], w.branching, slab=1 << 20),
+                           [(s, h) for s in range(w.batch) for h in range(w.n_kv_heads)]))
+    trees = [flat[s * w.n_kv_heads:(s + 1) * w.n_kv_heads] for s in range(w.batch)]
+    log(f"[bench] oracle tree built from the host keys in {time.perf_counter() - t0:.1f}s")
+    _CPU.update(w=w, trees=trees, Kf=Kf, Vf=Vf, q=q_host, top_p=w.top_p,
+                N={i: w.n_tokens + (i + 1) * app for i in range(last_step + 1)})
+    n = cpu_workers()
+    outs = {}
+    done = 0
+    ctx = mp.get_context("fork")
+    with ctx.Pool(n, initializer=_one_blas_thread) as pool:
+        t0 = time.perf_counter()
+        for step in range(first_step, last_step + 1):
+            tasks = [(step, s, hq) for s in range(w.batch) for hq in range(w.n_q_heads)]
+            for res in pool.map(_oracle_query, tasks, chunksize=1):
+                outs[res[:3]] = res[3:]
             done += 1
-    el = time.perf_counter() - t0
-    return {"value": round(done * w.batch / el, 3), "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} decode queries x {w.batch} sequence(s) x {w.n_q_heads} heads (route + exact "
-                      f"attention per head, NumPy fp64, one BLAS thread) against the GPU-built tree at "
-                      f"N={N}, {el:.1f}s"}
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        el = time.perf_counter() - t0
+    _CPU.clear()
+    rec = {"value": round(done * w.batch / el, 3), "unit": "queries/s", "cores": n, "kind": "oracle",
+           "sample": f"{done} decode steps (steps {first_step}..{first_step + done - 1} of the timed run) x "
+                     f"{w.batch} sequence(s) x {w.n_q_heads} heads: route + exact attention per head, NumPy "
+                     f"fp64, {n} worker processes with one BLAS thread each, the oracle's own tree built from "
+                     f"the host keys; {el:.1f}s"}
+    return rec, outs
+
+
+def cpu_parity(w, outs, gpu):
+    """End-to-end agreement of the GPU's timed steps with the oracle leg's outputs
+    on the same queries: kept leaf sets, then attention on the heads whose sets
+    are equal (other heads differ by a margin flip upstream, which the
+    teacher-forced parity tests cover)."""
+    equal, worst, n = 0, 0.0, 0
+    for (step, s, hq), (ids, o, lse) in outs.items():
+        if step not in gpu:
+            continue
+        sel, nsel, out, l = gpu[step]
+        n += 1
+        g_ids = sel[s, 0, hq, :nsel[s, 0, hq]]
+        if len(g_ids) == len(ids) and np.array_equal(np.sort(g_ids), ids):
+            equal += 1
+            worst = max(worst, float(np.abs(out[s, 0, hq] - o).max()), abs(float(l[s, 0, hq]) - lse))
+    tol = 2e-3 if w.kv_dtype == "bf16" else 1e-5
+    return {"heads": n, "index_sets_equal": equal, "max_abs_err_on_equal_sets": round(worst, 7), "tol": tol,
+            "ok": bool(n and worst <= tol)}
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -472,15 +521,28 @@ def main():
         write_traffic(*args.traffic_from, args.kernel, w.name, args.copy_probe_mib,
                       args.steps if args.steps is not None else w.steps)
         return
-    import torch
     w = W.get_workload(args.workload)
     if w.prefill_chunk:
         prefill_main(args, w)
         return
     steps = args.steps if args.steps is not None else w.steps
     warm = args.warmup
+    total = steps + warm
+    if w.append_per_step:
+        w.capacity = w.n_tokens + total * w.append_per_step
     log(f"[bench] workload {w.name}: {w.description}; steps {steps}, warmup {warm}")
-    b = Bench(w, steps, warm)
+    t0 = time.time()
+    K_host, V_host = W.kv_cache(w)
+    q_host = np.stack([W.queries(w, i) for i in range(total)])            # [S, B, 1, Hq, d]
+    kv_new = [W.appended_tokens(w, i) for i in range(total)] if w.append_per_step else []
+    log(f"[bench] generated the {w.n_tokens}-token cache and {total} steps of inputs in {time.time() - t0:.1f}s")
+    # the CPU oracle runs first, in worker processes forked before the GPU is touched
+    cpu, cpu_outs = None, {}
+    if not (args.no_cpu or args.timed_only):
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f}s on {cpu_workers()} worker processes")
+        cpu, cpu_outs = cpu_baseline(w, K_host, V_host, q_host, kv_new, warm, warm + steps - 1, args.cpu_seconds)
+    import torch
+    b = Bench(w, steps, warm, K_host, V_host, q_host, kv_new)
 
     # ---- warmup ----
     for i in range(warm):
@@ -499,13 +561,18 @@ def main():
         del src, dst
 
     # ---- timed pass: product calls only, one kernel family timed with events ----
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda") if (args.timed_only and args.cold) else None
+    fsum = torch.zeros((), dtype=torch.float32, device="cuda")
     Z.profile_start(args.kernel)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(warm, warm + steps):
+        if flush is not None:
+            torch.sum(flush, dim=0, out=fsum)          # reads 512 MiB: clean lines evict the step's bytes
         b.step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    del flush
     k_ms, k_launch, k_drop = Z.profile_collect()
     Z.profile_start(None)
     out_timed = b.out.clone()
@@ -513,7 +580,7 @@ def main():
     if args.timed_only:
         print(json.dumps({"workload": w.name, "steps": steps, "warmup": warm, "ms_per_step": wall * 1e3 / steps,
                           "kernel": args.kernel, "kernel_avg_us": k_ms / max(1, k_launch) * 1e3,
-                          "launches": k_launch, "device_status": status}), flush=True)
+                          "launches": k_launch, "device_status": status, "cold": bool(args.cold)}), flush=True)
         return
     log(f"[bench] timed {steps} steps in {wall * 1e3:.2f} ms; {args.kernel}: {k_launch} launches, "
         f"{k_ms / max(1, k_launch) * 1e3:.2f} us avg")
@@ -526,6 +593,7 @@ def main():
     lsel = torch.zeros(max(1, b.sizes.level_sel_bytes // 4), dtype=torch.int32, device="cuda")
     totals = {}
     kept1 = []
+    gpu_steps = {}
     for i in range(warm, warm + steps):
         b.step(i, level_stats=stats, level_sel=lsel)
         N = int(b.c.seq_lens[0].item())
@@ -533,8 +601,10 @@ def main():
         for k, v in by.items():
             totals[k] = totals.get(k, 0) + v
         kept1.append(b.nsel.cpu().numpy().reshape(-1))
+        if any(k[0] == i for k in cpu_outs):
+            gpu_steps[i] = (b.sel.cpu().numpy(), b.nsel.cpu().numpy(), b.out.cpu().numpy(), b.lse.cpu().numpy())
         if i == warm:
-            st0 = stats.cpu().numpy().reshape(w.n_q_heads, L, 2)
+            st0 = stats.cpu().numpy().reshape(w.batch, w.n_q_heads, L, 2)[0]      # the first sequence
     torch.cuda.synchronize()
     replay_same = bool(torch.equal(out_timed, b.out))
     step_total = sum(totals.values())
@@ -570,29 +640,35 @@ def main():
 
     # ---- cold run: flush MALL / L2 between steps, time each step with events ----
     cold_qps = None
+    cold_ms = ck_ms = 0.0
+    ck_launch = 0
     if not args.no_cold:
         b.restore(snap)
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+        fsum = torch.zeros((), dtype=torch.float32, device="cuda")
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        Z.profile_start(args.kernel)
         for j, i in enumerate(range(warm, warm + steps)):
-            flush.fill_(j & 0xff)
+            torch.sum(flush, dim=0, out=fsum)          # reads 512 MiB: clean lines evict the step's bytes
             ev[j][0].record()
             b.step(i)
             ev[j][1].record()
         torch.cuda.synchronize()
+        ck_ms, ck_launch, _ = Z.profile_collect()
+        Z.profile_start(None)
         cold_ms = sum(a.elapsed_time(z) for a, z in ev) / steps
         cold_qps = w.batch / (cold_ms / 1e3)
         del flush
 
-    cpu = None
-    if not args.no_cpu:
-        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f}s")
-        cpu = cpu_baseline(b, args.cpu_seconds)
+    if cpu is not None:
+        cpu["parity"] = cpu_parity(w, cpu_outs, gpu_steps)
 
     ms_step = wall * 1e3 / steps
     kb = sum(v for k, v in totals.items() if k == args.kernel or k.split("@")[0] == args.kernel)
     k_avg_s = (k_ms / 1e3) / max(1, k_launch)
     achieved = (kb / steps) / k_avg_s if k_avg_s > 0 else 0.0
+    ck_avg_s = (ck_ms / 1e3) / max(1, ck_launch)
+    cold_achieved = (kb / steps) / ck_avg_s if ck_avg_s > 0 else 0.0
     res = {
         "metric": METRIC,
         "value": round(w.batch * steps / wall, 2),
@@ -604,7 +680,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": w.kv_dtype,
+        "precision": {"kv_cache": w.kv_dtype, "summaries_scores_softmax": "f32",
+                      "attention_logits": ("q split into bf16 hi + lo parts on the matrix cores (about 2^-16 "
+                                           "relative), f32 accumulation") if w.kv_dtype == "bf16" else "f32"},
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_tokens": w.n_tokens, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "branching": w.branching,
@@ -613,9 +692,14 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 2), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK, 4), "traffic": measured_traffic(args.kernel, w.name),
                      "kernel": args.kernel, "bytes_per_launch": int(kb / steps),
-                     "avg_launch_us": round(k_avg_s * 1e6, 3), "launches": k_launch},
+                     "avg_launch_us": round(k_avg_s * 1e6, 3), "launches": k_launch,
+                     "cold": ({"achieved": round(cold_achieved / 1e9, 2), "frac": round(cold_achieved / HBM_PEAK, 4),
+                               "avg_launch_us": round(ck_avg_s * 1e6, 3), "launches": ck_launch,
+                               "note": "a 512 MiB buffer is read between steps, so the 256 MB Infinity Cache "
+                                       "holds none of the step's bytes"} if ck_launch else None)},
         "cpu_baseline": cpu,
         "step_hbm_frac": round((step_total / steps) / (ms_step / 1e3) / HBM_PEAK, 4),
+        "step_hbm_frac_cold": round((step_total / steps) / (cold_ms / 1e3) / HBM_PEAK, 4) if cold_ms else None,
         "step_bytes": int(step_total / steps),
         "bytes_by_kernel": {k: int(v / steps) for k, v in sorted(totals.items())},
         "zha_attend_ms": round(zha_ms, 5),
