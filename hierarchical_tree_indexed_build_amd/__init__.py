@@ -30,7 +30,8 @@ EXPORTED = ("zha_query_sizes", "zha_build_tree", "zha_append", "zha_route", "zha
 class Geom(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("branching", ctypes.c_int32), ("n_levels", ctypes.c_int32),
-                ("capacity", ctypes.c_int64), ("kv_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("capacity", ctypes.c_int64), ("kv_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("level_p", ctypes.c_float * ZHA_MAX_LEVELS)]
 
 
 class Sizes(ctypes.Structure):
@@ -94,9 +95,12 @@ def _check(code: int, where: str):
 
 
 def make_geom(batch, n_q_heads, n_kv_heads, head_dim, branching, n_levels, capacity, kv_dtype="bf16",
-              scale=0.0) -> Geom:
+              scale=0.0, level_p=None) -> Geom:
+    """A zha_geom. level_p (optional, n_levels floats, level 1 first): the cut
+    fraction of each level, overriding a call's top_p where non-zero."""
     kd = {"bf16": ZHA_KV_BF16, "fp32": ZHA_KV_F32}[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
-    return Geom(batch, n_q_heads, n_kv_heads, head_dim, branching, n_levels, capacity, kd, scale)
+    lp = (ctypes.c_float * ZHA_MAX_LEVELS)(*([float(x) for x in level_p] if level_p is not None else []))
+    return Geom(batch, n_q_heads, n_kv_heads, head_dim, branching, n_levels, capacity, kd, scale, lp)
 
 
 def query_sizes(geom: Geom, max_t: int) -> Sizes:

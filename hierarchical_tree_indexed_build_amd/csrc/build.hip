@@ -9,7 +9,8 @@
 // device function, so append-built and build-built summaries are bit-identical.
 //
 // Mapping: one wave64 per node. Pass 1 gives each child row 64/b lanes, each
-// holding d*b/64 contiguous elements, for the b dot products with r; pass 2
+// holding d*b/64 contiguous elements (for b > 64, b/64 rows per lane), for
+// the b dot products with r; pass 2
 // gives each lane d/64 dimensions and walks the b rows (re-read from L1/L2) to
 // form the weighted sum, so the node is read from HBM once and every store is a
 // coalesced 4*d-byte row.
@@ -24,9 +25,65 @@ __device__ __forceinline__ void load_n(const T* __restrict__ p, float (&x)[N]) {
     else load_row<N>(p, x);
 }
 
+// More children than lanes (b = 128, 256): lane l owns child rows l, l + 64,
+// ...; each row's dot product with r is taken 8 elements at a time (r is the
+// same for every lane). The softmax and the weighted sum are as below.
 template <typename CT, int B, int D>
-__device__ __forceinline__ void reduce_node_wave(const CT* __restrict__ ch, const float* __restrict__ r,
+__device__ __forceinline__ void reduce_node_wide(const CT* __restrict__ ch, const float* __restrict__ r,
                                                  float scale, float* __restrict__ out, int lane) {
+    constexpr int RPL = B / kWave;   // child rows per lane
+    constexpr int DPL = D / kWave;   // dimensions per lane in pass 2
+    float z[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) z[i] = 0.f;
+#pragma unroll 2
+    for (int e0 = 0; e0 < D; e0 += 8) {
+        float rr[8];
+        load_row<8>(r + e0, rr);
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            float x[8];
+            load_row<8>(ch + static_cast<int64_t>(i * kWave + lane) * D + e0, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[i] = fmaf(rr[e], x[e], z[i]);
+        }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        z[i] *= scale;
+        mloc = fmaxf(mloc, z[i]);
+    }
+    const float m = group_max<kWave>(mloc);
+    float w[RPL], sloc = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        w[i] = expf(z[i] - m);
+        sloc += w[i];
+    }
+    const float tot = group_sum<kWave>(sloc);
+
+    float acc[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+#pragma unroll 8
+        for (int j = 0; j < kWave; ++j) {
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[i]), j));
+            float v[DPL];
+            load_n<DPL>(ch + static_cast<int64_t>(i * kWave + j) * D + lane * DPL, v);
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wj, v[k], acc[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) out[lane * DPL + k] = acc[k] / tot;
+}
+
+template <typename CT, int B, int D>
+__device__ __forceinline__ void reduce_node_narrow(const CT* __restrict__ ch, const float* __restrict__ r,
+                                                   float scale, float* __restrict__ out, int lane) {
     constexpr int LPR = kWave / B;   // lanes per child row
     constexpr int EPL = D / LPR;     // elements per lane in pass 1
     constexpr int DPL = D / kWave;   // dimensions per lane in pass 2
@@ -56,6 +113,13 @@ __device__ __forceinline__ void reduce_node_wave(const CT* __restrict__ ch, cons
     }
 #pragma unroll
     for (int k = 0; k < DPL; ++k) out[lane * DPL + k] = acc[k] / tot;
+}
+
+template <typename CT, int B, int D>
+__device__ __forceinline__ void reduce_node_wave(const CT* __restrict__ ch, const float* __restrict__ r,
+                                                 float scale, float* __restrict__ out, int lane) {
+    if constexpr (B > kWave) reduce_node_wide<CT, B, D>(ch, r, scale, out, lane);
+    else reduce_node_narrow<CT, B, D>(ch, r, scale, out, lane);
 }
 
 struct BuildParams {
@@ -231,6 +295,8 @@ static hipError_t dispatch_b(int b, const BuildParams& bp, int64_t tw, int lv, h
         case 16: return launch_level_t<CT, 16, D>(bp, tw, lv, st);
         case 32: return launch_level_t<CT, 32, D>(bp, tw, lv, st);
         case 64: return launch_level_t<CT, 64, D>(bp, tw, lv, st);
+        case 128: return launch_level_t<CT, 128, D>(bp, tw, lv, st);
+        case 256: return launch_level_t<CT, 256, D>(bp, tw, lv, st);
     }
     return hipErrorInvalidValue;
 }
@@ -309,6 +375,8 @@ static hipError_t fused_b(int b, const FusedParams& fp, int B_, int Hkv, hipStre
         case 16: return launch_fused_t<KT, 16, D>(fp, B_, Hkv, st);
         case 32: return launch_fused_t<KT, 32, D>(fp, B_, Hkv, st);
         case 64: return launch_fused_t<KT, 64, D>(fp, B_, Hkv, st);
+        case 128: return launch_fused_t<KT, 128, D>(fp, B_, Hkv, st);
+        case 256: return launch_fused_t<KT, 256, D>(fp, B_, Hkv, st);
     }
     return hipErrorInvalidValue;
 }

@@ -1905,7 +1905,8 @@ struct UpperParams {
     int64_t rows;
     int64_t cap;
     int b, lb, L, li_lo, Hq, Hkv, G, T;
-    float top_p, scale;
+    float top_p_l[ZHA_MAX_LEVELS];   // cut fraction per level
+    float scale;
 };
 
 struct UpperShared {
@@ -2019,7 +2020,7 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
         if (ncand <= kWave) {                  // one wave, no block steps
             __syncthreads();                   // publishes sc[]
             if (wave == 0) {
-                const int mw = wave_cut_small(score, static_cast<int>(ncand), p.top_p, sh.bs,
+                const int mw = wave_cut_small(score, static_cast<int>(ncand), p.top_p_l[li], sh.bs,
                                               [&](int64_t pos, int64_t k) { emit(pos, k); mark(k, 1u); });
                 if (lane == 0) sh.bs.wcount = mw;
             }
@@ -2027,7 +2028,7 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
             m = sh.bs.wcount;
         } else {
             mx = block_max_f<NW>(mx, sh.bs);   // its barriers also publish sc[]
-            const CutBoundary cb = cut_boundary<NW>(score, ncand, mx, p.top_p, sh.bins, sh.bs);
+            const CutBoundary cb = cut_boundary<NW>(score, ncand, mx, p.top_p_l[li], sh.bins, sh.bs);
             m = cut_compact<NW>(score, ncand, cb, p.lb < 5 ? p.lb : 5, sh.bs, emit, mark);
         }
         uint32_t* bm = p.bitmap + rh * p.bm_words_total + p.bm_off[li];
@@ -2110,7 +2111,7 @@ static hipError_t launch_cut(const Geo& g, const RouteArgs& a, int li, hipStream
     cp.L = g.L;
     cp.Hq = g.Hq;
     cp.T = a.ri.T;
-    cp.top_p = a.top_p;
+    cp.top_p = a.top_p_l[li];
     cp.pairs = static_cast<int64_t>(a.rows) * g.Hq;
     {
         ProfScope ps("route_cut", li + 1, st);
@@ -2177,7 +2178,7 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
         up.Hkv = g.Hkv;
         up.G = g.G;
         up.T = a.ri.T;
-        up.top_p = a.top_p;
+        for (int l = 0; l < ZHA_MAX_LEVELS; ++l) up.top_p_l[l] = a.top_p_l[l];
         up.scale = g.scale;
         {
             ProfScope ps("route_upper", 0, st);
@@ -2264,7 +2265,7 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
             xp.L = g.L;
             xp.Hq = g.Hq;
             xp.T = a.ri.T;
-            xp.top_p = a.top_p;
+            xp.top_p = a.top_p_l[li];
             xp.pmax = reinterpret_cast<const float*>(ws + lay.pmax);
             xp.pruns = reinterpret_cast<const int32_t*>(ws + lay.pruns);
             xp.pmax_stride = lay.pmax_stride;

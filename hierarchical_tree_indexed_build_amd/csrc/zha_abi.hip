@@ -47,8 +47,8 @@ zha_status make_geo(const zha_geom* in, Geo* g) {
         return fail(ZHA_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4, 8 or 16 (got %d)", G);
     if (in->head_dim != 64 && in->head_dim != 128)
         return fail(ZHA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", in->head_dim);
-    if (!is_pow2_in(in->branching, 2, 64))
-        return fail(ZHA_ERR_UNSUPPORTED, "branching must be 2, 4, 8, 16, 32 or 64 (got %d)", in->branching);
+    if (!is_pow2_in(in->branching, 2, 256))
+        return fail(ZHA_ERR_UNSUPPORTED, "branching must be a power of two in [2, 256] (got %d)", in->branching);
     if (in->n_levels < 1 || in->n_levels > ZHA_MAX_LEVELS)
         return fail(ZHA_ERR_SHAPE, "n_levels must be in [1, %d] (got %d)", ZHA_MAX_LEVELS, in->n_levels);
     if (in->capacity < 1 || in->capacity >= (int64_t(1) << 31))
@@ -56,6 +56,13 @@ zha_status make_geo(const zha_geom* in, Geo* g) {
     if (in->kv_dtype != ZHA_KV_BF16 && in->kv_dtype != ZHA_KV_F32)
         return fail(ZHA_ERR_UNSUPPORTED, "kv_dtype must be ZHA_KV_BF16 or ZHA_KV_F32");
     if (!(in->scale >= 0.f) || std::isinf(in->scale)) return fail(ZHA_ERR_SHAPE, "scale must be finite and >= 0");
+    for (int l = 0; l < ZHA_MAX_LEVELS; ++l) {
+        const float v = in->level_p[l];
+        if (l < in->n_levels ? !(v == 0.f || (v > 0.f && v <= 1.f)) : v != 0.f)
+            return fail(ZHA_ERR_SHAPE, "level_p[%d] must be 0 or in (0, 1] for a level of the tree, 0 past it (got %g)",
+                        l, static_cast<double>(v));
+        g->level_p[l] = v;
+    }
     g->B = in->batch;
     g->Hq = in->n_q_heads;
     g->Hkv = in->n_kv_heads;
@@ -296,6 +303,7 @@ static zha_status route_impl(const Geo& g, const float* q, int32_t t, const int3
     a.rows = rows;
     a.summaries = summaries;
     a.top_p = top_p;
+    for (int l = 0; l < ZHA_MAX_LEVELS; ++l) a.top_p_l[l] = g.level_p[l] > 0.f ? g.level_p[l] : top_p;
     a.sel_cap = sel_capacity;
     a.sel_blocks = sel_blocks;
     a.n_sel = n_sel;

@@ -73,6 +73,7 @@ struct Geo {
     int64_t sum_off[ZHA_MAX_LEVELS];   // element offset of each level in the summary buffer
     int64_t sel_off[ZHA_MAX_LEVELS];   // element offset of each level in a level_sel buffer (per row count)
     int64_t nodes_total;               // sum of nodes[l]
+    float level_p[ZHA_MAX_LEVELS];     // per-level cut fraction, 0 = the call's top_p
 };
 
 // Byte layout of the workspace for `rows` query rows.
@@ -159,6 +160,7 @@ struct RouteArgs {
     int rows;
     const float* summaries;
     float top_p;
+    float top_p_l[ZHA_MAX_LEVELS];   // the cut fraction of each level (top_p or the geometry's schedule)
     int sel_cap;
     int32_t* sel_blocks;
     int32_t* n_sel;

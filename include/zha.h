@@ -99,11 +99,18 @@ typedef struct zha_geom {
     int32_t n_q_heads;   /* H_q, a multiple of H_kv, H_q / H_kv <= 16 */
     int32_t n_kv_heads;  /* H_kv >= 1 */
     int32_t head_dim;    /* d: 64 or 128 */
-    int32_t branching;   /* b: 2, 4, 8, 16, 32 or 64 */
+    int32_t branching;   /* b: a power of two in [2, 256] */
     int32_t n_levels;    /* L: 1..ZHA_MAX_LEVELS */
     int64_t capacity;    /* tokens allocated per sequence, < 2^31 */
     int32_t kv_dtype;    /* ZHA_KV_BF16 or ZHA_KV_F32 */
     float   scale;       /* score scale; 0 selects 1/sqrt(d) */
+    /* Per-level top-p schedule ("Subquadratic Attention with a Hierarchical
+     * Tree-Structured Indexer", Future Directions: scaling p with depth, since
+     * a fixed p < 1 keeps about p^L of the mass after L levels). Entry l-1 in
+     * (0, 1] is the cut fraction at level l and overrides a call's top_p
+     * there; 0 keeps the call's top_p. Entries at levels past n_levels must
+     * be 0. A zero-initialised struct routes every level with top_p. */
+    float   level_p[ZHA_MAX_LEVELS];
 } zha_geom;
 
 typedef struct zha_sizes {

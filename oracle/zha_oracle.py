@@ -256,15 +256,24 @@ def route_level(q, X_level, level, parents, n_visible, b, n_levels, p, scale, sc
     return topp_cut(ids, s, p, s64)
 
 
-def route(q: np.ndarray, tree: Sequence[np.ndarray], n_visible: int, b: int, p: float,
+def level_fraction(p, level: int) -> float:
+    """The cut fraction at ``level``: p itself, or p[level - 1] for a per-level
+    schedule [SAHTI §Future Directions: scaling p with depth]."""
+    return float(p) if np.ndim(p) == 0 else float(p[level - 1])
+
+
+def route(q: np.ndarray, tree: Sequence[np.ndarray], n_visible: int, b: int, p,
           scale: Optional[float] = None, score_dtype=F32) -> RouteResult:
-    """Top-down routing of one query through one (sequence, kv head) tree."""
+    """Top-down routing of one query through one (sequence, kv head) tree.
+
+    ``p`` is one fraction for every level or a schedule [p_1, ..., p_L]."""
     L = len(tree)
     scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
     cuts: List[Optional[CutResult]] = [None] * L
     parents = None
     for level in range(L, 0, -1):
-        c = route_level(q, tree[level - 1], level, parents, n_visible, b, L, p, scale, score_dtype)
+        c = route_level(q, tree[level - 1], level, parents, n_visible, b, L, level_fraction(p, level), scale,
+                        score_dtype)
         cuts[level - 1] = c
         parents = c.selected
     return RouteResult(cuts, [c.selected for c in cuts])

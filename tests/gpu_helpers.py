@@ -35,12 +35,12 @@ def kv_tensor(w, arr):
 class Staged:
     """A workload's cache, tree and buffers on cuda:0, plus host copies for the oracle."""
 
-    def __init__(self, w, max_t=None, build=True, n_tokens=None):
+    def __init__(self, w, max_t=None, build=True, n_tokens=None, level_p=None):
         t = torch()
         self.w = w
         self.T = w.queries_per_step if max_t is None else max_t
         self.geom = Z.make_geom(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.branching, w.n_levels,
-                                w.capacity, w.kv_dtype)
+                                w.capacity, w.kv_dtype, level_p=level_p)
         self.cache = Z.Cache(self.geom, self.T)
         self.K_np, self.V_np = W.kv_cache(w)
         self.cache.K.copy_(kv_tensor(w, self.K_np))
@@ -127,7 +127,8 @@ def attn_tol(w):
 
 def teacher_forced(st, qn, qpos_np, stats, lsel, p, trees, pairs=None):
     """Check every level's kept set of each (row, query head), teacher-forced: the
-    oracle cuts the candidates of the GPU's own kept parents. Candidate counts
+    oracle cuts the candidates of the GPU's own kept parents (p: one fraction, or
+    a per-level schedule, level 1 first). Candidate counts
     must be exact, kept ids ascending, and the sets equal up to the margin
     exemptions. ``pairs`` (a list of (sequence, query head)) restricts the check
     to a sample. Returns the number of exempt differences."""
@@ -146,11 +147,12 @@ def teacher_forced(st, qn, qpos_np, stats, lsel, p, trees, pairs=None):
             for level in range(w.n_levels, 0, -1):
                 v, cnt, cand = kept[level]
                 gpu_ids = v[r, hq, :cnt[r, hq]]
+                pl = O.level_fraction(p, level)
                 cut = O.route_level(qn[s, t_, hq], tree[level - 1], level, parents, N, w.branching,
-                                    w.n_levels, p, w.scale)
+                                    w.n_levels, pl, w.scale)
                 assert cand[r, hq] == len(cut.ids), (s, t_, hq, level, cand[r, hq], len(cut.ids))
                 assert np.all(np.diff(gpu_ids) > 0), "kept ids must be ascending"
-                flips += check_sets(gpu_ids, cut, p, f"row {r} head {hq} level {level}")
+                flips += check_sets(gpu_ids, cut, pl, f"row {r} head {hq} level {level}")
                 parents = gpu_ids
     return flips
 

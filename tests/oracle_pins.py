@@ -279,7 +279,7 @@ def pin_route_golden(orc):
     for c in _load("route_closed_forms.json")["cases"]:
         K, R, q = _golden_inputs(c)
         tree = orc.build_tree(K, R, c["b"])
-        r = orc.route(q, tree, c["N"], c["b"], c["p"])
+        r = orc.route(q, tree, c["N"], c["b"], c["p_levels"] if "p_levels" in c else c["p"])
         for lvl, rs in c["kept"].items():
             got = list(r.selected[int(lvl) - 1])
             assert got == list(_ranges(rs)), (c["name"], lvl, got)

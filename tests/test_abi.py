@@ -62,12 +62,21 @@ def test_sizes_match_layout_arithmetic():
     assert Z.query_sizes(g, 64).workspace_bytes > s.workspace_bytes
 
 
+def test_level_schedule_is_validated():
+    assert Z.query_sizes(_geom(level_p=[0.9, 1.0, 0.5, 0.0]), 1).max_rows == 1
+    for bad in ([1.5, 0, 0, 0], [-0.1, 0, 0, 0], [0.9, 0.9, 0.9, 0.9, 0.9], [float("nan"), 0, 0, 0]):
+        with pytest.raises(Z.ZhaError) as e:
+            Z.query_sizes(_geom(level_p=bad), 1)
+        assert e.value.code == Z.ZHA_ERR_SHAPE and b"level_p" in Z.lib().zha_last_error()
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(n_kv_heads=6), Z.ZHA_ERR_SHAPE),
     (dict(n_q_heads=24, n_kv_heads=8), Z.ZHA_ERR_UNSUPPORTED),      # group of 3
     (dict(head_dim=96), Z.ZHA_ERR_UNSUPPORTED),
     (dict(branching=24), Z.ZHA_ERR_UNSUPPORTED),
-    (dict(branching=128), Z.ZHA_ERR_UNSUPPORTED),
+    (dict(branching=512), Z.ZHA_ERR_UNSUPPORTED),
+    (dict(branching=96), Z.ZHA_ERR_UNSUPPORTED),
     (dict(n_levels=0), Z.ZHA_ERR_SHAPE),
     (dict(n_levels=9), Z.ZHA_ERR_SHAPE),
     (dict(capacity=0), Z.ZHA_ERR_SHAPE),

@@ -20,7 +20,8 @@ import pytest
 import hierarchical_tree_indexed_build_amd as Z
 import workloads as W
 from oracle import zha_oracle as O
-from tests.gpu_helpers import (Staged, attn_tol, kv_tensor, level_kept, say, summary_tol, teacher_forced, torch)
+from tests.gpu_helpers import (Staged, attn_tol, check_attention, kv_tensor, level_kept, say, summary_tol,
+                               teacher_forced, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -95,6 +96,33 @@ def test_route_parity(case):
         for h in range(w.n_q_heads):
             n = c1[r, h]
             assert np.array_equal(s_np[r, h, :n], v1[r, h, :n])
+
+
+# Per-level top-p schedules (level 1 first): through the fused upper-level
+# kernel, the split cut (one row) and the per-pair cut (batch 8), and the
+# attention over the resulting index sets.
+SCHEDULES = [(("decode1m", 1, 1), [0.8, 0.97, 0.999]), (("gqa128k", 1, 8), [0.99, 0.9, 0.7]),
+             (("tiny", 0, None), [0.5, 0.91, 1.0]), (("gqa128k", 0, 1), [0.95 ** 0.25] * 4)]
+
+
+@pytest.mark.parametrize("case,sched", SCHEDULES, ids=["decode1m-s1", "gqa128k-s1-b8", "tiny", "gqa128k-root"])
+def test_route_parity_level_schedule(case, sched):
+    t = torch()
+    w = _w(*case)
+    say(f"[schedule] {w.name} batch {w.batch}: level_p {sched}")
+    st = Staged(w, level_p=sched)
+    T = w.queries_per_step
+    q_pos = _qpos(st, T)
+    # top_p is overridden at every level by the schedule
+    qn, q, sel, nsel, stats, lsel, _ = _route(st, T, q_pos, top_p=0.123)
+    flips = teacher_forced(st, qn, q_pos.cpu().numpy(), stats, lsel, sched, st.oracle_trees())
+    out = t.zeros_like(q)
+    lse = t.zeros(q.shape[:3], dtype=t.float32, device="cuda")
+    Z.sparse_attend(st.geom, q, q_pos, st.cache.K, st.cache.V, st.cache.seq_lens, sel, nsel, out, lse, st.cache.ws)
+    t.cuda.synchronize()
+    worst = check_attention(st, qn, q_pos.cpu().numpy(), out, lse, sel, nsel)
+    say(f"  margin-exempt differences: {flips}; worst attention error {worst:.3g}; "
+        f"kept per level {[round(float(stats[..., l, 1].float().mean()), 1) for l in range(w.n_levels)]}")
 
 
 # Crafted key caches whose scores crowd the cut: every key equal (all scores

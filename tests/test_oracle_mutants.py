@@ -38,6 +38,10 @@ MUTANTS = {
     "attend-unnormalised": ("return (e @ v) / l, mx + math.log(l)", "return (e @ v) / e.max(), mx + math.log(l)"),
     "lse-no-max": ("return (e @ v) / l, mx + math.log(l)", "return (e @ v) / l, math.log(l)"),
     "span-off": ("return b ** level", "return b ** (level + 1)"),
+    "level-p-reversed": ("return float(p) if np.ndim(p) == 0 else float(p[level - 1])",
+                         "return float(p) if np.ndim(p) == 0 else float(p[-level])"),
+    "level-p-first-only": ("return float(p) if np.ndim(p) == 0 else float(p[level - 1])",
+                           "return float(p) if np.ndim(p) == 0 else float(p[0])"),
     "exempt-all": ("return np.array(sorted(ex), dtype=np.int64)",
                    "return np.array(sorted(int(i) for i in cut.ids), dtype=np.int64)"),
     "exempt-none": ("return np.array(sorted(ex), dtype=np.int64)", "return np.array([], dtype=np.int64)"),
