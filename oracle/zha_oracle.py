@@ -39,6 +39,18 @@ Readings where the pages leave a step open (each restated where used):
   tokens (its own token included); token 0 is always attended; I(q) is a set.
 * R-6 causal rows: a query at position t sees N = t + 1 tokens and only nodes
   complete within them.
+* R-7 the full scoring rule (the tangent tree, an option beside R-1/R-2): each
+  node keeps R tangents t_r(q) = q . k_hat_r / sqrt(d) + b_hat_r, one per
+  reference query of its level, and scores max_r t_r(q). At level 1 the
+  tangents are the page's: k_hat_r is the attention of q_hat_r over the chunk
+  with the keys as values, b_hat_r = F_C(q_hat_r) - q_hat_r . k_hat_r / sqrt(d).
+  Above, a node's log-mass is read as the log-sum-exp of its children's
+  estimates, F(q) = LSE_j max_r' t_{j,r'}(q), and its tangents are the
+  first-order expansion of that function at the level's reference queries: at
+  q_hat_r each child enters with its best tangent there (lowest r' on ties),
+  the logits z_j = t_{j,r*}(q_hat_r) include the child offsets, w =
+  softmax(z), k_hat_r = sum_j w_j k_hat_{j,r*}, b_hat_r = LSE(z) - q_hat_r .
+  k_hat_r / sqrt(d). Keys and offsets are stored in fp32.
 """
 from __future__ import annotations
 
@@ -140,6 +152,99 @@ def build_tree_incremental(K: np.ndarray, R: np.ndarray, b: int, scale: Optional
 
 
 # ----------------------------------------------------------------------------
+# The full scoring rule: R tangents per node [SAHTI §Tree Construction; R-7]
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class TangentLevel:
+    """One level of a tangent tree (R-7)."""
+    keys: np.ndarray     # (n, R, d) fp32: k_hat of each reference query
+    offs: np.ndarray     # (n, R) fp32: b_hat
+    gap: np.ndarray      # (n, R) fp64: smallest lead of a child's chosen tangent over its runner-up (inf at level 1)
+
+    @property
+    def shape(self):
+        return self.keys.shape[:1] + self.keys.shape[2:]
+
+    def __len__(self):
+        return self.keys.shape[0]
+
+
+def tangent_pool(child_keys: np.ndarray, child_offs: np.ndarray, refs: np.ndarray, b: int,
+                 scale: float) -> TangentLevel:
+    """Tangents of consecutive groups of b children, at reference queries refs (R, d).
+
+    child_keys (n, Rc, d) and child_offs (n, Rc) are the children's tangents:
+    raw keys with offset 0 at level 1 (Rc = 1). For reference query r, child j
+    enters with its tangent of largest value at refs[r] (lowest index on ties):
+    z_j = refs[r] . key * scale + off; w = softmax(z); k_hat = sum_j w_j key_j;
+    b_hat = LSE(z) - refs[r] . k_hat * scale.
+    """
+    X = np.asarray(child_keys, dtype=F64)
+    O = np.asarray(child_offs, dtype=F64)
+    n, Rc, d = X.shape
+    m = n // b
+    X = X[:m * b].reshape(m, b, Rc, d)
+    O = O[:m * b].reshape(m, b, Rc)
+    R = refs.shape[0]
+    keys = np.zeros((m, R, d), F32)
+    offs = np.zeros((m, R), F32)
+    gap = np.full((m, R), np.inf)
+    for r in range(R):
+        q = np.asarray(refs[r], dtype=F64)
+        t = scale * (X @ q) + O                          # (m, b, Rc): every child tangent at refs[r]
+        best = np.argmax(t, axis=2)                      # first maximum: lowest index on ties
+        z = np.take_along_axis(t, best[..., None], axis=2)[..., 0]
+        if Rc > 1:
+            runner = np.sort(t, axis=2)[..., -2]
+            gap[:, r] = (z - runner).min(axis=1) if m else gap[:, r]
+        ksel = np.take_along_axis(X, best[..., None, None], axis=2)[:, :, 0, :]   # (m, b, d)
+        zm = z.max(axis=1, keepdims=True)
+        e = np.exp(z - zm)
+        w = e / e.sum(axis=1, keepdims=True)
+        kh = np.einsum("mj,mjd->md", w, ksel)
+        lse = zm[:, 0] + np.log(e.sum(axis=1))
+        keys[:, r] = kh.astype(F32)
+        offs[:, r] = (lse - scale * (kh @ q)).astype(F32)
+    return TangentLevel(keys, offs, gap)
+
+
+def build_tangent_tree(K: np.ndarray, R: np.ndarray, b: int, scale: Optional[float] = None,
+                       slab: Optional[int] = None) -> List[TangentLevel]:
+    """Every level's tangents for one (sequence, kv head) (R-7).
+
+    K: (N, d) keys. R: (L, R, d) reference queries of this kv head. With
+    ``slab`` (a multiple of b), level 1 is pooled ``slab`` keys at a time."""
+    d = K.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    L = R.shape[0]
+    levels: List[TangentLevel] = []
+    if L == 0:
+        return levels
+    n1 = K.shape[0] // b
+    step = n1 * b if slab is None else slab
+    assert step == 0 or step % b == 0, "a slab must hold whole leaf chunks"
+    parts = []
+    for t0 in range(0, n1 * b, max(step, 1)):
+        Kc = np.asarray(K[t0:min(t0 + step, n1 * b)])
+        parts.append(tangent_pool(Kc[:, None, :], np.zeros((Kc.shape[0], 1)), R[0], b, scale))
+    if not parts:
+        parts = [tangent_pool(np.zeros((0, 1, d)), np.zeros((0, 1)), R[0], b, scale)]
+    levels.append(TangentLevel(np.concatenate([x.keys for x in parts]), np.concatenate([x.offs for x in parts]),
+                               np.concatenate([x.gap for x in parts])))
+    for l in range(1, L):
+        up = levels[-1]
+        levels.append(tangent_pool(up.keys, up.offs, R[l], b, scale))
+    return levels
+
+
+def tangent_logmass(q: np.ndarray, level: TangentLevel, ids: np.ndarray, scale: float) -> np.ndarray:
+    """max_r t_r(q) of nodes ``ids``, fp64 (R-7)."""
+    k = np.asarray(level.keys[ids], dtype=F64)            # (n, R, d)
+    o = np.asarray(level.offs[ids], dtype=F64)            # (n, R)
+    return (scale * (k @ np.asarray(q, dtype=F64)) + o).max(axis=1) if len(ids) else np.zeros(0)
+
+
+# ----------------------------------------------------------------------------
 # Top-p cut [SAHTI §Routing, m_l(q); R-3]
 # ----------------------------------------------------------------------------
 @dataclasses.dataclass
@@ -234,9 +339,13 @@ def level_candidates(level: int, parents: Optional[np.ndarray], n_visible: int, 
     return np.concatenate(out) if out else np.zeros(0, np.int64)
 
 
-def score_nodes(q: np.ndarray, X: np.ndarray, ids: np.ndarray, scale: float):
-    """(fp32-rounded scores, exact fp64 scores) of nodes ``ids`` of one level (R-2)."""
-    s64 = scale * (np.asarray(X[ids], dtype=F64) @ np.asarray(q, dtype=F64))
+def score_nodes(q: np.ndarray, X, ids: np.ndarray, scale: float):
+    """(fp32-rounded scores, exact fp64 scores) of nodes ``ids`` of one level:
+    q . x / sqrt(d) (R-2), or max_r t_r(q) for a tangent level (R-7)."""
+    if isinstance(X, TangentLevel):
+        s64 = tangent_logmass(q, X, ids, scale)
+    else:
+        s64 = scale * (np.asarray(X[ids], dtype=F64) @ np.asarray(q, dtype=F64))
     return s64.astype(F32).astype(F64), s64
 
 

@@ -435,9 +435,153 @@ def pin_split_merge(orc):
     assert abs(M - lse) < 1e-12
 
 
+# ----------------------------------------------------------------------------
+# the full scoring rule: tangents, offsets, max over R reference queries
+# ----------------------------------------------------------------------------
+def _entropy(z):
+    w = np.exp(z - z.max())
+    w = w / w.sum()
+    return float(-(w[w > 0] * np.log(w[w > 0])).sum())
+
+
+def pin_tangent_golden(orc):
+    """Hand-worked one-dimensional trees (d = 1, scale 1) where the offset, the
+    maximum over reference queries and the child offsets each change the answer."""
+    K = np.array([[0.0], [0.0], [1.0], [-1.0]], np.float32)     # chunk 0 = {0, 0}, chunk 1 = {1, -1}
+    th = math.tanh(10.0)
+    H = math.log(math.exp(10) + math.exp(-10)) - 10 * th         # entropy of softmax(+-10): chunk 1's offset
+    # one reference query q_hat = 10: chunk 0 is (k_hat 0, b_hat ln 2), chunk 1 is (tanh 10, H)
+    t1 = orc.build_tangent_tree(K, np.array([[[10.0]]], np.float32), 2, scale=1.0)
+    assert abs(float(t1[0].keys[0, 0, 0])) < 1e-7 and abs(float(t1[0].offs[0, 0]) - math.log(2)) < 1e-7
+    assert abs(float(t1[0].keys[1, 0, 0]) - th) < 1e-7 and abs(float(t1[0].offs[1, 0]) - H) < 1e-7
+    # q = 0.5: scores ln 2 (chunk 0) vs 0.5 tanh 10 + H (chunk 1); chunk 0 alone holds 2 / (2 + e^0.5) = 0.548
+    r = orc.route(np.array([0.5], np.float32), t1, 4, 2, 0.5, scale=1.0)
+    assert list(r.selected[0]) == [0], list(r.selected[0])
+    # the summary rule without offsets keeps chunk 1 (scores 0 and 0.5 tanh 10)
+    m = orc.build_tree(K, np.array([[10.0]], np.float32), 2, scale=1.0)
+    assert list(orc.route(np.array([0.5], np.float32), m, 4, 2, 0.5, scale=1.0).selected[0]) == [1]
+    # two reference queries +-10: chunk 1 scores max(+-q tanh 10) + H = 0.5 + H at q = -0.5, so at p = 0.6
+    # chunk 0 (mass 2 / (2 + e^0.5) = 0.548) no longer suffices; with q_hat = 10 alone chunk 1 scores
+    # -0.5 + H and chunk 0 holds 2 / (2 + e^-0.5) = 0.767
+    t2 = orc.build_tangent_tree(K, np.array([[[10.0], [-10.0]]], np.float32), 2, scale=1.0)
+    assert list(orc.route(np.array([-0.5], np.float32), t2, 4, 2, 0.6, scale=1.0).selected[0]) == [0, 1]
+    assert list(orc.route(np.array([-0.5], np.float32), t1, 4, 2, 0.6, scale=1.0).selected[0]) == [0]
+    # a parent over the two chunks with q_hat = 0: logits are the children's offsets (ln 2, H), so
+    # w = (2, e^H) / (2 + e^H), k_hat = tanh(10) e^H / (2 + e^H) and b_hat = ln(2 + e^H)
+    t3 = orc.build_tangent_tree(K, np.array([[[10.0]], [[0.0]]], np.float32), 2, scale=1.0)
+    eH = math.exp(H)
+    assert abs(float(t3[1].keys[0, 0, 0]) - th * eH / (2 + eH)) < 1e-7
+    assert abs(float(t3[1].offs[0, 0]) - math.log(2 + eH)) < 1e-7
+
+
+def pin_tangent_level1(orc):
+    """Level 1 against the definitions: b_hat is the entropy of the pooling weights
+    (0 <= b_hat <= ln b); every tangent lies below the chunk's log-sum-exp F_C and
+    touches it at its reference query (convexity); identical keys give the key
+    itself with offset ln b, a tangent exact everywhere."""
+    rng = np.random.default_rng(31)
+    b, d, R = 8, 16, 3
+    K = rng.standard_normal((20 * b, d)).astype(np.float32)
+    refs = rng.standard_normal((1, R, d)).astype(np.float32)
+    sc = 1 / math.sqrt(d)
+    t = orc.build_tangent_tree(K, refs, b)[0]
+    for i in range(20):
+        C = K[i * b:(i + 1) * b].astype(np.float64)
+        for r in range(R):
+            z = sc * (C @ refs[0, r].astype(np.float64))
+            assert abs(float(t.offs[i, r]) - _entropy(z)) < 1e-6
+            assert -1e-6 <= float(t.offs[i, r]) <= math.log(b) + 1e-6
+            tr = sc * float(t.keys[i, r].astype(np.float64) @ refs[0, r]) + float(t.offs[i, r])
+            assert abs(tr - logsumexp(z)) < 2e-6
+        for _ in range(5):
+            q = rng.standard_normal(d) * 2
+            F = logsumexp(sc * (C @ q))
+            assert np.all(sc * (t.keys[i].astype(np.float64) @ q) + t.offs[i] <= F + 2e-6)
+    same = np.repeat(K[:1], b, axis=0)
+    ts = orc.build_tangent_tree(same, refs, b)[0]
+    assert np.array_equal(ts.keys[0, 0], K[0]) and abs(float(ts.offs[0, 0]) - math.log(b)) < 1e-6
+
+
+def pin_tangent_upper_levels(orc):
+    """Levels above: every node's estimate max_r t_r(q) stays below the true
+    log-sum-exp of the keys it spans (each level of lower bounds, combined by a
+    monotone LSE); a parent's tangent touches the log-sum-exp of its children's
+    estimates at its reference query, and its key is that function's gradient
+    there (central differences, scale included)."""
+    rng = np.random.default_rng(32)
+    b, d, R, L = 4, 8, 3, 3
+    K = (rng.standard_normal((b ** L * 2, d)) * 1.5).astype(np.float32)
+    refs = rng.standard_normal((L, R, d)).astype(np.float32)
+    sc = 1 / math.sqrt(d)
+    tree = orc.build_tangent_tree(K, refs, b)
+    Kd = K.astype(np.float64)
+    for _ in range(6):
+        q = rng.standard_normal(d) * 2
+        for l in range(L):
+            est = orc.tangent_logmass(q, tree[l], np.arange(len(tree[l])), sc)
+            span = b ** (l + 1)
+            true = np.array([logsumexp(sc * (Kd[i * span:(i + 1) * span] @ q)) for i in range(len(tree[l]))])
+            assert np.all(est <= true + 1e-5), (l, (est - true).max())
+
+    def children_lse(l, i, x):
+        ch = tree[l - 1]
+        idx = np.arange(i * b, (i + 1) * b)
+        v = sc * (ch.keys[idx].astype(np.float64) @ x) + ch.offs[idx]
+        return logsumexp(v.max(axis=1))
+
+    for l in (1, 2):
+        for i in range(len(tree[l])):
+            for r in range(R):
+                x0 = refs[l, r].astype(np.float64)
+                tr = sc * float(tree[l].keys[i, r].astype(np.float64) @ x0) + float(tree[l].offs[i, r])
+                assert abs(tr - children_lse(l, i, x0)) < 1e-5
+                if tree[l].gap[i, r] < 1e-3:
+                    continue                                    # a child's best tangent is near a switch
+                eps = 1e-5
+                g = np.array([(children_lse(l, i, x0 + eps * e) - children_lse(l, i, x0 - eps * e)) / (2 * eps)
+                              for e in np.eye(d)])
+                assert np.abs(g - sc * tree[l].keys[i, r].astype(np.float64)).max() < 1e-4
+
+
+def pin_tangent_duplicate_refs(orc):
+    """A repeated reference query adds a tangent equal to an existing one: the
+    node estimates and the routing do not change."""
+    rng = np.random.default_rng(33)
+    b, d, L, N = 4, 8, 3, 200
+    K = rng.standard_normal((N, d)).astype(np.float32)
+    a = rng.standard_normal((L, 2, d)).astype(np.float32)
+    dup = np.concatenate([a, a[:, :1]], axis=1)
+    t1, t2 = orc.build_tangent_tree(K, a, b), orc.build_tangent_tree(K, dup, b)
+    sc = 1 / math.sqrt(d)
+    for _ in range(4):
+        q = (rng.standard_normal(d) * 2).astype(np.float32)
+        for l in range(L):
+            ids = np.arange(len(t1[l]))
+            # equal up to fp64 rounding (BLAS may round a repeated row differently by its position)
+            assert np.abs(orc.tangent_logmass(q, t1[l], ids, sc) - orc.tangent_logmass(q, t2[l], ids, sc)).max() < 1e-12
+        r1, r2 = orc.route(q, t1, N, b, 0.9), orc.route(q, t2, N, b, 0.9)
+        assert all(np.array_equal(x, y) for x, y in zip(r1.selected, r2.selected))
+
+
+def pin_tangent_route_golden(orc):
+    """With zero reference queries every node's offset is the same at a level
+    (l ln b: uniform weights all the way up), so the tangent tree routes the
+    hand-worked cases exactly as the summary rule does."""
+    for c in _load("route_closed_forms.json")["cases"]:
+        K, R, q = _golden_inputs(c)
+        if c["keys"] != "leafconst":
+            continue
+        tree = orc.build_tangent_tree(K, R[:, None, :], c["b"])
+        r = orc.route(q, tree, c["N"], c["b"], c["p_levels"] if "p_levels" in c else c["p"])
+        for lvl, rs in c["kept"].items():
+            assert list(r.selected[int(lvl) - 1]) == list(_ranges(rs)), (c["name"], lvl)
+
+
 ALL_PINS = [
     pin_geometry, pin_summary_sdpa, pin_summary_closed_forms, pin_incremental_equals_batch,
     pin_cut_golden, pin_cut_bruteforce, pin_cut_exemptions, pin_cut_uniform,
     pin_route_golden, pin_route_dense_mask, pin_causal_prefix,
     pin_attend_sdpa, pin_p1_dense, pin_eq1_identity, pin_split_merge,
+    pin_tangent_golden, pin_tangent_level1, pin_tangent_upper_levels, pin_tangent_duplicate_refs,
+    pin_tangent_route_golden,
 ]

@@ -42,6 +42,17 @@ MUTANTS = {
                          "return float(p) if np.ndim(p) == 0 else float(p[-level])"),
     "level-p-first-only": ("return float(p) if np.ndim(p) == 0 else float(p[level - 1])",
                            "return float(p) if np.ndim(p) == 0 else float(p[0])"),
+    "tangent-offset-sign": ("offs[:, r] = (lse - scale * (kh @ q)).astype(F32)",
+                            "offs[:, r] = (scale * (kh @ q) - lse).astype(F32)"),
+    "tangent-score-no-offset": ("return (scale * (k @ np.asarray(q, dtype=F64)) + o).max(axis=1)",
+                                "return (scale * (k @ np.asarray(q, dtype=F64))).max(axis=1)"),
+    "tangent-mean-over-refs": ("return (scale * (k @ np.asarray(q, dtype=F64)) + o).max(axis=1)",
+                               "return (scale * (k @ np.asarray(q, dtype=F64)) + o).mean(axis=1)"),
+    "tangent-child-offsets-dropped": ("t = scale * (X @ q) + O", "t = scale * (X @ q) + 0 * O"),
+    "tangent-first-child-tangent": ("best = np.argmax(t, axis=2)", "best = np.zeros_like(np.argmax(t, axis=2))"),
+    "tangent-lse-no-max": ("lse = zm[:, 0] + np.log(e.sum(axis=1))", "lse = np.log(e.sum(axis=1))"),
+    "tangent-same-ref-every-level": ("levels.append(tangent_pool(up.keys, up.offs, R[l], b, scale))",
+                                     "levels.append(tangent_pool(up.keys, up.offs, R[0], b, scale))"),
     "exempt-all": ("return np.array(sorted(ex), dtype=np.int64)",
                    "return np.array(sorted(int(i) for i in cut.ids), dtype=np.int64)"),
     "exempt-none": ("return np.array(sorted(ex), dtype=np.int64)", "return np.array([], dtype=np.int64)"),
