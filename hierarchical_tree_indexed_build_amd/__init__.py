@@ -20,6 +20,7 @@ ZHA_OK, ZHA_ERR_NULL, ZHA_ERR_SHAPE, ZHA_ERR_UNSUPPORTED, ZHA_ERR_WORKSPACE, ZHA
 ZHA_DEV_SEL_OVERFLOW = 1
 ZHA_DEV_APPEND_OVERFLOW = 2
 ZHA_KV_BF16, ZHA_KV_F32 = 0, 1
+ZHA_SCORE_SUMMARY, ZHA_SCORE_TANGENT = 0, 1
 ZHA_MAX_LEVELS = 8
 
 EXPORTED = ("zha_query_sizes", "zha_build_tree", "zha_append", "zha_route", "zha_sparse_attend", "zha_attend",
@@ -31,12 +32,13 @@ class Geom(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("branching", ctypes.c_int32), ("n_levels", ctypes.c_int32),
                 ("capacity", ctypes.c_int64), ("kv_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("level_p", ctypes.c_float * ZHA_MAX_LEVELS)]
+                ("level_p", ctypes.c_float * ZHA_MAX_LEVELS), ("n_refs", ctypes.c_int32), ("scoring", ctypes.c_int32)]
 
 
 class Sizes(ctypes.Structure):
     _fields_ = [("summaries_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t),
                 ("level_nodes", ctypes.c_int64 * ZHA_MAX_LEVELS), ("level_offset", ctypes.c_int64 * ZHA_MAX_LEVELS),
+                ("level_bias_offset", ctypes.c_int64 * ZHA_MAX_LEVELS),
                 ("level_sel_offset", ctypes.c_int64 * ZHA_MAX_LEVELS), ("level_sel_bytes", ctypes.c_size_t),
                 ("max_rows", ctypes.c_int32)]
 
@@ -95,12 +97,16 @@ def _check(code: int, where: str):
 
 
 def make_geom(batch, n_q_heads, n_kv_heads, head_dim, branching, n_levels, capacity, kv_dtype="bf16",
-              scale=0.0, level_p=None) -> Geom:
+              scale=0.0, level_p=None, n_refs=0, scoring="summary") -> Geom:
     """A zha_geom. level_p (optional, n_levels floats, level 1 first): the cut
-    fraction of each level, overriding a call's top_p where non-zero."""
+    fraction of each level, overriding a call's top_p where non-zero. scoring
+    "summary" (one reference query, q . summary) or "tangent" (n_refs
+    reference queries, the maximum of the node's tangents)."""
     kd = {"bf16": ZHA_KV_BF16, "fp32": ZHA_KV_F32}[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
     lp = (ctypes.c_float * ZHA_MAX_LEVELS)(*([float(x) for x in level_p] if level_p is not None else []))
-    return Geom(batch, n_q_heads, n_kv_heads, head_dim, branching, n_levels, capacity, kd, scale, lp)
+    sc = {"summary": ZHA_SCORE_SUMMARY, "tangent": ZHA_SCORE_TANGENT}[scoring] if isinstance(scoring, str) \
+        else int(scoring)
+    return Geom(batch, n_q_heads, n_kv_heads, head_dim, branching, n_levels, capacity, kd, scale, lp, n_refs, sc)
 
 
 def query_sizes(geom: Geom, max_t: int) -> Sizes:
@@ -208,11 +214,24 @@ def level_sel_view(level_sel, sizes: Sizes, geom: Geom, rows: int, level: int):
 
 
 def summaries_view(summaries, sizes: Sizes, geom: Geom, level: int):
-    """View of one level of the summary buffer: [B, H_kv, level_nodes, d]."""
+    """View of one level of the summary buffer: [B, H_kv, level_nodes, d], or
+    [B, H_kv, level_nodes, R, d] (the tangents' keys) with tangent scoring."""
     n = sizes.level_nodes[level - 1]
     off = sizes.level_offset[level - 1]
-    cnt = geom.batch * geom.n_kv_heads * n * geom.head_dim
-    return summaries[off:off + cnt].view(geom.batch, geom.n_kv_heads, n, geom.head_dim)
+    R = max(1, geom.n_refs)
+    cnt = geom.batch * geom.n_kv_heads * n * R * geom.head_dim
+    v = summaries[off:off + cnt]
+    if geom.scoring == ZHA_SCORE_TANGENT:
+        return v.view(geom.batch, geom.n_kv_heads, n, R, geom.head_dim)
+    return v.view(geom.batch, geom.n_kv_heads, n, geom.head_dim)
+
+
+def offsets_view(summaries, sizes: Sizes, geom: Geom, level: int):
+    """The tangents' offsets of one level (tangent scoring): [B, H_kv, level_nodes, R]."""
+    n = sizes.level_nodes[level - 1]
+    off = sizes.level_bias_offset[level - 1]
+    R = max(1, geom.n_refs)
+    return summaries[off:off + geom.batch * geom.n_kv_heads * n * R].view(geom.batch, geom.n_kv_heads, n, R)
 
 
 class Cache:

@@ -122,6 +122,155 @@ __device__ __forceinline__ void reduce_node_wave(const CT* __restrict__ ch, cons
     else reduce_node_narrow<CT, B, D>(ch, r, scale, out, lane);
 }
 
+// ---- tangent scoring ----
+// One tangent of a node: the first-order expansion, at reference query r, of
+// the log-sum-exp of its children's estimates. Child j offers Rc tangents
+// (key row (j Rc + r') of ch, offset choff[j Rc + r']; raw keys with no offset
+// at level 1) and enters with the one largest at r (lowest r' on ties):
+// z_j = scale r . key + off, w = softmax(z), key = sum_j w_j key_j, offset =
+// LSE(z) - scale r . key ("Subquadratic Attention with a Hierarchical
+// Tree-Structured Indexer", §Tree Construction: k_hat_r, b_hat_r).
+template <typename CT, int B, int D>
+__device__ __forceinline__ void tangent_node_narrow(const CT* __restrict__ ch, const float* __restrict__ choff, int Rc,
+                                                    const float* __restrict__ r, float scale, float* __restrict__ okey,
+                                                    float* __restrict__ ooff, int lane) {
+    // no implicit contraction: the append kernel (child count known to be 1)
+    // and the build kernel must round every step alike (explicit fmaf only)
+#pragma clang fp contract(off)
+    constexpr int LPR = kWave / B;   // lanes per child
+    constexpr int EPL = D / LPR;     // elements per lane in pass 1
+    constexpr int DPL = D / kWave;   // dimensions per lane in pass 2
+    const int row = lane / LPR, part = lane % LPR;
+    float rr[EPL];
+    load_n<EPL>(r + part * EPL, rr);
+    float z = -INFINITY;
+    int rs = 0;
+    for (int rc = 0; rc < Rc; ++rc) {
+        float x[EPL];
+        load_n<EPL>(ch + static_cast<int64_t>(row * Rc + rc) * D + part * EPL, x);
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) t = fmaf(rr[e], x[e], t);
+        t = group_sum<LPR>(t) * scale;
+        if (choff) t += choff[row * Rc + rc];
+        if (rc == 0 || t > z) {       // strict: the lowest index keeps a tie
+            z = t;
+            rs = rc;
+        }
+    }
+    const float m = group_max<kWave>(z);
+    const float w = expf(z - m);
+    const float tot = group_sum<kWave>(w) * (1.0f / LPR);   // each child is held by LPR lanes
+    float acc[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+#pragma unroll 4
+    for (int j = 0; j < B; ++j) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j * LPR));
+        const int rj = __builtin_amdgcn_readlane(rs, j * LPR);
+        float v[DPL];
+        load_n<DPL>(ch + static_cast<int64_t>(j * Rc + rj) * D + lane * DPL, v);
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wj, v[k], acc[k]);
+    }
+    float rq[DPL];
+    load_n<DPL>(r + lane * DPL, rq);
+    float dq = 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+        acc[k] = acc[k] / tot;
+        okey[lane * DPL + k] = acc[k];
+        dq = fmaf(rq[k], acc[k], dq);
+    }
+    dq = group_sum<kWave>(dq);
+    if (lane == 0) *ooff = (m + logf(tot)) - scale * dq;
+}
+
+// The same with more children than lanes: lane l owns children l, l + 64, ...
+template <typename CT, int B, int D>
+__device__ __forceinline__ void tangent_node_wide(const CT* __restrict__ ch, const float* __restrict__ choff, int Rc,
+                                                  const float* __restrict__ r, float scale, float* __restrict__ okey,
+                                                  float* __restrict__ ooff, int lane) {
+    // no implicit contraction: the append kernel (child count known to be 1)
+    // and the build kernel must round every step alike (explicit fmaf only)
+#pragma clang fp contract(off)
+    constexpr int RPL = B / kWave;
+    constexpr int DPL = D / kWave;
+    float z[RPL];
+    int rs[RPL];
+    for (int rc = 0; rc < Rc; ++rc) {
+        float t[RPL];
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) t[i] = 0.f;
+#pragma unroll 2
+        for (int e0 = 0; e0 < D; e0 += 8) {
+            float rr[8];
+            load_row<8>(r + e0, rr);
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                float x[8];
+                load_row<8>(ch + static_cast<int64_t>((i * kWave + lane) * Rc + rc) * D + e0, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t[i] = fmaf(rr[e], x[e], t[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            float v = t[i] * scale;
+            if (choff) v += choff[(i * kWave + lane) * Rc + rc];
+            if (rc == 0 || v > z[i]) {
+                z[i] = v;
+                rs[i] = rc;
+            }
+        }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) mloc = fmaxf(mloc, z[i]);
+    const float m = group_max<kWave>(mloc);
+    float w[RPL], sloc = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        w[i] = expf(z[i] - m);
+        sloc += w[i];
+    }
+    const float tot = group_sum<kWave>(sloc);
+    float acc[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+#pragma unroll 4
+        for (int j = 0; j < kWave; ++j) {
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[i]), j));
+            const int rj = __builtin_amdgcn_readlane(rs[i], j);
+            float v[DPL];
+            load_n<DPL>(ch + static_cast<int64_t>((i * kWave + j) * Rc + rj) * D + lane * DPL, v);
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wj, v[k], acc[k]);
+        }
+    }
+    float rq[DPL];
+    load_n<DPL>(r + lane * DPL, rq);
+    float dq = 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+        acc[k] = acc[k] / tot;
+        okey[lane * DPL + k] = acc[k];
+        dq = fmaf(rq[k], acc[k], dq);
+    }
+    dq = group_sum<kWave>(dq);
+    if (lane == 0) *ooff = (m + logf(tot)) - scale * dq;
+}
+
+template <typename CT, int B, int D>
+__device__ __forceinline__ void tangent_node_wave(const CT* __restrict__ ch, const float* __restrict__ choff, int Rc,
+                                                  const float* __restrict__ r, float scale, float* __restrict__ okey,
+                                                  float* __restrict__ ooff, int lane) {
+    if constexpr (B > kWave) tangent_node_wide<CT, B, D>(ch, choff, Rc, r, scale, okey, ooff, lane);
+    else tangent_node_narrow<CT, B, D>(ch, choff, Rc, r, scale, okey, ooff, lane);
+}
+
 struct BuildParams {
     const void* children;      // level-1: K; else summaries of level l-1
     float* out;                // summaries of level l
@@ -133,19 +282,27 @@ struct BuildParams {
     int64_t cap;
     int Hkv, BH, slots, mode, t_new;
     float scale;
+    // tangent scoring: R tangents per node, Rc per child (1 at level 1); offsets of the children
+    // (null at level 1) and of this level; r points at the level's [Hkv, R, D] reference queries
+    const float* child_off;
+    float* out_off;
+    int R, Rc;
 };
 
 enum { kModeBuild = 0, kModeAppend = 1 };
 
-template <typename CT, int B, int D>
+template <typename CT, int B, int D, bool TAN>
 __global__ __launch_bounds__(256) void build_level_kernel(BuildParams p) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t total = static_cast<int64_t>(p.BH) * p.slots;
+    const int RW = TAN ? p.R : 1;                        // waves per node: one per tangent
+    const int64_t total = static_cast<int64_t>(p.BH) * p.slots * RW;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * (blockDim.x / kWave);
     for (int64_t wv = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave; wv < total;
          wv += stride) {
-        const int bh = static_cast<int>(wv / p.slots);
-        const int64_t k = wv % p.slots;
+        const int64_t nw = wv / RW;
+        const int rr = static_cast<int>(wv % RW);
+        const int bh = static_cast<int>(nw / p.slots);
+        const int64_t k = nw % p.slots;
         const int s = bh / p.Hkv, h = bh % p.Hkv;
         const int64_t len = imin(imax(p.seq_lens[s], 0), p.cap);
         int64_t i, hi;
@@ -158,9 +315,18 @@ __global__ __launch_bounds__(256) void build_level_kernel(BuildParams p) {
             hi = (len + p.t_new) / p.span;
         }
         if (i >= hi) continue;
-        const CT* ch = static_cast<const CT*>(p.children) + (bh * p.child_rows + i * B) * D;
-        float* o = p.out + (bh * p.out_rows + i) * D;
-        reduce_node_wave<CT, B, D>(ch, p.r + h * D, p.scale, o, lane);
+        if constexpr (TAN) {
+            const int64_t c0 = (static_cast<int64_t>(bh) * p.child_rows + i * B) * p.Rc;   // first child row
+            const CT* ch = static_cast<const CT*>(p.children) + c0 * D;
+            const float* co = p.child_off ? p.child_off + c0 : nullptr;
+            const int64_t orow = (static_cast<int64_t>(bh) * p.out_rows + i) * p.R + rr;
+            tangent_node_wave<CT, B, D>(ch, co, p.Rc, p.r + (static_cast<int64_t>(h) * p.R + rr) * D, p.scale,
+                                        p.out + orow * D, p.out_off + orow, lane);
+        } else {
+            const CT* ch = static_cast<const CT*>(p.children) + (bh * p.child_rows + i * B) * D;
+            float* o = p.out + (bh * p.out_rows + i) * D;
+            reduce_node_wave<CT, B, D>(ch, p.r + h * D, p.scale, o, lane);
+        }
     }
 }
 
@@ -221,11 +387,13 @@ struct FusedParams {
     int64_t nodes[ZHA_MAX_LEVELS];
     int64_t sum_off[ZHA_MAX_LEVELS];
     int64_t span[ZHA_MAX_LEVELS];
-    int Hkv, L, t_new;
+    int64_t bias_off[ZHA_MAX_LEVELS];   // tangent scoring: each level's offsets in the summary buffer
+    int Hkv, L, t_new, R;
+    bool tangent;
     float scale;
 };
 
-template <typename KT, int B, int D>
+template <typename KT, int B, int D, bool TAN>
 __global__ __launch_bounds__(1024) void append_fused_kernel(FusedParams p) {
     const int s = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
@@ -257,15 +425,35 @@ __global__ __launch_bounds__(1024) void append_fused_kernel(FusedParams p) {
             // completes no node needs no fence
             __threadfence();
             float* lvl = p.summaries + p.sum_off[l];
-            const float* r = p.ref_q + (static_cast<int64_t>(l) * p.Hkv + h) * D;
-            for (int64_t i = lo; i < hi; ++i) {
-                float* o = lvl + (bh * p.nodes[l] + i) * D;
-                if (l == 0) {
-                    const KT* ch = reinterpret_cast<const KT*>(p.K) + (bh * p.cap + i * B) * D;
-                    reduce_node_wave<KT, B, D>(ch, r, p.scale, o, lane);
-                } else {
-                    const float* ch = p.summaries + p.sum_off[l - 1] + (bh * p.nodes[l - 1] + i * B) * D;
-                    reduce_node_wave<float, B, D>(ch, r, p.scale, o, lane);
+            if constexpr (TAN) {
+                const float* r0 = p.ref_q + (static_cast<int64_t>(l) * p.Hkv + h) * p.R * D;
+                for (int64_t i = lo; i < hi; ++i) {
+                    for (int rr = 0; rr < p.R; ++rr) {
+                        const int64_t orow = (bh * p.nodes[l] + i) * p.R + rr;
+                        float* ok = lvl + orow * D;
+                        float* oo = p.summaries + p.bias_off[l] + orow;
+                        if (l == 0) {
+                            const KT* ch = reinterpret_cast<const KT*>(p.K) + (bh * p.cap + i * B) * D;
+                            tangent_node_wave<KT, B, D>(ch, nullptr, 1, r0 + rr * D, p.scale, ok, oo, lane);
+                        } else {
+                            const int64_t c0 = (bh * p.nodes[l - 1] + i * B) * p.R;
+                            tangent_node_wave<float, B, D>(p.summaries + p.sum_off[l - 1] + c0 * D,
+                                                           p.summaries + p.bias_off[l - 1] + c0, p.R, r0 + rr * D,
+                                                           p.scale, ok, oo, lane);
+                        }
+                    }
+                }
+            } else {
+                const float* r = p.ref_q + (static_cast<int64_t>(l) * p.Hkv + h) * D;
+                for (int64_t i = lo; i < hi; ++i) {
+                    float* o = lvl + (bh * p.nodes[l] + i) * D;
+                    if (l == 0) {
+                        const KT* ch = reinterpret_cast<const KT*>(p.K) + (bh * p.cap + i * B) * D;
+                        reduce_node_wave<KT, B, D>(ch, r, p.scale, o, lane);
+                    } else {
+                        const float* ch = p.summaries + p.sum_off[l - 1] + (bh * p.nodes[l - 1] + i * B) * D;
+                        reduce_node_wave<float, B, D>(ch, r, p.scale, o, lane);
+                    }
                 }
             }
         }
@@ -279,10 +467,15 @@ __global__ __launch_bounds__(1024) void append_fused_kernel(FusedParams p) {
 // ----------------------------------------------------------------------------
 template <typename CT, int B, int D>
 static hipError_t launch_level_t(const BuildParams& bp, int64_t total_waves, int level, hipStream_t st) {
-    const int64_t blocks = std::min<int64_t>((total_waves + 3) / 4, 16384);
+    const bool tan = bp.out_off != nullptr;
+    const int64_t waves = total_waves * (tan ? bp.R : 1);
+    const int64_t blocks = std::min<int64_t>((waves + 3) / 4, 16384);
     if (blocks <= 0) return hipSuccess;
     ProfScope ps("build_level", level, st);
-    hipLaunchKernelGGL((build_level_kernel<CT, B, D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, bp);
+    if (tan)
+        hipLaunchKernelGGL((build_level_kernel<CT, B, D, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, bp);
+    else
+        hipLaunchKernelGGL((build_level_kernel<CT, B, D, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, bp);
     return hipGetLastError();
 }
 
@@ -307,7 +500,11 @@ hipError_t launch_build_level(const Geo& g, int level, const void* K, const floa
     const int l = level - 1;
     bp.children = (level == 1) ? K : static_cast<const void*>(summaries + g.sum_off[l - 1]);
     bp.out = summaries + g.sum_off[l];
-    bp.r = ref_q + static_cast<int64_t>(l) * g.Hkv * g.D;
+    bp.r = ref_q + static_cast<int64_t>(l) * g.Hkv * g.R * g.D;
+    bp.R = g.R;
+    bp.Rc = (level == 1) ? 1 : g.R;
+    bp.child_off = (g.tangent && level > 1) ? summaries + g.bias_off[l - 1] : nullptr;
+    bp.out_off = g.tangent ? summaries + g.bias_off[l] : nullptr;
     bp.seq_lens = seq_lens;
     bp.child_rows = (level == 1) ? g.cap : g.nodes[l - 1];
     bp.out_rows = g.nodes[l];
@@ -362,7 +559,10 @@ template <typename KT, int B, int D>
 static hipError_t launch_fused_t(const FusedParams& fp, int B_, int Hkv, hipStream_t st) {
     const int waves = std::min(Hkv, 16);
     ProfScope ps("append_fused", 0, st);
-    hipLaunchKernelGGL((append_fused_kernel<KT, B, D>), dim3(B_), dim3(waves * kWave), 0, st, fp);
+    if (fp.tangent)
+        hipLaunchKernelGGL((append_fused_kernel<KT, B, D, true>), dim3(B_), dim3(waves * kWave), 0, st, fp);
+    else
+        hipLaunchKernelGGL((append_fused_kernel<KT, B, D, false>), dim3(B_), dim3(waves * kWave), 0, st, fp);
     return hipGetLastError();
 }
 
@@ -398,7 +598,10 @@ hipError_t launch_append_fused(const Geo& g, void* K, void* V, const void* k_new
         fp.nodes[l] = g.nodes[l];
         fp.sum_off[l] = g.sum_off[l];
         fp.span[l] = g.span[l];
+        fp.bias_off[l] = g.bias_off[l];
     }
+    fp.R = g.R;
+    fp.tangent = g.tangent;
     fp.Hkv = g.Hkv;
     fp.L = g.L;
     fp.t_new = t_new;

@@ -49,7 +49,9 @@ namespace zha {
 struct ScoreParams {
     const float* q;            // [rows, Hq, D]
     RowInfo ri;
-    const float* summ;         // summaries of this level
+    const float* summ;         // summaries of this level (R tangent rows per node with tangent scoring)
+    const float* offs;         // tangent scoring: this level's offsets (R per node), else null
+    int R;                     // tangent rows per node (1 without tangent scoring)
     int64_t nodes_l;           // node slots per (batch, kv) at this level
     float* scores;             // ws scores base
     int64_t nodes_total;       // per (row, head) stride of the scores
@@ -154,7 +156,7 @@ __device__ __forceinline__ void score_deal(const ScoreParams& p, int* y_out, int
 // About 2048 waves in all, what the chip holds at once at this kernel's
 // register use; with few pairs they are dealt by parent counts (score_deal),
 // so a heavy pair's parents are spread as wide as the chip allows.
-template <int D, int G>
+template <int D, int G, bool TAN>
 __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams p) {
     static_assert(kScoreThreads == kWave, "a scoring workgroup is one wave");
     int y, run, N;
@@ -230,7 +232,10 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
     load_union(0);
     __asm__ volatile("" ::: "memory");      // keeps the loads above here, in one round
 
-    const float* summ = p.summ + (static_cast<int64_t>(s) * p.Hkv + kv) * p.nodes_l * D;
+    const int RT = TAN ? p.R : 1;                            // tangent rows per node
+    const int64_t nbase = (static_cast<int64_t>(s) * p.Hkv + kv) * p.nodes_l;   // this pair's first node
+    const float* summ = p.summ + nbase * RT * D;
+    const float* offs = TAN ? p.offs + nbase * RT : nullptr;
     float* sc0 = p.scores + rh0 * p.nodes_total + p.lvl_off;
     float hmx[G];                                            // per head: max over its own candidates
 #pragma unroll
@@ -242,14 +247,16 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
         const int64_t c0 = par << p.lb;
         const int64_t c1 = imin(c0 + p.b, nc);
         float x[UNR][DPL];
-        auto load_pass = [&](int64_t cb) {
+        float xo[UNR];                                   // tangent scoring: the rows' offsets
+        auto load_pass = [&](int64_t cb, int rr) {
 #pragma unroll
             for (int u2 = 0; u2 < UNR; ++u2) {
                 const int64_t c = imin(cb + u2 * RPP + sub, c1 - 1);   // a present row; extra results are dropped
-                load_row<DPL>(summ + c * D + part * DPL, x[u2]);
+                load_row<DPL>(summ + (c * RT + rr) * D + part * DPL, x[u2]);
+                if constexpr (TAN) xo[u2] = offs[c * RT + rr];
             }
         };
-        load_pass(c0);
+        load_pass(c0, 0);
         // split: which heads took the parent and where its children start in
         // each head's candidate order, read with the first summaries (without
         // the split, and for the incomplete parent past the ranked ones, from
@@ -278,21 +285,31 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
             }
         }
         for (int64_t cb = c0;;) {
+            // a node's score: q . summary * scale, or the largest of its R tangents
+            float best[UNR][G];
+            for (int rr = 0;;) {
+#pragma unroll
+                for (int u2 = 0; u2 < UNR; ++u2) {
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        float t = 0.f;
+#pragma unroll
+                        for (int e = 0; e < DPL; ++e) t = fmaf(qv[h][e], x[u2][e], t);
+                        t = fast_group_sum<LPR>(t) * p.scale;
+                        if constexpr (TAN) best[u2][h] = rr == 0 ? t + xo[u2] : fmaxf(best[u2][h], t + xo[u2]);
+                        else best[u2][h] = t;
+                    }
+                }
+                if (++rr >= RT) break;
+                load_pass(cb, rr);
+            }
 #pragma unroll
             for (int u2 = 0; u2 < UNR; ++u2) {
                 const int64_t c = cb + u2 * RPP + sub;
-                float acc[G];
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    float t = 0.f;
-#pragma unroll
-                    for (int e = 0; e < DPL; ++e) t = fmaf(qv[h][e], x[u2][e], t);
-                    acc[h] = fast_group_sum<LPR>(t);
-                }
                 if (c < c1) {
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
-                        const float sv = acc[h] * p.scale;
+                        const float sv = best[u2][h];
                         if (part == h) sc0[static_cast<int64_t>(h) * p.nodes_total + c] = sv;
                         if (split && cbase[h] >= 0) {
                             hmx[h] = fmaxf(hmx[h], sv);
@@ -307,7 +324,7 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
             }
             cb += UNR * RPP;
             if (cb >= c1) break;
-            load_pass(cb);
+            load_pass(cb, 0);
         }
     };
 
@@ -1907,6 +1924,8 @@ struct UpperParams {
     int b, lb, L, li_lo, Hq, Hkv, G, T;
     float top_p_l[ZHA_MAX_LEVELS];   // cut fraction per level
     float scale;
+    int64_t bias_off[ZHA_MAX_LEVELS];  // tangent scoring: each level's offsets
+    int R;                             // tangent rows per node (1 without tangent scoring)
 };
 
 struct UpperShared {
@@ -1918,7 +1937,7 @@ struct UpperShared {
     BlockScratch bs;
 };
 
-template <int D>
+template <int D, bool TAN>
 __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams p) {
     __shared__ UpperShared sh;
     constexpr int NW = kUpperWaves;
@@ -1978,21 +1997,35 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
         __syncthreads();
 
         // ---- score the candidates: a row per LPR lanes, RPP rows per wave pass ----
-        const float* summ = p.summaries + p.sum_off[li] + (static_cast<int64_t>(s) * p.Hkv + kv) * p.nodes[li] * D;
+        const int RT = TAN ? p.R : 1;                  // tangent rows per node
+        const int64_t nbase = (static_cast<int64_t>(s) * p.Hkv + kv) * p.nodes[li];
+        const float* summ = p.summaries + p.sum_off[li] + nbase * RT * D;
+        const float* offs = TAN ? p.summaries + p.bias_off[li] + nbase * RT : nullptr;
         float mx = -INFINITY;
         for (int64_t kb = static_cast<int64_t>(wave) * RPP * UNR; kb < ncand; kb += static_cast<int64_t>(nw) * RPP * UNR) {
-            float x[UNR][DPL];
+            float best[UNR];
+            for (int rr = 0; rr < RT; ++rr) {
+                float x[UNR][DPL], xo[UNR];
 #pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                const int64_t k = imin(kb + u * RPP + sub, ncand - 1);   // a present row; extra results are dropped
-                load_row<DPL>(summ + static_cast<int64_t>(sh.cid[k]) * D + part * DPL, x[u]);
+                for (int u = 0; u < UNR; ++u) {
+                    const int64_t k = imin(kb + u * RPP + sub, ncand - 1);   // a present row; extra results are dropped
+                    const int64_t row = static_cast<int64_t>(sh.cid[k]) * RT + rr;
+                    load_row<DPL>(summ + row * D + part * DPL, x[u]);
+                    if constexpr (TAN) xo[u] = offs[row];
+                }
+#pragma unroll
+                for (int u = 0; u < UNR; ++u) {
+                    float t = 0.f;
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) t = fmaf(qv[e], x[u][e], t);
+                    t = fast_group_sum<LPR>(t) * p.scale;
+                    if constexpr (TAN) best[u] = rr == 0 ? t + xo[u] : fmaxf(best[u], t + xo[u]);
+                    else best[u] = t;
+                }
             }
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
-                float t = 0.f;
-#pragma unroll
-                for (int e = 0; e < DPL; ++e) t = fmaf(qv[e], x[u][e], t);
-                t = fast_group_sum<LPR>(t) * p.scale;
+                const float t = best[u];
                 const int64_t k = kb + u * RPP + sub;
                 if (k < ncand) {
                     mx = fmaxf(mx, t);
@@ -2051,7 +2084,10 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
 template <int D, int G>
 static void launch_score_t(dim3 grid, const ScoreParams& sp, hipStream_t st) {
     ProfScope ps("route_score", sp.li + 1, st);
-    hipLaunchKernelGGL((route_score_kernel<D, G>), grid, dim3(kScoreThreads), 0, st, sp);
+    if (sp.offs)
+        hipLaunchKernelGGL((route_score_kernel<D, G, true>), grid, dim3(kScoreThreads), 0, st, sp);
+    else
+        hipLaunchKernelGGL((route_score_kernel<D, G, false>), grid, dim3(kScoreThreads), 0, st, sp);
 }
 
 template <int D>
@@ -2139,7 +2175,7 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
 
     // many rows per sequence: every level's scores on the matrix cores at
     // once, then the levels' cuts from the top
-    if (a.ri.T >= kDenseMinRows && dense_scores_fit(g, a.ri.T)) {
+    if (a.ri.T >= kDenseMinRows && dense_scores_fit(g, a.ri.T) && !g.tangent) {
         hipError_t e = launch_dense_scores(g, a.ri, a.q, a.summaries, scores, 0, g.L - 1, st);
         // one wave per pair while a level's candidates fit a wave's LDS
         for (int li = g.L - 1; e == hipSuccess && li >= 0; --li)
@@ -2180,12 +2216,18 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
         up.T = a.ri.T;
         for (int l = 0; l < ZHA_MAX_LEVELS; ++l) up.top_p_l[l] = a.top_p_l[l];
         up.scale = g.scale;
+        for (int l = 0; l < ZHA_MAX_LEVELS; ++l) up.bias_off[l] = g.bias_off[l];
+        up.R = g.R;
         {
             ProfScope ps("route_upper", 0, st);
-            if (g.D == 128)
-                hipLaunchKernelGGL(route_upper_kernel<128>, dim3(g.Hq, a.rows), dim3(kUpperThreads), 0, st, up);
-            else
-                hipLaunchKernelGGL(route_upper_kernel<64>, dim3(g.Hq, a.rows), dim3(kUpperThreads), 0, st, up);
+            const dim3 grid(g.Hq, a.rows), block(kUpperThreads);
+            if (g.D == 128) {
+                if (g.tangent) hipLaunchKernelGGL((route_upper_kernel<128, true>), grid, block, 0, st, up);
+                else hipLaunchKernelGGL((route_upper_kernel<128, false>), grid, block, 0, st, up);
+            } else {
+                if (g.tangent) hipLaunchKernelGGL((route_upper_kernel<64, true>), grid, block, 0, st, up);
+                else hipLaunchKernelGGL((route_upper_kernel<64, false>), grid, block, 0, st, up);
+            }
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -2197,6 +2239,8 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
         sp.q = a.q;
         sp.ri = a.ri;
         sp.summ = a.summaries + g.sum_off[li];
+        sp.offs = g.tangent ? a.summaries + g.bias_off[li] : nullptr;
+        sp.R = g.R;
         sp.nodes_l = g.nodes[li];
         sp.scores = scores;
         sp.nodes_total = g.nodes_total;

@@ -56,6 +56,12 @@ zha_status make_geo(const zha_geom* in, Geo* g) {
     if (in->kv_dtype != ZHA_KV_BF16 && in->kv_dtype != ZHA_KV_F32)
         return fail(ZHA_ERR_UNSUPPORTED, "kv_dtype must be ZHA_KV_BF16 or ZHA_KV_F32");
     if (!(in->scale >= 0.f) || std::isinf(in->scale)) return fail(ZHA_ERR_SHAPE, "scale must be finite and >= 0");
+    if (in->scoring != ZHA_SCORE_SUMMARY && in->scoring != ZHA_SCORE_TANGENT)
+        return fail(ZHA_ERR_UNSUPPORTED, "scoring must be ZHA_SCORE_SUMMARY or ZHA_SCORE_TANGENT (got %d)", in->scoring);
+    const int R = in->n_refs > 0 ? in->n_refs : 1;
+    if (in->n_refs < 0 || R > ZHA_MAX_REFS || (in->scoring == ZHA_SCORE_SUMMARY && R != 1))
+        return fail(ZHA_ERR_UNSUPPORTED, "n_refs must be 0 or 1 for summary scoring and 1..%d for tangent scoring (got %d)",
+                    ZHA_MAX_REFS, in->n_refs);
     for (int l = 0; l < ZHA_MAX_LEVELS; ++l) {
         const float v = in->level_p[l];
         if (l < in->n_levels ? !(v == 0.f || (v > 0.f && v <= 1.f)) : v != 0.f)
@@ -72,6 +78,8 @@ zha_status make_geo(const zha_geom* in, Geo* g) {
     g->lb = 0;
     while ((1 << g->lb) < g->b) ++g->lb;
     g->L = in->n_levels;
+    g->R = R;
+    g->tangent = in->scoring == ZHA_SCORE_TANGENT;
     g->kv_dtype = in->kv_dtype;
     g->cap = in->capacity;
     g->scale = in->scale > 0.f ? in->scale : 1.0f / std::sqrt(static_cast<float>(in->head_dim));
@@ -85,11 +93,17 @@ zha_status make_geo(const zha_geom* in, Geo* g) {
             g->nodes[l] = (l < g->L) ? g->cap / span : 0;
             g->sum_off[l] = soff;
             g->sel_off[l] = loff;
-            soff += static_cast<int64_t>(g->B) * g->Hkv * g->nodes[l] * g->D;
+            soff += static_cast<int64_t>(g->B) * g->Hkv * g->nodes[l] * g->R * g->D;
             loff += g->nodes[l];
         }
     }
     g->nodes_total = loff;
+    // tangent offsets follow every level's keys
+    for (int l = 0; l < ZHA_MAX_LEVELS; ++l) {
+        g->bias_off[l] = soff;
+        if (g->tangent) soff += static_cast<int64_t>(g->B) * g->Hkv * g->nodes[l] * g->R;
+    }
+    g->summ_total = soff;
     return ZHA_OK;
 }
 
@@ -236,12 +250,12 @@ zha_status zha_query_sizes(const zha_geom* geom, int32_t max_t, zha_sizes* out) 
     if ((st = check_rows(g, max_t, &rows))) return st;
     const WsLayout L = layout(g, rows);
     *out = zha_sizes{};
-    out->summaries_bytes = static_cast<size_t>(g.sum_off[ZHA_MAX_LEVELS - 1] +
-                                               int64_t(g.B) * g.Hkv * g.nodes[ZHA_MAX_LEVELS - 1] * g.D) * 4;
+    out->summaries_bytes = static_cast<size_t>(g.summ_total) * 4;
     out->workspace_bytes = L.total;
     for (int l = 0; l < ZHA_MAX_LEVELS; ++l) {
         out->level_nodes[l] = g.nodes[l];
         out->level_offset[l] = g.sum_off[l];
+        out->level_bias_offset[l] = g.bias_off[l];
         out->level_sel_offset[l] = g.sel_off[l];
     }
     out->level_sel_bytes = static_cast<size_t>(rows) * g.Hq * g.nodes_total * 4;

@@ -74,6 +74,10 @@ struct Geo {
     int64_t sel_off[ZHA_MAX_LEVELS];   // element offset of each level in a level_sel buffer (per row count)
     int64_t nodes_total;               // sum of nodes[l]
     float level_p[ZHA_MAX_LEVELS];     // per-level cut fraction, 0 = the call's top_p
+    int R;                             // tangents per node (reference queries per level and kv head)
+    bool tangent;                      // tangent scoring: offsets stored, score = max over the R tangents
+    int64_t bias_off[ZHA_MAX_LEVELS];  // element offset of each level's tangent offsets in the summary buffer
+    int64_t summ_total;                // elements of the summary buffer
 };
 
 // Byte layout of the workspace for `rows` query rows.

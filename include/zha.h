@@ -44,10 +44,13 @@
  *    zha_read_device_status.
  *  - Layouts (row-major, innermost last):
  *      K, V           [B, H_kv, capacity, d]   bf16 or fp32 (geom.kv_dtype)
- *      ref_q          [L, H_kv, d]             fp32
+ *      ref_q          [L, H_kv, R, d]          fp32 (R = n_refs, 1 for SUMMARY)
  *      summaries      fp32; level l (1-based) starts at element
- *                     sizes.level_offset[l-1]; node i of (batch s, kv head h)
- *                     is row (s*H_kv + h)*sizes.level_nodes[l-1] + i
+ *                     sizes.level_offset[l-1]; tangent r of node i of (batch
+ *                     s, kv head h) is row ((s*H_kv + h)*sizes.level_nodes[l-1]
+ *                     + i)*R + r (R = 1 for SUMMARY scoring); with TANGENT
+ *                     scoring its offset is element level_bias_offset[l-1] +
+ *                     that row index
  *      q, out         [B, T, H_q, d]           fp32
  *      lse            [B, T, H_q]              fp32 (natural log, scale included)
  *      seq_lens       [B]                      int32, tokens present per sequence
@@ -111,13 +114,34 @@ typedef struct zha_geom {
      * there; 0 keeps the call's top_p. Entries at levels past n_levels must
      * be 0. A zero-initialised struct routes every level with top_p. */
     float   level_p[ZHA_MAX_LEVELS];
+    /* Node scoring ("Subquadratic Attention with a Hierarchical
+     * Tree-Structured Indexer", §Tree Construction):
+     *  ZHA_SCORE_SUMMARY (0): one reference query per (level, kv head); a node
+     *    stores the softmax(r . c * scale)-weighted mean of its children and
+     *    scores q . summary * scale. n_refs must be 0 or 1.
+     *  ZHA_SCORE_TANGENT (1): n_refs = R reference queries per (level, kv
+     *    head); a node stores R tangents (key k_r, offset b_r) and scores
+     *    max_r (q . k_r * scale + b_r). At level 1, k_r is the attention of
+     *    reference query r over the chunk (keys as values) and b_r the chunk's
+     *    log-sum-exp at r minus r . k_r * scale. Above, each child enters with
+     *    its best tangent at r (lowest index on ties) and its offset added to
+     *    the pooling logit: the tangent at r of the log-sum-exp of the
+     *    children's estimates. Routing then runs the same top-p cut.
+     * ref_q is [L, H_kv, n_refs, d]. */
+    int32_t n_refs;      /* R: 0 or 1 for SUMMARY, 1..16 for TANGENT */
+    int32_t scoring;     /* ZHA_SCORE_SUMMARY or ZHA_SCORE_TANGENT */
 } zha_geom;
+
+#define ZHA_SCORE_SUMMARY 0
+#define ZHA_SCORE_TANGENT 1
+#define ZHA_MAX_REFS 16
 
 typedef struct zha_sizes {
     size_t  summaries_bytes;                 /* fp32 summary buffer for all levels */
     size_t  workspace_bytes;                 /* scratch for every call with up to max_rows query rows */
     int64_t level_nodes[ZHA_MAX_LEVELS];     /* node slots per (batch, kv head) and level: capacity / b^l */
-    int64_t level_offset[ZHA_MAX_LEVELS];    /* element offset of each level inside summaries */
+    int64_t level_offset[ZHA_MAX_LEVELS];    /* element offset of each level's keys inside summaries */
+    int64_t level_bias_offset[ZHA_MAX_LEVELS];/* element offset of each level's tangent offsets (TANGENT only) */
     int64_t level_sel_offset[ZHA_MAX_LEVELS];/* element offset of each level inside a level_sel buffer */
     size_t  level_sel_bytes;                 /* bytes of a level_sel buffer for max_rows rows */
     int32_t max_rows;                        /* B*T rows the workspace was sized for */

@@ -35,17 +35,20 @@ def kv_tensor(w, arr):
 class Staged:
     """A workload's cache, tree and buffers on cuda:0, plus host copies for the oracle."""
 
-    def __init__(self, w, max_t=None, build=True, n_tokens=None, level_p=None):
+    def __init__(self, w, max_t=None, build=True, n_tokens=None, level_p=None, n_refs=None):
+        """n_refs: tangent scoring with that many reference queries per (level, kv head)."""
         t = torch()
         self.w = w
         self.T = w.queries_per_step if max_t is None else max_t
+        self.tangent = n_refs is not None
         self.geom = Z.make_geom(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.branching, w.n_levels,
-                                w.capacity, w.kv_dtype, level_p=level_p)
+                                w.capacity, w.kv_dtype, level_p=level_p, n_refs=n_refs or 0,
+                                scoring="tangent" if self.tangent else "summary")
         self.cache = Z.Cache(self.geom, self.T)
         self.K_np, self.V_np = W.kv_cache(w)
         self.cache.K.copy_(kv_tensor(w, self.K_np))
         self.cache.V.copy_(kv_tensor(w, self.V_np))
-        self.R = W.ref_queries(w)
+        self.R = W.ref_queries(w, n_refs)
         self.ref_q = t.from_numpy(self.R).cuda()
         n = w.n_tokens if n_tokens is None else n_tokens
         self.cache.seq_lens.copy_(t.full((w.batch,), n, dtype=t.int32))
@@ -63,9 +66,15 @@ class Staged:
     def gpu_level(self, level):
         return self.cache.level(level).cpu().numpy()
 
+    def gpu_offsets(self, level):
+        return Z.offsets_view(self.cache.summaries, self.sizes, self.geom, level).cpu().numpy()
+
     def oracle_trees(self, n_tokens=None, slab=None):
         w = self.w
         lens = [w.n_tokens if n_tokens is None else n_tokens] * w.batch
+        if self.tangent:
+            return [[O.build_tangent_tree(self.Kf[s, h, :lens[s]], self.R[:, h], w.branching, slab=slab)
+                     for h in range(w.n_kv_heads)] for s in range(w.batch)]
         return O.build_all(self.Kf, self.R, lens, w.branching, slab=slab)
 
     def route_buffers(self, rows, sel_cap=None):

@@ -62,6 +62,26 @@ def test_sizes_match_layout_arithmetic():
     assert Z.query_sizes(g, 64).workspace_bytes > s.workspace_bytes
 
 
+def test_tangent_scoring_layout_and_validation():
+    g = _geom(n_refs=4, scoring="tangent")
+    s = Z.query_sizes(g, 1)
+    cap = (1 << 20) + 256
+    nodes = [cap // 32 ** l for l in range(1, 5)]
+    off = 0
+    for l in range(4):                       # keys: R rows of d per node
+        assert s.level_offset[l] == off
+        off += 8 * nodes[l] * 4 * 128
+    for l in range(4):                       # then the offsets: R per node
+        assert s.level_bias_offset[l] == off
+        off += 8 * nodes[l] * 4
+    assert s.summaries_bytes == off * 4
+    for kw in (dict(n_refs=2), dict(n_refs=17, scoring="tangent"), dict(n_refs=-1, scoring="tangent"),
+               dict(scoring=7)):
+        with pytest.raises(Z.ZhaError) as e:
+            Z.query_sizes(_geom(**kw), 1)
+        assert e.value.code == Z.ZHA_ERR_UNSUPPORTED, kw
+
+
 def test_level_schedule_is_validated():
     assert Z.query_sizes(_geom(level_p=[0.9, 1.0, 0.5, 0.0]), 1).max_rows == 1
     for bad in ([1.5, 0, 0, 0], [-0.1, 0, 0, 0], [0.9, 0.9, 0.9, 0.9, 0.9], [float("nan"), 0, 0, 0]):

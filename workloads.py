@@ -312,10 +312,16 @@ def as_f32(w: Workload, x: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(x) if w.kv_dtype == "bf16" else np.asarray(x, dtype=np.float32)
 
 
-def ref_queries(w: Workload) -> np.ndarray:
-    """Per-level, per-kv-head reference queries [L, H_kv, d] fp32."""
+def ref_queries(w: Workload, n_refs: Optional[int] = None) -> np.ndarray:
+    """Per-level, per-kv-head reference queries: [L, H_kv, d] fp32, or with
+    ``n_refs`` = R, [L, H_kv, R, d] whose first query of each (level, kv head)
+    is the one drawn without n_refs (the others from a stream of their own)."""
     rng = _rng(w.seed, _TAG_R)
     r = rng.standard_normal((w.n_levels, w.n_kv_heads, w.head_dim), dtype=np.float32)
+    if n_refs is not None:
+        more = _rng(w.seed, _TAG_R, 1).standard_normal((w.n_levels, w.n_kv_heads, max(0, n_refs - 1), w.head_dim),
+                                                       dtype=np.float32)
+        r = np.concatenate([r[:, :, None, :], more], axis=2)
     if w.cluster_mode == "needles":
         r *= np.float32(1.0 / math.sqrt(w.head_dim))
     return r
