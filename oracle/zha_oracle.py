@@ -51,6 +51,17 @@ Readings where the pages leave a step open (each restated where used):
   the logits z_j = t_{j,r*}(q_hat_r) include the child offsets, w =
   softmax(z), k_hat_r = sum_j w_j k_hat_{j,r*}, b_hat_r = LSE(z) - q_hat_r .
   k_hat_r / sqrt(d). Keys and offsets are stored in fp32.
+* R-8 compressed value summaries (an option beside exact attention over I):
+  a node also stores a value summary, its children's values (raw values at
+  level 1) pooled with the weights of its key summary. After routing, every
+  candidate a level's cut did not keep joins the attention as one
+  pseudo-token: value its value summary, logit its routing score plus the log
+  of the number of tokens it stands for, i.e. its span b^l less the tokens of
+  it the exact part already attends (the sink and the current chunk), so no
+  token is counted twice. The output is the softmax over the exact tokens of
+  I and these pseudo-tokens. It is exact when every pruned subtree holds one
+  repeated key and value, and it equals exact attention over I when nothing is
+  pruned (p = 1).
 """
 from __future__ import annotations
 
@@ -80,13 +91,9 @@ def complete_nodes(n_tokens: int, b: int, n_levels: int) -> List[int]:
 # ----------------------------------------------------------------------------
 # Tree build [SAHTI §Tree Construction: k_hat_r; recursion over children]
 # ----------------------------------------------------------------------------
-def pool_children(children: np.ndarray, r: np.ndarray, b: int, scale: float) -> np.ndarray:
-    """Summaries of consecutive groups of ``b`` rows of ``children`` (R-1).
-
-    For each group C: weights w = softmax(scale * C r) and summary sum_j w_j C_j,
-    i.e. single-query attention of r over C with C as both keys and values.
-    Returned in fp32, the storage precision of summaries.
-    """
+def pool_weights(children: np.ndarray, r: np.ndarray, b: int, scale: float):
+    """softmax(scale * C r) over each group C of b consecutive children (R-1):
+    returns the weights (m, b) and the groups (m, b, d), fp64."""
     X = np.asarray(children, dtype=F64)
     m = X.shape[0] // b
     X = X[: m * b].reshape(m, b, X.shape[-1])
@@ -94,8 +101,48 @@ def pool_children(children: np.ndarray, r: np.ndarray, b: int, scale: float) -> 
     z = z - z.max(axis=1, keepdims=True)
     w = np.exp(z)
     w = w / w.sum(axis=1, keepdims=True)
+    return w, X
+
+
+def pool_children(children: np.ndarray, r: np.ndarray, b: int, scale: float) -> np.ndarray:
+    """Summaries of consecutive groups of ``b`` rows of ``children`` (R-1).
+
+    For each group C: weights w = softmax(scale * C r) and summary sum_j w_j C_j,
+    i.e. single-query attention of r over C with C as both keys and values.
+    Returned in fp32, the storage precision of summaries.
+    """
+    w, X = pool_weights(children, r, b, scale)
     s = np.einsum("mj,mjd->md", w, X)
     return s.astype(F32)
+
+
+def pool_values(children: np.ndarray, child_values: np.ndarray, r: np.ndarray, b: int, scale: float) -> np.ndarray:
+    """Value summaries of consecutive groups of b children (R-8): the children's
+    values pooled with the weights of the key summary."""
+    w, _ = pool_weights(children, r, b, scale)
+    Y = np.asarray(child_values, dtype=F64)
+    Y = Y[: w.shape[0] * b].reshape(w.shape[0], b, Y.shape[-1])
+    return np.einsum("mj,mjd->md", w, Y).astype(F32)
+
+
+def build_value_tree(K: np.ndarray, V: np.ndarray, R: np.ndarray, b: int, scale: Optional[float] = None,
+                     slab: Optional[int] = None) -> List[np.ndarray]:
+    """Every level's value summaries for one (sequence, kv head) (R-8), beside
+    the key summaries of build_tree (whose weights they reuse)."""
+    d = K.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    keys = build_tree(K, R, b, scale, slab)
+    vals = []
+    n1 = K.shape[0] // b
+    step = n1 * b if slab is None else slab
+    for l in range(R.shape[0]):
+        if l == 0:
+            parts = [pool_values(K[t0:min(t0 + step, n1 * b)], V[t0:min(t0 + step, n1 * b)], R[0], b, scale)
+                     for t0 in range(0, n1 * b, max(step, 1))]
+            vals.append(np.concatenate(parts) if parts else np.zeros((0, d), F32))
+        else:
+            vals.append(pool_values(keys[l - 1], vals[l - 1], R[l], b, scale))
+    return vals
 
 
 def build_tree(K: np.ndarray, R: np.ndarray, b: int, scale: Optional[float] = None,
@@ -418,6 +465,48 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray, scale: 
 
 def dense_attend(q, K, V, n_visible, scale=None):
     return attend(q, K, V, np.arange(n_visible), scale)
+
+
+def pseudo_tokens(route_res: "RouteResult", values: Sequence[np.ndarray], n_visible: int, b: int):
+    """The pruned candidates of every level as (logit, value summary) pairs (R-8):
+    logit = routing score (exact fp64) + ln(the node's tokens outside the sink
+    and the current chunk); nodes with no such token are left out."""
+    cur = b * ((n_visible - 1) // b) if n_visible > 0 else 0
+    logits, vals = [], []
+    for level, cut in enumerate(route_res.levels, start=1):
+        if cut is None or len(cut.ids) == 0:
+            continue
+        kept = set(int(x) for x in cut.selected)
+        span = b ** level
+        for j, node in enumerate(cut.ids):
+            node = int(node)
+            if node in kept:
+                continue
+            lo, hi = node * span, (node + 1) * span
+            count = span - (1 if lo == 0 else 0) - max(0, min(n_visible, hi) - max(cur, lo))
+            if lo == 0 and cur == 0:
+                count += 1                              # the sink lies in the current chunk: counted once
+            if count <= 0:
+                continue
+            logits.append(float(cut.scores64[j]) + math.log(count))
+            vals.append(np.asarray(values[level - 1][node], dtype=F64))
+    return np.array(logits, dtype=F64), (np.stack(vals) if vals else np.zeros((0, 0)))
+
+
+def attend_compressed(q, K, V, idx, logits, pvals, scale=None):
+    """Softmax attention over the exact tokens idx and the pseudo-tokens (logit,
+    value) of the pruned subtrees (R-8): returns (o (d,), lse)."""
+    scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+    idx = np.asarray(idx, dtype=np.int64)
+    z = scale * (np.asarray(K[idx], dtype=F64) @ np.asarray(q, dtype=F64))
+    vv = np.asarray(V[idx], dtype=F64)
+    if len(logits):
+        z = np.concatenate([z, logits])
+        vv = np.concatenate([vv, pvals])
+    mx = z.max()
+    e = np.exp(z - mx)
+    l = e.sum()
+    return (e @ vv) / l, mx + math.log(l)
 
 
 # ----------------------------------------------------------------------------

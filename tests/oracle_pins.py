@@ -577,6 +577,107 @@ def pin_tangent_route_golden(orc):
             assert list(r.selected[int(lvl) - 1]) == list(_ranges(rs)), (c["name"], lvl)
 
 
+# ----------------------------------------------------------------------------
+# compressed value summaries: pruned subtrees as pseudo-tokens
+# ----------------------------------------------------------------------------
+def pin_value_summaries(orc):
+    """A value summary pools the children's values with the key summary's
+    weights: zero reference query -> the plain mean of the values; a huge
+    reference query along e_0 -> the value of the child with the largest e_0
+    key component; children permuted together -> the same summary."""
+    rng = np.random.default_rng(41)
+    b, d = 8, 16
+    C = rng.standard_normal((b, d)).astype(np.float32)
+    Y = rng.standard_normal((b, d)).astype(np.float32)
+    sc = 1 / math.sqrt(d)
+    v0 = orc.pool_values(C, Y, np.zeros(d, np.float32), b, sc)[0]
+    assert np.abs(v0 - Y.astype(np.float64).mean(0)).max() < 1e-6
+    r = np.zeros(d, np.float32)
+    r[0] = 1e5
+    assert np.abs(orc.pool_values(C, Y, r, b, sc)[0] - Y[np.argmax(C[:, 0])]).max() < 1e-6
+    rr = rng.standard_normal(d).astype(np.float32)
+    perm = rng.permutation(b)
+    a1 = orc.pool_values(C, Y, rr, b, sc)[0]
+    a2 = orc.pool_values(C[perm], Y[perm], rr, b, sc)[0]
+    assert np.abs(a1.astype(np.float64) - a2).max() < 1e-6
+    # values = keys: the value summary is the key summary
+    K = rng.standard_normal((17 * b, d)).astype(np.float32)
+    R = rng.standard_normal((2, d)).astype(np.float32)
+    kt, vt = orc.build_tree(K, R, b), orc.build_value_tree(K, K, R, b)
+    for x, y in zip(kt, vt):
+        assert x.shape == y.shape and (x.size == 0 or np.abs(x.astype(np.float64) - y).max() < 1e-6)
+
+
+def _uniform_spans(rng, b, L, N, d):
+    """Keys and values constant over every span of b^L tokens: every subtree a
+    cut can prune holds one repeated key and value."""
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    n_top = N // b ** L + 1
+    a = rng.standard_normal(n_top) * 3
+    vals = rng.standard_normal((n_top, d))
+    t = np.arange(N) // b ** L
+    return (a[t, None] * u[None, :]).astype(np.float32), vals[t].astype(np.float32)
+
+
+def pin_compressed_exact_on_uniform_subtrees(orc):
+    """Where every pruned subtree repeats one key and one value, the pseudo-token
+    of a pruned node carries exactly its tokens' mass and value, so the output
+    equals dense attention; this needs the right logit offset (the log of the
+    node's tokens outside the sink and the current chunk), the right value and
+    every pruned candidate of every level."""
+    rng = np.random.default_rng(42)
+    for b, L, N, d in [(4, 3, 64 * 5 + 3, 8), (4, 3, 64 * 5, 8), (2, 4, 80, 4), (8, 2, 64 * 3 + 7, 16)]:
+        K, V = _uniform_spans(rng, b, L, N, d)
+        R = rng.standard_normal((L, d)).astype(np.float32)
+        tree, vals = orc.build_tree(K, R, b), orc.build_value_tree(K, V, R, b)
+        pruned_total = 0
+        for p in (0.3, 0.6, 0.9):
+            for _ in range(3):
+                q = (rng.standard_normal(d) * 3).astype(np.float32)
+                r = orc.route(q, tree, N, b, p)
+                I = orc.index_set(r.selected[0], N, b)
+                lg, pv = orc.pseudo_tokens(r, vals, N, b)
+                pruned_total += len(lg)
+                o, l = orc.attend_compressed(q, K, V, I, lg, pv)
+                od, ld = orc.dense_attend(q, K, V, N)
+                assert np.abs(o - od).max() < 1e-9 and abs(l - ld) < 1e-9, (b, L, N, p, np.abs(o - od).max())
+        assert pruned_total > 10
+
+
+def pin_compressed_p1_and_sdpa(orc):
+    """p = 1 prunes nothing: the compressed output is exact attention over I
+    (= dense). For p < 1 the combination equals torch's SDPA in fp64 over the
+    exact keys plus one zero key per pseudo-token whose logit enters as an
+    additive mask, with the value summaries as its values."""
+    rng = np.random.default_rng(43)
+    b, L, N, d = 4, 3, 203, 8
+    K = rng.standard_normal((N, d)).astype(np.float32)
+    V = rng.standard_normal((N, d)).astype(np.float32)
+    R = rng.standard_normal((L, d)).astype(np.float32)
+    tree, vals = orc.build_tree(K, R, b), orc.build_value_tree(K, V, R, b)
+    for _ in range(4):
+        q = (rng.standard_normal(d) * 2).astype(np.float32)
+        r = orc.route(q, tree, N, b, 1.0)
+        lg, pv = orc.pseudo_tokens(r, vals, N, b)
+        assert len(lg) == 0
+        o, l = orc.attend_compressed(q, K, V, orc.index_set(r.selected[0], N, b), lg, pv)
+        od, ld = orc.dense_attend(q, K, V, N)
+        assert np.abs(o - od).max() < 1e-12 and abs(l - ld) < 1e-12
+        r = orc.route(q, tree, N, b, 0.7)
+        I = orc.index_set(r.selected[0], N, b)
+        lg, pv = orc.pseudo_tokens(r, vals, N, b)
+        assert len(lg) > 0
+        o, _ = orc.attend_compressed(q, K, V, I, lg, pv)
+        keys = np.concatenate([K[I].astype(np.float64), np.zeros((len(lg), d))])
+        vv = np.concatenate([V[I].astype(np.float64), pv])
+        bias = np.concatenate([np.zeros(len(I)), lg])
+        qt = torch.from_numpy(q.astype(np.float64))[None, None, None, :]
+        ref = F.scaled_dot_product_attention(qt, torch.from_numpy(keys)[None, None], torch.from_numpy(vv)[None, None],
+                                             attn_mask=torch.from_numpy(bias)[None, None, None, :])[0, 0, 0].numpy()
+        assert np.abs(o - ref).max() < 1e-12
+
+
 ALL_PINS = [
     pin_geometry, pin_summary_sdpa, pin_summary_closed_forms, pin_incremental_equals_batch,
     pin_cut_golden, pin_cut_bruteforce, pin_cut_exemptions, pin_cut_uniform,
@@ -584,4 +685,5 @@ ALL_PINS = [
     pin_attend_sdpa, pin_p1_dense, pin_eq1_identity, pin_split_merge,
     pin_tangent_golden, pin_tangent_level1, pin_tangent_upper_levels, pin_tangent_duplicate_refs,
     pin_tangent_route_golden,
+    pin_value_summaries, pin_compressed_exact_on_uniform_subtrees, pin_compressed_p1_and_sdpa,
 ]

@@ -53,6 +53,14 @@ MUTANTS = {
     "tangent-lse-no-max": ("lse = zm[:, 0] + np.log(e.sum(axis=1))", "lse = np.log(e.sum(axis=1))"),
     "tangent-same-ref-every-level": ("levels.append(tangent_pool(up.keys, up.offs, R[l], b, scale))",
                                      "levels.append(tangent_pool(up.keys, up.offs, R[0], b, scale))"),
+    "values-uniform-weights": ("w, _ = pool_weights(children, r, b, scale)",
+                               "w, _ = pool_weights(children, 0 * np.asarray(r), b, scale)"),
+    "pseudo-no-count-offset": ("logits.append(float(cut.scores64[j]) + math.log(count))",
+                               "logits.append(float(cut.scores64[j]))"),
+    "pseudo-whole-span": ("count = span - (1 if lo == 0 else 0) - max(0, min(n_visible, hi) - max(cur, lo))",
+                          "count = span"),
+    "pseudo-includes-kept": ("            if node in kept:\n                continue\n", ""),
+    "pseudo-level-span-off": ("span = b ** level\n        for j, node", "span = b ** (level - 1)\n        for j, node"),
     "exempt-all": ("return np.array(sorted(ex), dtype=np.int64)",
                    "return np.array(sorted(int(i) for i in cut.ids), dtype=np.int64)"),
     "exempt-none": ("return np.array(sorted(ex), dtype=np.int64)", "return np.array([], dtype=np.int64)"),
