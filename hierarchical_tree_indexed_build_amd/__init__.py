@@ -32,13 +32,15 @@ class Geom(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("branching", ctypes.c_int32), ("n_levels", ctypes.c_int32),
                 ("capacity", ctypes.c_int64), ("kv_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("level_p", ctypes.c_float * ZHA_MAX_LEVELS), ("n_refs", ctypes.c_int32), ("scoring", ctypes.c_int32)]
+                ("level_p", ctypes.c_float * ZHA_MAX_LEVELS), ("n_refs", ctypes.c_int32), ("scoring", ctypes.c_int32),
+                ("value_summaries", ctypes.c_int32)]
 
 
 class Sizes(ctypes.Structure):
     _fields_ = [("summaries_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t),
                 ("level_nodes", ctypes.c_int64 * ZHA_MAX_LEVELS), ("level_offset", ctypes.c_int64 * ZHA_MAX_LEVELS),
                 ("level_bias_offset", ctypes.c_int64 * ZHA_MAX_LEVELS),
+                ("level_value_offset", ctypes.c_int64 * ZHA_MAX_LEVELS),
                 ("level_sel_offset", ctypes.c_int64 * ZHA_MAX_LEVELS), ("level_sel_bytes", ctypes.c_size_t),
                 ("max_rows", ctypes.c_int32)]
 
@@ -64,7 +66,7 @@ def lib() -> ctypes.CDLL:
         i32, f32, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
         sig = {
             "zha_query_sizes": [GP, i32, ctypes.POINTER(Sizes)],
-            "zha_build_tree": [GP, _P, _P, _P, _P, _P, sz, _P],
+            "zha_build_tree": [GP, _P, _P, _P, _P, _P, _P, sz, _P],
             "zha_append": [GP, _P, _P, _P, _P, i32, _P, _P, _P, _P, sz, _P],
             "zha_route": [GP, _P, i32, _P, _P, _P, f32, i32, _P, _P, _P, _P, _P, sz, _P],
             "zha_sparse_attend": [GP, _P, i32, _P, _P, _P, _P, _P, _P, i32, _P, _P, _P, sz, _P],
@@ -97,16 +99,18 @@ def _check(code: int, where: str):
 
 
 def make_geom(batch, n_q_heads, n_kv_heads, head_dim, branching, n_levels, capacity, kv_dtype="bf16",
-              scale=0.0, level_p=None, n_refs=0, scoring="summary") -> Geom:
+              scale=0.0, level_p=None, n_refs=0, scoring="summary", value_summaries=False) -> Geom:
     """A zha_geom. level_p (optional, n_levels floats, level 1 first): the cut
     fraction of each level, overriding a call's top_p where non-zero. scoring
     "summary" (one reference query, q . summary) or "tangent" (n_refs
-    reference queries, the maximum of the node's tangents)."""
+    reference queries, the maximum of the node's tangents). value_summaries:
+    pruned subtrees join zha_attend's softmax as pseudo-tokens."""
     kd = {"bf16": ZHA_KV_BF16, "fp32": ZHA_KV_F32}[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
     lp = (ctypes.c_float * ZHA_MAX_LEVELS)(*([float(x) for x in level_p] if level_p is not None else []))
     sc = {"summary": ZHA_SCORE_SUMMARY, "tangent": ZHA_SCORE_TANGENT}[scoring] if isinstance(scoring, str) \
         else int(scoring)
-    return Geom(batch, n_q_heads, n_kv_heads, head_dim, branching, n_levels, capacity, kd, scale, lp, n_refs, sc)
+    return Geom(batch, n_q_heads, n_kv_heads, head_dim, branching, n_levels, capacity, kd, scale, lp, n_refs, sc,
+                1 if value_summaries else 0)
 
 
 def query_sizes(geom: Geom, max_t: int) -> Sizes:
@@ -136,8 +140,9 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
 
-def build_tree(geom, K, ref_q, seq_lens, summaries, ws, stream=None):
-    _check(lib().zha_build_tree(ctypes.byref(geom), _ptr(K), _ptr(ref_q), _ptr(seq_lens), _ptr(summaries),
+def build_tree(geom, K, ref_q, seq_lens, summaries, ws, stream=None, V=None):
+    """V is read only for value summaries."""
+    _check(lib().zha_build_tree(ctypes.byref(geom), _ptr(K), _ptr(V), _ptr(ref_q), _ptr(seq_lens), _ptr(summaries),
                                 _ptr(ws), _nbytes(ws), _stream(stream)), "zha_build_tree")
 
 
@@ -224,6 +229,14 @@ def summaries_view(summaries, sizes: Sizes, geom: Geom, level: int):
     if geom.scoring == ZHA_SCORE_TANGENT:
         return v.view(geom.batch, geom.n_kv_heads, n, R, geom.head_dim)
     return v.view(geom.batch, geom.n_kv_heads, n, geom.head_dim)
+
+
+def values_view(summaries, sizes: Sizes, geom: Geom, level: int):
+    """The value summaries of one level (value summaries on): [B, H_kv, level_nodes, d]."""
+    n = sizes.level_nodes[level - 1]
+    off = sizes.level_value_offset[level - 1]
+    cnt = geom.batch * geom.n_kv_heads * n * geom.head_dim
+    return summaries[off:off + cnt].view(geom.batch, geom.n_kv_heads, n, geom.head_dim)
 
 
 def offsets_view(summaries, sizes: Sizes, geom: Geom, level: int):

@@ -28,9 +28,10 @@ __device__ __forceinline__ void load_n(const T* __restrict__ p, float (&x)[N]) {
 // More children than lanes (b = 128, 256): lane l owns child rows l, l + 64,
 // ...; each row's dot product with r is taken 8 elements at a time (r is the
 // same for every lane). The softmax and the weighted sum are as below.
-template <typename CT, int B, int D>
+template <typename CT, int B, int D, bool VAL = false>
 __device__ __forceinline__ void reduce_node_wide(const CT* __restrict__ ch, const float* __restrict__ r,
-                                                 float scale, float* __restrict__ out, int lane) {
+                                                 float scale, float* __restrict__ out, int lane,
+                                                 const CT* __restrict__ vch = nullptr, float* __restrict__ vout = nullptr) {
     constexpr int RPL = B / kWave;   // child rows per lane
     constexpr int DPL = D / kWave;   // dimensions per lane in pass 2
     float z[RPL];
@@ -63,9 +64,9 @@ __device__ __forceinline__ void reduce_node_wide(const CT* __restrict__ ch, cons
     }
     const float tot = group_sum<kWave>(sloc);
 
-    float acc[DPL];
+    float acc[DPL], vacc[DPL];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+    for (int k = 0; k < DPL; ++k) acc[k] = vacc[k] = 0.f;
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
 #pragma unroll 8
@@ -75,15 +76,25 @@ __device__ __forceinline__ void reduce_node_wide(const CT* __restrict__ ch, cons
             load_n<DPL>(ch + static_cast<int64_t>(i * kWave + j) * D + lane * DPL, v);
 #pragma unroll
             for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wj, v[k], acc[k]);
+            if constexpr (VAL) {
+                float y[DPL];
+                load_n<DPL>(vch + static_cast<int64_t>(i * kWave + j) * D + lane * DPL, y);
+#pragma unroll
+                for (int k = 0; k < DPL; ++k) vacc[k] = fmaf(wj, y[k], vacc[k]);
+            }
         }
     }
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) out[lane * DPL + k] = acc[k] / tot;
+    for (int k = 0; k < DPL; ++k) {
+        out[lane * DPL + k] = acc[k] / tot;
+        if constexpr (VAL) vout[lane * DPL + k] = vacc[k] / tot;
+    }
 }
 
-template <typename CT, int B, int D>
+template <typename CT, int B, int D, bool VAL = false>
 __device__ __forceinline__ void reduce_node_narrow(const CT* __restrict__ ch, const float* __restrict__ r,
-                                                   float scale, float* __restrict__ out, int lane) {
+                                                   float scale, float* __restrict__ out, int lane,
+                                                   const CT* __restrict__ vch = nullptr, float* __restrict__ vout = nullptr) {
     constexpr int LPR = kWave / B;   // lanes per child row
     constexpr int EPL = D / LPR;     // elements per lane in pass 1
     constexpr int DPL = D / kWave;   // dimensions per lane in pass 2
@@ -100,9 +111,9 @@ __device__ __forceinline__ void reduce_node_narrow(const CT* __restrict__ ch, co
     const float w = expf(z - m);
     const float tot = group_sum<kWave>(w) * (1.0f / LPR);   // each row is held by LPR lanes
 
-    float acc[DPL];
+    float acc[DPL], vacc[DPL];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+    for (int k = 0; k < DPL; ++k) acc[k] = vacc[k] = 0.f;
 #pragma unroll 8
     for (int j = 0; j < B; ++j) {
         const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j * LPR));
@@ -110,16 +121,28 @@ __device__ __forceinline__ void reduce_node_narrow(const CT* __restrict__ ch, co
         load_n<DPL>(ch + j * D + lane * DPL, v);
 #pragma unroll
         for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wj, v[k], acc[k]);
+        if constexpr (VAL) {
+            float y[DPL];
+            load_n<DPL>(vch + j * D + lane * DPL, y);
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) vacc[k] = fmaf(wj, y[k], vacc[k]);
+        }
     }
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) out[lane * DPL + k] = acc[k] / tot;
+    for (int k = 0; k < DPL; ++k) {
+        out[lane * DPL + k] = acc[k] / tot;
+        if constexpr (VAL) vout[lane * DPL + k] = vacc[k] / tot;
+    }
 }
 
-template <typename CT, int B, int D>
+// The node's key summary; with VAL also its value summary (the children's
+// values vch pooled with the same weights) into vout.
+template <typename CT, int B, int D, bool VAL = false>
 __device__ __forceinline__ void reduce_node_wave(const CT* __restrict__ ch, const float* __restrict__ r,
-                                                 float scale, float* __restrict__ out, int lane) {
-    if constexpr (B > kWave) reduce_node_wide<CT, B, D>(ch, r, scale, out, lane);
-    else reduce_node_narrow<CT, B, D>(ch, r, scale, out, lane);
+                                                 float scale, float* __restrict__ out, int lane,
+                                                 const CT* __restrict__ vch = nullptr, float* __restrict__ vout = nullptr) {
+    if constexpr (B > kWave) reduce_node_wide<CT, B, D, VAL>(ch, r, scale, out, lane, vch, vout);
+    else reduce_node_narrow<CT, B, D, VAL>(ch, r, scale, out, lane, vch, vout);
 }
 
 // ---- tangent scoring ----
@@ -287,12 +310,18 @@ struct BuildParams {
     const float* child_off;
     float* out_off;
     int R, Rc;
+    // value summaries: the children's values (V at level 1, value summaries above) and this level's
+    const void* values;
+    float* out_val;
 };
+
+enum { kBuildPlain = 0, kBuildTangent = 1, kBuildValues = 2 };
 
 enum { kModeBuild = 0, kModeAppend = 1 };
 
-template <typename CT, int B, int D, bool TAN>
+template <typename CT, int B, int D, int MODE>
 __global__ __launch_bounds__(256) void build_level_kernel(BuildParams p) {
+    constexpr bool TAN = MODE == kBuildTangent;
     const int lane = threadIdx.x & (kWave - 1);
     const int RW = TAN ? p.R : 1;                        // waves per node: one per tangent
     const int64_t total = static_cast<int64_t>(p.BH) * p.slots * RW;
@@ -322,6 +351,11 @@ __global__ __launch_bounds__(256) void build_level_kernel(BuildParams p) {
             const int64_t orow = (static_cast<int64_t>(bh) * p.out_rows + i) * p.R + rr;
             tangent_node_wave<CT, B, D>(ch, co, p.Rc, p.r + (static_cast<int64_t>(h) * p.R + rr) * D, p.scale,
                                         p.out + orow * D, p.out_off + orow, lane);
+        } else if constexpr (MODE == kBuildValues) {
+            const int64_t c0 = (bh * p.child_rows + i * B) * D;
+            const int64_t o0 = (bh * p.out_rows + i) * D;
+            reduce_node_wave<CT, B, D, true>(static_cast<const CT*>(p.children) + c0, p.r + h * D, p.scale, p.out + o0,
+                                             lane, static_cast<const CT*>(p.values) + c0, p.out_val + o0);
         } else {
             const CT* ch = static_cast<const CT*>(p.children) + (bh * p.child_rows + i * B) * D;
             float* o = p.out + (bh * p.out_rows + i) * D;
@@ -388,13 +422,15 @@ struct FusedParams {
     int64_t sum_off[ZHA_MAX_LEVELS];
     int64_t span[ZHA_MAX_LEVELS];
     int64_t bias_off[ZHA_MAX_LEVELS];   // tangent scoring: each level's offsets in the summary buffer
+    int64_t val_off[ZHA_MAX_LEVELS];    // value summaries: each level's in the summary buffer
     int Hkv, L, t_new, R;
-    bool tangent;
+    bool tangent, values;
     float scale;
 };
 
-template <typename KT, int B, int D, bool TAN>
+template <typename KT, int B, int D, int MODE>
 __global__ __launch_bounds__(1024) void append_fused_kernel(FusedParams p) {
+    constexpr bool TAN = MODE == kBuildTangent, VAL = MODE == kBuildValues;
     const int s = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave, nwaves = blockDim.x / kWave;
@@ -447,12 +483,15 @@ __global__ __launch_bounds__(1024) void append_fused_kernel(FusedParams p) {
                 const float* r = p.ref_q + (static_cast<int64_t>(l) * p.Hkv + h) * D;
                 for (int64_t i = lo; i < hi; ++i) {
                     float* o = lvl + (bh * p.nodes[l] + i) * D;
+                    float* vo = VAL ? p.summaries + p.val_off[l] + (bh * p.nodes[l] + i) * D : nullptr;
                     if (l == 0) {
-                        const KT* ch = reinterpret_cast<const KT*>(p.K) + (bh * p.cap + i * B) * D;
-                        reduce_node_wave<KT, B, D>(ch, r, p.scale, o, lane);
+                        const int64_t c0 = (bh * p.cap + i * B) * D;
+                        reduce_node_wave<KT, B, D, VAL>(reinterpret_cast<const KT*>(p.K) + c0, r, p.scale, o, lane,
+                                                        reinterpret_cast<const KT*>(p.V) + c0, vo);
                     } else {
-                        const float* ch = p.summaries + p.sum_off[l - 1] + (bh * p.nodes[l - 1] + i * B) * D;
-                        reduce_node_wave<float, B, D>(ch, r, p.scale, o, lane);
+                        const int64_t c0 = (bh * p.nodes[l - 1] + i * B) * D;
+                        reduce_node_wave<float, B, D, VAL>(p.summaries + p.sum_off[l - 1] + c0, r, p.scale, o, lane,
+                                                           VAL ? p.summaries + p.val_off[l - 1] + c0 : nullptr, vo);
                     }
                 }
             }
@@ -472,10 +511,10 @@ static hipError_t launch_level_t(const BuildParams& bp, int64_t total_waves, int
     const int64_t blocks = std::min<int64_t>((waves + 3) / 4, 16384);
     if (blocks <= 0) return hipSuccess;
     ProfScope ps("build_level", level, st);
-    if (tan)
-        hipLaunchKernelGGL((build_level_kernel<CT, B, D, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, bp);
-    else
-        hipLaunchKernelGGL((build_level_kernel<CT, B, D, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, bp);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+    if (tan) hipLaunchKernelGGL((build_level_kernel<CT, B, D, kBuildTangent>), grid, block, 0, st, bp);
+    else if (bp.out_val) hipLaunchKernelGGL((build_level_kernel<CT, B, D, kBuildValues>), grid, block, 0, st, bp);
+    else hipLaunchKernelGGL((build_level_kernel<CT, B, D, kBuildPlain>), grid, block, 0, st, bp);
     return hipGetLastError();
 }
 
@@ -494,8 +533,8 @@ static hipError_t dispatch_b(int b, const BuildParams& bp, int64_t tw, int lv, h
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_build_level(const Geo& g, int level, const void* K, const float* ref_q, float* summaries,
-                              const int32_t* seq_lens, int mode, int t_new, hipStream_t st) {
+hipError_t launch_build_level(const Geo& g, int level, const void* K, const void* V, const float* ref_q,
+                              float* summaries, const int32_t* seq_lens, int mode, int t_new, hipStream_t st) {
     BuildParams bp{};
     const int l = level - 1;
     bp.children = (level == 1) ? K : static_cast<const void*>(summaries + g.sum_off[l - 1]);
@@ -505,6 +544,8 @@ hipError_t launch_build_level(const Geo& g, int level, const void* K, const floa
     bp.Rc = (level == 1) ? 1 : g.R;
     bp.child_off = (g.tangent && level > 1) ? summaries + g.bias_off[l - 1] : nullptr;
     bp.out_off = g.tangent ? summaries + g.bias_off[l] : nullptr;
+    bp.values = g.vsum ? ((level == 1) ? V : static_cast<const void*>(summaries + g.val_off[l - 1])) : nullptr;
+    bp.out_val = g.vsum ? summaries + g.val_off[l] : nullptr;
     bp.seq_lens = seq_lens;
     bp.child_rows = (level == 1) ? g.cap : g.nodes[l - 1];
     bp.out_rows = g.nodes[l];
@@ -559,10 +600,10 @@ template <typename KT, int B, int D>
 static hipError_t launch_fused_t(const FusedParams& fp, int B_, int Hkv, hipStream_t st) {
     const int waves = std::min(Hkv, 16);
     ProfScope ps("append_fused", 0, st);
-    if (fp.tangent)
-        hipLaunchKernelGGL((append_fused_kernel<KT, B, D, true>), dim3(B_), dim3(waves * kWave), 0, st, fp);
-    else
-        hipLaunchKernelGGL((append_fused_kernel<KT, B, D, false>), dim3(B_), dim3(waves * kWave), 0, st, fp);
+    const dim3 grid(B_), block(waves * kWave);
+    if (fp.tangent) hipLaunchKernelGGL((append_fused_kernel<KT, B, D, kBuildTangent>), grid, block, 0, st, fp);
+    else if (fp.values) hipLaunchKernelGGL((append_fused_kernel<KT, B, D, kBuildValues>), grid, block, 0, st, fp);
+    else hipLaunchKernelGGL((append_fused_kernel<KT, B, D, kBuildPlain>), grid, block, 0, st, fp);
     return hipGetLastError();
 }
 
@@ -599,9 +640,11 @@ hipError_t launch_append_fused(const Geo& g, void* K, void* V, const void* k_new
         fp.sum_off[l] = g.sum_off[l];
         fp.span[l] = g.span[l];
         fp.bias_off[l] = g.bias_off[l];
+        fp.val_off[l] = g.val_off[l];
     }
     fp.R = g.R;
     fp.tangent = g.tangent;
+    fp.values = g.vsum;
     fp.Hkv = g.Hkv;
     fp.L = g.L;
     fp.t_new = t_new;

@@ -1926,6 +1926,7 @@ struct UpperParams {
     float scale;
     int64_t bias_off[ZHA_MAX_LEVELS];  // tangent scoring: each level's offsets
     int R;                             // tangent rows per node (1 without tangent scoring)
+    float* scores;                     // value summaries: the dense-by-node scores its levels also go to (else null)
 };
 
 struct UpperShared {
@@ -2029,7 +2030,10 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
                 const int64_t k = kb + u * RPP + sub;
                 if (k < ncand) {
                     mx = fmaxf(mx, t);
-                    if (part == 0) sh.sc[k] = t;
+                    if (part == 0) {
+                        sh.sc[k] = t;
+                        if (p.scores) p.scores[rh * p.nodes_total + p.sel_off[li] + sh.cid[k]] = t;
+                    }
                 }
             }
         }
@@ -2218,6 +2222,7 @@ hipError_t launch_route(const Geo& g, const RouteArgs& a, hipStream_t st) {
         up.scale = g.scale;
         for (int l = 0; l < ZHA_MAX_LEVELS; ++l) up.bias_off[l] = g.bias_off[l];
         up.R = g.R;
+        up.scores = g.vsum ? scores : nullptr;
         {
             ProfScope ps("route_upper", 0, st);
             const dim3 grid(g.Hq, a.rows), block(kUpperThreads);

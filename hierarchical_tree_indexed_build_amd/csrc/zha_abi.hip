@@ -58,6 +58,10 @@ zha_status make_geo(const zha_geom* in, Geo* g) {
     if (!(in->scale >= 0.f) || std::isinf(in->scale)) return fail(ZHA_ERR_SHAPE, "scale must be finite and >= 0");
     if (in->scoring != ZHA_SCORE_SUMMARY && in->scoring != ZHA_SCORE_TANGENT)
         return fail(ZHA_ERR_UNSUPPORTED, "scoring must be ZHA_SCORE_SUMMARY or ZHA_SCORE_TANGENT (got %d)", in->scoring);
+    if (in->value_summaries != 0 && in->value_summaries != 1)
+        return fail(ZHA_ERR_SHAPE, "value_summaries must be 0 or 1 (got %d)", in->value_summaries);
+    if (in->value_summaries && in->scoring != ZHA_SCORE_SUMMARY)
+        return fail(ZHA_ERR_UNSUPPORTED, "value summaries need summary scoring");
     const int R = in->n_refs > 0 ? in->n_refs : 1;
     if (in->n_refs < 0 || R > ZHA_MAX_REFS || (in->scoring == ZHA_SCORE_SUMMARY && R != 1))
         return fail(ZHA_ERR_UNSUPPORTED, "n_refs must be 0 or 1 for summary scoring and 1..%d for tangent scoring (got %d)",
@@ -80,6 +84,7 @@ zha_status make_geo(const zha_geom* in, Geo* g) {
     g->L = in->n_levels;
     g->R = R;
     g->tangent = in->scoring == ZHA_SCORE_TANGENT;
+    g->vsum = in->value_summaries != 0;
     g->kv_dtype = in->kv_dtype;
     g->cap = in->capacity;
     g->scale = in->scale > 0.f ? in->scale : 1.0f / std::sqrt(static_cast<float>(in->head_dim));
@@ -102,6 +107,11 @@ zha_status make_geo(const zha_geom* in, Geo* g) {
     for (int l = 0; l < ZHA_MAX_LEVELS; ++l) {
         g->bias_off[l] = soff;
         if (g->tangent) soff += static_cast<int64_t>(g->B) * g->Hkv * g->nodes[l] * g->R;
+    }
+    // then the value summaries
+    for (int l = 0; l < ZHA_MAX_LEVELS; ++l) {
+        g->val_off[l] = soff;
+        if (g->vsum) soff += static_cast<int64_t>(g->B) * g->Hkv * g->nodes[l] * g->D;
     }
     g->summ_total = soff;
     return ZHA_OK;
@@ -132,6 +142,11 @@ WsLayout layout(const Geo& g, int rows) {
     L.acnt = take(R * g.Hkv * 4);
     L.plan = take(2 * (R * g.Hkv + 1) * 8);
     L.partial = take((static_cast<size_t>(kAttnWorkgroups) + R * g.Hkv) * g.G * (g.D + 4) * 4);
+    if (g.vsum) {
+        const int64_t pairs = static_cast<int64_t>(R) * g.Hkv;
+        L.pseudo_runs = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kPseudoMaxRuns, 2048 / pairs)));
+        L.pseudo = take(static_cast<size_t>(g.L) * pairs * L.pseudo_runs * g.G * (g.D + 4) * 4);
+    }
     // the split cut: candidates of a level are at most its node slots
     const int64_t cand = g.nodes[0];
     const int64_t slices = (cand + kSplitSlice - 1) / kSplitSlice;
@@ -256,6 +271,7 @@ zha_status zha_query_sizes(const zha_geom* geom, int32_t max_t, zha_sizes* out) 
         out->level_nodes[l] = g.nodes[l];
         out->level_offset[l] = g.sum_off[l];
         out->level_bias_offset[l] = g.bias_off[l];
+        out->level_value_offset[l] = g.val_off[l];
         out->level_sel_offset[l] = g.sel_off[l];
     }
     out->level_sel_bytes = static_cast<size_t>(rows) * g.Hq * g.nodes_total * 4;
@@ -263,16 +279,17 @@ zha_status zha_query_sizes(const zha_geom* geom, int32_t max_t, zha_sizes* out) 
     return ZHA_OK;
 }
 
-zha_status zha_build_tree(const zha_geom* geom, const void* K, const float* ref_q, const int32_t* seq_lens,
-                          float* summaries, void* ws, size_t ws_bytes, void* stream) {
+zha_status zha_build_tree(const zha_geom* geom, const void* K, const void* V, const float* ref_q,
+                          const int32_t* seq_lens, float* summaries, void* ws, size_t ws_bytes, void* stream) {
     Geo g;
     zha_status st = make_geo(geom, &g);
     if (st) return st;
     if (!K || !ref_q || !seq_lens || !summaries) return fail(ZHA_ERR_NULL, "K, ref_q, seq_lens and summaries are required");
+    if (g.vsum && !V) return fail(ZHA_ERR_NULL, "V is required with value summaries");
     if ((st = check_ws(ws, ws_bytes, 256))) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int level = 1; level <= g.L; ++level) {
-        const hipError_t e = launch_build_level(g, level, K, ref_q, summaries, seq_lens, 0, 0, s);
+        const hipError_t e = launch_build_level(g, level, K, V, ref_q, summaries, seq_lens, 0, 0, s);
         if (e != hipSuccess) return hip_fail(e, "build level launch");
     }
     return ZHA_OK;
@@ -299,7 +316,7 @@ zha_status zha_append(const zha_geom* geom, void* K, void* V, const void* k_new,
     e = launch_append_rows(g, K, V, k_new, v_new, t_new, seq_lens, status, s);
     if (e != hipSuccess) return hip_fail(e, "append rows launch");
     for (int level = 1; level <= g.L; ++level) {
-        e = launch_build_level(g, level, K, ref_q, summaries, seq_lens, 1, t_new, s);
+        e = launch_build_level(g, level, K, V, ref_q, summaries, seq_lens, 1, t_new, s);
         if (e != hipSuccess) return hip_fail(e, "append level launch");
     }
     e = launch_advance_seq(g, seq_lens, t_new, s);
@@ -357,7 +374,7 @@ zha_status zha_route(const zha_geom* geom, const float* q, int32_t t, const int3
 static zha_status attend_impl(const Geo& g, const float* q, int32_t t, const int32_t* q_pos, const void* K,
                               const void* V, const int32_t* seq_lens, const int32_t* sel_blocks, const int32_t* n_sel,
                               int32_t sel_capacity, float* out, float* lse, void* ws, const WsLayout& L, int rows,
-                              bool dense, bool bitmaps_ready, hipStream_t s) {
+                              bool dense, bool bitmaps_ready, hipStream_t s, const float* summaries = nullptr) {
     AttendArgs a{};
     a.q = q;
     a.ri = RowInfo{seq_lens, q_pos, t};
@@ -373,8 +390,13 @@ static zha_status attend_impl(const Geo& g, const float* q, int32_t t, const int
     a.lay = &L;
     a.dense = dense;
     a.bitmaps_ready = bitmaps_ready;
-    const hipError_t e = launch_attend(g, a, s);
+    hipError_t e = launch_attend(g, a, s);
     if (e != hipSuccess) return hip_fail(e, "attend launch");
+    // after a route in the same call: the pruned candidates as pseudo-tokens
+    if (g.vsum && summaries && bitmaps_ready) {
+        e = launch_pseudo(g, a, summaries, s);
+        if (e != hipSuccess) return hip_fail(e, "pseudo-token launch");
+    }
     return ZHA_OK;
 }
 
@@ -413,7 +435,7 @@ zha_status zha_attend(const zha_geom* geom, const float* q, int32_t t, const int
                          level_sel, ws, L, rows, s)))
         return st;
     return attend_impl(g, q, t, q_pos, K, V, seq_lens, sel_blocks, n_sel, sel_capacity, out, lse, ws, L, rows, false,
-                       true, s);
+                       true, s, summaries);
 }
 
 zha_status zha_attend_noalloc(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos, const void* K,
@@ -462,7 +484,7 @@ zha_status zha_attend_noalloc(const zha_geom* geom, const float* q, int32_t t, c
                          level_sel, ws, L, rows, s)))
         return st;
     if ((st = attend_impl(g, q, t, q_pos, K, V, seq_lens, sel_blocks, n_sel, sel_capacity, out, lse, ws, L, rows,
-                          false, true, s)))
+                          false, true, s, summaries)))
         return st;
     if (dev_status) {
         hipLaunchKernelGGL(copy_word_kernel, dim3(1), dim3(1), 0, s, static_cast<const uint32_t*>(ws), dev_status);

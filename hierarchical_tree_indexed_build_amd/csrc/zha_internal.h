@@ -77,8 +77,12 @@ struct Geo {
     int R;                             // tangents per node (reference queries per level and kv head)
     bool tangent;                      // tangent scoring: offsets stored, score = max over the R tangents
     int64_t bias_off[ZHA_MAX_LEVELS];  // element offset of each level's tangent offsets in the summary buffer
+    bool vsum;                         // compressed value summaries
+    int64_t val_off[ZHA_MAX_LEVELS];   // element offset of each level's value summaries
     int64_t summ_total;                // elements of the summary buffer
 };
+
+constexpr int kPseudoMaxRuns = 64;     // pseudo-token waves per (row, kv head) and level
 
 // Byte layout of the workspace for `rows` query rows.
 struct WsLayout {
@@ -93,6 +97,8 @@ struct WsLayout {
     size_t acnt;          // int32  [rows, Hkv]
     size_t plan;          // int64  [2, rows * Hkv + 1] exclusive prefixes of attention groups and workgroup shares per (row, kv head)
     size_t partial;       // float  [kAttnWorkgroups + rows * Hkv, G, D + 4] split-K partial state per workgroup (max, sum, 2 pad, acc)
+    size_t pseudo;        // float  [L, rows * Hkv, pseudo_runs, G, D + 4] pseudo-token partials (value summaries only)
+    int pseudo_runs;
     // split cut (rows * Hq <= kSplitMaxPairs and every level small enough); absent otherwise
     bool split;
     size_t rank;          // int32  [rows, Hq, nodes_total] a kept node's place in its head's kept list
@@ -149,8 +155,8 @@ class ProfScope {
 };
 
 // Launchers (defined in the kernel translation units). All return hipError_t.
-hipError_t launch_build_level(const Geo& g, int level, const void* K, const float* ref_q, float* summaries,
-                              const int32_t* seq_lens, int mode, int t_new, hipStream_t st);
+hipError_t launch_build_level(const Geo& g, int level, const void* K, const void* V, const float* ref_q,
+                              float* summaries, const int32_t* seq_lens, int mode, int t_new, hipStream_t st);
 hipError_t launch_append_rows(const Geo& g, void* K, void* V, const void* k_new, const void* v_new, int t_new,
                               const int32_t* seq_lens, uint32_t* status, hipStream_t st);
 hipError_t launch_append_fused(const Geo& g, void* K, void* V, const void* k_new, const void* v_new, int t_new,
@@ -199,5 +205,9 @@ struct AttendArgs {
     bool bitmaps_ready;       // the route already wrote the level-1 kept bitmaps
 };
 hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st);
+
+// Pseudo-tokens of the pruned candidates of every level, merged into out / lse
+// (value summaries). Needs the route's kept bitmaps and every level's scores.
+hipError_t launch_pseudo(const Geo& g, const AttendArgs& a, const float* summaries, hipStream_t st);
 
 }  // namespace zha

@@ -130,6 +130,17 @@ typedef struct zha_geom {
      * ref_q is [L, H_kv, n_refs, d]. */
     int32_t n_refs;      /* R: 0 or 1 for SUMMARY, 1..16 for TANGENT */
     int32_t scoring;     /* ZHA_SCORE_SUMMARY or ZHA_SCORE_TANGENT */
+    /* Compressed value summaries ("Subquadratic Attention with a Hierarchical
+     * Tree-Structured Indexer", Future Directions: pruned subtrees contribute
+     * coarse attention outputs). 1: every node also stores a value summary,
+     * its children's values pooled with its key summary's weights (build and
+     * append then read V), and zha_attend / zha_attend_noalloc add one
+     * pseudo-token per candidate a level's cut did not keep: logit its score
+     * plus ln(its tokens outside the sink and the current chunk), value its
+     * value summary; out and lse are the softmax over the exact tokens and the
+     * pseudo-tokens. zha_sparse_attend stays exact over I. SUMMARY scoring
+     * only. 0: off. */
+    int32_t value_summaries;
 } zha_geom;
 
 #define ZHA_SCORE_SUMMARY 0
@@ -142,6 +153,8 @@ typedef struct zha_sizes {
     int64_t level_nodes[ZHA_MAX_LEVELS];     /* node slots per (batch, kv head) and level: capacity / b^l */
     int64_t level_offset[ZHA_MAX_LEVELS];    /* element offset of each level's keys inside summaries */
     int64_t level_bias_offset[ZHA_MAX_LEVELS];/* element offset of each level's tangent offsets (TANGENT only) */
+    int64_t level_value_offset[ZHA_MAX_LEVELS];/* element offset of each level's value summaries [B, H_kv, nodes, d]
+                                                  (value_summaries only) */
     int64_t level_sel_offset[ZHA_MAX_LEVELS];/* element offset of each level inside a level_sel buffer */
     size_t  level_sel_bytes;                 /* bytes of a level_sel buffer for max_rows rows */
     int32_t max_rows;                        /* B*T rows the workspace was sized for */
@@ -152,9 +165,10 @@ typedef struct zha_sizes {
 ZHA_API zha_status zha_query_sizes(const zha_geom* geom, int32_t max_t, zha_sizes* out);
 
 /* Build every complete node of every level for the first seq_lens[s] tokens of
- * each sequence [Tree Construction]. K is read, summaries are written. ws must
- * hold zha_query_sizes(...).workspace_bytes (any max_t). */
-ZHA_API zha_status zha_build_tree(const zha_geom* geom, const void* K, const float* ref_q,
+ * each sequence [Tree Construction]. K is read, summaries are written. V is
+ * read only with geom.value_summaries (else it may be NULL). ws must hold
+ * zha_query_sizes(...).workspace_bytes (any max_t). */
+ZHA_API zha_status zha_build_tree(const zha_geom* geom, const void* K, const void* V, const float* ref_q,
                           const int32_t* seq_lens, float* summaries,
                           void* ws, size_t ws_bytes, void* stream);
 

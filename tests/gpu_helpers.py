@@ -35,15 +35,16 @@ def kv_tensor(w, arr):
 class Staged:
     """A workload's cache, tree and buffers on cuda:0, plus host copies for the oracle."""
 
-    def __init__(self, w, max_t=None, build=True, n_tokens=None, level_p=None, n_refs=None):
-        """n_refs: tangent scoring with that many reference queries per (level, kv head)."""
+    def __init__(self, w, max_t=None, build=True, n_tokens=None, level_p=None, n_refs=None, values=False):
+        """n_refs: tangent scoring with that many reference queries per (level, kv head);
+        values: compressed value summaries."""
         t = torch()
         self.w = w
         self.T = w.queries_per_step if max_t is None else max_t
         self.tangent = n_refs is not None
         self.geom = Z.make_geom(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.branching, w.n_levels,
                                 w.capacity, w.kv_dtype, level_p=level_p, n_refs=n_refs or 0,
-                                scoring="tangent" if self.tangent else "summary")
+                                scoring="tangent" if self.tangent else "summary", value_summaries=values)
         self.cache = Z.Cache(self.geom, self.T)
         self.K_np, self.V_np = W.kv_cache(w)
         self.cache.K.copy_(kv_tensor(w, self.K_np))
@@ -56,7 +57,7 @@ class Staged:
         self.Vf = W.as_f32(w, self.V_np)
         if build:
             Z.build_tree(self.geom, self.cache.K, self.ref_q, self.cache.seq_lens, self.cache.summaries,
-                         self.cache.ws)
+                         self.cache.ws, V=self.cache.V)
             t.cuda.synchronize()
 
     @property

@@ -82,6 +82,23 @@ def test_tangent_scoring_layout_and_validation():
         assert e.value.code == Z.ZHA_ERR_UNSUPPORTED, kw
 
 
+def test_value_summaries_layout_and_validation():
+    g = _geom(value_summaries=True)
+    s = Z.query_sizes(g, 1)
+    cap = (1 << 20) + 256
+    nodes = [cap // 32 ** l for l in range(1, 5)]
+    keys = sum(8 * n * 128 for n in nodes)
+    off = keys
+    for l in range(4):                       # value summaries follow the keys: d floats per node
+        assert s.level_value_offset[l] == off
+        off += 8 * nodes[l] * 128
+    assert s.summaries_bytes == off * 4
+    assert s.workspace_bytes > Z.query_sizes(_geom(), 1).workspace_bytes     # the pseudo-token partials
+    with pytest.raises(Z.ZhaError) as e:
+        Z.query_sizes(_geom(value_summaries=True, n_refs=4, scoring="tangent"), 1)
+    assert e.value.code == Z.ZHA_ERR_UNSUPPORTED
+
+
 def test_level_schedule_is_validated():
     assert Z.query_sizes(_geom(level_p=[0.9, 1.0, 0.5, 0.0]), 1).max_rows == 1
     for bad in ([1.5, 0, 0, 0], [-0.1, 0, 0, 0], [0.9, 0.9, 0.9, 0.9, 0.9], [float("nan"), 0, 0, 0]):
@@ -115,8 +132,10 @@ def test_null_and_workspace_errors_return_before_launch():
     g = _geom()
     gp = ctypes.byref(g)
     fake = ctypes.c_void_p(1 << 40)          # never dereferenced: validation fails first
-    assert L.zha_build_tree(gp, None, None, None, None, None, 0, None) == Z.ZHA_ERR_NULL
-    assert L.zha_build_tree(None, fake, fake, fake, fake, fake, 1 << 20, None) == Z.ZHA_ERR_NULL
+    assert L.zha_build_tree(gp, None, None, None, None, None, None, 0, None) == Z.ZHA_ERR_NULL
+    assert L.zha_build_tree(None, fake, fake, fake, fake, fake, fake, 1 << 20, None) == Z.ZHA_ERR_NULL
+    gv = _geom(value_summaries=True)
+    assert L.zha_build_tree(ctypes.byref(gv), fake, None, fake, fake, fake, fake, 1 << 20, None) == Z.ZHA_ERR_NULL
     need = Z.query_sizes(g, 1).workspace_bytes
     rc = L.zha_route(gp, fake, 1, None, fake, fake, ctypes.c_float(0.95), 16, fake, fake, None, None, fake,
                      need - 1, None)
