@@ -319,7 +319,8 @@ def _counter_rows(run_dir: str, counter: str):
     return [(d, n, v) for d, (n, v) in sorted(acc.items())]
 
 
-def write_traffic(fetch_dir: str, write_dir: str, kernel: str, workload: str, probe_mib: int, steps: int):
+def write_traffic(fetch_dir: str, write_dir: str, kernel: str, workload: str, probe_mib: int, steps: int,
+                  cold: bool = False):
     """Turn two counter runs of `bench.py --timed-only --copy-probe-mib M` (FETCH_SIZE, then
     WRITE_SIZE, both in KiB per dispatch) into HBM bytes per launch of `kernel`: each counter is
     scaled by (copy size / its reading for the copy probe) and averaged over the last `steps`
@@ -342,7 +343,7 @@ def write_traffic(fetch_dir: str, write_dir: str, kernel: str, workload: str, pr
     with open(os.path.join(ROOT, "hierarchical_tree_indexed_build_amd", "csrc", KERNEL_SOURCES[name]), "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
     rec = {"kernel": kernel, "workload": workload, "source_sha256": sha, "launches": steps,
-           "copy_probe_bytes": probe,
+           "cold": cold, "copy_probe_bytes": probe,
            "fetch": per["FETCH_SIZE"], "write": per["WRITE_SIZE"],
            "traffic_bytes_per_launch": int(round(per["FETCH_SIZE"]["bytes_per_launch"]
                                                  + per["WRITE_SIZE"]["bytes_per_launch"]))}
@@ -519,7 +520,7 @@ def main():
     if args.traffic_from:
         w = W.get_workload(args.workload)
         write_traffic(*args.traffic_from, args.kernel, w.name, args.copy_probe_mib,
-                      args.steps if args.steps is not None else w.steps)
+                      args.steps if args.steps is not None else w.steps, cold=args.cold)
         return
     w = W.get_workload(args.workload)
     if w.prefill_chunk:
