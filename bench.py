@@ -370,18 +370,25 @@ def prefill_main(args, w):
     warm = min(args.warmup, 2)
     T, n0 = w.prefill_chunk, w.n_tokens
     log(f"[bench] workload {w.name}: {w.description}; steps {steps}, warmup {warm}")
+    K_host, V_host = W.kv_cache(w)
+    kn, vn = W.prefill_chunk_kv(w)
+    q_host = W.queries(w, 0, rows=T)
+    cpu, cpu_outs = None, {}
+    if not (args.no_cpu or args.timed_only):
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f}s on {cpu_workers()} worker processes")
+        cpu, cpu_outs = prefill_cpu_baseline(w, q_host, K_host, V_host, kn, vn, args.cpu_seconds)
+    import torch
     geom = Z.make_geom(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.branching, w.n_levels, w.capacity,
                        w.kv_dtype)
-    c = Z.Cache(geom, T)
+    c = Z.Cache(geom, T, tiled=True)         # row tiles: the workspace of one tile, not of all T rows
+    log(f"[bench] workspace {c.ws.numel() * 4 / 2**30:.2f} GiB (rows in tiles of {c.sizes.tile_rows}; "
+        f"{c.sizes.workspace_bytes / 2**30:.1f} GiB for every row at once)")
     kdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
-    K_host, V_host = W.kv_cache(w)
     c.K.copy_(torch.from_numpy(K_host).view(kdt))
     c.V.copy_(torch.from_numpy(V_host).view(kdt))
-    kn, vn = W.prefill_chunk_kv(w)
     k_new = torch.from_numpy(kn).view(kdt).cuda()
     v_new = torch.from_numpy(vn).view(kdt).cuda()
     ref_q = torch.from_numpy(W.ref_queries(w)).cuda()
-    q_host = W.queries(w, 0, rows=T)
     q = torch.from_numpy(q_host).cuda()
     q_pos = (n0 + torch.arange(T, dtype=torch.int32, device="cuda")).view(1, T).repeat(w.batch, 1).contiguous()
     lens0 = torch.full((w.batch,), n0, dtype=torch.int32, device="cuda")
@@ -442,12 +449,16 @@ def prefill_main(args, w):
     seen = sum(int((Nv // bb ** l).sum()) for l in range(1, w.n_levels + 1))
     flops = 2.0 * d * seen * w.batch * w.n_q_heads
     k_avg_s = (k_ms / 1e3) / max(1, k_launch)
-    achieved = flops / k_avg_s if (kernel == "route_dense" and k_avg_s > 0) else 0.0
+    # a row tile per launch: the chunk's flops over the launches of its steps
+    flops_launch = flops * steps / max(1, k_launch)
+    achieved = flops_launch / k_avg_s if (kernel == "route_dense" and k_avg_s > 0) else 0.0
 
-    cpu = None
-    if not args.no_cpu:
-        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f}s")
-        cpu = prefill_cpu_baseline(w, c, q_host, K_host, V_host, kn, vn, args.cpu_seconds)
+    if cpu is not None:
+        # the GPU's rows against the oracle leg's, end to end
+        s_np, n_np, o_np, l_np = sel.cpu().numpy(), nsel.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+        gpu = {t_: (s_np[:, t_:t_ + 1], n_np[:, t_:t_ + 1], o_np[:, t_:t_ + 1], l_np[:, t_:t_ + 1])
+               for t_ in {k[0] for k in cpu_outs}}
+        cpu["parity"] = cpu_parity(w, cpu_outs, gpu)
     ms_step = wall * 1e3 / steps
     res = {
         "metric": PREFILL_METRIC,
@@ -467,47 +478,58 @@ def prefill_main(args, w):
                    "top_p": w.top_p, "kv_cache": w.kv_dtype},
         "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": FP32_MFMA_PEAK / 1e12,
                      "unit": "TFLOP/s", "frac": round(achieved / FP32_MFMA_PEAK, 4), "traffic": None,
-                     "kernel": kernel, "flops_per_launch": flops, "avg_launch_us": round(k_avg_s * 1e6, 3),
+                     "kernel": kernel, "flops_per_launch": flops_launch, "avg_launch_us": round(k_avg_s * 1e6, 3),
                      "launches": k_launch},
         "cpu_baseline": cpu,
         "ms_by_kernel_family": fam_ms,
+        "workspace_bytes": int(c.ws.numel() * 4),
+        "row_tile": int(c.sizes.tile_rows),
+        "workspace_bytes_one_pass": int(c.sizes.workspace_bytes),
         "candidates_per_row_head": [round(float(st[..., l, 0].mean()), 1) for l in range(w.n_levels)],
         "kept_per_row_head": [round(float(st[..., l, 1].mean()), 2) for l in range(w.n_levels)],
     }
     print(json.dumps(res), flush=True)
 
 
-def prefill_cpu_baseline(w, c, q_host, K_host, V_host, kn, vn, budget_s):
-    """The oracle routes and attends the chunk's rows in order (every head),
-    against the GPU-built tree copied to the host, until the budget is spent."""
-    from threadpoolctl import threadpool_limits
+def prefill_cpu_baseline(w, q_host, K_host, V_host, kn, vn, budget_s):
+    """The oracle routes and attends the chunk's rows in order (every head), each
+    row seeing the tokens up to its own position, on the same process pool as
+    the decode leg (run before the GPU is touched), against its own tree built
+    from the host keys, until the budget is spent. Returns the record and the
+    outputs per (row, 0, head)."""
+    import multiprocessing as mp
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import zha_oracle as O
     T, n0 = w.prefill_chunk, w.n_tokens
-    N = n0 + T
-    summ = c.summaries.cpu().numpy()
-    sizes = c.sizes
-    trees = [[[summ[sizes.level_offset[l - 1] + (s * w.n_kv_heads + h) * sizes.level_nodes[l - 1] * w.head_dim:]
-               [:(N // w.branching ** l) * w.head_dim].reshape(-1, w.head_dim)
-               for l in range(1, w.n_levels + 1)] for h in range(w.n_kv_heads)] for s in range(w.batch)]
     Kf = np.concatenate([W.as_f32(w, K_host[:, :, :n0]), W.as_f32(w, kn)], axis=2)
     Vf = np.concatenate([W.as_f32(w, V_host[:, :, :n0]), W.as_f32(w, vn)], axis=2)
+    R = W.ref_queries(w)
+    with ThreadPoolExecutor(W.host_threads()) as ex:
+        flat = list(ex.map(lambda sh: O.build_tree(Kf[sh[0], sh[1]], R[:, sh[1]], w.branching),
+                           [(s, h) for s in range(w.batch) for h in range(w.n_kv_heads)]))
+    trees = [flat[s * w.n_kv_heads:(s + 1) * w.n_kv_heads] for s in range(w.batch)]
+    # a row of the chunk plays the part of a decode step: its query and the tokens it sees
+    qsteps = [q_host[:, t:t + 1] for t in range(T)]
+    _CPU.update(w=w, trees=trees, Kf=[[Kf[s, h] for h in range(w.n_kv_heads)] for s in range(w.batch)],
+                Vf=[[Vf[s, h] for h in range(w.n_kv_heads)] for s in range(w.batch)], q=qsteps, top_p=w.top_p,
+                N={t: n0 + t + 1 for t in range(T)})
+    n = cpu_workers()
     done = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while time.perf_counter() - t0 < budget_s and done < T:
-            n = n0 + done + 1
-            for s in range(w.batch):
-                for hq in range(w.n_q_heads):
-                    kv = hq // w.group
-                    r = O.route(q_host[s, done, hq], trees[s][kv], n, w.branching, w.top_p)
-                    I = O.index_set(r.selected[0], n, w.branching)
-                    O.attend(q_host[s, done, hq], Kf[s, kv], Vf[s, kv], I)
+    outs = {}
+    with mp.get_context("fork").Pool(n, initializer=_one_blas_thread) as pool:
+        t0 = time.perf_counter()
+        while done < T and time.perf_counter() - t0 < budget_s:
+            tasks = [(done, s, hq) for s in range(w.batch) for hq in range(w.n_q_heads)]
+            for res in pool.map(_oracle_query, tasks, chunksize=1):
+                outs[res[:3]] = res[3:]
             done += 1
-    el = time.perf_counter() - t0
-    return {"value": round(done * w.batch / el, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"the chunk's first {done} rows x {w.batch} sequence(s) x {w.n_q_heads} heads (route + "
-                      f"exact attention per head, NumPy fp64, one BLAS thread) against the GPU-built tree, "
-                      f"{el:.1f}s"}
+        el = time.perf_counter() - t0
+    _CPU.clear()
+    rec = {"value": round(done * w.batch / el, 3), "unit": "rows/s", "cores": n, "kind": "oracle",
+           "sample": f"the chunk's first {done} rows x {w.batch} sequence(s) x {w.n_q_heads} heads: route + exact "
+                     f"attention per head, NumPy fp64, {n} worker processes with one BLAS thread each, the oracle's "
+                     f"own tree built from the host keys; {el:.1f}s"}
+    return rec, outs
 
 
 # ----------------------------------------------------------------------------

@@ -42,7 +42,7 @@ class Sizes(ctypes.Structure):
                 ("level_bias_offset", ctypes.c_int64 * ZHA_MAX_LEVELS),
                 ("level_value_offset", ctypes.c_int64 * ZHA_MAX_LEVELS),
                 ("level_sel_offset", ctypes.c_int64 * ZHA_MAX_LEVELS), ("level_sel_bytes", ctypes.c_size_t),
-                ("max_rows", ctypes.c_int32)]
+                ("max_rows", ctypes.c_int32), ("tile_rows", ctypes.c_int32), ("workspace_bytes_tiled", ctypes.c_size_t)]
 
 
 class ZhaError(RuntimeError):
@@ -250,7 +250,8 @@ def offsets_view(summaries, sizes: Sizes, geom: Geom, level: int):
 class Cache:
     """Device buffers for one geometry: K, V, summaries, seq_lens, workspace (torch-allocated)."""
 
-    def __init__(self, geom: Geom, max_t: int = 1, device: str = "cuda"):
+    def __init__(self, geom: Geom, max_t: int = 1, device: str = "cuda", tiled: bool = False):
+        """tiled: a workspace for row tiles (zha_sizes.workspace_bytes_tiled) instead of every row at once."""
         import torch
         self.geom = geom
         self.sizes = query_sizes(geom, max_t)
@@ -260,7 +261,8 @@ class Cache:
         self.V = torch.zeros(shape, dtype=kdt, device=device)
         self.summaries = torch.zeros(max(1, self.sizes.summaries_bytes // 4), dtype=torch.float32, device=device)
         self.seq_lens = torch.zeros(geom.batch, dtype=torch.int32, device=device)
-        self.ws = torch.zeros(max(256, self.sizes.workspace_bytes) // 4 + 64, dtype=torch.int32, device=device)
+        wsb = self.sizes.workspace_bytes_tiled if tiled else self.sizes.workspace_bytes
+        self.ws = torch.zeros(max(256, wsb) // 4 + 64, dtype=torch.int32, device=device)
 
     def level(self, level: int):
         return summaries_view(self.summaries, self.sizes, self.geom, level)

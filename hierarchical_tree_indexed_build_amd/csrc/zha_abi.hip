@@ -128,6 +128,7 @@ WsLayout layout(const Geo& g, int rows) {
     };
     const size_t R = static_cast<size_t>(rows);
     L.status = take(256);
+    L.qpos = take(R * 4);
     L.scores = take(R * g.Hq * g.nodes_total * 4);
     L.kept = take(R * g.Hq * g.nodes_total * 4);
     L.kept_cnt = take(R * g.Hq * g.L * 4);
@@ -187,6 +188,58 @@ zha_status check_rows(const Geo& g, int32_t t, int* rows) {
     const int64_t r = static_cast<int64_t>(g.B) * t;
     if (r > (int64_t(1) << 24)) return fail(ZHA_ERR_SHAPE, "too many query rows (%lld)", static_cast<long long>(r));
     *rows = static_cast<int>(r);
+    return ZHA_OK;
+}
+
+// ---- row tiles ----
+// A call of t rows of one sequence whose workspace holds only part of the
+// layout runs in tiles of rows (the largest halving of t whose layout fits),
+// each a complete route and attention of its rows; a tiled workspace for
+// max_t rows (zha_query_sizes) keeps under kTileBytes.
+constexpr size_t kTileBytes = size_t(4) << 30;
+
+int tile_rows_fitting(const Geo& g, int t, size_t bytes) {
+    int r = t;
+    while (r > 1 && layout(g, r).total > bytes) r = (r + 1) / 2;
+    return layout(g, r).total <= bytes ? r : 0;
+}
+
+// Default positions of a tile's rows (seq_lens[0] - t + t0 + i), written into the workspace.
+__global__ void tile_positions_kernel(int32_t* pos, const int32_t* seq_lens, int t, int t0, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) pos[i] = seq_lens[0] - t + t0 + i;
+}
+
+// Runs body(t0, rows, q_pos, layout) once with every row, or over row tiles
+// when the workspace is smaller than the full layout and tiling is allowed
+// (one sequence; the caller asked for no per-call buffer laid out by row count).
+template <class Body>
+zha_status run_rows(const Geo& g, int32_t t, const int32_t* q_pos, const int32_t* seq_lens, void* ws,
+                    size_t ws_bytes, bool can_tile, hipStream_t s, Body&& body) {
+    int rows;
+    zha_status st = check_rows(g, t, &rows);
+    if (st) return st;
+    const WsLayout full = layout(g, rows);
+    if (ws_bytes >= full.total || !can_tile || g.B != 1 || !ws) {
+        if ((st = check_ws(ws, ws_bytes, full.total))) return st;
+        return body(0, t, q_pos, full);
+    }
+    const int tile = tile_rows_fitting(g, t, ws_bytes);
+    if (tile == 0) return check_ws(ws, ws_bytes, layout(g, 1).total);
+    for (int t0 = 0; t0 < t; t0 += tile) {
+        const int tt = std::min(tile, t - t0);
+        const WsLayout Lt = layout(g, tt);
+        if ((st = check_ws(ws, ws_bytes, Lt.total))) return st;
+        const int32_t* qp = q_pos ? q_pos + t0 : nullptr;
+        if (!qp) {
+            int32_t* pos = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + Lt.qpos);
+            hipLaunchKernelGGL(tile_positions_kernel, dim3((tt + 255) / 256), dim3(256), 0, s, pos, seq_lens, t, t0, tt);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail(e, "tile positions launch");
+            qp = pos;
+        }
+        if ((st = body(t0, tt, qp, Lt))) return st;
+    }
     return ZHA_OK;
 }
 
@@ -276,6 +329,13 @@ zha_status zha_query_sizes(const zha_geom* geom, int32_t max_t, zha_sizes* out) 
     }
     out->level_sel_bytes = static_cast<size_t>(rows) * g.Hq * g.nodes_total * 4;
     out->max_rows = rows;
+    out->tile_rows = max_t;
+    out->workspace_bytes_tiled = L.total;
+    if (g.B == 1 && L.total > kTileBytes) {
+        const int tile = std::max(tile_rows_fitting(g, max_t, kTileBytes), 1);
+        out->tile_rows = tile;
+        out->workspace_bytes_tiled = layout(g, tile).total;
+    }
     return ZHA_OK;
 }
 
@@ -363,12 +423,15 @@ zha_status zha_route(const zha_geom* geom, const float* q, int32_t t, const int3
     zha_status st = make_geo(geom, &g);
     if (st) return st;
     if ((st = check_route_args(q, summaries, seq_lens, top_p, sel_capacity, sel_blocks, n_sel))) return st;
-    int rows;
-    if ((st = check_rows(g, t, &rows))) return st;
-    const WsLayout L = layout(g, rows);
-    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
-    return route_impl(g, q, t, q_pos, summaries, seq_lens, top_p, sel_capacity, sel_blocks, n_sel, level_stats,
-                      level_sel, ws, L, rows, static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return run_rows(g, t, q_pos, seq_lens, ws, ws_bytes, level_sel == nullptr, s,
+                    [&](int t0, int tt, const int32_t* qp, const WsLayout& L) {
+                        const int64_t r0 = static_cast<int64_t>(t0) * g.Hq;
+                        return route_impl(g, q + r0 * g.D, tt, qp, summaries, seq_lens, top_p, sel_capacity,
+                                          sel_blocks + r0 * sel_capacity, n_sel + r0,
+                                          level_stats ? level_stats + r0 * g.L * 2 : nullptr, level_sel, ws, L,
+                                          g.B * tt, s);
+                    });
 }
 
 static zha_status attend_impl(const Geo& g, const float* q, int32_t t, const int32_t* q_pos, const void* K,
@@ -409,12 +472,14 @@ zha_status zha_sparse_attend(const zha_geom* geom, const float* q, int32_t t, co
     if (!q || !K || !V || !seq_lens || !sel_blocks || !n_sel || !out || !lse)
         return fail(ZHA_ERR_NULL, "q, K, V, seq_lens, sel_blocks, n_sel, out and lse are required");
     if (sel_capacity < 1) return fail(ZHA_ERR_SHAPE, "sel_capacity must be >= 1");
-    int rows;
-    if ((st = check_rows(g, t, &rows))) return st;
-    const WsLayout L = layout(g, rows);
-    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
-    return attend_impl(g, q, t, q_pos, K, V, seq_lens, sel_blocks, n_sel, sel_capacity, out, lse, ws, L, rows, false,
-                       false, static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return run_rows(g, t, q_pos, seq_lens, ws, ws_bytes, true, s,
+                    [&](int t0, int tt, const int32_t* qp, const WsLayout& L) {
+                        const int64_t r0 = static_cast<int64_t>(t0) * g.Hq;
+                        return attend_impl(g, q + r0 * g.D, tt, qp, K, V, seq_lens, sel_blocks + r0 * sel_capacity,
+                                           n_sel + r0, sel_capacity, out + r0 * g.D, lse + r0, ws, L, g.B * tt,
+                                           false, false, s);
+                    });
 }
 
 zha_status zha_attend(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos, const void* K,
@@ -426,16 +491,19 @@ zha_status zha_attend(const zha_geom* geom, const float* q, int32_t t, const int
     if (st) return st;
     if ((st = check_route_args(q, summaries, seq_lens, top_p, sel_capacity, sel_blocks, n_sel))) return st;
     if (!K || !V || !out || !lse) return fail(ZHA_ERR_NULL, "K, V, out and lse are required");
-    int rows;
-    if ((st = check_rows(g, t, &rows))) return st;
-    const WsLayout L = layout(g, rows);
-    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = route_impl(g, q, t, q_pos, summaries, seq_lens, top_p, sel_capacity, sel_blocks, n_sel, level_stats,
-                         level_sel, ws, L, rows, s)))
-        return st;
-    return attend_impl(g, q, t, q_pos, K, V, seq_lens, sel_blocks, n_sel, sel_capacity, out, lse, ws, L, rows, false,
-                       true, s, summaries);
+    return run_rows(g, t, q_pos, seq_lens, ws, ws_bytes, level_sel == nullptr, s,
+                    [&](int t0, int tt, const int32_t* qp, const WsLayout& L) {
+                        const int64_t r0 = static_cast<int64_t>(t0) * g.Hq;
+                        int32_t* sb = sel_blocks + r0 * sel_capacity;
+                        int32_t* ns = n_sel + r0;
+                        zha_status e = route_impl(g, q + r0 * g.D, tt, qp, summaries, seq_lens, top_p, sel_capacity,
+                                                  sb, ns, level_stats ? level_stats + r0 * g.L * 2 : nullptr,
+                                                  level_sel, ws, L, g.B * tt, s);
+                        if (e) return e;
+                        return attend_impl(g, q + r0 * g.D, tt, qp, K, V, seq_lens, sb, ns, sel_capacity,
+                                           out + r0 * g.D, lse + r0, ws, L, g.B * tt, false, true, s, summaries);
+                    });
 }
 
 zha_status zha_attend_noalloc(const zha_geom* geom, const float* q, int32_t t, const int32_t* q_pos, const void* K,
@@ -501,12 +569,13 @@ zha_status zha_dense_attend(const zha_geom* geom, const float* q, int32_t t, con
     if (st) return st;
     if (!q || !K || !V || !seq_lens || !out || !lse)
         return fail(ZHA_ERR_NULL, "q, K, V, seq_lens, out and lse are required");
-    int rows;
-    if ((st = check_rows(g, t, &rows))) return st;
-    const WsLayout L = layout(g, rows);
-    if ((st = check_ws(ws, ws_bytes, L.total))) return st;
-    return attend_impl(g, q, t, q_pos, K, V, seq_lens, nullptr, nullptr, 1, out, lse, ws, L, rows, true,
-                       false, static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return run_rows(g, t, q_pos, seq_lens, ws, ws_bytes, true, s,
+                    [&](int t0, int tt, const int32_t* qp, const WsLayout& L) {
+                        const int64_t r0 = static_cast<int64_t>(t0) * g.Hq;
+                        return attend_impl(g, q + r0 * g.D, tt, qp, K, V, seq_lens, nullptr, nullptr, 1,
+                                           out + r0 * g.D, lse + r0, ws, L, g.B * tt, true, false, s);
+                    });
 }
 
 zha_status zha_read_device_status(void* ws, void* stream, uint32_t* out, int32_t clear) {

@@ -87,6 +87,7 @@ constexpr int kPseudoMaxRuns = 64;     // pseudo-token waves per (row, kv head) 
 // Byte layout of the workspace for `rows` query rows.
 struct WsLayout {
     size_t status;        // uint32 device status word (256-byte header)
+    size_t qpos;          // int32  [rows] positions of a row tile's rows when the caller passes none
     size_t scores;        // float  [rows, Hq, nodes_total] dense-by-node scores, level offsets = sel_off
     size_t kept;          // int32  [rows, Hq, nodes_total] kept lists per level (level 1 unused)
     size_t kept_cnt;      // int32  [rows, Hq, L]

@@ -158,6 +158,14 @@ typedef struct zha_sizes {
     int64_t level_sel_offset[ZHA_MAX_LEVELS];/* element offset of each level inside a level_sel buffer */
     size_t  level_sel_bytes;                 /* bytes of a level_sel buffer for max_rows rows */
     int32_t max_rows;                        /* B*T rows the workspace was sized for */
+    /* Row tiles (one sequence, B = 1): zha_route, zha_attend, zha_sparse_attend
+     * and zha_dense_attend accept a workspace smaller than workspace_bytes and
+     * then run their rows in tiles, the largest halving of t whose layout fits
+     * (not with level_sel, whose layout follows the whole call). For max_t rows
+     * a workspace of workspace_bytes_tiled (at most 4 GiB where the whole call
+     * needs more) runs tiles of tile_rows rows. */
+    int32_t tile_rows;
+    size_t  workspace_bytes_tiled;
 } zha_sizes;
 
 /* Sizes of the summary buffer and workspace for `geom` and calls with at most

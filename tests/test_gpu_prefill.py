@@ -201,3 +201,46 @@ def test_many_rows_deep_levels():
         assert n1 == len(parents)
         assert np.array_equal(np.sort(sel[0, t_, 0, :n1].cpu().numpy()), parents)
     say(f"  margin-exempt differences: {flips}")
+
+
+@pytest.mark.parametrize("shrink", [1, 0], ids=["s1", "full"])
+def test_prefill_row_tiles_match_one_pass(shrink):
+    """A workspace that holds only a tile of rows: zha_attend runs the chunk in
+    row tiles. Kept leaves, counts per level and the positions the rows see are
+    those of one pass over every row (each row's route is its own); the
+    attention differs only by the split-K partition's fp32 rounding."""
+    t = torch()
+    w = W.get_workload("prefill256k", shrink=shrink)
+    n0, T = w.n_tokens, w.prefill_chunk
+    st = Staged(w, max_t=T)
+    kn, vn = W.prefill_chunk_kv(w)
+    Z.append(st.geom, st.cache.K, st.cache.V, kv_tensor(w, kn), kv_tensor(w, vn), st.cache.seq_lens, st.ref_q,
+             st.cache.summaries, st.cache.ws)
+    qn, q = st.queries(0, rows=T)
+    sizes = Z.query_sizes(st.geom, T)
+    tile = 128 if shrink else sizes.tile_rows
+    small = Z.query_sizes(st.geom, tile).workspace_bytes
+    say(f"[prefill tiles] {w.name}: {T} rows; one pass {sizes.workspace_bytes / 2**30:.2f} GiB, "
+        f"tiles of {tile} rows {small / 2**30:.3f} GiB (tile_rows {sizes.tile_rows})")
+    ws_small = t.zeros(small // 4 + 64, dtype=t.int32, device="cuda")
+    cap = 4096
+    res = []
+    for ws in (st.cache.ws, ws_small):
+        sel = t.full((1, T, w.n_q_heads, cap), -1, dtype=t.int32, device="cuda")
+        nsel = t.zeros((1, T, w.n_q_heads), dtype=t.int32, device="cuda")
+        stats = t.zeros((1, T, w.n_q_heads, w.n_levels, 2), dtype=t.int32, device="cuda")
+        out = t.zeros_like(q)
+        lse = t.zeros(q.shape[:3], dtype=t.float32, device="cuda")
+        # no q_pos: the rows are the last T positions, which the tiles must reproduce
+        Z.attend(st.geom, q, None, st.cache.K, st.cache.V, st.cache.summaries, st.cache.seq_lens, w.top_p, sel,
+                 nsel, out, lse, ws, level_stats=stats)
+        t.cuda.synchronize()
+        res.append((sel, nsel, stats, out, lse))
+    (s1, n1, a1, o1, l1), (s2, n2, a2, o2, l2) = res
+    assert t.equal(n1, n2) and t.equal(a1, a2)
+    m = n1.clamp(max=cap)
+    keep = t.arange(cap, device="cuda")[None, None, None, :] < m[..., None]
+    assert t.equal(t.where(keep, s1, -1), t.where(keep, s2, -1))
+    e = max((o1 - o2).abs().max().item(), (l1 - l2).abs().max().item())
+    say(f"  kept sets and counts identical; |tiled - one pass| = {e:.3g}")
+    assert e <= 1e-4
