@@ -90,14 +90,71 @@ struct ItemsParams {
     int2* items;               // [rows, Hkv, item_stride]
     int64_t item_stride;
     int32_t* acnt;             // [rows, Hkv]
+    int32_t* segcnt;           // [rows, Hkv, seg_stride] items per segment, or null: each segment re-counts
+    int64_t seg_stride;
     int64_t cap;
     int lb, Hq, Hkv;
     int seg_words;             // words per segment: kItemsSegFew or kItemsThreads
 };
 
-constexpr int kItemsThreads = 256;
-constexpr int kItemsSegFew = kWave;             // with few pairs: one word per lane of the first wave
-constexpr int kItemsFewPairs = 64;
+// One pair's view of the level-1 bitmaps: complete chunks are valid below nc1,
+// the sink and the current chunk are always in.
+template <int G>
+struct ItemsView {
+    const uint32_t* bm0;
+    int64_t stride, nc1, nblk, cur;
+
+    __device__ __forceinline__ ItemsView(const ItemsParams& p, int row, int kv) {
+        const int N = visible_clamped(p.ri, row, p.cap);
+        nc1 = static_cast<int64_t>(N) >> p.lb;                                    // complete leaf chunks
+        nblk = N > 0 ? ((static_cast<int64_t>(N) - 1) >> p.lb) + 1 : 0;          // chunks incl. the current one
+        cur = nblk - 1;
+        stride = p.stride;
+        bm0 = p.bm + (static_cast<int64_t>(row) * p.Hq + static_cast<int64_t>(kv) * G) * p.stride;
+    }
+    __device__ __forceinline__ int64_t words() const { return (nblk + 31) >> 5; }
+    // word wd of the union: kept complete chunks of any head, the sink, the current chunk
+    __device__ __forceinline__ uint32_t word(int64_t wd, uint32_t (&heads)[G]) const {
+        const int64_t base = wd << 5;
+        const uint32_t valid = base >= nc1 ? 0u : (nc1 - base >= 32 ? 0xffffffffu : ((1u << (nc1 - base)) - 1u));
+        uint32_t u = 0;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            heads[h] = bm0[static_cast<int64_t>(h) * stride + wd] & valid;
+            u |= heads[h];
+        }
+        if (wd == 0 && nblk > 0) u |= 1u;
+        if ((cur >> 5) == wd) u |= 1u << (cur & 31);
+        return u;
+    }
+};
+
+// Items per segment, for pairs whose bitmaps span many segments: the items
+// kernel then adds the counts before its segment instead of re-reading every
+// earlier word, which for a 16M-token row costs O(segments^2) word reads.
+template <int G>
+__global__ __launch_bounds__(kItemsThreads) void attn_segcount_kernel(ItemsParams p) {
+    constexpr int NW = kItemsThreads / kWave;
+    __shared__ uint32_t red[NW];
+    const int seg = blockIdx.x, y = blockIdx.y;
+    const int row = y / p.Hkv, kv = y % p.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const ItemsView<G> v(p, row, kv);
+    const int64_t words = v.words();
+    const int64_t nseg = (words + p.seg_words - 1) / p.seg_words;
+    if (seg >= nseg) return;
+    const int64_t wd = static_cast<int64_t>(seg) * p.seg_words + tid;
+    uint32_t heads[G];
+    const uint64_t c = wave_scan_u64((tid < p.seg_words && wd < words) ? __popc(v.word(wd, heads)) : 0u);
+    if (lane == 63) red[w] = static_cast<uint32_t>(c);
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) t += red[i];
+        p.segcnt[static_cast<int64_t>(y) * p.seg_stride + seg] = static_cast<int32_t>(t);
+    }
+}
 
 template <int G>
 __global__ __launch_bounds__(kItemsThreads) void attn_items_kernel(ItemsParams p) {
@@ -107,39 +164,26 @@ __global__ __launch_bounds__(kItemsThreads) void attn_items_kernel(ItemsParams p
     const int seg = blockIdx.x, y = blockIdx.y;
     const int row = y / p.Hkv, kv = y % p.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int N = visible_clamped(p.ri, row, p.cap);
-    const int64_t nc1 = static_cast<int64_t>(N) >> p.lb;                        // complete leaf chunks
-    const int64_t nblk = N > 0 ? ((static_cast<int64_t>(N) - 1) >> p.lb) + 1 : 0;  // chunks incl. the current one
-    const int64_t cur = nblk - 1;
-    const int64_t words = (nblk + 31) >> 5;
+    const ItemsView<G> v(p, row, kv);
+    const int64_t words = v.words();
     const int64_t nseg = (words + p.seg_words - 1) / p.seg_words;
     const int64_t last = nseg > 0 ? nseg - 1 : 0;      // the last segment writes the count
     if (seg > last) return;
-    const uint32_t* bm0 = p.bm + (static_cast<int64_t>(row) * p.Hq + static_cast<int64_t>(kv) * G) * p.stride;
-    // word wd of the union: kept complete chunks of any head, the sink, the current chunk
-    auto word = [&](int64_t wd, uint32_t (&heads)[G]) -> uint32_t {
-        const int64_t base = wd << 5;
-        const uint32_t valid = base >= nc1 ? 0u : (nc1 - base >= 32 ? 0xffffffffu : ((1u << (nc1 - base)) - 1u));
-        uint32_t u = 0;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            heads[h] = bm0[static_cast<int64_t>(h) * p.stride + wd] & valid;
-            u |= heads[h];
-        }
-        if (wd == 0 && nblk > 0) u |= 1u;
-        if ((cur >> 5) == wd) u |= 1u << (cur & 31);
-        return u;
-    };
     const int64_t w0 = static_cast<int64_t>(seg) * p.seg_words;
     const int64_t wd = w0 + tid;
     uint32_t heads[G];
-    const uint32_t mine = (tid < p.seg_words && wd < words) ? word(wd, heads) : 0u;
+    const uint32_t mine = (tid < p.seg_words && wd < words) ? v.word(wd, heads) : 0u;
     // items before the segment
     uint64_t pre = 0;
+    if (p.segcnt) {
+        const int32_t* sc = p.segcnt + static_cast<int64_t>(y) * p.seg_stride;
+        for (int64_t x = tid; x < seg; x += kItemsThreads) pre += static_cast<uint32_t>(sc[x]);
+    } else {
 #pragma unroll 4
-    for (int64_t x = tid; x < w0; x += kItemsThreads) {
-        uint32_t hx[G];
-        pre += __popc(word(x, hx));
+        for (int64_t x = tid; x < w0; x += kItemsThreads) {
+            uint32_t hx[G];
+            pre += __popc(v.word(x, hx));
+        }
     }
     const uint64_t cnt = __popc(mine);
     const uint64_t inc = wave_scan_u64(cnt);
@@ -168,7 +212,7 @@ __global__ __launch_bounds__(kItemsThreads) void attn_items_kernel(ItemsParams p
         uint32_t mask = 0;
 #pragma unroll
         for (int h = 0; h < G; ++h) mask |= ((heads[h] >> bit) & 1u) << h;
-        if (chunk == cur) mask |= kAllHeads;
+        if (chunk == v.cur) mask |= kAllHeads;
         items[pos++] = make_int2(static_cast<int>(chunk), static_cast<int>(mask));
     }
     if (seg == last && tid == 0) p.acnt[y] = static_cast<int32_t>(total);
@@ -1022,13 +1066,26 @@ hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st) {
         ip.lb = g.lb;
         ip.Hq = g.Hq;
         ip.Hkv = g.Hkv;
-        ip.seg_words = pairs <= kItemsFewPairs ? kItemsSegFew : kItemsThreads;
+        ip.seg_words = items_seg_words(pairs);
+        const int64_t nseg = items_segments(g, pairs);
+        if (nseg > kItemsRecountSegs) {
+            ip.segcnt = reinterpret_cast<int32_t*>(ws + lay.segcnt);
+            ip.seg_stride = nseg;
+        }
+        const dim3 gi(static_cast<unsigned>(nseg), pairs), bi(kItemsThreads);
+        if (ip.segcnt) {
+            ProfScope ps("attn_segcount", 0, st);
+            switch (g.G) {
+                case 1: hipLaunchKernelGGL(attn_segcount_kernel<1>, gi, bi, 0, st, ip); break;
+                case 2: hipLaunchKernelGGL(attn_segcount_kernel<2>, gi, bi, 0, st, ip); break;
+                case 4: hipLaunchKernelGGL(attn_segcount_kernel<4>, gi, bi, 0, st, ip); break;
+                case 8: hipLaunchKernelGGL(attn_segcount_kernel<8>, gi, bi, 0, st, ip); break;
+                case 16: hipLaunchKernelGGL(attn_segcount_kernel<16>, gi, bi, 0, st, ip); break;
+                default: return hipErrorInvalidValue;
+            }
+        }
         {
             ProfScope ps("attn_items", 0, st);
-            const int64_t iwords = (g.nodes[0] + 1 + 31) / 32;                  // chunks incl. the current one
-            const dim3 gi(static_cast<unsigned>(std::max<int64_t>(1, (iwords + ip.seg_words - 1) / ip.seg_words)),
-                          pairs),
-                bi(kItemsThreads);
             switch (g.G) {
                 case 1: hipLaunchKernelGGL(attn_items_kernel<1>, gi, bi, 0, st, ip); break;
                 case 2: hipLaunchKernelGGL(attn_items_kernel<2>, gi, bi, 0, st, ip); break;

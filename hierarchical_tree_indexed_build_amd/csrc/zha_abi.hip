@@ -141,6 +141,10 @@ WsLayout layout(const Geo& g, int rows) {
     L.bitmap = take(R * g.Hq * static_cast<size_t>(bw) * 4);
     L.aitems = take(R * g.Hkv * static_cast<size_t>(g.nodes[0] + 2) * 8);
     L.acnt = take(R * g.Hkv * 4);
+    {
+        const int64_t nseg = items_segments(g, static_cast<int64_t>(R) * g.Hkv);
+        L.segcnt = take(nseg > kItemsRecountSegs ? R * g.Hkv * static_cast<size_t>(nseg) * 4 : 0);
+    }
     L.plan = take(2 * (R * g.Hkv + 1) * 8);
     L.partial = take((static_cast<size_t>(kAttnWorkgroups) + R * g.Hkv) * g.G * (g.D + 4) * 4);
     if (g.vsum) {

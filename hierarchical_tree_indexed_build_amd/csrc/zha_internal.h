@@ -82,6 +82,20 @@ struct Geo {
     int64_t summ_total;                // elements of the summary buffer
 };
 
+// Level-1 bitmap words -> attention items: a pair's words in segments, one
+// workgroup per segment (kItemsSegFew words with few pairs, else one per thread).
+constexpr int kItemsThreads = 256;
+constexpr int kItemsSegFew = kWave;
+constexpr int kItemsFewPairs = 64;
+constexpr int kItemsRecountSegs = 32;  // more segments per pair than this: count them in a pass of their own
+inline int items_seg_words(int64_t pairs) { return pairs <= kItemsFewPairs ? kItemsSegFew : kItemsThreads; }
+inline int64_t items_segments(const Geo& g, int64_t pairs) {
+    const int64_t words = (g.nodes[0] + 1 + 31) / 32;     // chunks incl. the current one
+    const int sw = items_seg_words(pairs);
+    const int64_t n = (words + sw - 1) / sw;
+    return n > 1 ? n : 1;
+}
+
 constexpr int kPseudoMaxRuns = 64;     // pseudo-token waves per (row, kv head) and level
 
 // Byte layout of the workspace for `rows` query rows.
@@ -96,6 +110,7 @@ struct WsLayout {
     int64_t bm_words_total;
     size_t aitems;        // int2   [rows, Hkv, nodes[0] + 2] attention items (block, head mask)
     size_t acnt;          // int32  [rows, Hkv]
+    size_t segcnt;        // int32  [rows, Hkv, items_segments] items per bitmap segment (long bitmaps only)
     size_t plan;          // int64  [2, rows * Hkv + 1] exclusive prefixes of attention groups and workgroup shares per (row, kv head)
     size_t partial;       // float  [kAttnWorkgroups + rows * Hkv, G, D + 4] split-K partial state per workgroup (max, sum, 2 pad, acc)
     size_t pseudo;        // float  [L, rows * Hkv, pseudo_runs, G, D + 4] pseudo-token partials (value summaries only)
