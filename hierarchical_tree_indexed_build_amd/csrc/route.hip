@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
     // parents' in a head's candidate order)
     float qv[G][DPL];
 #pragma unroll
-    for (int h = 0; h < G; ++h) load_row<DPL>(p.q + (rh0 + h) * D + part * DPL, qv[h]);
+    for (int h = 0; h < G; ++h) load_row_il<DPL, LPR>(p.q + (rh0 + h) * D + part * 4, qv[h]);
     const int lup = p.li + 1 < p.L ? p.li + 1 : p.L - 1;
     int32_t kc[G];
 #pragma unroll
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
 #pragma unroll
             for (int u2 = 0; u2 < UNR; ++u2) {
                 const int64_t c = imin(cb + u2 * RPP + sub, c1 - 1);   // a present row; extra results are dropped
-                load_row<DPL>(summ + (c * RT + rr) * D + part * DPL, x[u2]);
+                load_row_il<DPL, LPR>(summ + (c * RT + rr) * D + part * 4, x[u2]);
                 if constexpr (TAN) xo[u2] = offs[c * RT + rr];
             }
         };
@@ -1953,7 +1953,7 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
     const int N = clamp_visible(p.ri, row, p.cap);
     const int64_t rh = static_cast<int64_t>(row) * p.Hq + hq;
     float qv[DPL];
-    load_row<DPL>(p.q + rh * D + part * DPL, qv);
+    load_row_il<DPL, LPR>(p.q + rh * D + part * 4, qv);
 
     int64_t npar = 0;                          // kept nodes of the level above
     int32_t par0 = -1;                         // their one id when a lone candidate was kept (not in LDS)
@@ -2011,7 +2011,7 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
                 for (int u = 0; u < UNR; ++u) {
                     const int64_t k = imin(kb + u * RPP + sub, ncand - 1);   // a present row; extra results are dropped
                     const int64_t row = static_cast<int64_t>(sh.cid[k]) * RT + rr;
-                    load_row<DPL>(summ + row * D + part * DPL, x[u]);
+                    load_row_il<DPL, LPR>(summ + row * D + part * 4, x[u]);
                     if constexpr (TAN) xo[u] = offs[row];
                 }
 #pragma unroll

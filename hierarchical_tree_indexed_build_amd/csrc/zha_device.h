@@ -47,6 +47,21 @@ __device__ __forceinline__ void load_row(const float* __restrict__ p, float (&x)
     }
 }
 
+// A row of an fp32 matrix shared by LPR lanes, interleaved: lane `part` holds
+// float4 number part, part + LPR, part + 2 LPR, ... of the row, so each load
+// instruction covers LPR * 16 contiguous bytes of every row it touches. `p`
+// points at the lane's first float4 (row + 4 * part).
+template <int N, int LPR>
+__device__ __forceinline__ void load_row_il(const float* __restrict__ p, float (&x)[N]) {
+    static_assert(N % 4 == 0, "fp32 rows load in groups of 4");
+    const float4* v = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+        const float4 u = v[i * LPR];
+        x[4 * i + 0] = u.x; x[4 * i + 1] = u.y; x[4 * i + 2] = u.z; x[4 * i + 3] = u.w;
+    }
+}
+
 // Load M (1, 2 or 4) consecutive elements.
 template <int M>
 __device__ __forceinline__ void load_few(const uint16_t* __restrict__ p, float (&x)[M]) {
