@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
     // so a pair's parents spread evenly over its waves however the cut
     // clustered them. Below the top the wave finds them from the union of
     // the heads' kept bits, kWpl words a lane per pass.
-    constexpr int kWpl = 8;
+    constexpr int kWpl = 4;
     const int64_t nwords = top ? 0 : (nc_up + 31) >> 5;
     // first round of loads, every address valid whatever the level: the
     // heads' queries, the first pass's kept bits, and the heads' kept counts
@@ -240,51 +240,77 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
     float hmx[G];                                            // per head: max over its own candidates
 #pragma unroll
     for (int h = 0; h < G; ++h) hmx[h] = -INFINITY;
-    // scores parent par's children for all G heads; the heads of `hm` (bit h)
-    // take them as candidates (read with the summaries when the split cut
-    // needs them: all heads for the incomplete parent and at the top)
-    auto score_parent = [&](int64_t par, bool every) {
-        const int64_t c0 = par << p.lb;
-        const int64_t c1 = imin(c0 + p.b, nc);
-        float x[UNR][DPL];
-        float xo[UNR];                                   // tangent scoring: the rows' offsets
-        auto load_pass = [&](int64_t cb, int rr) {
+    // Active parents are scored in groups: with b below the S = UNR * RPP
+    // rows of a pass, one pass holds min(PPM, S / b) parents, so each of the
+    // wave's round trips to memory carries S summary rows instead of b. Slot
+    // (u2, sub) of a pass is row u2 * RPP + sub of the group; with b >= S the
+    // group is one parent and the passes step through its children. Every
+    // head's score of every child is written; for the split cut, the heads
+    // that take a parent (all of them at the top and for the incomplete
+    // parent, else those that kept it at the level above) also get its
+    // children as candidates, at the parent's place in their candidate order.
+    constexpr int S = UNR * RPP;
+    // (at most two: each parent's values are named variables, since an array
+    // selected by the lane's slot would be indexed dynamically and leave registers)
+    constexpr int PPM = (G <= 4 && !TAN) ? 2 : 1;
+    const int pp = p.b >= S ? 1 : imin(PPM, S >> p.lb);    // parents per group
+    int64_t gpar0 = 0, gpar1 = 0;
+    int gn = 0;
+    auto score_group = [&]() {
+        const int np = gn;
+        gn = 0;
+        // rows of the group past its first child's (b >= S: the parent's children)
+        const int64_t ext = p.b >= S ? imin((gpar0 << p.lb) + p.b, nc) - (gpar0 << p.lb) : S;
+        // the slot's parent within the group
+        auto slot_parent = [&](int u2) { return p.b >= S ? 0 : ((u2 * RPP + sub) >> p.lb); };
+        int32_t c_[UNR];                                 // the slot's node, or -1 where the slot is empty
+        auto slot_rows = [&](int64_t cb) {
 #pragma unroll
             for (int u2 = 0; u2 < UNR; ++u2) {
-                const int64_t c = imin(cb + u2 * RPP + sub, c1 - 1);   // a present row; extra results are dropped
+                const int slot = u2 * RPP + sub;
+                const int pi = slot_parent(u2);
+                const int64_t co = p.b >= S ? cb + slot : static_cast<int64_t>(slot & (p.b - 1));
+                const int64_t par = (PPM > 1 && pi == 1 && np > 1) ? gpar1 : gpar0;
+                const int64_t c = (par << p.lb) + co;
+                c_[u2] = (pi < np && c < imin((par << p.lb) + p.b, nc)) ? static_cast<int32_t>(c) : -1;
+            }
+        };
+        float x[UNR][DPL];
+        float xo[UNR];                                   // tangent scoring: the rows' offsets
+        auto load_pass = [&](int rr) {
+#pragma unroll
+            for (int u2 = 0; u2 < UNR; ++u2) {
+                // an empty slot reads the group's first row; its results are dropped
+                const int64_t c = c_[u2] >= 0 ? static_cast<int64_t>(c_[u2]) : (gpar0 << p.lb);
                 load_row_il<DPL, LPR>(summ + (c * RT + rr) * D + part * 4, x[u2]);
                 if constexpr (TAN) xo[u2] = offs[c * RT + rr];
             }
         };
-        load_pass(c0, 0);
-        // split: which heads took the parent and where its children start in
-        // each head's candidate order, read with the first summaries (without
-        // the split, and for the incomplete parent past the ranked ones, from
-        // valid stand-in addresses, unused)
-        const bool orph = !top && par == nc_up;
-        const int64_t pr = (top || nc_up == 0) ? 0 : imin(par, nc_up - 1);
-        const int32_t* rp = split ? p.rank_up + rh0 * p.nodes_total + p.lvl_off_up + pr : p.kept_cnt;
-        const int64_t rstride = split ? p.nodes_total : 0;
-        const uint32_t* bp = split ? p.bm_up + rh0 * p.bm_words_total + (pr >> 5) : p.bm_up;
-        const int64_t bstride = split ? p.bm_words_total : 0;
-        int32_t rk[G];
-        uint32_t bw[G];
+        slot_rows(0);
+        load_pass(0);
+        // split: each parent's candidate base per head, read with the first summaries
+        int32_t cbp0[G], cbp1[G];
+        auto cand_base = [&](int64_t par, int32_t (&cbp)[G]) {
+            const bool orph = !top && par == nc_up;
+            const int64_t pr = (top || nc_up == 0) ? 0 : imin(par, nc_up - 1);
+            const int32_t* rp = p.rank_up + rh0 * p.nodes_total + p.lvl_off_up + pr;
+            const uint32_t* bp = p.bm_up + rh0 * p.bm_words_total + (pr >> 5);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            rk[h] = rp[h * rstride];
-            bw[h] = bp[h * bstride];
-        }
-        int64_t cbase[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            cbase[h] = -1;
-            if (split && (every || ((bw[h] >> (pr & 31)) & 1u))) {
-                if (top) cbase[h] = c0;
-                else if (orph) cbase[h] = static_cast<int64_t>(kc[h]) << p.lb;
-                else cbase[h] = static_cast<int64_t>(rk[h]) << p.lb;
+            for (int h = 0; h < G; ++h) {
+                const int32_t rk = rp[h * p.nodes_total];
+                const uint32_t bw = bp[h * p.bm_words_total];
+                int32_t cb = -1;
+                if (top) cb = static_cast<int32_t>(par << p.lb);
+                else if (orph) cb = kc[h] << p.lb;
+                else if ((bw >> (pr & 31)) & 1u) cb = rk << p.lb;
+                cbp[h] = cb;
             }
+        };
+        if (split) {
+            cand_base(gpar0, cbp0);
+            if (PPM > 1) cand_base(np > 1 ? gpar1 : gpar0, cbp1);
         }
-        for (int64_t cb = c0;;) {
+        for (int64_t cb = 0;;) {
             // a node's score: q . summary * scale, or the largest of its R tangents
             float best[UNR][G];
             for (int rr = 0;;) {
@@ -301,47 +327,64 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
                     }
                 }
                 if (++rr >= RT) break;
-                load_pass(cb, rr);
+                load_pass(rr);
             }
 #pragma unroll
             for (int u2 = 0; u2 < UNR; ++u2) {
-                const int64_t c = cb + u2 * RPP + sub;
-                if (c < c1) {
+                const int64_t c = c_[u2];
+                const int pi = slot_parent(u2);
+                if (c >= 0) {
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
                         const float sv = best[u2][h];
                         if (part == h) sc0[static_cast<int64_t>(h) * p.nodes_total + c] = sv;
-                        if (split && cbase[h] >= 0) {
-                            hmx[h] = fmaxf(hmx[h], sv);
-                            if (part == h) {
-                                const int64_t at = (rh0 + h) * p.cand_stride + cbase[h] + (c - c0);
-                                p.cand_sc[at] = sv;
-                                p.cand_nd[at] = static_cast<int32_t>(c);
+                        if (split) {
+                            const int32_t cbh = (PPM > 1 && pi == 1) ? cbp1[h] : cbp0[h];
+                            if (cbh >= 0) {
+                                hmx[h] = fmaxf(hmx[h], sv);
+                                if (part == h) {
+                                    const int64_t at = (rh0 + h) * p.cand_stride + cbh + (c & (p.b - 1));
+                                    p.cand_sc[at] = sv;
+                                    p.cand_nd[at] = static_cast<int32_t>(c);
+                                }
                             }
                         }
                     }
                 }
             }
-            cb += UNR * RPP;
-            if (cb >= c1) break;
-            load_pass(cb, 0);
+            cb += S;
+            if (cb >= ext) break;
+            slot_rows(cb);
+            load_pass(0);
         }
     };
-
+    // The wave's active parents one after another: at the top every b-block
+    // of nodes; below, the kept parents from the union bits, then the
+    // incomplete parent.
     int64_t j = run;                       // the next active parent this wave takes
-    if (top) {
-        const int64_t blocks = (nc + p.b - 1) >> p.lb;
-        for (; j < blocks; j += W) score_parent(j, true);
-    } else {
-        int64_t base = 0;                  // active parents before this pass
-        for (int64_t w0 = 0; w0 < nwords; w0 += static_cast<int64_t>(kWave) * kWpl) {
-            if (w0) load_union(w0);
-            uint32_t cnt = 0;
+    int64_t base = 0;                      // active parents before the current pass of union words
+    int64_t w0 = 0;                        // the pass's first word
+    int64_t pass_n = 0;                    // active parents in the pass
+    uint64_t incl = 0;                     // the lane's inclusive count of them
+    bool orph_left = !top && orphans > 0;
+    const int64_t blocks = top ? (nc + p.b - 1) >> p.lb : 0;
+    auto count_pass = [&]() {
+        uint32_t cnt = 0;
 #pragma unroll
-            for (int k = 0; k < kWpl; ++k) cnt += __popc(u[k]);
-            const uint64_t incl = wave_scan_u64(cnt);
-            const int64_t pass_n = static_cast<int64_t>(lane63_u64(incl));
-            for (; j < base + pass_n; j += W) {
+        for (int k = 0; k < kWpl; ++k) cnt += __popc(u[k]);
+        incl = wave_scan_u64(cnt);
+        pass_n = static_cast<int64_t>(lane63_u64(incl));
+    };
+    if (!top && nwords > 0) count_pass();
+    auto next_parent = [&]() -> int64_t {
+        if (top) {
+            if (j >= blocks) return -1;
+            const int64_t r = j;
+            j += W;
+            return r;
+        }
+        while (w0 < nwords) {
+            if (j < base + pass_n) {
                 // the lane whose words hold active parent j, then the word and the bit
                 const uint64_t rel = static_cast<uint64_t>(j - base);
                 const int L = __popcll(__ballot(incl <= rel));
@@ -362,12 +405,36 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
                         }
                     }
                 }
-                score_parent(par, false);
+                j += W;
+                return par;
             }
             base += pass_n;
+            w0 += static_cast<int64_t>(kWave) * kWpl;
+            pass_n = 0;
+            if (w0 < nwords) {
+                load_union(w0);
+                count_pass();
+            }
         }
         // the incomplete parent is active parent `base`
-        if (orphans > 0 && j == base) score_parent(nc_up, true);
+        if (orph_left && j == base) {
+            orph_left = false;
+            return nc_up;
+        }
+        return -1;
+    };
+    for (;;) {
+        int n = 0;
+        for (; n < pp; ++n) {
+            const int64_t par = next_parent();
+            if (par < 0) break;
+            if (n == 0) gpar0 = par;
+            else gpar1 = par;
+        }
+        if (n == 0) break;
+        gn = n;
+        score_group();
+        if (n < pp) break;
     }
     if (split) {
         float m = -INFINITY;

@@ -27,6 +27,9 @@ from tests.gpu_helpers import EPS32, Staged, check_attention, kv_tensor, level_k
 pytestmark = pytest.mark.gpu
 
 GAP = 1e-3
+# units of eps32 * (2 + max|z|) * max|c| in the tangent key bound: the worst key
+# error seen off the near ties is 0.55 of it (offsets 0.04)
+TANGENT_FACTOR = 16.0
 
 
 def _unstable(trees, w):
@@ -74,8 +77,8 @@ def _check_tangent_tree(st, trees, n_tokens):
                 r = st.R[level - 1, h].astype(np.float64)                  # (R, d)
                 zmax = w.scale * np.abs(ch.reshape(-1, ch.shape[-1]) @ r.T).max() + np.abs(co).max()
                 cmax = max(1.0, np.abs(ch).max())
-                tol_k = 64 * EPS32 * (2.0 + zmax) * cmax
-                tol_o = tol_k * (1.0 + w.scale * np.abs(r).sum(axis=1).max()) + 64 * EPS32 * (2.0 + zmax)
+                tol_k = TANGENT_FACTOR * EPS32 * (2.0 + zmax) * cmax
+                tol_o = tol_k * (1.0 + w.scale * np.abs(r).sum(axis=1).max()) + TANGENT_FACTOR * EPS32 * (2.0 + zmax)
                 ek = np.abs(keys[s, h, :n].astype(np.float64) - ref.keys).max(axis=(1, 2))
                 eo = np.abs(offs[s, h, :n].astype(np.float64) - ref.offs).max(axis=1)
                 bad = (ek > tol_k) | (eo > tol_o)
