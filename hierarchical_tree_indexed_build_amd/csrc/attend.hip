@@ -1013,6 +1013,47 @@ __global__ __launch_bounds__(kCombineThreads) void attend_combine_kernel(AttnPar
 // ----------------------------------------------------------------------------
 // launchers
 // ----------------------------------------------------------------------------
+// Attention workgroups of one launch: what the chip holds at once at the
+// kernel's register use (blocks per compute unit x compute units), at most
+// kAttnWorkgroups. A kernel that holds one block per compute unit then runs
+// its shares in one round rather than two with a tail. Read once per device.
+template <typename F>
+static int resident_workgroups(F* kernel, int block) {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kAttnWorkgroups;
+    int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+    if (n > 0) return n;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), block, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 || cus < 1) {
+        (void)hipGetLastError();
+        return kAttnWorkgroups;
+    }
+    n = per_cu * cus < kAttnWorkgroups ? per_cu * cus : kAttnWorkgroups;
+    __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
+    return n;
+}
+
+template <typename KT, int D, int G>
+static int attn_workgroups_t() {
+    if constexpr (sizeof(KT) == 2) return resident_workgroups(attend_mfma_kernel<D, G>, 256);
+    else return resident_workgroups(attend_kernel<KT, D, G>, 256);
+}
+
+template <typename KT, int D>
+static int attn_workgroups_g(int G) {
+    switch (G) {
+        case 1: return attn_workgroups_t<KT, D, 1>();
+        case 2: return attn_workgroups_t<KT, D, 2>();
+        case 4: return attn_workgroups_t<KT, D, 4>();
+        case 8: return attn_workgroups_t<KT, D, 8>();
+        case 16: return attn_workgroups_t<KT, D, 16>();
+        default: return kAttnWorkgroups;
+    }
+}
+
 template <typename KT, int D, int G>
 static hipError_t launch_attn_t(const AttnParams& ap, int rows, int Hq, float* out, float* lse, hipStream_t st) {
     {
@@ -1115,7 +1156,11 @@ hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st) {
     ap.Hq = g.Hq;
     ap.Hkv = g.Hkv;
     ap.pairs = pairs;
-    ap.nwg = kAttnWorkgroups;
+    {
+        const bool bf16 = g.kv_dtype == ZHA_KV_BF16;
+        ap.nwg = g.D == 128 ? (bf16 ? attn_workgroups_g<uint16_t, 128>(g.G) : attn_workgroups_g<float, 128>(g.G))
+                            : (bf16 ? attn_workgroups_g<uint16_t, 64>(g.G) : attn_workgroups_g<float, 64>(g.G));
+    }
     ap.dense = a.dense ? 1 : 0;
     ap.wave_plan = pairs <= kWave ? 1 : 0;
     ap.qscale = g.scale * kLog2e;
