@@ -32,6 +32,14 @@ namespace zha {
 
 constexpr uint32_t kAllHeads = 1u << 30;     // item flag: every head attends the chunk (current chunk)
 
+// An item read through the scalar data cache: the list is not written while
+// the attention runs, so it can be read as constant memory.
+typedef __attribute__((address_space(4))) const int const_i32;
+__device__ __forceinline__ int2 scalar_item(const int2* items, int64_t i) {
+    const const_i32* c = (const const_i32*)(items);
+    return make_int2(c[2 * i], c[2 * i + 1]);
+}
+
 __device__ __forceinline__ int visible_clamped(const RowInfo& ri, int row, int64_t cap) {
     const int s = row / ri.T;
     int n = row_visible(ri, row);
@@ -436,7 +444,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
     __shared__ float sm_acc[NW][G][D];
 
     const int wg = blockIdx.x;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform in the wave
     const int part = lane % LPT, tsub = lane / LPT;
     const PlanView pv(p);
     const int pr = pv.pair_of_wg(wg);           // the one pair this workgroup works on
@@ -471,22 +480,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
             for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
         }
 
-        // group g -> (chunk id, head mask). For the sparse path the chunk ids of
-        // 64 of this wave's upcoming groups are loaded at once, one per lane, and
-        // read back with readlane, so no dependent load sits in the pipeline.
-        int64_t batch_k0 = -1;
-        int2 batch = make_int2(0, 0);
+        // group g -> (chunk id, head mask): a scalar load (the address is
+        // wave-uniform), issued two groups ahead of its use; its wait counts
+        // scalar loads only, so the K/V rows in flight stay in flight
         auto item_of = [&](int64_t g) -> int2 {
             const int64_t it = g >> p.lgpi;
             if (p.dense) return make_int2(static_cast<int>(it), static_cast<int>(kAllHeads));
-            const int64_t k = (g - ga - wave) / NW;                 // this wave's k-th group
-            if (batch_k0 < 0 || k >= batch_k0 + kWave) {
-                batch_k0 = k;
-                const int64_t gl = g + static_cast<int64_t>(lane) * NW;
-                batch = gl < gb ? items[gl >> p.lgpi] : make_int2(0, 0);
-            }
-            const int src = static_cast<int>(k - batch_k0);
-            return make_int2(__builtin_amdgcn_readlane(batch.x, src), __builtin_amdgcn_readlane(batch.y, src));
+            return scalar_item(items, it);
         };
         auto first_token = [&](int64_t g, int2 e) -> int64_t {
             return (static_cast<int64_t>(e.x) << p.lb) + (g & (gpi - 1)) * kGroupTokens;
@@ -548,37 +548,36 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
 
         // Software pipeline over this wave's groups ga+wave, +NW, +2NW, ...: while a
         // group is consumed, the K/V rows of the next one and the chunk id of the
-        // one after are already in flight. Buffers A and B alternate.
+        // one after are already in flight. Buffers A and B alternate. Every load
+        // in the loop is unconditional (past the wave's last group the indices
+        // stay on that group, whose rows the caches hold), so the waits before a
+        // group's use leave the loads issued after it in flight.
         uint32_t kA[NP][WPP], vA[NP][WPP], kB[NP][WPP], vB[NP][WPP];
-        int64_t g = ga + wave;
-        if (g < gb) {
-            int2 e0 = item_of(g);                                          // chunk of group g
-            int2 e1 = (g + NW < gb) ? item_of(g + NW) : make_int2(0, 0);   // chunk of group g + NW
-            issue(first_token(g, e0), kA, vA);
-            for (;;) {
-                int64_t gn = g + NW;
-                int2 e2 = make_int2(0, 0);
-                if (gn < gb) {
-                    issue(first_token(gn, e1), kB, vB);
-                    if (gn + NW < gb) e2 = item_of(gn + NW);
-                }
-                consume(first_token(g, e0), static_cast<uint32_t>(e0.y), kA, vA);
-                if (gn >= gb) break;
-                g = gn;
+        const int64_t g0 = ga + wave;
+        // this wave's groups (32-bit counters: their compares stay on the scalar unit)
+        const int nk = g0 < gb ? static_cast<int>((gb - g0 + NW - 1) / NW) : 0;
+        auto grp = [&](int k) { return g0 + static_cast<int64_t>(k < nk ? k : nk - 1) * NW; };
+        if (nk > 0) {
+            int2 e0 = item_of(grp(0));
+            int2 e1 = item_of(grp(1));
+            issue(first_token(grp(0), e0), kA, vA);
+            // one exit, at the top: a path that left the loop from its middle
+            // would reach the loop head with B's loads unwaited, and the wait
+            // placed for it there would drain every load each iteration
+            int k = 0;
+            for (; k + 1 < nk; k += 2) {
+                int2 e2 = item_of(grp(k + 2));
+                issue(first_token(grp(k + 1), e1), kB, vB);
+                consume(first_token(grp(k), e0), static_cast<uint32_t>(e0.y), kA, vA);
                 e0 = e1;
                 e1 = e2;
-                gn = g + NW;
-                e2 = make_int2(0, 0);
-                if (gn < gb) {
-                    issue(first_token(gn, e1), kA, vA);
-                    if (gn + NW < gb) e2 = item_of(gn + NW);
-                }
-                consume(first_token(g, e0), static_cast<uint32_t>(e0.y), kB, vB);
-                if (gn >= gb) break;
-                g = gn;
+                e2 = item_of(grp(k + 3));
+                issue(first_token(grp(k + 2), e1), kA, vA);
+                consume(first_token(grp(k + 1), e0), static_cast<uint32_t>(e0.y), kB, vB);
                 e0 = e1;
                 e1 = e2;
             }
+            if (k < nk) consume(first_token(grp(k), e0), static_cast<uint32_t>(e0.y), kA, vA);   // odd count
         }
 
         // ---- merge the token slots of each wave, then the waves ----
@@ -674,7 +673,8 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
     __shared__ float sm_p[NW][kGroupTokens][G];   // a group's probabilities, token-major
 
     const int wg = blockIdx.x;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform in the wave
     const int part = lane % LPT, tsub = lane / LPT;       // value-pass layout
     const int mrow = lane & 15, mblk = lane >> 4;          // MFMA layout: token/head, dim block
     const PlanView pv(p);
@@ -726,19 +726,13 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
 #pragma unroll
             for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
 
-        int64_t batch_k0 = -1;
-        int2 batch = make_int2(0, 0);
+        // group g -> (chunk id, head mask): a scalar load (the address is
+        // wave-uniform), issued two groups ahead of its use; its wait counts
+        // scalar loads only, so the K/V rows in flight stay in flight
         auto item_of = [&](int64_t g) -> int2 {
             const int64_t it = g >> p.lgpi;
             if (p.dense) return make_int2(static_cast<int>(it), static_cast<int>(kAllHeads));
-            const int64_t k = (g - ga - wave) / NW;                 // this wave's k-th group
-            if (batch_k0 < 0 || k >= batch_k0 + kWave) {
-                batch_k0 = k;
-                const int64_t gl = g + static_cast<int64_t>(lane) * NW;
-                batch = gl < gb ? items[gl >> p.lgpi] : make_int2(0, 0);
-            }
-            const int src = static_cast<int>(k - batch_k0);
-            return make_int2(__builtin_amdgcn_readlane(batch.x, src), __builtin_amdgcn_readlane(batch.y, src));
+            return scalar_item(items, it);
         };
         auto first_token = [&](int64_t g, int2 e) -> int64_t {
             return (static_cast<int64_t>(e.x) << p.lb) + (g & (gpi - 1)) * kGroupTokens;
@@ -819,37 +813,31 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
             __builtin_amdgcn_wave_barrier();                       // sm_p is rewritten by the next group
         };
 
+        // the pipeline of attend_kernel: unconditional loads, A and B alternating
         uint32_t kA[KW], vA[NP][WPP], kB[KW], vB[NP][WPP];
-        int64_t g = ga + wave;
-        if (g < gb) {
-            int2 e0 = item_of(g);                                          // chunk of group g
-            int2 e1 = (g + NW < gb) ? item_of(g + NW) : make_int2(0, 0);   // chunk of group g + NW
-            issue(first_token(g, e0), kA, vA);
+        const int64_t g0 = ga + wave;
+        // this wave's groups (32-bit counters: their compares stay on the scalar unit)
+        const int nk = g0 < gb ? static_cast<int>((gb - g0 + NW - 1) / NW) : 0;
+        auto grp = [&](int k) { return g0 + static_cast<int64_t>(k < nk ? k : nk - 1) * NW; };
+        if (nk > 0) {
+            int2 e0 = item_of(grp(0));
+            int2 e1 = item_of(grp(1));
+            issue(first_token(grp(0), e0), kA, vA);
             split_q();
-            for (;;) {
-                int64_t gn = g + NW;
-                int2 e2 = make_int2(0, 0);
-                if (gn < gb) {
-                    issue(first_token(gn, e1), kB, vB);
-                    if (gn + NW < gb) e2 = item_of(gn + NW);
-                }
-                consume(first_token(g, e0), static_cast<uint32_t>(e0.y), kA, vA);
-                if (gn >= gb) break;
-                g = gn;
+            int k = 0;
+            for (; k + 1 < nk; k += 2) {          // one exit, at the top (see attend_kernel)
+                int2 e2 = item_of(grp(k + 2));
+                issue(first_token(grp(k + 1), e1), kB, vB);
+                consume(first_token(grp(k), e0), static_cast<uint32_t>(e0.y), kA, vA);
                 e0 = e1;
                 e1 = e2;
-                gn = g + NW;
-                e2 = make_int2(0, 0);
-                if (gn < gb) {
-                    issue(first_token(gn, e1), kA, vA);
-                    if (gn + NW < gb) e2 = item_of(gn + NW);
-                }
-                consume(first_token(g, e0), static_cast<uint32_t>(e0.y), kB, vB);
-                if (gn >= gb) break;
-                g = gn;
+                e2 = item_of(grp(k + 3));
+                issue(first_token(grp(k + 2), e1), kA, vA);
+                consume(first_token(grp(k + 1), e0), static_cast<uint32_t>(e0.y), kB, vB);
                 e0 = e1;
                 e1 = e2;
             }
+            if (k < nk) consume(first_token(grp(k), e0), static_cast<uint32_t>(e0.y), kA, vA);   // odd count
         }
 
         // ---- merge: the four dim blocks' shares of l, the token slots of the
