@@ -466,11 +466,26 @@ struct BlockScratch {
     uint32_t list[kCutList];    // candidates of the boundary bin
     float list_s[kCutList];     // and their scores
     uint32_t list_n;
-    uint64_t wpk[kWave];        // single-wave ranking: (key, candidate) pairs, masses in rank order, prefixes
-    uint64_t wmass[kWave];
-    uint64_t wpre[kWave];
     int32_t wcount;
 };
+
+// For lanes 0..m-1 holding distinct sort keys pk (m <= 64, wave-uniform) and
+// masses F: the sum of the masses of the members whose key is below the lane's
+// own, i.e. the mass ranked before it in key order. Every member's key and
+// mass are broadcast from registers (readlane), one member a step.
+__device__ __forceinline__ uint64_t mass_ranked_before(uint64_t pk, uint64_t F, int m) {
+    uint64_t pre = 0;
+    for (int j = 0; j < m; ++j) {
+        const uint64_t pj = (static_cast<uint64_t>(static_cast<uint32_t>(
+                                 __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(pk >> 32)), j))) << 32) |
+                            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(pk)), j));
+        const uint64_t fj = (static_cast<uint64_t>(static_cast<uint32_t>(
+                                 __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(F >> 32)), j))) << 32) |
+                            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(F)), j));
+        pre += pj < pk ? fj : 0ull;
+    }
+    return pre;
+}
 
 // The boundary bin's members resolved by one wave (m <= 64, member i on lane
 // i, candidate ids lk[] and scores ls[]): each lane ranks its member in (key,
@@ -488,17 +503,9 @@ __device__ __forceinline__ void wave_resolve(const uint32_t* lk, const float* ls
     const uint32_t key = valid ? desc_key(s) : 0xffffffffu;
     const uint64_t F = valid ? mass_fx(s, mx) : 0;
     const uint64_t pk = valid ? ((static_cast<uint64_t>(key) << 32) | k) : ~0ull;   // distinct per member
-    bs.wpk[lane] = pk;
-    __builtin_amdgcn_wave_barrier();
-    int rank = 0;
-#pragma unroll 8
-    for (int j = 0; j < kWave; ++j) rank += bs.wpk[j] < pk;
-    if (valid) bs.wmass[rank] = F;
-    __builtin_amdgcn_wave_barrier();
-    const uint64_t mj = lane < m ? bs.wmass[lane] : 0;
-    bs.wpre[lane] = wave_scan_u64(mj) - mj;
-    __builtin_amdgcn_wave_barrier();
-    const bool kept = valid && bs.wpre[rank] < rem;
+    // the mass ranked before each member, summed over the members in registers
+    const uint64_t pre = mass_ranked_before(pk, F, m);
+    const bool kept = valid && pre < rem;
     const uint32_t kap = static_cast<uint32_t>(
         __builtin_amdgcn_readlane(static_cast<int>(wave_scan_max_u32(kept ? key : 0u)), 63));
     const uint64_t ties = __popcll(__ballot(kept && key == kap));
@@ -918,17 +925,8 @@ __device__ __forceinline__ int wave_cut_small(ScoreAt score, int n, float top_p,
     uint64_t rem = static_cast<uint64_t>(ceil(static_cast<double>(top_p) * static_cast<double>(E)));
     if (rem == 0) rem = 1;
     const uint64_t pk = valid ? ((static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(lane)) : ~0ull;
-    bs.wpk[lane] = pk;
-    __builtin_amdgcn_wave_barrier();
-    int rank = 0;
-#pragma unroll 4
-    for (int j = 0; j < n; ++j) rank += bs.wpk[j] < pk;
-    if (valid) bs.wmass[rank] = F;
-    __builtin_amdgcn_wave_barrier();
-    const uint64_t mj = lane < n ? bs.wmass[lane] : 0;
-    bs.wpre[lane] = wave_scan_u64(mj) - mj;
-    __builtin_amdgcn_wave_barrier();
-    const bool kept = valid && (take_all || bs.wpre[rank] < rem);
+    const uint64_t pre = mass_ranked_before(pk, F, n);
+    const bool kept = valid && (take_all || pre < rem);
     const unsigned long long bal = __ballot(kept);
     if (kept) emit(static_cast<int64_t>(__popcll(bal & ((1ull << lane) - 1ull))), static_cast<int64_t>(lane));
     return __popcll(bal);
@@ -1220,9 +1218,6 @@ constexpr int kWaveBmWords = kWaveStage / 32 + 1;          // the level's kept b
 struct WaveScratch {
     static constexpr bool staged = true;
     static constexpr int bm_words = kWaveBmWords;
-    uint64_t wpk[kWave];       // wave_resolve / wave_cut_small ranking
-    uint64_t wmass[kWave];
-    uint64_t wpre[kWave];
     uint64_t bcast_u64[2];
     uint32_t bcast_u32[2];
     uint64_t bins[kWaveBins];  // mass per bin, then per radix digit
@@ -1282,9 +1277,6 @@ constexpr int kPassU = 8;
 struct WaveScratchU {           // the unstaged variant's scratch
     static constexpr bool staged = false;
     static constexpr int bm_words = 576;     // levels of up to 18432 nodes keep the bitmap in LDS
-    uint64_t wpk[kWave];
-    uint64_t wmass[kWave];
-    uint64_t wpre[kWave];
     uint64_t bcast_u64[2];
     uint32_t bcast_u32[2];
     uint64_t bins[kWaveBins];
