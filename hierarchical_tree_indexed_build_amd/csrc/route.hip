@@ -308,7 +308,12 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
         };
         if (split) {
             cand_base(gpar0, cbp0);
-            if (PPM > 1) cand_base(np > 1 ? gpar1 : gpar0, cbp1);
+            if (PPM > 1 && pp > 1) {
+                cand_base(np > 1 ? gpar1 : gpar0, cbp1);
+            } else {
+#pragma unroll
+                for (int h = 0; h < G; ++h) cbp1[h] = cbp0[h];
+            }
         }
         for (int64_t cb = 0;;) {
             // a node's score: q . summary * scale, or the largest of its R tangents
