@@ -8,12 +8,14 @@
 // nodes are built, each exactly once; appends complete nodes in the same
 // device function, so append-built and build-built summaries are bit-identical.
 //
-// Mapping: one wave64 per node. Pass 1 gives each child row 64/b lanes, each
-// holding d*b/64 contiguous elements (for b > 64, b/64 rows per lane), for
-// the b dot products with r; pass 2
-// gives each lane d/64 dimensions and walks the b rows (re-read from L1/L2) to
-// form the weighted sum, so the node is read from HBM once and every store is a
-// coalesced 4*d-byte row.
+// Mapping: one wave64 per node. Up to 64 bf16 children (level 1, the bulk of
+// the bytes): each 16-byte load instruction reads whole child rows (a row
+// spread over d/8 lanes) and the node stays in registers for the dot products
+// with r and the weighted sum. fp32 children (levels above): pass 1 gives each
+// child row 64/b lanes for the dot products and pass 2 walks the rows again
+// (re-read from L1/L2) with d/64 dimensions a lane. More children (b = 128,
+// 256): each lane owns b/64 rows, and pass 2 walks them again. The node is
+// read from HBM once and every store is a coalesced 4*d-byte row.
 #include "zha_device.h"
 #include "zha_internal.h"
 
@@ -91,6 +93,90 @@ __device__ __forceinline__ void reduce_node_wide(const CT* __restrict__ ch, cons
     }
 }
 
+// Up to 64 bf16 children (raw keys). Each load instruction covers whole child rows: a row is
+// read by LPW lanes, 16 bytes each (EPW elements), so one instruction reads
+// RPI = 64 / LPW complete rows, and lane (sub, col) holds column block col of
+// rows sub, sub + RPI, ... The node's rows stay in registers for both passes:
+// the dot products with r are summed over each row's LPW lanes, and the
+// weighted sum is formed per lane over its rows and then summed over the RPI
+// lanes that share a column block.
+template <typename CT, int B, int D, bool VAL = false>
+__device__ __forceinline__ void reduce_node_rows(const CT* __restrict__ ch, const float* __restrict__ r,
+                                                 float scale, float* __restrict__ out, int lane,
+                                                 const CT* __restrict__ vch = nullptr, float* __restrict__ vout = nullptr) {
+    constexpr int EPW = 16 / static_cast<int>(sizeof(CT));   // elements in one 16-byte piece
+    constexpr int LPW = D / EPW;                             // lanes per row
+    constexpr int RPI = kWave / LPW;                         // rows per load instruction
+    constexpr int NI = (B + RPI - 1) / RPI;                  // rows per lane
+    static_assert(LPW >= 1 && LPW <= kWave && kWave % LPW == 0, "a row spans a power-of-two lane group");
+    const int col = lane % LPW, sub = lane / LPW;
+
+    // the pieces as loaded (16 bytes a row), widened where they are used
+    uint4 x[NI], y[VAL ? NI : 1];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int row = i * RPI + sub;
+        const int rw = row < B ? row : B - 1;                // a present row; its weight is 0
+        x[i] = *reinterpret_cast<const uint4*>(ch + rw * D + col * EPW);
+        if constexpr (VAL) y[i] = *reinterpret_cast<const uint4*>(vch + rw * D + col * EPW);
+    }
+    auto elem = [](const uint4& q, int e) -> float {
+        const uint32_t w = e / (EPW / 4) == 0 ? q.x : e / (EPW / 4) == 1 ? q.y : e / (EPW / 4) == 2 ? q.z : q.w;
+        if constexpr (sizeof(CT) == 2) return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+        else return __uint_as_float(w);
+    };
+    float rr[EPW];
+    load_n<EPW>(r + col * EPW, rr);
+    float z[NI], mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPW; ++e) t = fmaf(rr[e], elem(x[i], e), t);
+        z[i] = fast_group_sum<LPW>(t) * scale;
+        if (i * RPI + sub < B) mloc = fmaxf(mloc, z[i]);
+    }
+    // pass 2 widens the pieces again rather than keeping pass 1's floats live
+#pragma unroll
+    for (int i = 0; i < NI; ++i) __asm__ volatile("" : "+v"(x[i].x), "+v"(x[i].y), "+v"(x[i].z), "+v"(x[i].w));
+    const float m = strided_max<LPW>(mloc);
+    float w[NI], sloc = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        w[i] = (i * RPI + sub < B) ? expf(z[i] - m) : 0.f;
+        sloc += w[i];
+    }
+    const float tot = strided_sum<LPW>(sloc);
+    float acc[EPW], vacc[EPW];
+#pragma unroll
+    for (int e = 0; e < EPW; ++e) acc[e] = vacc[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int e = 0; e < EPW; ++e) {
+            acc[e] = fmaf(w[i], elem(x[i], e), acc[e]);
+            if constexpr (VAL) vacc[e] = fmaf(w[i], elem(y[i], e), vacc[e]);
+        }
+#pragma unroll
+    for (int e = 0; e < EPW; ++e) {
+        acc[e] = strided_sum<LPW>(acc[e]);
+        if constexpr (VAL) vacc[e] = strided_sum<LPW>(vacc[e]);
+    }
+    if (sub == 0) {
+#pragma unroll
+        for (int e = 0; e < EPW; ++e) {
+            out[col * EPW + e] = acc[e] / tot;
+            if constexpr (VAL) vout[col * EPW + e] = vacc[e] / tot;
+        }
+    }
+}
+
+// Up to 64 fp32 children (summaries of the level below): pass 1 gives each
+// child row 64/b lanes, each holding d*b/64 contiguous elements, for the b
+// dot products with r; pass 2 gives each lane d/64 dimensions and walks the b
+// rows (re-read from L1/L2) to form the weighted sum. It holds fewer registers
+// than the row layout with 512-byte rows, which matters in the 1024-thread
+// append kernel.
 template <typename CT, int B, int D, bool VAL = false>
 __device__ __forceinline__ void reduce_node_narrow(const CT* __restrict__ ch, const float* __restrict__ r,
                                                    float scale, float* __restrict__ out, int lane,
@@ -142,6 +228,7 @@ __device__ __forceinline__ void reduce_node_wave(const CT* __restrict__ ch, cons
                                                  float scale, float* __restrict__ out, int lane,
                                                  const CT* __restrict__ vch = nullptr, float* __restrict__ vout = nullptr) {
     if constexpr (B > kWave) reduce_node_wide<CT, B, D, VAL>(ch, r, scale, out, lane, vch, vout);
+    else if constexpr (sizeof(CT) == 2) reduce_node_rows<CT, B, D, VAL>(ch, r, scale, out, lane, vch, vout);
     else reduce_node_narrow<CT, B, D, VAL>(ch, r, scale, out, lane, vch, vout);
 }
 
@@ -429,7 +516,7 @@ struct FusedParams {
 };
 
 template <typename KT, int B, int D, int MODE>
-__global__ __launch_bounds__(1024) void append_fused_kernel(FusedParams p) {
+__global__ __launch_bounds__(512) void append_fused_kernel(FusedParams p) {
     constexpr bool TAN = MODE == kBuildTangent, VAL = MODE == kBuildValues;
     const int s = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
@@ -598,7 +685,7 @@ hipError_t launch_advance_seq(const Geo& g, int32_t* seq_lens, int t_new, hipStr
 
 template <typename KT, int B, int D>
 static hipError_t launch_fused_t(const FusedParams& fp, int B_, int Hkv, hipStream_t st) {
-    const int waves = std::min(Hkv, 16);
+    const int waves = std::min(Hkv, 8);             // more kv heads: a wave takes several in turn
     ProfScope ps("append_fused", 0, st);
     const dim3 grid(B_), block(waves * kWave);
     if (fp.tangent) hipLaunchKernelGGL((append_fused_kernel<KT, B, D, kBuildTangent>), grid, block, 0, st, fp);
