@@ -629,13 +629,42 @@ struct CutBoundary {
 // entry(e, key, F) accepts: returns the key at which the mass of the smaller
 // keys, plus its own, first reaches rem, and lowers rem by the mass of the
 // smaller keys. hist[0] must be zero and published before the call. Rounds
-// alternate between two histograms, so a round needs two barriers.
-template <class Entry>
+// alternate between two histograms, so a round needs two barriers. The
+// entries' keys usually share their top digits (they come from one narrow
+// score bin): a first pass finds their smallest and largest key, and the
+// rounds start at the digit where those differ (a digit all entries share
+// would hold all the mass and nothing before it).
+template <int NW, class Entry>
 __device__ __forceinline__ uint32_t radix_kappa(Entry entry, int64_t cnt, uint64_t& rem, BlockScratch& bs) {
     const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t prefix = 0;
+    uint32_t kmin_n = 0u, kmax = 0u;           // largest ~key and largest key of the entries with mass
+    for (int64_t e = tid; e < cnt; e += nt) {
+        uint32_t key;
+        uint64_t F;
+        if (!entry(e, key, F) || F == 0) continue;
+        kmin_n = max(kmin_n, ~key);
+        kmax = max(kmax, key);
+    }
+    kmin_n = wave_scan_max_u32(kmin_n);
+    kmax = wave_scan_max_u32(kmax);
+    if (lane == 63) {
+        bs.red_u32[wave] = kmax;
+        bs.red_u64[wave] = kmin_n;
+    }
+    __syncthreads();
+    uint32_t a = 0u, b = 0u;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        a = max(a, static_cast<uint32_t>(bs.red_u64[i]));
+        b = max(b, bs.red_u32[i]);
+    }
+    __syncthreads();
+    const uint32_t kmin = ~a;
+    const int common = (kmin == b) ? 32 : __clz(static_cast<int>(kmin ^ b));
+    int known = (common / 8) * 8;
+    uint32_t prefix = kmin & top_bits_mask(known);
     int cur = 0;
-    for (int known = 0; known < 32; known += 8) {
+    for (; known < 32; known += 8) {
         const int shift = 24 - known;
         const uint32_t hmask = top_bits_mask(known);
         uint64_t* hist = bs.hist[cur];
@@ -888,14 +917,14 @@ __device__ __forceinline__ CutBoundary cut_boundary(ScoreAt score, int64_t n, fl
     }
     uint32_t kap;
     if (m <= kCutList) {
-        kap = radix_kappa([&](int64_t e, uint32_t& key, uint64_t& F) {
+        kap = radix_kappa<NW>([&](int64_t e, uint32_t& key, uint64_t& F) {
             const float s = bs.list_s[e];
             key = desc_key(s);
             F = mass_fx(s, mx);
             return true;
         }, m, rem, bs);
     } else {
-        kap = radix_kappa([&](int64_t k, uint32_t& key, uint64_t& F) {
+        kap = radix_kappa<NW>([&](int64_t k, uint32_t& key, uint64_t& F) {
             const float s = score(k);
             if (cut_bin(s, mx) != bstar) return false;
             key = desc_key(s);
@@ -1820,14 +1849,14 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitPa
             need = bs.bcast_u64[1];
         } else {
             if (m <= kCutList) {
-                kappa = radix_kappa([&](int64_t e, uint32_t& key, uint64_t& F) {
+                kappa = radix_kappa<kSplitWaves>([&](int64_t e, uint32_t& key, uint64_t& F) {
                     const float s = bs.list_s[e];
                     key = desc_key(s);
                     F = mass_fx(s, mx);
                     return true;
                 }, m, rem, bs);
             } else {
-                kappa = radix_kappa([&](int64_t e, uint32_t& key, uint64_t& F) {
+                kappa = radix_kappa<kSplitWaves>([&](int64_t e, uint32_t& key, uint64_t& F) {
                     uint32_t k;
                     float s;
                     member(static_cast<uint32_t>(e), k, s);
