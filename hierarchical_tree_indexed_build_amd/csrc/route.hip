@@ -37,6 +37,7 @@
 // the kept ids in ascending order and the head's kept bitmap. The small upper
 // levels use a radix select over all their candidates.
 #include <algorithm>
+#include <type_traits>
 
 #include "zha_device.h"
 #include "zha_internal.h"
@@ -1238,8 +1239,10 @@ __global__ __launch_bounds__(NW * kWave) void route_cut_kernel(CutParams p) {
 //     ceil(top_p * total); its members, if at most 64, are ranked exactly by
 //     wave_resolve, else an MSB-first radix select over their keys pins the
 //     boundary key and the ties it needs;
-//  3. a stable ballot compaction writes the kept ids in ascending order and
-//     the kept bitmap.
+//  3. the kept ids in ascending order and the kept bitmap: when the pass that
+//     gathers the boundary bin's members also lists every candidate of the
+//     earlier bins (at most kWaveSure), from those two lists; otherwise a
+//     stable ballot compaction over all candidates.
 // The kept set is the one cut_boundary and cut_compact produce.
 // ----------------------------------------------------------------------------
 constexpr int kWaveCutThreads = 256;
@@ -1248,6 +1251,7 @@ constexpr int kWaveBins = 256;
 constexpr float kWaveBinScale = 256.0f / 28.0f;
 constexpr int kWaveStage = 2048;        // candidate scores staged per wave: levels of up to 2048 nodes
 constexpr int kWaveBmWords = kWaveStage / 32 + 1;          // the level's kept bitmap, in LDS
+constexpr int kWaveSure = 128;          // candidates above the boundary bin listed in LDS (more: a compaction pass)
 
 struct WaveScratch {
     static constexpr bool staged = true;
@@ -1257,6 +1261,8 @@ struct WaveScratch {
     uint64_t bins[kWaveBins];  // mass per bin, then per radix digit
     uint32_t list[kWave];      // members of the boundary bin
     float list_s[kWave];
+    uint32_t sure[kWaveSure];  // candidates in earlier bins (all kept), in candidate order
+    uint32_t kmem[kWave];      // the kept members, in candidate order
     uint32_t bm[kWaveBmWords];
     float sc[kWaveStage];      // the candidates' scores, in candidate order
 };
@@ -1316,8 +1322,21 @@ struct WaveScratchU {           // the unstaged variant's scratch
     uint64_t bins[kWaveBins];
     uint32_t list[kWave];
     float list_s[kWave];
+    uint32_t sure[kWaveSure];
+    uint32_t kmem[kWave];
     uint32_t bm[bm_words];
 };
+
+// Entries of the ascending list a[0..cnt) below x (a binary search).
+__device__ __forceinline__ int count_below(const uint32_t* a, int cnt, uint32_t x) {
+    int lo = 0, hi = cnt;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] < x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
 
 template <class WS>
 __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutParams p) {
@@ -1345,6 +1364,21 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
     cc.ncand = cc.nkids + (nc - (cc.nc_up << p.lb));
     const int n = static_cast<int>(cc.ncand);        // staged: <= nodes of the level <= kWaveStage
     const bool leaf = (p.li == 0);
+    // Candidate k's node id without a branch: every lane loads a kept parent's
+    // id (its index clamped into the list), so the loads of a whole group of
+    // blocks go out together; lanes past the children take the uncovered tail.
+    // With no kept parents (the top level) the pair's count slot stands in as
+    // a valid address whose value is never used.
+    const int lbw = p.lb;
+    const int32_t lmask = (1 << lbw) - 1;
+    const int32_t nkids32 = static_cast<int32_t>(cc.nkids);
+    const int32_t tail0 = static_cast<int32_t>(cc.nc_up << lbw) - nkids32;
+    const int32_t* upp = kc > 0 ? cc.up : p.kept_cnt + rh * p.L;
+    const int32_t plast = kc > 0 ? static_cast<int32_t>(kc) - 1 : 0;
+    auto node_of = [&](int k) -> int32_t {
+        const int32_t par = upp[min(k >> lbw, plast)];
+        return k < nkids32 ? ((par << lbw) | (k & lmask)) : k + tail0;
+    };
 
     int32_t* kept_out = leaf ? nullptr : p.kept + rh * p.nodes_total + p.lvl_off;
     int32_t* sel_out = leaf ? p.sel_blocks + rh * p.sel_cap : nullptr;
@@ -1359,14 +1393,12 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
         __threadfence_block();
     }
     __builtin_amdgcn_wave_barrier();
-    auto emit = [&](int64_t pos, int64_t k) {
-        const int32_t node = static_cast<int32_t>(cc.node(k));
+    auto emit_node = [&](int64_t pos, int32_t node) {
         if (kept_out) kept_out[pos] = node;
         if (sel_out && pos < p.sel_cap) sel_out[pos] = node;
         if (lsel_out) lsel_out[pos] = node;
     };
-    auto mark = [&](int64_t k, uint32_t bits) {
-        const int64_t node = cc.node(k);
+    auto mark_node = [&](int32_t node, uint32_t bits) {
         if (lds_bm) atomicOr(&ws.bm[node >> 5], bits << (node & 31));
         else __hip_atomic_fetch_or(bm + (node >> 5), bits << (node & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
     };
@@ -1374,43 +1406,69 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
     int64_t m;
     if (n <= kWave) {
         m = wave_cut_small([&](int64_t k) -> float { return cc.sc[cc.node(k)]; }, n, p.top_p, ws,
-                           [&](int64_t pos, int64_t k) { emit(pos, k); mark(k, 1u); });
+                           [&](int64_t pos, int64_t k) {
+                               const int32_t node = static_cast<int32_t>(cc.node(k));
+                               emit_node(pos, node);
+                               mark_node(node, 1u);
+                           });
     } else {
         const int nblk = (n + kWave - 1) / kWave;
-        // blocks r0 .. r0 + kPassU - 1 of the candidates (block r holds k = 64 r + lane)
-        auto fetch_global = [&](int r0, float (&v)[kPassU]) {
-            int64_t nd[kPassU];
+        // blocks r0 .. r0 + kPassU - 1 of the candidates (block r holds k = 64 r + lane);
+        // lanes past the candidates get node 0 (a valid address) and are masked by the caller
+        auto fetch_nodes = [&](int r0, int32_t (&nd)[kPassU]) {
+            int32_t par[kPassU];
 #pragma unroll
             for (int u = 0; u < kPassU; ++u) {
                 const int k = lane + (r0 + u) * kWave;
-                nd[u] = k < n ? cc.node(k) : -1;
+                par[u] = upp[min(k >> lbw, plast)];
             }
+            // taken as used here, so no load is sunk into a branch of the select below
 #pragma unroll
-            for (int u = 0; u < kPassU; ++u) v[u] = nd[u] >= 0 ? cc.sc[nd[u]] : 0.f;
+            for (int u = 0; u < kPassU; ++u) asm volatile("" : "+v"(par[u]));
+#pragma unroll
+            for (int u = 0; u < kPassU; ++u) {
+                const int k = lane + (r0 + u) * kWave;
+                const int32_t node = k < nkids32 ? ((par[u] << lbw) | (k & lmask)) : k + tail0;
+                nd[u] = k < n ? node : 0;
+            }
         };
-        auto pass = [&](auto&& body) {             // body(r, score): whole waves, blocks in order
+        auto fetch_global = [&](int r0, float (&v)[kPassU], int32_t (&nd)[kPassU]) {
+            fetch_nodes(r0, nd);
+#pragma unroll
+            for (int u = 0; u < kPassU; ++u) v[u] = cc.sc[nd[u]];
+        };
+        // body(r, score, node): whole waves, blocks in order; WithNodes: the
+        // staged variant also looks up the node ids (the unstaged one has them)
+        auto pass_impl = [&](auto with_nodes, auto&& body) {
             for (int r0 = 0; r0 < nblk; r0 += kPassU) {
                 float v[kPassU];
+                int32_t nd[kPassU];
                 if constexpr (kStaged) {
+                    if constexpr (decltype(with_nodes)::value) fetch_nodes(r0, nd);
 #pragma unroll
                     for (int u = 0; u < kPassU; ++u) {
                         const int k = lane + (r0 + u) * kWave;
                         v[u] = k < n ? ws.sc[k] : 0.f;
                     }
                 } else {
-                    fetch_global(r0, v);
+                    fetch_global(r0, v, nd);
                 }
 #pragma unroll
                 for (int u = 0; u < kPassU; ++u)
-                    if (r0 + u < nblk) body(r0 + u, v[u]);
+                    if (r0 + u < nblk) body(r0 + u, v[u], nd[u]);
             }
         };
+        auto pass = [&](auto&& body) {
+            pass_impl(std::false_type{}, [&](int r, float sv, int32_t) { body(r, sv); });
+        };
+        auto pass_nodes = [&](auto&& body) { pass_impl(std::true_type{}, body); };
         // the maximum (staged: while the scores go to LDS)
         float mx = -INFINITY;
         if constexpr (kStaged) {
             for (int r0 = 0; r0 < nblk; r0 += kPassU) {
                 float v[kPassU];
-                fetch_global(r0, v);
+                int32_t nd[kPassU];
+                fetch_global(r0, v, nd);
 #pragma unroll
                 for (int u = 0; u < kPassU; ++u) {
                     const int k = lane + (r0 + u) * kWave;
@@ -1430,6 +1488,8 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
         const bool take_all = p.top_p >= 1.0f;
         uint32_t kappa = 0;
         uint64_t need = 0;
+        bool listed = false;             // the kept set is in the two LDS lists: no compaction pass
+        uint32_t lnm = 0, lns = 0;       // members of the boundary bin, candidates of earlier bins
         if (!take_all) {
             // 1. masses, in total and per bin
             for (int i = lane; i < kWaveBins; i += kWave) ws.bins[i] = 0;
@@ -1449,19 +1509,32 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
             uint64_t before;
             const int bstar = wave_find_digit(ws.bins, rem, &before);
             rem -= before;
-            uint32_t nm = 0;
+            // Members may include candidates of zero mass (only the last bins
+            // hold any): ranked after every member of nonzero mass above them,
+            // they leave the boundary key and its ties as they are, and one
+            // ranked before the boundary is kept, as the compaction keeps it.
+            // Candidates of earlier bins rank above every member: all kept.
+            uint32_t nm = 0, ns = 0;
             pass([&](int r, float sv) {
                 const int k = lane + r * kWave;
-                const bool mem = k < n && wave_bin(sv, mx) == bstar && mass_fx(sv, mx) != 0;
-                const unsigned long long bal = __ballot(mem);
+                const int bin = wave_bin(sv, mx);
+                const bool mem = k < n && bin == bstar;
+                const bool sure = k < n && bin < bstar;
+                const unsigned long long bal = __ballot(mem), bsu = __ballot(sure);
                 const uint32_t pos = nm + static_cast<uint32_t>(__popcll(bal & ((1ull << lane) - 1ull)));
+                const uint32_t spos = ns + static_cast<uint32_t>(__popcll(bsu & ((1ull << lane) - 1ull)));
                 if (mem && pos < kWave) {
                     ws.list[pos] = static_cast<uint32_t>(k);
                     ws.list_s[pos] = sv;
                 }
+                if (sure && spos < kWaveSure) ws.sure[spos] = static_cast<uint32_t>(k);
                 nm += static_cast<uint32_t>(__popcll(bal));
+                ns += static_cast<uint32_t>(__popcll(bsu));
             });
             __builtin_amdgcn_wave_barrier();
+            listed = nm <= kWave && ns <= kWaveSure;
+            lnm = nm;
+            lns = ns;
             if (nm <= kWave) {
                 wave_resolve(ws.list, ws.list_s, static_cast<int>(nm), mx, rem, ws);
                 __builtin_amdgcn_wave_barrier();
@@ -1495,31 +1568,61 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
                 need = Fk ? (rem + Fk - 1) / Fk : 0;
             }
         }
-        // 3. stable compaction, 64 candidates (one block) at a time
-        const int run_lg = p.lb < 5 ? p.lb : 5;
-        const int run = 1 << run_lg;
-        const unsigned long long run_mask = (1ull << run) - 1ull;
-        const unsigned long long below = (1ull << lane) - 1ull;
-        uint64_t lt_b = 0, tie_b = 0;
-        pass([&](int r, float sv) {
-            const int64_t k = lane + r * kWave;
-            const bool valid = k < n;
-            const uint32_t key = valid ? desc_key(sv) : 0u;
-            const bool lt = valid && (take_all || key < kappa);
-            const bool tie = valid && !take_all && key == kappa;
-            const unsigned long long blt = __ballot(lt), btie = __ballot(tie);
-            const uint64_t my_lt = lt_b + __popcll(blt & below), my_tie = tie_b + __popcll(btie & below);
-            const bool keep = lt || (tie && my_tie < need);
-            if (keep) emit(static_cast<int64_t>(my_lt + (lt ? (my_tie < need ? my_tie : need) : my_tie)), k);
+        if (listed) {
+            // 3'. the kept members (key below the boundary key, or among the
+            // first `need` ties in candidate order) merged with the list of the
+            // earlier bins: an entry's place is its rank in its own list plus
+            // the entries of the other list before it (candidate order is node
+            // order, so the ids come out ascending as the compaction writes them)
+            const unsigned long long below = (1ull << lane) - 1ull;
+            const bool valid = lane < static_cast<int>(lnm);
+            const uint32_t k = valid ? ws.list[lane] : 0u;
+            const uint32_t key = desc_key(valid ? ws.list_s[lane] : 0.f);
+            const unsigned long long btie = __ballot(valid && key == kappa);
+            const bool keep = valid && (key < kappa || (key == kappa && static_cast<uint64_t>(__popcll(btie & below)) < need));
             const unsigned long long bkeep = __ballot(keep);
-            if ((lane & (run - 1)) == 0) {
-                const uint32_t bits = static_cast<uint32_t>((bkeep >> lane) & run_mask);
-                if (bits) mark(k, bits);
+            const int km = __popcll(bkeep & below), nkm = __popcll(bkeep);
+            if (keep) ws.kmem[km] = k;
+            __builtin_amdgcn_wave_barrier();
+            if (keep) {
+                const int32_t node = node_of(static_cast<int>(k));
+                emit_node(km + count_below(ws.sure, static_cast<int>(lns), k), node);
+                mark_node(node, 1u);
             }
-            lt_b += __popcll(blt);
-            tie_b += __popcll(btie);
-        });
-        m = static_cast<int64_t>(lt_b + (tie_b < need ? tie_b : need));
+            for (int j = lane; j < static_cast<int>(lns); j += kWave) {
+                const uint32_t ks = ws.sure[j];
+                const int32_t node = node_of(static_cast<int>(ks));
+                emit_node(j + count_below(ws.kmem, nkm, ks), node);
+                mark_node(node, 1u);
+            }
+            m = static_cast<int64_t>(lns) + nkm;
+        } else {
+            // 3. stable compaction, 64 candidates (one block) at a time
+            const int run_lg = p.lb < 5 ? p.lb : 5;
+            const int run = 1 << run_lg;
+            const unsigned long long run_mask = (1ull << run) - 1ull;
+            const unsigned long long below = (1ull << lane) - 1ull;
+            uint64_t lt_b = 0, tie_b = 0;
+            pass_nodes([&](int r, float sv, int32_t node) {
+                const int64_t k = lane + r * kWave;
+                const bool valid = k < n;
+                const uint32_t key = valid ? desc_key(sv) : 0u;
+                const bool lt = valid && (take_all || key < kappa);
+                const bool tie = valid && !take_all && key == kappa;
+                const unsigned long long blt = __ballot(lt), btie = __ballot(tie);
+                const uint64_t my_lt = lt_b + __popcll(blt & below), my_tie = tie_b + __popcll(btie & below);
+                const bool keep = lt || (tie && my_tie < need);
+                if (keep) emit_node(static_cast<int64_t>(my_lt + (lt ? (my_tie < need ? my_tie : need) : my_tie)), node);
+                const unsigned long long bkeep = __ballot(keep);
+                if ((lane & (run - 1)) == 0) {
+                    const uint32_t bits = static_cast<uint32_t>((bkeep >> lane) & run_mask);
+                    if (bits) mark_node(node, bits);
+                }
+                lt_b += __popcll(blt);
+                tie_b += __popcll(btie);
+            });
+            m = static_cast<int64_t>(lt_b + (tie_b < need ? tie_b : need));
+        }
     }
     if (lds_bm) {
         __builtin_amdgcn_wave_barrier();

@@ -161,6 +161,69 @@ def test_many_rows_crowded_scores(kind, noise):
     say(f"  margin-exempt differences: {flips}")
 
 
+# exact ties at the cut boundary through the one-wave cut: every chunk of
+# the cache repeats one of 256 key patterns, so the nodes of a pattern score
+# identically and the index rule splits a boundary tie group. The cache of
+# 131072 tokens puts 8192 nodes at level 1 (the variant that re-reads
+# scores); peaked scores (amplitude 2) keep few leaves, so the kept set comes
+# from the boundary bin's members and the list of earlier bins, flat ones
+# (amplitude 0.5) keep hundreds and take the compaction over all candidates.
+TIES = [2.0, 0.5]
+
+
+@pytest.mark.parametrize("amp", TIES, ids=[f"amp{a:g}" for a in TIES])
+def test_many_rows_boundary_ties(amp):
+    t = torch()
+    w = W.get_workload("gqa128k", shrink=0, batch=1)
+    T, M = 64, 256
+    say(f"[many rows ties] amplitude {amp:g}, {M} chunk patterns: {w.n_tokens} tokens, {T} causal rows")
+    st = Staged(w, max_t=T, build=False)
+    rng = np.random.default_rng(20261205)
+    B, H, C, D = st.K_np.shape
+    pat = (amp * rng.standard_normal((H, M, D))).astype(np.float32)
+    chunk = np.arange(C) // w.branching
+    st.K_np = W.f32_to_bf16_bits(np.ascontiguousarray(pat[:, chunk % M][None]))
+    st.Kf = W.as_f32(w, st.K_np)
+    st.cache.K.copy_(kv_tensor(w, st.K_np))
+    Z.build_tree(st.geom, st.cache.K, st.ref_q, st.cache.seq_lens, st.cache.summaries, st.cache.ws)
+    qn, q = st.queries(0, rows=T)
+    q_pos = (w.n_tokens - T + t.arange(T, dtype=t.int32, device="cuda")).view(1, T).contiguous()
+    sel, nsel, stats, lsel = st.route_buffers(T)
+    Z.route(st.geom, q, q_pos, st.cache.summaries, st.cache.seq_lens, w.top_p, sel, nsel, st.cache.ws,
+            level_stats=stats, level_sel=lsel)
+    t.cuda.synchronize()
+    trees = st.oracle_trees()
+    kept = {level: level_kept(st, lsel, stats, T, level) for level in range(1, w.n_levels + 1)}
+    flips = split_ties = 0
+    leaf_kept = []
+    for t_ in _sample_rows(T, 16):
+        N = w.n_tokens - T + t_ + 1
+        for hq in range(w.n_q_heads):
+            kv = hq // w.group
+            parents = None
+            for level in range(w.n_levels, 0, -1):
+                v, cnt, cand = kept[level]
+                gpu_ids = v[t_, hq, :cnt[t_, hq]]
+                cut = O.route_level(qn[0, t_, hq], trees[0][kv][level - 1], level, parents, N, w.branching,
+                                    w.n_levels, w.top_p, w.scale)
+                assert cand[t_, hq] == len(cut.ids), (t_, hq, level, cand[t_, hq], len(cut.ids))
+                assert np.all(np.diff(gpu_ids) > 0), "kept ids must be ascending"
+                flips += check_sets(gpu_ids, cut, w.top_p, f"row {t_} head {hq} level {level}")
+                last = cut.scores64[cut.order[cut.m - 1]]
+                split_ties += int(np.sum(cut.scores64 == last) > np.sum(cut.scores64[cut.order[:cut.m]] == last))
+                if level == 1:
+                    leaf_kept.append(len(gpu_ids))
+                parents = gpu_ids
+    leaf_kept = np.array(leaf_kept)
+    say(f"  margin-exempt differences: {flips}; cuts splitting a tie group: {split_ties}; "
+        f"leaves kept min/median/max {leaf_kept.min()}/{int(np.median(leaf_kept))}/{leaf_kept.max()}")
+    assert split_ties > 0, "no cut split a tie group"
+    if amp > 1:
+        assert np.median(leaf_kept) <= 128, "peaked scores should keep few leaves"
+    else:
+        assert np.median(leaf_kept) > 128, "flat scores should keep many leaves"
+
+
 def test_many_rows_deep_levels():
     """b = 2 puts levels of 32768 and 16384 nodes under 64 causal rows: the
     one-wave cut re-reads their scores from global memory, and the larger
