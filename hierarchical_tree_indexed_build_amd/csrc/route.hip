@@ -1415,13 +1415,15 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
         const int nblk = (n + kWave - 1) / kWave;
         // blocks r0 .. r0 + kPassU - 1 of the candidates (block r holds k = 64 r + lane);
         // lanes past the candidates get node 0 (a valid address) and are masked by the caller
-        auto fetch_nodes = [&](int r0, int32_t (&nd)[kPassU]) {
-            int32_t par[kPassU];
+        // (the parent index is clamped, so the loads of blocks past the end are valid too)
+        auto load_parents = [&](int r0, int32_t (&par)[kPassU]) {
 #pragma unroll
             for (int u = 0; u < kPassU; ++u) {
                 const int k = lane + (r0 + u) * kWave;
                 par[u] = upp[min(k >> lbw, plast)];
             }
+        };
+        auto nodes_from = [&](int r0, int32_t (&par)[kPassU], int32_t (&nd)[kPassU]) {
             // taken as used here, so no load is sunk into a branch of the select below
 #pragma unroll
             for (int u = 0; u < kPassU; ++u) asm volatile("" : "+v"(par[u]));
@@ -1432,14 +1434,23 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
                 nd[u] = k < n ? node : 0;
             }
         };
+        auto fetch_nodes = [&](int r0, int32_t (&nd)[kPassU]) {
+            int32_t par[kPassU];
+            load_parents(r0, par);
+            nodes_from(r0, par, nd);
+        };
         auto fetch_global = [&](int r0, float (&v)[kPassU], int32_t (&nd)[kPassU]) {
             fetch_nodes(r0, nd);
 #pragma unroll
             for (int u = 0; u < kPassU; ++u) v[u] = cc.sc[nd[u]];
         };
         // body(r, score, node): whole waves, blocks in order; WithNodes: the
-        // staged variant also looks up the node ids (the unstaged one has them)
+        // staged variant also looks up the node ids (the unstaged one has them).
+        // Unstaged, the next group's parent ids are loaded while this group's
+        // scores are in flight, so a group waits for one round trip, not two.
         auto pass_impl = [&](auto with_nodes, auto&& body) {
+            int32_t par[kPassU];
+            if constexpr (!kStaged) load_parents(0, par);
             for (int r0 = 0; r0 < nblk; r0 += kPassU) {
                 float v[kPassU];
                 int32_t nd[kPassU];
@@ -1451,11 +1462,14 @@ __global__ __launch_bounds__(kWaveCutThreads) void route_wave_cut_kernel(CutPara
                         v[u] = k < n ? ws.sc[k] : 0.f;
                     }
                 } else {
-                    fetch_global(r0, v, nd);
+                    nodes_from(r0, par, nd);
+#pragma unroll
+                    for (int u = 0; u < kPassU; ++u) v[u] = cc.sc[nd[u]];
+                    load_parents(r0 + kPassU, par);
                 }
 #pragma unroll
-                for (int u = 0; u < kPassU; ++u)
-                    if (r0 + u < nblk) body(r0 + u, v[u], nd[u]);
+                for (int u = 0; u < kPassU; ++u)     // block r0 always exists: its load stays out of a branch
+                    if (u == 0 || r0 + u < nblk) body(r0 + u, v[u], nd[u]);
             }
         };
         auto pass = [&](auto&& body) {
