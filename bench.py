@@ -273,7 +273,7 @@ def cpu_parity(w, outs, gpu):
         if len(g_ids) == len(ids) and np.array_equal(np.sort(g_ids), ids):
             equal += 1
             worst = max(worst, float(np.abs(out[s, 0, hq] - o).max()), abs(float(l[s, 0, hq]) - lse))
-    tol = 2e-3 if w.kv_dtype == "bf16" else 1e-5
+    tol = 2e-4 if w.kv_dtype == "bf16" else 1e-5
     return {"heads": n, "index_sets_equal": equal, "max_abs_err_on_equal_sets": round(worst, 7), "tol": tol,
             "ok": bool(n and worst <= tol)}
 
@@ -705,8 +705,9 @@ def main():
         "vs_baseline": None,
         "dtype": w.kv_dtype,
         "precision": {"kv_cache": w.kv_dtype, "summaries_scores_softmax": "f32",
-                      "attention_logits": ("q split into bf16 hi + lo parts on the matrix cores (about 2^-16 "
-                                           "relative), f32 accumulation") if w.kv_dtype == "bf16" else "f32"},
+                      "attention_logits": ("f32 dot products of the bf16 keys with q, which goes to the matrix "
+                                           "cores as three bf16 parts summing to it within about 2^-25, "
+                                           "f32 accumulation") if w.kv_dtype == "bf16" else "f32"},
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_tokens": w.n_tokens, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "branching": w.branching,

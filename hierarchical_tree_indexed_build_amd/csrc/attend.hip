@@ -646,8 +646,11 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
 //   S^T[token][head] = sum_d K[token][d] * q[head][d],
 // A = the group's K rows (lane l: token l % 16, dims [(l/16) D/4, +D/4), read
 // straight from HBM as bf16), B = q (lane l: head l % 16, same dims; heads
-// >= g are zero). q is split into bf16 hi + lo parts, so q . k is exact to
-// about 2^-16 of |q| |k| (two MFMAs per slice). The result holds token
+// >= g are zero). The scaled q is split into three bf16 parts, hi + mid + lo,
+// that sum to it exactly but for the last part's rounding (about 2^-25 of
+// |q|): every product of a bf16 key with a bf16 part is exact in fp32 and the
+// MFMA accumulates in fp32, so q . k is an fp32 dot product of the bf16 key
+// and the fp32 query (three MFMAs per slice). The result holds token
 // 4 (l/16) + r, head l % 16 in lane l, register r: the online softmax runs in
 // that layout, and the probabilities go through LDS to the value pass, which
 // stays on the VALU (lanes own 4 tokens x D/LPT dims as in attend_kernel).
@@ -691,8 +694,8 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
         const int N = visible_clamped(p.ri, row, p.cap);
 
         // q of head mrow (zero beyond g): its load is issued here, its split into
-        // scaled bf16 hi + lo parts waits until the first K/V rows are in flight
-        bf16x8_t qh[NS], ql[NS];
+        // scaled bf16 hi + mid + lo parts waits until the first K/V rows are in flight
+        bf16x8_t qh[NS], qm[NS], ql[NS];
         float qf[D / 4];
         if (mrow < G) {
             load_vec<D / 4>(p.q + (static_cast<int64_t>(row) * p.Hq + kv * G + mrow) * D + mblk * (D / 4), qf);
@@ -705,11 +708,15 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
             for (int sl = 0; sl < NS; ++sl)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
+                    // x - hi and x - hi - mid are exact in fp32; hi + mid + lo
+                    // equals x up to lo's rounding
                     const float x = qf[sl * 8 + j] * p.qscale;
                     const uint32_t hb = bf16_bits_rn(x);
-                    const float hi = __uint_as_float(hb << 16);
-                    const uint32_t lb = bf16_bits_rn(x - hi);
+                    const float r1 = x - __uint_as_float(hb << 16);
+                    const uint32_t mb = bf16_bits_rn(r1);
+                    const uint32_t lb = bf16_bits_rn(r1 - __uint_as_float(mb << 16));
                     qh[sl][j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hb));
+                    qm[sl][j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(mb));
                     ql[sl][j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lb));
                 }
         };
@@ -763,6 +770,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
                     a[2 * j + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w >> 16));
                 }
                 sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[sl], sc, 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qm[sl], sc, 0, 0, 0);
                 sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[sl], sc, 0, 0, 0);
             }
             // online softmax of head mrow over tokens 4 * mblk + r

@@ -136,7 +136,12 @@ def check_sets(gpu_ids, cut, p, where=""):
 
 
 def attn_tol(w):
-    return 1e-5 if w.kv_dtype == "fp32" else 2e-3
+    # bf16 caches: the logits are fp32 dot products of the bf16 keys with q (q
+    # goes to the matrix cores as three bf16 parts that sum to it to about
+    # 2^-25), so what is left is fp32 rounding in the logits, the softmax and
+    # the accumulation; worst seen 1.7e-5. The bar is ten times that, tighter
+    # than the 2e-3 the method's tolerance allows for bf16 KV.
+    return 1e-5 if w.kv_dtype == "fp32" else 2e-4
 
 
 def teacher_forced(st, qn, qpos_np, stats, lsel, p, trees, pairs=None):

@@ -19,7 +19,7 @@ timed step's calls).
 
 Bars as in test_gpu_parity: summaries within the fp32 accumulation bound, kept
 sets equal up to the 1e-5 margin exemptions with exact candidate counts,
-attention within 2e-3 max-abs (bf16 KV).
+attention within 2e-4 max-abs (bf16 KV).
 """
 import math
 

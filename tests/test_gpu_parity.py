@@ -9,7 +9,7 @@ Bars (fixed by the method's precision statement):
 * kept sets per level, teacher-forced on the GPU's own kept parents: equal up to
   candidates whose cumulative-mass margin at the cut is below 1e-5;
 * candidate counts per level: exact;
-* attention on the GPU's own index set: 1e-5 max-abs for fp32 caches, 2e-3 for bf16;
+* attention on the GPU's own index set: 1e-5 max-abs for fp32 caches, 2e-4 for bf16;
 * append-built and build-built summaries: bit-identical.
 """
 import math

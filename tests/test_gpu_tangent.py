@@ -12,7 +12,7 @@ oracle's tangent tree.
   nodes must stay rare;
 * routing, teacher-forced: candidate counts exact, kept sets equal up to the
   1e-5 margin exemptions (and the skipped nodes);
-* attention over the GPU's own index set within 2e-3 (bf16) / 1e-5 (fp32);
+* attention over the GPU's own index set within 2e-4 (bf16) / 1e-5 (fp32);
 * appends: the fused single-token path and the multi-token path give the bits
   of a fresh build over the same cache.
 """

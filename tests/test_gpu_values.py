@@ -7,7 +7,7 @@ contribute coarse attention outputs) against the CPU oracle.
 * zha_attend: out and lse match the oracle's softmax over the exact tokens of
   the GPU's own index set and one pseudo-token per pruned candidate of every
   level, the candidates and kept sets taken from the GPU's route
-  (teacher-forced), the logits from the oracle's scores; within 2e-3 (bf16
+  (teacher-forced), the logits from the oracle's scores; within 2e-4 (bf16
   KV) and 1e-5 (fp32 KV);
 * on keys and values repeated over every top-level span, every pruned subtree
   is uniform and the output equals the dense kernel's;
