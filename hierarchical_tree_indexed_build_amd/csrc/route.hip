@@ -16,7 +16,10 @@
 // and only the next kernel reads them.
 //  * route_upper_kernel - one workgroup per (row, query head) walks the small
 //    upper levels in one launch: candidates, scores and the cut stay in LDS
-//    from level to level.
+//    from level to level. When the levels above the lowest fused one hold at
+//    most 64 nodes each, every node of the fused levels is scored up front:
+//    wave 0 scores and cuts the small levels while the other waves score the
+//    lowest one, so its scoring no longer waits for the cuts above it.
 //  * per remaining level (the leaf level always):
 //    - route_score_kernel - a workgroup owns up to 64 interleaved parent slots of one
 //      (row, kv head). It ORs the group's kept bitmaps of level l+1 over its
@@ -2107,9 +2110,14 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitPa
 // flight per wave), and the same
 // exact cut runs on the LDS-resident scores. The kept set stays in LDS for the
 // next level and is written out (kept list, count, bitmap) for the levels
-// below li_lo.
+// below li_lo. With small levels above li_lo (at most 64 nodes each) and at
+// most kUpperPre nodes in all, the scores of every complete node of the fused
+// levels are computed first instead (see "scoring up front" below), the
+// levels above li_lo are cut by wave 0 alone meanwhile, and level li_lo's
+// candidates then take their scores from LDS.
 // ----------------------------------------------------------------------------
 constexpr int kUpperNodes = 8192;
+constexpr int kUpperPre = 4096;        // fused levels' nodes scored up front
 constexpr int kUpperThreads = 512;     // 8 waves: rows in flight for the scoring, cheap barriers for the cut
 constexpr int kUpperWaves = kUpperThreads / kWave;
 
@@ -2145,8 +2153,16 @@ struct UpperShared {
     int32_t par[kUpperNodes];          // kept nodes of the level above, ascending
     uint32_t bm[kUpperNodes / 32 + 1];
     uint64_t bins[kCutBins];           // mass bins of the boundary search
+    float nsc[kUpperPre];              // scores of every complete node of the fused levels, top level first
+    int64_t npar;                      // kept nodes of the level above the lowest fused one (wave 0's cuts)
     BlockScratch bs;
 };
+
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) v |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave));
+    return v;
+}
 
 template <int D, bool TAN>
 __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams p) {
@@ -2164,10 +2180,147 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
     const int64_t rh = static_cast<int64_t>(row) * p.Hq + hq;
     float qv[DPL];
     load_row_il<DPL, LPR>(p.q + rh * D + part * 4, qv);
+    const int RT = TAN ? p.R : 1;                  // tangent rows per node
+    const int64_t pair_sk = static_cast<int64_t>(s) * p.Hkv + kv;
+
+    // ---- scoring up front ----
+    // When every level above the lowest fused one has at most a wave's worth
+    // of nodes and all fused levels together fit kUpperPre, every complete
+    // node of those levels is scored at once (level l's node n at
+    // sh.nsc[off(l) + n], levels top first): wave 0 scores the small levels and
+    // runs their one-wave cuts while the other waves score the lowest level,
+    // whose cut then only picks its candidates' scores. A level of one node
+    // is never scored (its lone candidate is kept unscored). Scores are
+    // computed exactly as below, so the cuts are the same.
+    int64_t hi_tot = 0;                        // nsc slots of the levels above li_lo
+    bool pre = p.li_lo + 1 < p.L;
+    for (int l = p.L - 1; l > p.li_lo; --l) {
+        const int64_t n_l = static_cast<int64_t>(N) >> (p.lb * (l + 1));
+        pre = pre && n_l <= kWave;
+        hi_tot += n_l;
+    }
+    const int64_t n_lo = static_cast<int64_t>(N) >> (p.lb * (p.li_lo + 1));
+    pre = pre && hi_tot + n_lo <= kUpperPre;
+    // scores of nodes [0, n) of level l into sh.nsc[at + node], by wave wi of nw2
+    auto score_level = [&](int l, int64_t at, int64_t n, int wi, int nw2) {
+        const int64_t nb = pair_sk * p.nodes[l];
+        const float* summ = p.summaries + p.sum_off[l] + nb * RT * D;
+        const float* offs = TAN ? p.summaries + p.bias_off[l] + nb * RT : nullptr;
+        for (int64_t kb = static_cast<int64_t>(wi) * RPP * UNR; kb < n; kb += static_cast<int64_t>(nw2) * RPP * UNR) {
+            float best[UNR];
+            for (int rr = 0; rr < RT; ++rr) {
+                float x[UNR][DPL], xo[UNR];
+#pragma unroll
+                for (int u = 0; u < UNR; ++u) {
+                    const int64_t row = imin(kb + u * RPP + sub, n - 1) * RT + rr;   // a present row
+                    load_row_il<DPL, LPR>(summ + row * D + part * 4, x[u]);
+                    if constexpr (TAN) xo[u] = offs[row];
+                }
+#pragma unroll
+                for (int u = 0; u < UNR; ++u) {
+                    float t = 0.f;
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) t = fmaf(qv[e], x[u][e], t);
+                    t = fast_group_sum<LPR>(t) * p.scale;
+                    if constexpr (TAN) best[u] = rr == 0 ? t + xo[u] : fmaxf(best[u], t + xo[u]);
+                    else best[u] = t;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int64_t k = kb + u * RPP + sub;
+                if (k < n && part == 0) sh.nsc[at + k] = best[u];
+            }
+        }
+    };
 
     int64_t npar = 0;                          // kept nodes of the level above
     int32_t par0 = -1;                         // their one id when a lone candidate was kept (not in LDS)
-    for (int li = p.L - 1; li >= p.li_lo; --li) {
+    int li_first = p.L - 1;                    // the first level the block loop below takes
+    if (pre) {
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        if (wv == 0) {
+            {
+                int64_t at = 0;
+                for (int l = p.L - 1; l > p.li_lo; --l) {
+                    const int64_t n_l = static_cast<int64_t>(N) >> (p.lb * (l + 1));
+                    if (n_l > 1) score_level(l, at, n_l, 0, 1);
+                    at += n_l;
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            // the small levels' cuts, one wave each; their kept lists go to sh.par
+            int64_t off = 0;
+            for (int li = p.L - 1; li > p.li_lo; --li) {
+                const bool top = (li == p.L - 1);
+                const int64_t nc = static_cast<int64_t>(N) >> (p.lb * (li + 1));
+                const int64_t nc_up = top ? 0 : (static_cast<int64_t>(N) >> (p.lb * (li + 2)));
+                const int64_t nkids = npar << p.lb;
+                const int ncand = static_cast<int>(nkids + (nc - (nc_up << p.lb)));   // <= nc <= 64
+                int32_t* kept_out = p.kept + rh * p.nodes_total + p.sel_off[li];
+                int32_t* lsel_out = p.level_sel ? p.level_sel + p.rows * p.Hq * p.sel_off[li] + rh * p.nodes[li] : nullptr;
+                int32_t* rank_out = p.rank ? p.rank + rh * p.nodes_total + p.sel_off[li] : nullptr;
+                // candidate k on lane k: its node and score
+                int32_t node = 0;
+                float t = -INFINITY;
+                if (lane < ncand) {
+                    node = static_cast<int32_t>(lane < nkids ? ((static_cast<int64_t>(sh.par[lane >> p.lb]) << p.lb) | (lane & (p.b - 1)))
+                                                             : (nc_up << p.lb) + (lane - nkids));
+                    t = sh.nsc[off + node];
+                    if (p.scores && ncand > 1) p.scores[rh * p.nodes_total + p.sel_off[li] + node] = t;
+                }
+                bool kl = false;                   // this lane's candidate is kept
+                int m;
+                if (ncand == 1) {
+                    // a lone candidate carries the whole mass and is kept unscored
+                    if (lane == 0) {
+                        kept_out[0] = node;
+                        if (rank_out) rank_out[node] = 0;
+                        if (lsel_out) lsel_out[0] = node;
+                    }
+                    m = 1;
+                    kl = lane == 0;
+                    __builtin_amdgcn_wave_barrier();
+                    if (lane == 0) sh.par[0] = node;
+                } else {
+                    __builtin_amdgcn_wave_barrier();   // sh.par is read above and rewritten below
+                    // wave_cut_small asks each lane for its own candidate (k == lane)
+                    m = wave_cut_small([&](int64_t) { return t; }, ncand, p.top_p_l[li], sh.bs,
+                                       [&](int64_t pos, int64_t) {
+                        const int32_t nd = node;
+                        kl = true;
+                        sh.par[pos] = nd;
+                        kept_out[pos] = nd;
+                        if (rank_out) rank_out[nd] = static_cast<int32_t>(pos);
+                        if (lsel_out) lsel_out[pos] = nd;
+                    });
+                    __builtin_amdgcn_wave_barrier();
+                }
+                // the level's kept bits (nc <= 64: two words), OR-reduced over the kept lanes
+                const uint32_t b0 = wave_or_u32(kl && node < 32 ? 1u << (node & 31) : 0u);
+                const uint32_t b1 = wave_or_u32(kl && node >= 32 ? 1u << (node & 31) : 0u);
+                uint32_t* bmg = p.bitmap + rh * p.bm_words_total + p.bm_off[li];
+                if (lane < ((nc + 31) >> 5)) bmg[lane] = lane == 0 ? b0 : b1;
+                if (lane == 0) {
+                    p.kept_cnt[rh * p.L + li] = m;
+                    if (p.level_stats) {
+                        p.level_stats[(rh * p.L + li) * 2 + 0] = ncand;
+                        p.level_stats[(rh * p.L + li) * 2 + 1] = m;
+                    }
+                }
+                npar = m;
+                off += nc;
+                __builtin_amdgcn_wave_barrier();
+            }
+            if (lane == 0) sh.npar = npar;
+        } else {
+            if (n_lo > 1) score_level(p.li_lo, hi_tot, n_lo, wv - 1, nw - 1);
+        }
+        __syncthreads();
+        npar = sh.npar;
+        li_first = p.li_lo;
+    }
+    for (int li = li_first; li >= p.li_lo; --li) {
         const bool top = (li == p.L - 1);
         const int64_t nc = static_cast<int64_t>(N) >> (p.lb * (li + 1));
         const int64_t nc_up = top ? 0 : (static_cast<int64_t>(N) >> (p.lb * (li + 2)));
@@ -2207,13 +2360,21 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
         for (int64_t w = tid; w < words; w += nt) sh.bm[w] = 0u;
         __syncthreads();
 
+        float mx = -INFINITY;
+        if (pre) {
+            // scored up front: pick the candidates' scores
+            for (int64_t k = tid; k < ncand; k += nt) {
+                const float t = sh.nsc[hi_tot + sh.cid[k]];
+                sh.sc[k] = t;
+                mx = fmaxf(mx, t);
+                if (p.scores) p.scores[rh * p.nodes_total + p.sel_off[li] + sh.cid[k]] = t;
+            }
+        }
         // ---- score the candidates: a row per LPR lanes, RPP rows per wave pass ----
-        const int RT = TAN ? p.R : 1;                  // tangent rows per node
-        const int64_t nbase = (static_cast<int64_t>(s) * p.Hkv + kv) * p.nodes[li];
+        const int64_t nbase = pair_sk * p.nodes[li];
         const float* summ = p.summaries + p.sum_off[li] + nbase * RT * D;
         const float* offs = TAN ? p.summaries + p.bias_off[li] + nbase * RT : nullptr;
-        float mx = -INFINITY;
-        for (int64_t kb = static_cast<int64_t>(wave) * RPP * UNR; kb < ncand; kb += static_cast<int64_t>(nw) * RPP * UNR) {
+        for (int64_t kb = static_cast<int64_t>(wave) * RPP * UNR; !pre && kb < ncand; kb += static_cast<int64_t>(nw) * RPP * UNR) {
             float best[UNR];
             for (int rr = 0; rr < RT; ++rr) {
                 float x[UNR][DPL], xo[UNR];
