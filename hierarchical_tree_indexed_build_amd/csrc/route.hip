@@ -476,23 +476,34 @@ struct BlockScratch {
     float list_s[kCutList];     // and their scores
     uint32_t list_n;
     int32_t wcount;
+    uint64_t rk[2][kWave];      // one wave's (key, mass) pairs for mass_ranked_before
 };
 
 // For lanes 0..m-1 holding distinct sort keys pk (m <= 64, wave-uniform) and
-// masses F: the sum of the masses of the members whose key is below the lane's
-// own, i.e. the mass ranked before it in key order. Every member's key and
-// mass are broadcast from registers (readlane), one member a step.
-__device__ __forceinline__ uint64_t mass_ranked_before(uint64_t pk, uint64_t F, int m) {
+// masses F (lanes m..63 hold pk = ~0 and F = 0): the sum of the masses of the
+// members whose key is below the lane's own, i.e. the mass ranked before it in
+// key order. Every lane stores its (key, mass) in the wave's scratch; each
+// lane then reads the members back eight at a time (every lane reads the same
+// address, a broadcast) and sums the masses of the smaller keys. The scratch
+// belongs to one wave at a time.
+template <class Scratch>
+__device__ __forceinline__ uint64_t mass_ranked_before(uint64_t pk, uint64_t F, int m, Scratch& bs) {
+    const int lane = threadIdx.x & 63;
+    bs.rk[0][lane] = pk;
+    bs.rk[1][lane] = F;
+    __builtin_amdgcn_wave_barrier();
     uint64_t pre = 0;
-    for (int j = 0; j < m; ++j) {
-        const uint64_t pj = (static_cast<uint64_t>(static_cast<uint32_t>(
-                                 __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(pk >> 32)), j))) << 32) |
-                            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(pk)), j));
-        const uint64_t fj = (static_cast<uint64_t>(static_cast<uint32_t>(
-                                 __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(F >> 32)), j))) << 32) |
-                            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(F)), j));
-        pre += pj < pk ? fj : 0ull;
+    for (int j0 = 0; j0 < m; j0 += 8) {        // j0 + 8 <= 64: entries past m never count
+        uint64_t pj[8], fj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            pj[u] = bs.rk[0][j0 + u];
+            fj[u] = bs.rk[1][j0 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pre += pj[u] < pk ? fj[u] : 0ull;
     }
+    __builtin_amdgcn_wave_barrier();           // the scratch is rewritten by the next call
     return pre;
 }
 
@@ -513,7 +524,7 @@ __device__ __forceinline__ void wave_resolve(const uint32_t* lk, const float* ls
     const uint64_t F = valid ? mass_fx(s, mx) : 0;
     const uint64_t pk = valid ? ((static_cast<uint64_t>(key) << 32) | k) : ~0ull;   // distinct per member
     // the mass ranked before each member, summed over the members in registers
-    const uint64_t pre = mass_ranked_before(pk, F, m);
+    const uint64_t pre = mass_ranked_before(pk, F, m, bs);
     const bool kept = valid && pre < rem;
     const uint32_t kap = static_cast<uint32_t>(
         __builtin_amdgcn_readlane(static_cast<int>(wave_scan_max_u32(kept ? key : 0u)), 63));
@@ -963,7 +974,7 @@ __device__ __forceinline__ int wave_cut_small(ScoreAt score, int n, float top_p,
     uint64_t rem = static_cast<uint64_t>(ceil(static_cast<double>(top_p) * static_cast<double>(E)));
     if (rem == 0) rem = 1;
     const uint64_t pk = valid ? ((static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(lane)) : ~0ull;
-    const uint64_t pre = mass_ranked_before(pk, F, n);
+    const uint64_t pre = mass_ranked_before(pk, F, n, bs);
     const bool kept = valid && (take_all || pre < rem);
     const unsigned long long bal = __ballot(kept);
     if (kept) emit(static_cast<int64_t>(__popcll(bal & ((1ull << lane) - 1ull))), static_cast<int64_t>(lane));
@@ -1268,6 +1279,7 @@ struct WaveScratch {
     uint32_t kmem[kWave];      // the kept members, in candidate order
     uint32_t bm[kWaveBmWords];
     float sc[kWaveStage];      // the candidates' scores, in candidate order
+    uint64_t rk[2][kWave];     // (key, mass) pairs for mass_ranked_before
 };
 
 __device__ __forceinline__ int wave_bin(float s, float mx) {
@@ -1328,6 +1340,7 @@ struct WaveScratchU {           // the unstaged variant's scratch
     uint32_t sure[kWaveSure];
     uint32_t kmem[kWave];
     uint32_t bm[bm_words];
+    uint64_t rk[2][kWave];
 };
 
 // Entries of the ascending list a[0..cnt) below x (a binary search).
