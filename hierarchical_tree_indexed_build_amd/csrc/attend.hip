@@ -663,10 +663,11 @@ __device__ __forceinline__ uint32_t bf16_bits_rn(float x) {   // round to neares
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(256) void attend_mfma_kernel(AttnParams p) {
+// NW waves a workgroup: 8 when the pairs are few and g <= 4 (half the
+// workgroups, so half the partial slots for the combine to merge), else 4.
+template <int D, int G, int NW>
+__global__ __launch_bounds__(NW * kWave) void attend_mfma_kernel(AttnParams p) {
     using C = AttnCfg<uint16_t, D, G>;
-    constexpr int NW = 4;
     constexpr int NP = C::NP, WPP = C::WPP, DPL = C::DPL, LPT = C::LPT, TPP = C::TPP;
     constexpr int KW = D / 8;                    // 32-bit words of K per lane (D/4 bf16)
     constexpr int NS = D / 32;                   // MFMA slices of 32 dimensions
@@ -1013,15 +1014,15 @@ __global__ __launch_bounds__(kCombineThreads) void attend_combine_kernel(AttnPar
 // kernel's register use (blocks per compute unit x compute units), at most
 // kAttnWorkgroups. A kernel that holds one block per compute unit then runs
 // its shares in one round rather than two with a tail. Read once per device.
-template <typename F>
-static int resident_workgroups(F* kernel, int block) {
-    static int cached[64] = {0};
+template <auto Kernel>
+static int resident_workgroups(int block) {
+    static int cached[64] = {0};        // per kernel and device
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kAttnWorkgroups;
     int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
     if (n > 0) return n;
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), block, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(Kernel), block, 0) !=
             hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 || cus < 1) {
         (void)hipGetLastError();
@@ -1032,30 +1033,50 @@ static int resident_workgroups(F* kernel, int block) {
     return n;
 }
 
+// Eight-wave bf16 workgroups: few pairs (the kernels build the plan
+// themselves) and g <= 4, where the kernel holds two waves a SIMD.
+static bool attn_wide(bool bf16, int G, int pairs) { return bf16 && G <= 4 && pairs <= kWave; }
+
 template <typename KT, int D, int G>
-static int attn_workgroups_t() {
-    if constexpr (sizeof(KT) == 2) return resident_workgroups(attend_mfma_kernel<D, G>, 256);
-    else return resident_workgroups(attend_kernel<KT, D, G>, 256);
+static int attn_workgroups_t(bool wide) {
+    if constexpr (sizeof(KT) == 2) {
+        if constexpr (G <= 4)
+            if (wide) return resident_workgroups<attend_mfma_kernel<D, G, 8>>(8 * kWave);
+        return resident_workgroups<attend_mfma_kernel<D, G, 4>>(4 * kWave);
+    } else {
+        return resident_workgroups<attend_kernel<KT, D, G>>(256);
+    }
 }
 
 template <typename KT, int D>
-static int attn_workgroups_g(int G) {
+static int attn_workgroups_g(int G, bool wide) {
     switch (G) {
-        case 1: return attn_workgroups_t<KT, D, 1>();
-        case 2: return attn_workgroups_t<KT, D, 2>();
-        case 4: return attn_workgroups_t<KT, D, 4>();
-        case 8: return attn_workgroups_t<KT, D, 8>();
-        case 16: return attn_workgroups_t<KT, D, 16>();
+        case 1: return attn_workgroups_t<KT, D, 1>(wide);
+        case 2: return attn_workgroups_t<KT, D, 2>(wide);
+        case 4: return attn_workgroups_t<KT, D, 4>(wide);
+        case 8: return attn_workgroups_t<KT, D, 8>(wide);
+        case 16: return attn_workgroups_t<KT, D, 16>(wide);
         default: return kAttnWorkgroups;
     }
 }
 
 template <typename KT, int D, int G>
-static hipError_t launch_attn_t(const AttnParams& ap, int rows, int Hq, float* out, float* lse, hipStream_t st) {
+static hipError_t launch_attn_t(const AttnParams& ap, int rows, int Hq, float* out, float* lse, bool wide,
+                                hipStream_t st) {
     {
         ProfScope ps("attend", 0, st);
         if constexpr (sizeof(KT) == 2)       // bf16 cache: scores on the matrix cores
-            hipLaunchKernelGGL((attend_mfma_kernel<D, G>), dim3(ap.nwg + ap.pairs), dim3(256), 0, st, ap);
+        {
+            bool launched = false;
+            if constexpr (G <= 4) {
+                if (wide) {
+                    hipLaunchKernelGGL((attend_mfma_kernel<D, G, 8>), dim3(ap.nwg + ap.pairs), dim3(8 * kWave), 0, st, ap);
+                    launched = true;
+                }
+            }
+            if (!launched)
+                hipLaunchKernelGGL((attend_mfma_kernel<D, G, 4>), dim3(ap.nwg + ap.pairs), dim3(4 * kWave), 0, st, ap);
+        }
         else
             hipLaunchKernelGGL((attend_kernel<KT, D, G>), dim3(ap.nwg + ap.pairs), dim3(256), 0, st, ap);
     }
@@ -1067,13 +1088,14 @@ static hipError_t launch_attn_t(const AttnParams& ap, int rows, int Hq, float* o
 }
 
 template <typename KT, int D>
-static hipError_t attn_g(int G, const AttnParams& ap, int rows, int Hq, float* out, float* lse, hipStream_t st) {
+static hipError_t attn_g(int G, const AttnParams& ap, int rows, int Hq, float* out, float* lse, bool wide,
+                         hipStream_t st) {
     switch (G) {
-        case 1: return launch_attn_t<KT, D, 1>(ap, rows, Hq, out, lse, st);
-        case 2: return launch_attn_t<KT, D, 2>(ap, rows, Hq, out, lse, st);
-        case 4: return launch_attn_t<KT, D, 4>(ap, rows, Hq, out, lse, st);
-        case 8: return launch_attn_t<KT, D, 8>(ap, rows, Hq, out, lse, st);
-        case 16: return launch_attn_t<KT, D, 16>(ap, rows, Hq, out, lse, st);
+        case 1: return launch_attn_t<KT, D, 1>(ap, rows, Hq, out, lse, wide, st);
+        case 2: return launch_attn_t<KT, D, 2>(ap, rows, Hq, out, lse, wide, st);
+        case 4: return launch_attn_t<KT, D, 4>(ap, rows, Hq, out, lse, wide, st);
+        case 8: return launch_attn_t<KT, D, 8>(ap, rows, Hq, out, lse, wide, st);
+        case 16: return launch_attn_t<KT, D, 16>(ap, rows, Hq, out, lse, wide, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1152,10 +1174,11 @@ hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st) {
     ap.Hq = g.Hq;
     ap.Hkv = g.Hkv;
     ap.pairs = pairs;
+    const bool wide = attn_wide(g.kv_dtype == ZHA_KV_BF16, g.G, pairs);
     {
         const bool bf16 = g.kv_dtype == ZHA_KV_BF16;
-        ap.nwg = g.D == 128 ? (bf16 ? attn_workgroups_g<uint16_t, 128>(g.G) : attn_workgroups_g<float, 128>(g.G))
-                            : (bf16 ? attn_workgroups_g<uint16_t, 64>(g.G) : attn_workgroups_g<float, 64>(g.G));
+        ap.nwg = g.D == 128 ? (bf16 ? attn_workgroups_g<uint16_t, 128>(g.G, wide) : attn_workgroups_g<float, 128>(g.G, wide))
+                            : (bf16 ? attn_workgroups_g<uint16_t, 64>(g.G, wide) : attn_workgroups_g<float, 64>(g.G, wide));
     }
     ap.dense = a.dense ? 1 : 0;
     ap.wave_plan = pairs <= kWave ? 1 : 0;
@@ -1172,10 +1195,10 @@ hipError_t launch_attend(const Geo& g, const AttendArgs& a, hipStream_t st) {
     }
     const bool bf = g.kv_dtype == ZHA_KV_BF16;
     if (g.D == 128)
-        return bf ? attn_g<uint16_t, 128>(g.G, ap, a.rows, g.Hq, a.out, a.lse, st)
-                  : attn_g<float, 128>(g.G, ap, a.rows, g.Hq, a.out, a.lse, st);
-    return bf ? attn_g<uint16_t, 64>(g.G, ap, a.rows, g.Hq, a.out, a.lse, st)
-              : attn_g<float, 64>(g.G, ap, a.rows, g.Hq, a.out, a.lse, st);
+        return bf ? attn_g<uint16_t, 128>(g.G, ap, a.rows, g.Hq, a.out, a.lse, wide, st)
+                  : attn_g<float, 128>(g.G, ap, a.rows, g.Hq, a.out, a.lse, wide, st);
+    return bf ? attn_g<uint16_t, 64>(g.G, ap, a.rows, g.Hq, a.out, a.lse, wide, st)
+              : attn_g<float, 64>(g.G, ap, a.rows, g.Hq, a.out, a.lse, wide, st);
 }
 
 }  // namespace zha
