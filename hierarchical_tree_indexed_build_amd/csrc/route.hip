@@ -67,8 +67,8 @@ struct ScoreParams {
     float scale;
     // split cut of this level (pmax null otherwise): every workgroup leaves the
     // maximum of each head's own candidates it scored and writes their scores
-    // and ids in the head's candidate order; workgroup 0 of a (row, kv head)
-    // clears the heads' mass bins and this level's bitmaps
+    // and ids in the head's candidate order; the workgroups of a (row, kv
+    // head) clear the heads' mass bins and this level's bitmaps between them
     float* pmax;               // [rows, Hq, pmax_stride], column = the workgroup's run within its pair
     int64_t pmax_stride;
     int32_t* pruns;            // [rows, Hq]: runs (workgroups) of the head's pair
@@ -182,14 +182,6 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
     const int64_t rh0 = static_cast<int64_t>(row) * p.Hq + kv * G;      // the group's first (row, head)
     const bool split = p.pmax != nullptr;
     if (split && run == 0 && threadIdx.x < G) p.pruns[rh0 + threadIdx.x] = static_cast<int32_t>(W);
-    if (split) {
-        // the runs of the pair clear its heads' bins and this level's bitmaps between them
-        const int64_t stride = W * blockDim.x, first = static_cast<int64_t>(run) * blockDim.x + threadIdx.x;
-        for (int64_t i = first; i < G * kCutBins; i += stride) p.chist[rh0 * kCutBins + i] = 0ull;
-        const int64_t words = (nc + 31) >> 5;
-        for (int64_t i = first; i < G * words; i += stride)
-            p.bm_cur[(rh0 + i / words) * p.bm_words_total + i % words] = 0u;
-    }
     const int lane = threadIdx.x & (kWave - 1);
     constexpr int DPL = (G <= 4) ? 16 : (G == 8 ? 8 : 4);   // dims per lane
     constexpr int LPR = D / DPL;                             // lanes per summary row
@@ -453,6 +445,15 @@ __global__ __launch_bounds__(kScoreThreads) void route_score_kernel(ScoreParams 
             if (lane == h) m = mh;
         }
         if (lane < G) p.pmax[(rh0 + lane) * p.pmax_stride + run] = m;
+        // the runs of the pair clear its heads' bins and this level's bitmaps
+        // between them, for the cut's kernels (nothing here reads them). Done
+        // last: stores issued before the first loads would hold up the wait
+        // for those loads, which counts stores too.
+        const int64_t stride = W * blockDim.x, first = static_cast<int64_t>(run) * blockDim.x + threadIdx.x;
+        for (int64_t i = first; i < G * kCutBins; i += stride) p.chist[rh0 * kCutBins + i] = 0ull;
+        const int64_t words = (nc + 31) >> 5;
+        for (int64_t i = first; i < G * words; i += stride)
+            p.bm_cur[(rh0 + i / words) * p.bm_words_total + i % words] = 0u;
     }
 }
 
