@@ -2059,13 +2059,17 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitPa
         lt = valid && key < kappa;
         tie = valid && key == kappa;
     };
+    // the blocks' below / tie masks, kept for the writing pass (wave-uniform)
+    unsigned long long mlt[BPW], mtie[BPW];
     uint64_t c_lt = 0, c_tie = 0;
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
         bool lt, tie;
         classify(j, lt, tie);
-        c_lt += __popcll(__ballot(lt));
-        c_tie += __popcll(__ballot(tie));
+        mlt[j] = __ballot(lt);
+        mtie[j] = __ballot(tie);
+        c_lt += __popcll(mlt[j]);
+        c_tie += __popcll(mtie[j]);
     }
     if (lane == 0) sh.wcnt[w] = (c_tie << 32) | c_lt;
     __syncthreads();
@@ -2084,9 +2088,8 @@ __global__ __launch_bounds__(kSplitThreads) void route_split_emit_kernel(SplitPa
     const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
-        bool lt, tie;
-        classify(j, lt, tie);
-        const unsigned long long blt = __ballot(lt), btie = __ballot(tie);
+        const unsigned long long blt = mlt[j], btie = mtie[j];
+        const bool lt = (blt >> lane) & 1ull, tie = (btie >> lane) & 1ull;
         const uint64_t my_lt = lt_b + __popcll(blt & below), my_tie = tie_b + __popcll(btie & below);
         const bool keep = lt || (tie && my_tie < need);
         if (keep) {
