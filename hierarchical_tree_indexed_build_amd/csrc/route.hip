@@ -854,14 +854,17 @@ __device__ __forceinline__ CutBoundary cut_boundary_radix(ScoreAt score, int64_t
 //     is below what rem still needs; a longer list goes through a radix select.
 // The result is the same key and tie count as a radix select over all the
 // candidates: bins only narrow the search.
-template <int NW = kCutWaves, class ScoreAt>
+// kBinsClear: the caller cleared bins[] and published it with a barrier.
+template <int NW = kCutWaves, bool kBinsClear = false, class ScoreAt>
 __device__ __forceinline__ CutBoundary cut_boundary(ScoreAt score, int64_t n, float mx, float top_p,
                                                     uint64_t* bins, BlockScratch& bs) {
     const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
     CutBoundary cb{(top_p >= 1.0f) || n == 0, 0u, 0u};
     if (cb.take_all) return cb;
-    for (int i = tid; i < kCutBins; i += nt) bins[i] = 0;
-    __syncthreads();
+    if constexpr (!kBinsClear) {
+        for (int i = tid; i < kCutBins; i += nt) bins[i] = 0;
+        __syncthreads();
+    }
     uint64_t E = 0;
     for (int64_t kb = 0; kb < n; kb += nt) {                  // uniform trip count: whole waves update
         const int64_t k = kb + tid;
@@ -2366,26 +2369,30 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
             par0 = node;
             continue;
         }
+        // scored up front: each thread picks the scores of the candidates it
+        // lists, and clears the cut's bins; the barriers of the block max
+        // below publish all of it (no thread reads another's candidates before)
+        float mx = -INFINITY;
         for (int64_t k = tid; k < ncand; k += nt) {
             const int64_t pk = k >> p.lb;
             const int32_t par = par0 >= 0 ? par0 : sh.par[pk];
-            sh.cid[k] = static_cast<int32_t>(k < nkids ? ((static_cast<int64_t>(par) << p.lb) | (k & (p.b - 1)))
-                                                       : (nc_up << p.lb) + (k - nkids));
+            const int32_t c = static_cast<int32_t>(k < nkids ? ((static_cast<int64_t>(par) << p.lb) | (k & (p.b - 1)))
+                                                            : (nc_up << p.lb) + (k - nkids));
+            sh.cid[k] = c;
+            if (pre) {
+                const float t = sh.nsc[hi_tot + c];
+                sh.sc[k] = t;
+                mx = fmaxf(mx, t);
+                if (p.scores) p.scores[rh * p.nodes_total + p.sel_off[li] + c] = t;
+            }
         }
         par0 = -1;
         const int64_t words = (nc + 31) >> 5;
         for (int64_t w = tid; w < words; w += nt) sh.bm[w] = 0u;
-        __syncthreads();
-
-        float mx = -INFINITY;
         if (pre) {
-            // scored up front: pick the candidates' scores
-            for (int64_t k = tid; k < ncand; k += nt) {
-                const float t = sh.nsc[hi_tot + sh.cid[k]];
-                sh.sc[k] = t;
-                mx = fmaxf(mx, t);
-                if (p.scores) p.scores[rh * p.nodes_total + p.sel_off[li] + sh.cid[k]] = t;
-            }
+            for (int i = tid; i < kCutBins; i += nt) sh.bins[i] = 0;
+        } else {
+            __syncthreads();                   // the scoring below reads every thread's candidates
         }
         // ---- score the candidates: a row per LPR lanes, RPP rows per wave pass ----
         const int64_t nbase = pair_sk * p.nodes[li];
@@ -2452,8 +2459,9 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
             __syncthreads();
             m = sh.bs.wcount;
         } else {
-            mx = block_max_f<NW>(mx, sh.bs);   // its barriers also publish sc[]
-            const CutBoundary cb = cut_boundary<NW>(score, ncand, mx, p.top_p_l[li], sh.bins, sh.bs);
+            mx = block_max_f<NW>(mx, sh.bs);   // its barriers also publish sc[] (and, scored up front, the cleared bins)
+            const CutBoundary cb = pre ? cut_boundary<NW, true>(score, ncand, mx, p.top_p_l[li], sh.bins, sh.bs)
+                                       : cut_boundary<NW, false>(score, ncand, mx, p.top_p_l[li], sh.bins, sh.bs);
             m = cut_compact<NW>(score, ncand, cb, p.lb < 5 ? p.lb : 5, sh.bs, emit, mark);
         }
         uint32_t* bm = p.bitmap + rh * p.bm_words_total + p.bm_off[li];
