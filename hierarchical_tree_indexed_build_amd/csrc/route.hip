@@ -2192,7 +2192,13 @@ __global__ __launch_bounds__(kUpperThreads) void route_upper_kernel(UpperParams 
     constexpr int LPR = D / DPL;               // lanes per summary row
     constexpr int RPP = kWave / LPR;           // rows per wave pass
     constexpr int UNR = 4;                     // passes issued together: 4 * RPP rows in flight per wave
-    const int hq = blockIdx.x, row = blockIdx.y;
+    // Workgroups go to the eight XCDs in turn (linear id mod 8 = blockIdx.x
+    // mod 8 when H_q is a multiple of 8): XCD c takes query heads
+    // [c H_q/8, (c + 1) H_q/8), so the heads of a kv group, which read the
+    // same summary rows, share one XCD's L2.
+    const int hq = (p.Hq & 7) ? static_cast<int>(blockIdx.x)
+                              : static_cast<int>(blockIdx.x & 7) * (p.Hq >> 3) + static_cast<int>(blockIdx.x >> 3);
+    const int row = blockIdx.y;
     const int kv = hq / p.G, s = row / p.T;
     const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nw = NW;
     const int sub = lane / LPR, part = lane % LPR;
