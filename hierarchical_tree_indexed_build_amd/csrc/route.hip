@@ -89,7 +89,8 @@ struct ScoreParams {
 
 // The pair and run of this scoring wave when the waves are dealt by parent
 // counts: lane l < pairs weighs pair l by the parents its heads kept at the
-// level above (all its slots at the top), and pair l owns waves
+// level above (their summed counts capped at the level's complete parents;
+// all its slots at the top), and pair l owns waves
 // [end(l-1), end(l)) with end(l) = need (l+1) + extra * (weights of pairs
 // 0..l) / (all weights), extra = the waves beyond need per pair. Every wave
 // derives the same split from the same counts.
@@ -132,6 +133,11 @@ __device__ __forceinline__ void score_deal(const ScoreParams& p, int* y_out, int
         } else {
 #pragma unroll
             for (int h = 0; h < G; ++h) wgt += static_cast<uint64_t>(kcs[h]);
+            // the pair's active parents are the union of its heads' kept sets:
+            // at most their summed counts and at most the complete parents
+            // (heads that keep most of a level overlap, and the sum overstates)
+            const uint64_t ncu = static_cast<uint64_t>(static_cast<int64_t>(nl) >> (p.lb * (p.li + 2)));
+            wgt = wgt < ncu ? wgt : ncu;
             wgt += 1;                                    // the incomplete parent
         }
     }
